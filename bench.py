@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the indexer-selected sparse attention library.
+
+One step = the whole hot path for one layer over the whole batch:
+append the new token (K/V rows + FP8 projected key), fused index scoring +
+exact top-M per KV head, and gather-free sparse attention over the selected
+rows.  Inputs are synthetic (``workloads``) and resident in HBM before the
+timed region starts.
+
+Prints ONE JSON line:
+  value         decode steps/s (N=1 GPU; whole-job throughput)
+  hbm_gbps      algorithmic bytes per step / step time
+  roofline      the dominant kernel (fused score + top-M) against 8 TB/s
+  cpu_baseline  the fp64 oracle on the host, on a bounded sample of units
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode steps/sec and achieved HBM GB/s at N=128K, M=2048, r=32"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def algorithmic_bytes(wl):
+    """Bytes the method itself must move per step, by kernel."""
+    units = wl.B * wl.Hkv
+    q = wl.B * wl.Hq * wl.d * 2
+    idx = units * wl.M * 4
+    P = wl.Hkv * wl.d * wl.r * 4
+    append = units * (2 * wl.d * 2 + wl.r) * 2 + wl.B * 4 + P   # read new rows + write rows
+    index_topm = units * wl.N * wl.r + q + P + idx               # FP8 stream + q, P, idx out
+    decode = units * wl.M * wl.d * 2 * 2 + idx + q + wl.B * wl.Hq * wl.d * 2
+    return {"append_kv": append, "index_topm": index_topm, "decode": decode}
+
+
+def _source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_attention_long_kv_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, src_hash):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel_key)
+    if not e or e.get("source_hash") != src_hash:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, wl, n_units, seed=0):
+    """Time the oracle on a bounded sample of (batch row, KV head) units."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from workloads import default_scale
+
+    rng = np.random.default_rng(seed)
+    units = rng.choice(wl.B * wl.Hkv, size=min(n_units, wl.B * wl.Hkv), replace=False)
+    G = wl.G
+    P64 = inp.P.double().cpu().numpy()
+    q64 = inp.q.double().cpu().numpy()
+    total = 0.0
+    with threadpool_limits(limits=1):
+        for u in units:
+            b, h = divmod(int(u), wl.Hkv)
+            K = inp.k_cache[b, h].double().cpu().numpy()
+            V = inp.v_cache[b, h].double().cpu().numpy()
+            kp = oracle.project_keys(K, P64[h])            # cache state: not timed
+            kn = inp.k_new[b, h].double().cpu().numpy()
+            t0 = time.perf_counter()
+            kp[wl.N - 1] = oracle.project_keys(kn, P64[h])[0]
+            K[wl.N - 1] = kn[0]
+            oracle.decode_step_unit(q64[b, h * G:(h + 1) * G], K, V, kp, P64[h], wl.N, wl.M,
+                                    default_scale(wl.d))
+            total += time.perf_counter() - t0
+    per_unit = total / len(units)
+    step_s = per_unit * wl.B * wl.Hkv
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": "%d of %d (batch row, KV head) units of one step, scaled to the "
+                      "whole step (%.3f s per unit, numpy fp64, BLAS pinned to 1 thread)"
+                      % (len(units), wl.B * wl.Hkv, per_unit),
+            "seconds_measured": total}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="longctx_128k")
+    ap.add_argument("--cpu-units", type=int, default=12,
+                    help="units of the step timed for the oracle baseline (0 = skip)")
+    ap.add_argument("--seed", type=int, default=0)
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: every step of this path is independent per "
+              "(batch row, KV head) unit and this build runs on a single MI355X; "
+              "--gpus %d is not supported." % a.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_long_kv_amd as sa
+    from workloads import WORKLOADS, make_decode_inputs, default_scale
+
+    wl = WORKLOADS[a.workload]
+    if wl.layers != 1:
+        raise SystemExit("bench.py times single-layer workloads")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sa.load()
+    print("bench: generating %s inputs" % wl.name, file=sys.stderr, flush=True)
+    inp = make_decode_inputs(wl, seed=a.seed, device="cuda")
+    sh = sa.make_shape(wl.B, wl.Hq, wl.Hkv, wl.d, wl.r, wl.N)
+    kp = torch.empty(wl.B, wl.Hkv, wl.N, wl.r, dtype=torch.uint8, device=dev)
+    sa.sparse_attn_project_keys(sh, inp.k_cache, inp.P, 0, wl.N, kp)     # prefill (untimed)
+    ws = sa.alloc_workspace(sh, wl.N, wl.M, device=dev)
+    idx = torch.empty(wl.B, wl.Hkv, wl.M, dtype=torch.int32, device=dev)
+    out = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.bfloat16, device=dev)
+    scale = default_scale(wl.d)
+    torch.cuda.synchronize()
+
+    ev = {k: [] for k in ("append_kv", "index_topm", "decode")}
+
+    def step(record):
+        if record:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record()
+        sa.sparse_attn_append_kv(sh, inp.pos, inp.k_new, inp.v_new, inp.P, inp.k_cache,
+                                 inp.v_cache, kp)
+        if record:
+            e[1].record()
+        sa.sparse_attn_index_topm(sh, inp.q, inp.P, kp, inp.seq_lens, wl.N, wl.M, idx, ws)
+        if record:
+            e[2].record()
+        sa.sparse_attn_decode(sh, inp.q, inp.k_cache, inp.v_cache, idx, wl.M, scale, out,
+                              None, ws)
+        if record:
+            e[3].record()
+            ev["append_kv"].append((e[0], e[1]))
+            ev["index_topm"].append((e[1], e[2]))
+            ev["decode"].append((e[2], e[3]))
+
+    print("bench: warmup %d" % a.warmup, file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, back to back, synchronised on both sides
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(a.steps):
+        step(True)                  # HIP events between the calls, on the same stream
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(end)
+    ms_per_step = 1e3 * wall / a.steps          # host clock around the K steps
+    kern_us = {k: 1e3 * sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in ev.items()}
+
+    bytes_k = algorithmic_bytes(wl)
+    step_bytes = sum(bytes_k.values())
+    steps_per_s = 1e3 / ms_per_step
+    hbm_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    dom = "index_topm"
+    dom_gbps = bytes_k[dom] / (kern_us[dom] * 1e-6) / 1e9
+    src_hash = _source_hash(["indexer.hip", "device_common.hpp"])
+    traffic = measured_traffic(dom, src_hash)
+    roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "kernel": "select_kernel (sparse_attn_index_topm)",
+                "bytes_per_launch": bytes_k[dom], "avg_launch_us": round(kern_us[dom], 2),
+                "source_hash": src_hash}
+
+    res = {
+        "metric": METRIC, "value": round(steps_per_s, 2), "unit": "steps/s",
+        "hbm_gbps": round(hbm_gbps, 1), "hbm_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4), "gpu_event_ms_per_step": round(gpu_ms / a.steps, 4),
+        "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32",
+        "storage": "bf16 K/V/q, fp8-e4m3 projected-key cache, int32 indices",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+                   "head_dim": wl.d, "context_N": wl.N, "rank_r": wl.r, "budget_M": wl.M},
+        "tokens_per_s": round(steps_per_s * wl.B, 1),
+        "step_bytes": step_bytes,
+        "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "kernel_gbps": {k: round(bytes_k[k] / (kern_us[k] * 1e-6) / 1e9, 1) for k in kern_us},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if a.cpu_units > 0:
+        print("bench: cpu baseline (%d units)" % a.cpu_units, file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp, wl, a.cpu_units)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,229 @@
+/*
+ * sparse_attn.h -- C ABI of the MI355X (gfx950) indexer-selected sparse decode
+ * library (libsparse_attn.so).
+ *
+ * One decode step of token-sparse attention over a long KV cache, as the JSSA
+ * article (rit.work blog, "Joint Subspace Sparse Attention for Efficient
+ * Long-Context Decoding") describes it in "How JSSA preserves token order":
+ *
+ *   1. append the new token's key/value rows to the bf16 KV cache and its
+ *      low-rank projection (k . P, rounded to FP8 E4M3) to the projected-key
+ *      cache;                                        -> sparse_attn_append_kv
+ *   2. average the GQA group's queries, project them onto the KV head's basis
+ *      P and score every cached position against the FP8 cache;
+ *                                                    -> sparse_attn_index_score
+ *   3. keep the M highest-scoring positions per KV head (the "top-k" of the
+ *      DeepSeek Sparse Attention indexer in the IndexCache article, "DeepSeek
+ *      Sparse Attention: a step towards efficiency");  -> sparse_attn_topm
+ *      (steps 2 and 3 fused, scores never written:    -> sparse_attn_index_topm)
+ *   4. run exact softmax attention over only the selected full-size bf16 rows,
+ *      read in place from the cache, with a separate index set per KV head, all
+ *      heads in one launch (JSSA article, same section, last paragraph).
+ *                                                    -> sparse_attn_decode
+ *   Extension: the gated linear-attention branch of LISA (aikraft.ru news item,
+ *   "LISA architecture").                            -> sparse_attn_linear_gate
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers to dense row-major arrays in the
+ *   layouts stated per argument, except `shape`, which is a host pointer.
+ *   The caller owns every buffer; the library allocates nothing and keeps no
+ *   state between calls.
+ * - bf16 is IEEE bfloat16 stored as uint16; FP8 is the OCP E4M3 format
+ *   ("e4m3fn": bias 7, max 448, NaN codes 0x7F/0xFF, no infinities).
+ * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *   enqueues work on `stream`; none synchronises the host (unless the
+ *   environment variable SPARSE_ATTN_SYNC=1 is set, a debugging aid that
+ *   synchronises after each call and reports asynchronous errors).
+ * - Return value: SA_OK (0) or a negative sa_status.  Arguments are checked on
+ *   the host before anything is launched; a call that fails a check launches
+ *   nothing and changes no memory.  Launch failures return SA_ERR_HIP.
+ * - Pointer alignment: 16 bytes for bf16 and FP8 tensors, 4 bytes for int32
+ *   and fp32 tensors; a misaligned pointer is SA_ERR_INVALID.
+ * - Shape limits: head_dim in {64, 128}; rank in {16, 32}; num_q_heads a
+ *   multiple of num_kv_heads with G = num_q_heads / num_kv_heads <= 16;
+ *   batch, num_kv_heads >= 1; capacity >= 1.
+ * - Results are bitwise deterministic run to run (no floating-point atomics).
+ * - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Shape of one attention layer's caches.  B = batch, Hq = num_q_heads,
+ * Hkv = num_kv_heads, d = head_dim, r = rank (indexer basis width),
+ * Ncap = capacity (rows per (batch row, KV head) in every cache). */
+typedef struct sa_shape {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t rank;
+  int32_t capacity;
+} sa_shape;
+
+typedef enum sa_status {
+  SA_OK = 0,
+  SA_ERR_INVALID = -1,     /* bad argument: null/misaligned pointer, bad size */
+  SA_ERR_UNSUPPORTED = -2, /* valid but outside the supported shape limits */
+  SA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  SA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} sa_status;
+
+/* ---------------------------------------------------------------------------
+ * sparse_attn_append_kv -- append T tokens per batch row (step 1).
+ *
+ * JSSA article, "How JSSA preserves token order": each key gets a projection
+ * onto its KV head's basis, stored as FP8 beside the bf16 KV cache.
+ *
+ * pos      [B] int32: first cache row written for batch row b.
+ * T        tokens per batch row (T = 0 is a no-op).
+ * k_new, v_new [B][Hkv][T][d] bf16.
+ * P        [Hkv][d][r] fp32 basis per KV head.
+ * k_cache, v_cache [B][Hkv][Ncap][d] bf16 (row pos[b]+t <- token t).
+ * kp_cache [B][Hkv][Ncap][r] uint8 FP8 codes:
+ *          kp[n][j] = e4m3( sum_i k[i] * P[h][i][j] ), the sum formed in fp64
+ *          starting from +0 and rounded once, to nearest-even, saturating at
+ *          +-448.
+ * Rows pos[b]+t outside [0, Ncap) are skipped (device data is not checked on
+ * the host).
+ * ------------------------------------------------------------------------- */
+int sparse_attn_append_kv(const sa_shape* shape, const int32_t* pos, int32_t T,
+                          const void* k_new, const void* v_new, const float* P,
+                          void* k_cache, void* v_cache, uint8_t* kp_cache,
+                          void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sparse_attn_project_keys -- (re)build the FP8 projected-key cache from rows
+ * already in k_cache: rows [n_begin, n_begin + n_count) of every (b, KV head),
+ * with the same arithmetic as sparse_attn_append_kv.  Used to fill the
+ * indexer cache after a prefill wrote K.  Requires 0 <= n_begin and
+ * n_begin + n_count <= Ncap.
+ * ------------------------------------------------------------------------- */
+int sparse_attn_project_keys(const sa_shape* shape, const void* k_cache,
+                             const float* P, int32_t n_begin, int32_t n_count,
+                             uint8_t* kp_cache, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sparse_attn_index_score -- indexer scores of every position (step 2).
+ *
+ * JSSA article, "How JSSA preserves token order": the queries of one KV head's
+ * group are averaged and projected, then every position is scored.
+ *
+ * q        [B][Hq][d] bf16; query head hq belongs to KV head hq / G.
+ * seq_lens [B] int32 valid positions per batch row, or NULL (= n_max);
+ *          values are clamped to [0, n_max].
+ * n_max    positions scored per (b, KV head); 1 <= n_max <= Ncap.
+ * scores   [B][Hkv][n_max] fp32 out:
+ *          s[n] = sum_j qt[j] * dec(kp[n][j]) for n < len, -inf otherwise,
+ *          where qt = P[h]^T * mean_g q[h*G+g] is formed in fp64 and rounded
+ *          to fp32, and each score is accumulated in fp32 as two 16-term fused
+ *          multiply-add chains (j < 16, then j >= 16) added together.
+ * ------------------------------------------------------------------------- */
+int sparse_attn_index_score(const sa_shape* shape, const void* q, const float* P,
+                            const uint8_t* kp_cache, const int32_t* seq_lens,
+                            int32_t n_max, float* scores, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sparse_attn_topm -- exact top-M positions per (b, KV head) (step 3).
+ *
+ * IndexCache article, "DeepSeek Sparse Attention": keep the k most relevant
+ * positions; JSSA article: every KV head (GQA group) selects its own set.
+ *
+ * scores   [B][Hkv][n_max] fp32 (as written by sparse_attn_index_score).
+ * idx      [B][Hkv][M] int32 out: the positions n < len with the M largest
+ *          scores, equal scores ordered by lower position; ascending; when
+ *          fewer than M positions are valid, all of them followed by -1.
+ * M        1 <= M <= n_max.
+ * workspace device buffer of >= sparse_attn_workspace_size(shape, n_max, M)
+ *          bytes whose first sparse_attn_workspace_counter_bytes(shape) bytes
+ *          are zero before its first use (sparse_attn_workspace_init does
+ *          that); every call that completes leaves them zero again.
+ * ------------------------------------------------------------------------- */
+int sparse_attn_topm(const sa_shape* shape, const float* scores,
+                     const int32_t* seq_lens, int32_t n_max, int32_t M,
+                     int32_t* idx, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sparse_attn_index_topm -- steps 2 and 3 fused in one launch: the scores are
+ * kept on chip and never written.  Produces exactly the idx that
+ * sparse_attn_index_score followed by sparse_attn_topm produces.
+ * Arguments as in those two calls.
+ * ------------------------------------------------------------------------- */
+int sparse_attn_index_topm(const sa_shape* shape, const void* q, const float* P,
+                           const uint8_t* kp_cache, const int32_t* seq_lens,
+                           int32_t n_max, int32_t M, int32_t* idx,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sparse_attn_decode -- gather-free sparse attention (step 4).
+ *
+ * JSSA article, "How JSSA preserves token order": final attention uses the
+ * original full-size keys and values of the selected positions, read directly
+ * from the cache without an intermediate buffer, with separate index sets per
+ * head in a single launch.
+ *
+ * q        [B][Hq][d] bf16.
+ * k_cache, v_cache [B][Hkv][Ncap][d] bf16.
+ * idx      [B][Hkv][M] int32; entries outside [0, Ncap) are padding and
+ *          skipped (duplicates count once per occurrence).
+ * softmax_scale  multiplies q.k (normally 1/sqrt(d)); must be finite.
+ * out      [B][Hq][d] bf16: softmax(scale * q.K[idx]) . V[idx], rounded to
+ *          nearest-even; all-zero when no entry is valid.
+ * lse      [B][Hq] fp32 natural-log log-sum-exp of the scaled logits, or NULL;
+ *          -inf when no entry is valid.
+ * workspace as for sparse_attn_topm.
+ * ------------------------------------------------------------------------- */
+int sparse_attn_decode(const sa_shape* shape, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* idx, int32_t M,
+                       float softmax_scale, void* out, float* lse,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sparse_attn_linear_gate -- LISA-style gated linear branch.
+ *
+ * LISA news items (aikraft.ru "LISA architecture"; opennieuws.be "Hybrid
+ * architecture for efficiency"): a linear-attention branch with linear-time
+ * memory is merged with the sparse branch by a gate.  Feature map
+ * phi(x) = x + 1 (x > 0), exp(x) (x <= 0).
+ *
+ * q        [B][Hq][d] bf16; k_new, v_new [B][Hkv][d] bf16 (the new token).
+ * S        [B][Hkv][d][d] fp32 in/out, S[i][j] = sum phi(k)[i] * v[j].
+ * z        [B][Hkv][d] fp32 in/out, z = sum phi(k).
+ * update_state != 0: first S += phi(k_new) v_new^T, z += phi(k_new).
+ * w_gate   [Hq][d] fp32; g = 1 / (1 + exp(-(w[hq] . q[hq]))).
+ * o_sparse [B][Hq][d] bf16 (output of sparse_attn_decode).
+ * out      [B][Hq][d] bf16: g * o_sparse + (1 - g) * (phi(q)^T S) / (phi(q)^T z).
+ * ------------------------------------------------------------------------- */
+int sparse_attn_linear_gate(const sa_shape* shape, const void* q,
+                            const void* k_new, const void* v_new, float* S,
+                            float* z, const float* w_gate, const void* o_sparse,
+                            void* out, int32_t update_state, void* stream);
+
+/* Bytes of workspace that sparse_attn_topm, sparse_attn_index_topm and
+ * sparse_attn_decode need for this shape, n_max and M (host only, pure).
+ * Returns 0 when the arguments are invalid. */
+size_t sparse_attn_workspace_size(const sa_shape* shape, int32_t n_max, int32_t M);
+
+/* Bytes at the start of the workspace that must be zero before first use. */
+size_t sparse_attn_workspace_counter_bytes(const sa_shape* shape);
+
+/* Zero the counter region of a workspace (enqueued on `stream`). */
+int sparse_attn_workspace_init(const sa_shape* shape, void* workspace,
+                               size_t ws_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* sparse_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -1,0 +1,176 @@
+// C-ABI entry points: host-side checks, planning, launches.
+#include <cmath>
+#include <cstdlib>
+
+#include "host_plan.h"
+#include "kernels.h"
+#include "sparse_attn.h"
+
+namespace {
+
+using namespace sa;
+
+bool sync_mode() {
+  static const bool on = [] {
+    const char* e = std::getenv("SPARSE_ATTN_SYNC");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+int finish(hipError_t launch, hipStream_t stream) {
+  if (launch != hipSuccess) return SA_ERR_HIP;
+  if (sync_mode()) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return SA_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
+  }
+  return SA_OK;
+}
+
+LaunchCommon common(const sa_shape& s, void* stream) {
+  LaunchCommon c;
+  c.B = s.batch;
+  c.Hq = s.num_q_heads;
+  c.Hkv = s.num_kv_heads;
+  c.G = s.num_q_heads / s.num_kv_heads;
+  c.D = s.head_dim;
+  c.R = s.rank;
+  c.Ncap = s.capacity;
+  c.units = s.batch * s.num_kv_heads;
+  c.stream = (hipStream_t)stream;
+  return c;
+}
+
+constexpr size_t A16 = 16, A4 = 4;
+
+int check_topm_common(const sa_shape* shape, const int32_t* seq_lens, int32_t n_max,
+                      int32_t M, const int32_t* idx, const void* ws, size_t ws_bytes,
+                      TopmPlan* plan) {
+  if (seq_lens && !ptr_ok(seq_lens, A4)) return SA_ERR_INVALID;
+  if (!ptr_ok(idx, A4)) return SA_ERR_INVALID;
+  if (n_max < 1 || n_max > shape->capacity) return SA_ERR_INVALID;
+  if (M < 1 || M > n_max) return SA_ERR_INVALID;
+  const int st = plan_topm(*shape, n_max, M, plan);
+  if (st != SA_OK) return st;
+  if (!ptr_ok(ws, kAlign) || ws_bytes < workspace_bytes(*shape, n_max, M)) return SA_ERR_WORKSPACE;
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" int sparse_attn_append_kv(const sa_shape* shape, const int32_t* pos, int32_t T,
+                                     const void* k_new, const void* v_new, const float* P,
+                                     void* k_cache, void* v_cache, uint8_t* kp_cache,
+                                     void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  if (T < 0 || T > shape->capacity) return SA_ERR_INVALID;
+  if (!ptr_ok(pos, A4) || !ptr_ok(k_new, A16) || !ptr_ok(v_new, A16) || !ptr_ok(P, A4) ||
+      !ptr_ok(k_cache, A16) || !ptr_ok(v_cache, A16) || !ptr_ok(kp_cache, A16))
+    return SA_ERR_INVALID;
+  if (T == 0) return SA_OK;
+  const LaunchCommon c = common(*shape, stream);
+  return finish(run_append_kv(c, pos, T, k_new, v_new, P, k_cache, v_cache, kp_cache), c.stream);
+}
+
+extern "C" int sparse_attn_project_keys(const sa_shape* shape, const void* k_cache,
+                                        const float* P, int32_t n_begin, int32_t n_count,
+                                        uint8_t* kp_cache, void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  if (n_begin < 0 || n_count < 0 || (int64_t)n_begin + n_count > shape->capacity)
+    return SA_ERR_INVALID;
+  if (!ptr_ok(k_cache, A16) || !ptr_ok(P, A4) || !ptr_ok(kp_cache, A16)) return SA_ERR_INVALID;
+  if (n_count == 0) return SA_OK;
+  const LaunchCommon c = common(*shape, stream);
+  return finish(run_project_keys(c, k_cache, P, n_begin, n_count, kp_cache), c.stream);
+}
+
+extern "C" int sparse_attn_index_score(const sa_shape* shape, const void* q, const float* P,
+                                       const uint8_t* kp_cache, const int32_t* seq_lens,
+                                       int32_t n_max, float* scores, void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  if (!ptr_ok(q, A16) || !ptr_ok(P, A4) || !ptr_ok(kp_cache, A16) || !ptr_ok(scores, A4))
+    return SA_ERR_INVALID;
+  if (seq_lens && !ptr_ok(seq_lens, A4)) return SA_ERR_INVALID;
+  if (n_max < 1 || n_max > shape->capacity) return SA_ERR_INVALID;
+  const LaunchCommon c = common(*shape, stream);
+  return finish(run_index_score(c, q, P, kp_cache, seq_lens, n_max, scores), c.stream);
+}
+
+extern "C" int sparse_attn_topm(const sa_shape* shape, const float* scores,
+                                const int32_t* seq_lens, int32_t n_max, int32_t M, int32_t* idx,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  if (!ptr_ok(scores, A4)) return SA_ERR_INVALID;
+  TopmPlan plan;
+  st = check_topm_common(shape, seq_lens, n_max, M, idx, workspace, ws_bytes, &plan);
+  if (st != SA_OK) return st;
+  const LaunchCommon c = common(*shape, stream);
+  return finish(run_select(c, plan, false, nullptr, nullptr, nullptr, scores, seq_lens, n_max, M,
+                           idx, workspace),
+                c.stream);
+}
+
+extern "C" int sparse_attn_index_topm(const sa_shape* shape, const void* q, const float* P,
+                                      const uint8_t* kp_cache, const int32_t* seq_lens,
+                                      int32_t n_max, int32_t M, int32_t* idx, void* workspace,
+                                      size_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  if (!ptr_ok(q, A16) || !ptr_ok(P, A4) || !ptr_ok(kp_cache, A16)) return SA_ERR_INVALID;
+  TopmPlan plan;
+  st = check_topm_common(shape, seq_lens, n_max, M, idx, workspace, ws_bytes, &plan);
+  if (st != SA_OK) return st;
+  const LaunchCommon c = common(*shape, stream);
+  return finish(run_select(c, plan, true, q, P, kp_cache, nullptr, seq_lens, n_max, M, idx,
+                           workspace),
+                c.stream);
+}
+
+extern "C" int sparse_attn_decode(const sa_shape* shape, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* idx, int32_t M,
+                                  float softmax_scale, void* out, float* lse, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  if (!ptr_ok(q, A16) || !ptr_ok(k_cache, A16) || !ptr_ok(v_cache, A16) || !ptr_ok(idx, A4) ||
+      !ptr_ok(out, A16))
+    return SA_ERR_INVALID;
+  if (lse && !ptr_ok(lse, A4)) return SA_ERR_INVALID;
+  if (M < 1 || !std::isfinite(softmax_scale)) return SA_ERR_INVALID;
+  DecodePlan plan;
+  st = plan_decode(*shape, M, &plan);
+  if (st != SA_OK) return st;
+  if (!ptr_ok(workspace, kAlign) || ws_bytes < plan.end) return SA_ERR_WORKSPACE;
+  const LaunchCommon c = common(*shape, stream);
+  return finish(run_decode(c, plan, q, k_cache, v_cache, idx, M, softmax_scale, out, lse,
+                           workspace),
+                c.stream);
+}
+
+extern "C" int sparse_attn_linear_gate(const sa_shape* shape, const void* q, const void* k_new,
+                                       const void* v_new, float* S, float* z,
+                                       const float* w_gate, const void* o_sparse, void* out,
+                                       int32_t update_state, void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  if (!ptr_ok(q, A16) || !ptr_ok(k_new, A16) || !ptr_ok(v_new, A16) || !ptr_ok(S, A4) ||
+      !ptr_ok(z, A4) || !ptr_ok(w_gate, A4) || !ptr_ok(o_sparse, A16) || !ptr_ok(out, A16))
+    return SA_ERR_INVALID;
+  const LaunchCommon c = common(*shape, stream);
+  return finish(run_linear_gate(c, q, k_new, v_new, S, z, w_gate, o_sparse, out, update_state),
+                c.stream);
+}
+
+extern "C" int sparse_attn_workspace_init(const sa_shape* shape, void* workspace,
+                                          size_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  const size_t need = counter_bytes(*shape);
+  if (!ptr_ok(workspace, kAlign) || ws_bytes < need) return SA_ERR_WORKSPACE;
+  return finish(run_zero_u32((uint32_t*)workspace, need / 4, (hipStream_t)stream),
+                (hipStream_t)stream);
+}

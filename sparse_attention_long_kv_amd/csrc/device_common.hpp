@@ -1,0 +1,134 @@
+// Device helpers shared by the gfx950 kernels: bf16/FP8 conversions, DPP
+// row reductions, order-preserving score keys and workgroup scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// 8 bf16 values packed in a uint4 -> 8 floats (exact)
+__device__ __forceinline__ void bf16x8_to_f32(const uint4& v, float* f) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays a quiet NaN)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- FP8 E4M3
+
+// Four OCP E4M3 codes (one per byte, byte 0 first) -> four floats, exact.
+// gfx950's packed conversion reads the OCP "fn" encoding.
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
+  auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = hi[0]; f[3] = hi[1];
+}
+
+// float64 -> OCP E4M3 code, round to nearest even, saturating to +-448.
+// The code's sign is the sign bit of x.  Every step is exact in fp64.
+__device__ __forceinline__ uint32_t f64_to_e4m3(double x) {
+  const uint32_t sign = signbit(x) ? 0x80u : 0u;
+  const double a = fabs(x);
+  if (!(a < 448.0)) return sign | 0x7Eu;            // saturate (and NaN)
+  if (a < 0x1p-6) {                                  // subnormal: m * 2^-9
+    return sign | (uint32_t)rint(a * 512.0);         // m <= 8; 8 == 2^-6 code
+  }
+  int e;
+  const double f = frexp(a, &e);                     // a = f * 2^e, f in [0.5,1)
+  int biased = e - 1 + 7;
+  int q = (int)rint((2.0 * f - 1.0) * 8.0);          // 0..8
+  if (q == 8) { q = 0; biased += 1; }
+  if (biased > 15 || (biased == 15 && q == 7)) return sign | 0x7Eu;
+  return sign | (uint32_t)(biased << 3) | (uint32_t)q;
+}
+
+// ---------------------------------------------------------------- DPP sums
+
+// DPP control words (gfx9 encoding)
+constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of W lanes (W in 2, 4, 8, 16); every lane of the
+// group receives the same bits (the pairings are symmetric).
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16, "group width");
+  x = x + dpp_f<kDppQuadSwap1>(x);
+  if (W >= 4) x = x + dpp_f<kDppQuadSwap2>(x);
+  if (W >= 8) x = x + dpp_f<kDppHalfMirror>(x);
+  if (W >= 16) x = x + dpp_f<kDppMirror>(x);
+  return x;
+}
+
+// ---------------------------------------------------------------- keys
+
+// Order-preserving map fp32 score -> uint32 (larger score, larger key).
+// Key 0 is reserved for "no position"; the one float that would map to it
+// (a negative NaN with every payload bit set) is moved to 1.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return k == 0u ? 1u : k;
+}
+
+// ---------------------------------------------------------------- lanes
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) {
+  return __builtin_amdgcn_ballot_w64(p);
+}
+
+__device__ __forceinline__ int popc64(uint64_t m) { return __builtin_popcountll(m); }
+
+// Inclusive prefix sum across the 64 lanes of a wave (uint32).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off, kWave);
+    if (l >= off) x += y;
+  }
+  return x;
+}
+
+// Sum across a wave (every lane receives it).
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+}  // namespace sa

@@ -1,0 +1,115 @@
+// Host-side argument checks, launch planning and status strings (plain C++).
+#include "host_plan.h"
+
+#include <algorithm>
+
+namespace sa {
+
+int check_shape(const sa_shape* s) {
+  if (!s) return SA_ERR_INVALID;
+  if (s->batch < 1 || s->num_kv_heads < 1 || s->num_q_heads < 1 || s->capacity < 1)
+    return SA_ERR_INVALID;
+  if (s->num_q_heads % s->num_kv_heads != 0) return SA_ERR_INVALID;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (G > 16) return SA_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return SA_ERR_UNSUPPORTED;
+  if (s->rank != 16 && s->rank != 32) return SA_ERR_UNSUPPORTED;
+  // every per-unit row index and in-unit byte offset must fit in int32
+  if ((int64_t)s->capacity * s->head_dim * 2 > INT32_MAX) return SA_ERR_UNSUPPORTED;
+  if ((int64_t)s->batch * s->num_kv_heads > (1 << 24)) return SA_ERR_UNSUPPORTED;
+  return SA_OK;
+}
+
+bool ptr_ok(const void* p, size_t align) {
+  return p != nullptr && (reinterpret_cast<uintptr_t>(p) % align) == 0;
+}
+
+size_t counter_bytes(const sa_shape& s) {
+  return align_up((size_t)s.batch * s.num_kv_heads * sizeof(uint32_t), kAlign);
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int plan_topm(const sa_shape& s, int n_max, int M, TopmPlan* p) {
+  const int64_t units = (int64_t)s.batch * s.num_kv_heads;
+  int chunk = kMaxChunk;
+  // shrink chunks until the grid fills the chip, but never below one block
+  while (chunk > kMinChunk && units * ceil_div(n_max, chunk) < kTargetBlocks) chunk >>= 1;
+  const int64_t splits = ceil_div(n_max, chunk);
+  if (splits > kMaxSplits) return SA_ERR_UNSUPPORTED;
+  p->units = (int)units;
+  p->chunk = chunk;
+  p->kpt = chunk / kBlock;
+  p->splits = (int)splits;
+  p->mc = std::min(M, chunk);
+  p->multi_tile = splits * p->mc > kMergeTile;
+  size_t off = counter_bytes(s);
+  p->off_cnt = off;
+  off = align_up(off + (size_t)units * splits * sizeof(int32_t), kAlign);
+  p->off_key = off;
+  off = align_up(off + (size_t)units * splits * p->mc * sizeof(uint32_t), kAlign);
+  p->off_pos = off;
+  off = align_up(off + (size_t)units * splits * p->mc * sizeof(int32_t), kAlign);
+  p->end = off;
+  return SA_OK;
+}
+
+int plan_decode(const sa_shape& s, int M, DecodePlan* p) {
+  const int64_t units = (int64_t)s.batch * s.num_kv_heads;
+  const int G = s.num_q_heads / s.num_kv_heads;
+  int64_t splits = std::max<int64_t>(1, ceil_div(kTargetBlocks, units));
+  splits = std::min<int64_t>(splits, std::max<int64_t>(1, ceil_div(M, kMinRowsPerSplit)));
+  const int64_t rps = ceil_div(M, splits);
+  splits = ceil_div(M, rps);          // no empty workgroups
+  p->units = (int)units;
+  p->splits = (int)splits;
+  p->rows_per_split = (int)rps;
+  size_t off = counter_bytes(s);
+  const size_t parts = (size_t)units * splits * G;
+  p->off_m = off;
+  off = align_up(off + parts * sizeof(float), kAlign);
+  p->off_l = off;
+  off = align_up(off + parts * sizeof(float), kAlign);
+  p->off_o = off;
+  off = align_up(off + parts * s.head_dim * sizeof(float), kAlign);
+  p->end = off;
+  return SA_OK;
+}
+
+size_t workspace_bytes(const sa_shape& s, int n_max, int M) {
+  if (check_shape(&s) != SA_OK) return 0;
+  if (n_max < 1 || n_max > s.capacity || M < 1) return 0;
+  DecodePlan dp;
+  if (plan_decode(s, M, &dp) != SA_OK) return 0;
+  size_t need = dp.end;
+  if (M <= n_max) {
+    TopmPlan tp;
+    if (plan_topm(s, n_max, M, &tp) != SA_OK) return 0;
+    need = std::max(need, tp.end);
+  }
+  return need;
+}
+
+}  // namespace sa
+
+extern "C" size_t sparse_attn_workspace_size(const sa_shape* shape, int32_t n_max,
+                                             int32_t M) {
+  if (!shape) return 0;
+  return sa::workspace_bytes(*shape, n_max, M);
+}
+
+extern "C" size_t sparse_attn_workspace_counter_bytes(const sa_shape* shape) {
+  if (sa::check_shape(shape) != SA_OK) return 0;
+  return sa::counter_bytes(*shape);
+}
+
+extern "C" const char* sparse_attn_status_string(int status) {
+  switch (status) {
+    case SA_OK: return "ok";
+    case SA_ERR_INVALID: return "invalid argument";
+    case SA_ERR_UNSUPPORTED: return "unsupported shape or size";
+    case SA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SA_ERR_HIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}

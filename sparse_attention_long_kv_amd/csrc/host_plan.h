@@ -1,0 +1,52 @@
+// Host-side argument checks and launch planning.  No HIP types: this part is
+// plain C++ so that its logic can be exercised without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sparse_attn.h"
+
+namespace sa {
+
+// Fixed launch geometry shared with the kernels.
+constexpr int kBlock = 256;              // threads per workgroup (4 waves of 64)
+constexpr int kMaxKeysPerThread = 64;    // register-resident selection keys
+constexpr int kMaxChunk = kBlock * kMaxKeysPerThread;   // 16384 positions
+constexpr int kMinChunk = kBlock;                       // 256 positions
+constexpr int kMergeTile = kBlock * kMaxKeysPerThread;  // keys per merge tile
+constexpr int kMaxSplits = 1024;         // chunks per (b, KV head) unit
+constexpr int kTargetBlocks = 2048;      // enough workgroups for 256 CUs
+constexpr int kMinRowsPerSplit = 64;     // attention rows per workgroup (min)
+constexpr size_t kAlign = 256;
+
+struct TopmPlan {
+  int units;        // B * Hkv
+  int chunk;        // positions per chunk workgroup (multiple of 256)
+  int kpt;          // keys per thread = chunk / 256
+  int splits;       // chunks per unit
+  int mc;           // candidate slots per chunk = min(M, chunk)
+  bool multi_tile;  // merge input exceeds one register tile
+  size_t off_cnt, off_key, off_pos, end;   // byte offsets in the workspace
+};
+
+struct DecodePlan {
+  int units;
+  int splits;           // workgroups per unit
+  int rows_per_split;   // selected rows per workgroup
+  size_t off_m, off_l, off_o, end;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Shape checks shared by every entry point (SA_OK or a negative status).
+int check_shape(const sa_shape* s);
+// Non-null and aligned to `align` bytes.
+bool ptr_ok(const void* p, size_t align);
+
+size_t counter_bytes(const sa_shape& s);
+int plan_topm(const sa_shape& s, int n_max, int M, TopmPlan* out);
+int plan_decode(const sa_shape& s, int M, DecodePlan* out);
+size_t workspace_bytes(const sa_shape& s, int n_max, int M);
+
+}  // namespace sa

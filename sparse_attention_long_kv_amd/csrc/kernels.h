@@ -1,0 +1,37 @@
+// Launch entry points of the kernel translation units (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "host_plan.h"
+
+namespace sa {
+
+struct LaunchCommon {
+  int B, Hq, Hkv, G, D, R, Ncap, units;
+  hipStream_t stream;
+};
+
+hipError_t run_append_kv(const LaunchCommon& c, const int32_t* pos, int T, const void* k_new,
+                         const void* v_new, const float* P, void* k_cache, void* v_cache,
+                         uint8_t* kp);
+hipError_t run_project_keys(const LaunchCommon& c, const void* k_cache, const float* P,
+                            int n_begin, int n_count, uint8_t* kp);
+hipError_t run_index_score(const LaunchCommon& c, const void* q, const float* P,
+                           const uint8_t* kp, const int32_t* seq_lens, int n_max,
+                           float* scores);
+// fused == true: scores computed from (q, P, kp); otherwise read from `scores`.
+hipError_t run_select(const LaunchCommon& c, const TopmPlan& plan, bool fused, const void* q,
+                      const float* P, const uint8_t* kp, const float* scores,
+                      const int32_t* seq_lens, int n_max, int M, int32_t* idx,
+                      void* workspace);
+hipError_t run_decode(const LaunchCommon& c, const DecodePlan& plan, const void* q,
+                      const void* k_cache, const void* v_cache, const int32_t* idx, int M,
+                      float scale, void* out, float* lse, void* workspace);
+hipError_t run_linear_gate(const LaunchCommon& c, const void* q, const void* k_new,
+                           const void* v_new, float* S, float* z, const float* w_gate,
+                           const void* o_sparse, void* out, int update_state);
+hipError_t run_zero_u32(uint32_t* p, size_t n, hipStream_t stream);
+
+}  // namespace sa

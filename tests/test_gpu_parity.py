@@ -1,0 +1,448 @@
+"""GPU parity: every C-ABI entry point against the fp64 oracle.
+
+Inputs are seeded and synthetic (``workloads``); every input the oracle sees is
+either generated or computed by the oracle itself (the FP8 projected-key cache
+handed to the scoring tests is the oracle's, never the GPU's).  Sizes span
+several chunks/tiles and ragged tails; edge cases cover empty rows, M = 1,
+M = N, ties and multi-tile merges.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_long_kv_amd as sa
+from workloads import WORKLOADS, make_decode_inputs, orthonormal_basis, scaled, default_scale
+from _helpers import (f64, oracle_kp, kp_codes_match, score_tolerance, check_topm_unit,
+                      check_attention)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sa.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(x, dtype=None):
+    t = torch.as_tensor(x)
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.contiguous().cuda()
+
+
+def _shape_of(B, Hq, Hkv, d, r, Ncap):
+    return sa.make_shape(B, Hq, Hkv, d, r, Ncap)
+
+
+def _rand_inputs(B, Hq, Hkv, d, r, N, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, Hq, d, generator=g).to(torch.bfloat16)
+    K = torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16)
+    V = torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16)
+    P = torch.from_numpy(np.stack([orthonormal_basis(d, r, seed * 31 + h)
+                                   for h in range(Hkv)]).astype(np.float32))
+    return q, K, V, P
+
+
+# ------------------------------------------------------------------ FP8 decode
+
+def test_fp8_decode_of_every_code_via_scores():
+    """score[n] = dec(code n) exactly when qt = e_0 (G = 1, P = identity)."""
+    _say("case: fp8 decode table via index_score")
+    d, r, N = 64, 16, 256
+    sh = _shape_of(1, 1, 1, d, r, N)
+    q = torch.zeros(1, 1, d, dtype=torch.bfloat16)
+    q[0, 0, 0] = 1.0
+    P = torch.zeros(1, d, r, dtype=torch.float32)
+    P[0, :r, :r] = torch.eye(r)
+    kp = torch.zeros(1, 1, N, r, dtype=torch.uint8)
+    kp[0, 0, :, 0] = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    scores = torch.empty(1, 1, N, dtype=torch.float32, device="cuda")
+    sa.sparse_attn_index_score(sh, _dev(q), _dev(P), _dev(kp), None, N, scores)
+    got = scores.cpu().double().numpy()[0, 0]
+    want = oracle.decode_table()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+# ------------------------------------------------------------------ append / project
+
+@pytest.mark.parametrize("d,r", [(128, 32), (64, 16), (128, 16), (64, 32)])
+def test_append_kv_matches_oracle(d, r):
+    _say("case: append d=%d r=%d" % (d, r))
+    B, Hq, Hkv, Ncap, T = 2, 8, 2, 64, 5
+    sh = _shape_of(B, Hq, Hkv, d, r, Ncap)
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, Ncap, seed=d + r)
+    g = torch.Generator().manual_seed(7)
+    kn = (3 * torch.randn(B, Hkv, T, d, generator=g)).to(torch.bfloat16)
+    vn = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16)
+    pos = torch.tensor([3, 61], dtype=torch.int32)       # second row: 3 of 5 fit
+    kp0 = torch.full((B, Hkv, Ncap, r), 0x11, dtype=torch.uint8)
+    Kd, Vd, kpd = _dev(K), _dev(V), _dev(kp0)
+    sa.sparse_attn_append_kv(sh, _dev(pos), _dev(kn), _dev(vn), _dev(P), Kd, Vd, kpd)
+    K2, V2, kp2 = oracle.append_kv(f64(K), f64(V), kp0.numpy(), pos.numpy(), f64(kn), f64(vn),
+                                   P.double().numpy())
+    assert np.array_equal(f64(Kd), K2) and np.array_equal(f64(Vd), V2)
+    ok, nbad = kp_codes_match(kpd.cpu().numpy(), kp2, K2, P.double().numpy())
+    assert ok, "projected-key codes differ outside the rounding-midpoint band (%d)" % nbad
+
+
+def test_project_keys_matches_oracle():
+    _say("case: project_keys bulk")
+    B, Hq, Hkv, d, r, Ncap = 2, 4, 2, 128, 32, 3000
+    sh = _shape_of(B, Hq, Hkv, d, r, Ncap)
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, Ncap, seed=5)
+    kpd = torch.zeros(B, Hkv, Ncap, r, dtype=torch.uint8, device="cuda")
+    sa.sparse_attn_project_keys(sh, _dev(K), _dev(P), 37, 2900, kpd)
+    want = oracle_kp(f64(K), P.double().numpy())
+    got = kpd.cpu().numpy()
+    assert np.all(got[:, :, :37] == 0) and np.all(got[:, :, 2937:] == 0)
+    ok, nbad = kp_codes_match(got[:, :, 37:2937], want[:, :, 37:2937], f64(K)[:, :, 37:2937],
+                              P.double().numpy())
+    assert ok, nbad
+
+
+# ------------------------------------------------------------------ scores
+
+@pytest.mark.parametrize("case", ["tiny", "gqa7"])
+def test_index_score_matches_oracle(case):
+    _say("case: index_score", case)
+    if case == "tiny":
+        B, Hq, Hkv, d, r, N, lens = 1, 4, 1, 64, 16, 1024, [1000]
+    else:
+        B, Hq, Hkv, d, r, N, lens = 2, 14, 2, 128, 32, 9000, [9000, 1234]
+    n_max = N - 5
+    sh = _shape_of(B, Hq, Hkv, d, r, N)
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, N, seed=11)
+    P64 = P.double().numpy()
+    kp = oracle_kp(f64(K), P64)
+    scores = torch.empty(B, Hkv, n_max, dtype=torch.float32, device="cuda")
+    sl = torch.tensor(lens, dtype=torch.int32)
+    sa.sparse_attn_index_score(sh, _dev(q), _dev(P), _dev(kp), _dev(sl), n_max, scores)
+    got = scores.cpu().double().numpy()
+    G = Hq // Hkv
+    for b in range(B):
+        L = min(lens[b], n_max)
+        for h in range(Hkv):
+            qt = oracle.indexer_query(f64(q)[b, h * G:(h + 1) * G], P64[h])
+            want = oracle.index_scores(qt, kp[b, h, :L])
+            tol = score_tolerance(qt, kp[b, h, :L])
+            assert np.all(np.abs(got[b, h, :L] - want) <= tol)
+            assert np.all(np.isneginf(got[b, h, L:]))
+
+
+# ------------------------------------------------------------------ top-M
+
+TOPM_CASES = {
+    # name: (B, Hq, Hkv, d, r, N(cap), n_max, seq_lens, M)
+    "tiny": (1, 4, 1, 64, 16, 1024, 1024, None, 64),
+    "ragged": (3, 8, 2, 128, 32, 20000, 19997, [19997, 300, 0], 512),
+    "multitile": (1, 2, 1, 128, 32, 65613, 65613, None, 256),
+    "m_equals_n": (2, 4, 2, 64, 32, 700, 700, None, 700),
+    "m_one": (2, 4, 2, 64, 16, 5000, 5000, [5000, 17], 1),
+    "many_chunks": (2, 28, 4, 128, 32, 16384, 16384, [16384, 9000], 2048),
+}
+
+
+def _topm_case(name, seed=3):
+    B, Hq, Hkv, d, r, N, n_max, lens, M = TOPM_CASES[name]
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, N, seed=seed)
+    G = Hq // Hkv
+    # plant rows aligned with the group-mean query, as in the workloads
+    qbar = f64(q).reshape(B, Hkv, G, d).mean(axis=2)
+    rng = np.random.default_rng(seed)
+    K64 = f64(K)
+    for b in range(B):
+        for h in range(Hkv):
+            rows = rng.choice(N, size=max(1, N // 100), replace=False)
+            K64[b, h, rows] += 2.0 * qbar[b, h]
+    K = torch.from_numpy(K64).to(torch.bfloat16)
+    return (B, Hq, Hkv, d, r, N, n_max, lens, M), q, K, V, P
+
+
+@pytest.mark.parametrize("name", list(TOPM_CASES))
+def test_topm_fused_and_unfused_match_oracle(name):
+    (B, Hq, Hkv, d, r, N, n_max, lens, M), q, K, V, P = _topm_case(name)
+    _say("case: topm", name, "B=%d Hkv=%d n_max=%d M=%d" % (B, Hkv, n_max, M))
+    sh = _shape_of(B, Hq, Hkv, d, r, N)
+    P64 = P.double().numpy()
+    kp = oracle_kp(f64(K), P64)
+    qd, Pd, kpd = _dev(q), _dev(P), _dev(kp)
+    sl = None if lens is None else _dev(torch.tensor(lens, dtype=torch.int32))
+    ws = sa.alloc_workspace(sh, n_max, M)
+    scores = torch.empty(B, Hkv, n_max, dtype=torch.float32, device="cuda")
+    idx_u = torch.empty(B, Hkv, M, dtype=torch.int32, device="cuda")
+    idx_f = torch.empty(B, Hkv, M, dtype=torch.int32, device="cuda")
+    sa.sparse_attn_index_score(sh, qd, Pd, kpd, sl, n_max, scores)
+    sa.sparse_attn_topm(sh, scores, sl, n_max, M, idx_u, ws)
+    sa.sparse_attn_index_topm(sh, qd, Pd, kpd, sl, n_max, M, idx_f, ws)
+    # the workspace counters are back at zero after each call
+    nctr = sa.sparse_attn_workspace_counter_bytes(sh)
+    assert int(ws[:nctr].sum().item()) == 0
+    gu, gf = idx_u.cpu().numpy(), idx_f.cpu().numpy()
+    assert np.array_equal(gu, gf), "fused and unfused index sets differ"
+    G = Hq // Hkv
+    swaps = 0
+    for b in range(B):
+        L = n_max if lens is None else min(lens[b], n_max)
+        for h in range(Hkv):
+            qt = oracle.indexer_query(f64(q)[b, h * G:(h + 1) * G], P64[h])
+            s = oracle.index_scores(qt, kp[b, h, :L])
+            swaps += check_topm_unit(gf[b, h], s, M, L)
+    _say("  band swaps:", swaps)
+
+
+def test_topm_ties_take_lowest_positions():
+    _say("case: topm ties")
+    B, Hq, Hkv, d, r, N, M = 1, 1, 1, 64, 16, 4096, 100
+    sh = _shape_of(B, Hq, Hkv, d, r, N)
+    q = torch.zeros(B, Hq, d, dtype=torch.bfloat16)
+    q[0, 0, 0] = 1.0
+    P = torch.zeros(Hkv, d, r, dtype=torch.float32)
+    P[0, :r, :r] = torch.eye(r)
+    # score = dec(code in column 0): 300 rows share the top code, so the top-100
+    # are the 100 lowest of those rows
+    rng = np.random.default_rng(0)
+    col = np.full(N, 0x30, dtype=np.uint8)                 # 0.5 everywhere
+    top_rows = np.sort(rng.choice(N, 300, replace=False))
+    col[top_rows] = 0x40                                   # 2.0
+    kp = np.zeros((B, Hkv, N, r), dtype=np.uint8)
+    kp[0, 0, :, 0] = col
+    ws = sa.alloc_workspace(sh, N, M)
+    idx = torch.empty(B, Hkv, M, dtype=torch.int32, device="cuda")
+    sa.sparse_attn_index_topm(sh, _dev(q), _dev(P), _dev(kp), None, N, M, idx, ws)
+    assert idx.cpu().numpy()[0, 0].tolist() == top_rows[:M].tolist()
+    scores = torch.empty(B, Hkv, N, dtype=torch.float32, device="cuda")
+    sa.sparse_attn_index_score(sh, _dev(q), _dev(P), _dev(kp), None, N, scores)
+    idx2 = torch.empty_like(idx)
+    sa.sparse_attn_topm(sh, scores, None, N, M, idx2, ws)
+    assert torch.equal(idx, idx2)
+
+
+# ------------------------------------------------------------------ attention
+
+DECODE_CASES = [
+    # (B, Hq, Hkv, d, Ncap, M, pad_mode)
+    (2, 8, 2, 128, 3000, 2048, "none"),
+    (2, 28, 4, 128, 5000, 1000, "pad"),
+    (1, 16, 16, 64, 700, 97, "dups"),
+    (1, 16, 1, 64, 4000, 3000, "oob"),
+    (3, 4, 1, 128, 500, 1, "none"),
+    (2, 12, 4, 128, 300, 300, "all"),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES)
+def test_decode_matches_oracle(case):
+    B, Hq, Hkv, d, Ncap, M, mode = case
+    _say("case: decode", case)
+    r = 16
+    sh = _shape_of(B, Hq, Hkv, d, r, Ncap)
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, Ncap, seed=B * 100 + Hq)
+    rng = np.random.default_rng(M)
+    idx = np.zeros((B, Hkv, M), dtype=np.int32)
+    for b in range(B):
+        for h in range(Hkv):
+            if mode == "all":
+                idx[b, h] = np.arange(M)
+            else:
+                idx[b, h] = np.sort(rng.choice(Ncap, M, replace=False))
+            if mode == "pad":
+                idx[b, h, M - 1 - b * 300:] = -1
+            elif mode == "dups":
+                idx[b, h, ::3] = idx[b, h, 0]
+            elif mode == "oob":
+                idx[b, h, ::7] = Ncap + 5
+    if mode == "pad" and B > 1:
+        idx[B - 1, 0, :] = -1                    # a unit with no valid row
+    scale = default_scale(d)
+    ws = sa.alloc_workspace(sh, min(M, Ncap), M)
+    out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+    sa.sparse_attn_decode(sh, _dev(q), _dev(K), _dev(V), _dev(idx), M, scale, out, lse, ws)
+    G = Hq // Hkv
+    got, gl = f64(out), lse.cpu().double().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            o, l = oracle.sparse_attention(f64(q)[b, h * G:(h + 1) * G], f64(K)[b, h],
+                                           f64(V)[b, h], idx[b, h], scale)
+            check_attention(got[b, h * G:(h + 1) * G], o, "decode %s b=%d h=%d" % (case, b, h))
+            fin = np.isfinite(l)
+            assert np.array_equal(np.isfinite(gl[b, h * G:(h + 1) * G]), fin)
+            assert np.all(np.abs(gl[b, h * G:(h + 1) * G][fin] - l[fin]) <= 1e-3 * (1 + np.abs(l[fin])))
+            if M == 1 and idx[b, h, 0] >= 0:
+                assert np.array_equal(got[b, h * G:(h + 1) * G],
+                                      np.repeat(f64(V)[b, h, idx[b, h, 0]][None], G, 0))
+
+
+def test_decode_split_count_and_order_invariance():
+    _say("case: decode invariances")
+    B, Hq, Hkv, d, Ncap, M = 1, 4, 1, 128, 5000, 2048
+    sh = _shape_of(B, Hq, Hkv, d, 16, Ncap)
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, 16, Ncap, seed=9)
+    rng = np.random.default_rng(1)
+    idx = np.sort(rng.choice(Ncap, M, replace=False)).astype(np.int32)[None, None]
+    ws = sa.alloc_workspace(sh, M, M)
+    outs = []
+    for perm in (None, rng.permutation(M)):
+        ii = idx if perm is None else idx[:, :, perm]
+        out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device="cuda")
+        sa.sparse_attn_decode(sh, _dev(q), _dev(K), _dev(V), _dev(ii), M, default_scale(d),
+                              out, None, ws)
+        outs.append(f64(out))
+    o, _ = oracle.sparse_attention(f64(q)[0], f64(K)[0, 0], f64(V)[0, 0], idx[0, 0],
+                                   default_scale(d))
+    for x in outs:
+        check_attention(x[0], o)
+
+
+# ------------------------------------------------------------------ linear + gate
+
+@pytest.mark.parametrize("G,d", [(4, 128), (7, 128), (2, 64)])
+def test_linear_gate_matches_oracle(G, d):
+    _say("case: linear_gate G=%d d=%d" % (G, d))
+    B, Hkv, N = 2, 2, 300
+    Hq = G * Hkv
+    sh = _shape_of(B, Hq, Hkv, d, 16, N)
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, 16, N, seed=G)
+    g = torch.Generator().manual_seed(3)
+    w = (0.5 * torch.randn(Hq, d, generator=g)).float()
+    o_sp = torch.randn(B, Hq, d, generator=g).to(torch.bfloat16)
+    K64, V64, q64 = f64(K), f64(V), f64(q)
+    S0 = np.zeros((B, Hkv, d, d))
+    z0 = np.zeros((B, Hkv, d))
+    for b in range(B):
+        for h in range(Hkv):
+            S0[b, h], z0[b, h] = oracle.linear_state(K64[b, h, :N - 1], V64[b, h, :N - 1])
+    Sd = _dev(torch.from_numpy(S0).float())
+    zd = _dev(torch.from_numpy(z0).float())
+    out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device="cuda")
+    sa.sparse_attn_linear_gate(sh, _dev(q), _dev(K[:, :, N - 1]), _dev(V[:, :, N - 1]), Sd, zd,
+                               _dev(w), _dev(o_sp), out, True)
+    got = f64(out)
+    for b in range(B):
+        for h in range(Hkv):
+            S, z = oracle.linear_state(K64[b, h], V64[b, h])
+            np.testing.assert_allclose(Sd[b, h].cpu().double().numpy(), S, rtol=1e-5, atol=1e-3)
+            np.testing.assert_allclose(zd[b, h].cpu().double().numpy(), z, rtol=1e-5)
+            o, _, _ = oracle.linear_gate(q64[b, h * G:(h + 1) * G], S, z,
+                                         w.double().numpy()[h * G:(h + 1) * G],
+                                         f64(o_sp)[b, h * G:(h + 1) * G])
+            check_attention(got[b, h * G:(h + 1) * G], o, "linear gate")
+    # read-only call leaves the state untouched
+    S_before = Sd.clone()
+    sa.sparse_attn_linear_gate(sh, _dev(q), _dev(K[:, :, N - 1]), _dev(V[:, :, N - 1]), Sd, zd,
+                               _dev(w), _dev(o_sp), out, False)
+    assert torch.equal(S_before, Sd)
+
+
+# ------------------------------------------------------------------ whole step
+
+def _run_step(inp, sh, M, ws, fused=True):
+    wl = inp.wl
+    kp = torch.zeros(wl.B, wl.Hkv, sh.capacity, wl.r, dtype=torch.uint8, device="cuda")
+    sa.sparse_attn_project_keys(sh, inp.k_cache, inp.P, 0, sh.capacity, kp)
+    sa.sparse_attn_append_kv(sh, inp.pos, inp.k_new, inp.v_new, inp.P, inp.k_cache,
+                             inp.v_cache, kp)
+    idx = torch.empty(wl.B, wl.Hkv, M, dtype=torch.int32, device="cuda")
+    n_max = int(inp.seq_lens.max().item())
+    if fused:
+        sa.sparse_attn_index_topm(sh, inp.q, inp.P, kp, inp.seq_lens, n_max, M, idx, ws)
+    else:
+        scores = torch.empty(wl.B, wl.Hkv, n_max, dtype=torch.float32, device="cuda")
+        sa.sparse_attn_index_score(sh, inp.q, inp.P, kp, inp.seq_lens, n_max, scores)
+        sa.sparse_attn_topm(sh, scores, inp.seq_lens, n_max, M, idx, ws)
+    out = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(wl.B, wl.Hq, dtype=torch.float32, device="cuda")
+    sa.sparse_attn_decode(sh, inp.q, inp.k_cache, inp.v_cache, idx, M, default_scale(wl.d),
+                          out, lse, ws)
+    return kp, idx, out, lse
+
+
+@pytest.mark.parametrize("name,N", [("tiny", None), ("gqa7_16k", 4096)])
+def test_decode_step_end_to_end(name, N):
+    wl = WORKLOADS[name] if N is None else scaled(WORKLOADS[name], N=N, M=512)
+    _say("case: step", wl.name, wl.N, wl.M)
+    inp = make_decode_inputs(wl, seed=4, device="cuda")
+    K0, V0 = f64(inp.k_cache), f64(inp.v_cache)
+    sh = _shape_of(wl.B, wl.Hq, wl.Hkv, wl.d, wl.r, wl.N)
+    ws = sa.alloc_workspace(sh, wl.N, wl.M)
+    kp, idx, out, lse = _run_step(inp, sh, wl.M, ws)
+    _, idx2, out2, _ = _run_step(make_decode_inputs(wl, seed=4, device="cuda"), sh, wl.M, ws,
+                                 fused=False)
+    assert torch.equal(idx, idx2)
+    P64 = inp.P.double().cpu().numpy()
+    kp0 = oracle_kp(K0, P64)
+    K2, V2, kp2 = oracle.append_kv(K0, V0, kp0, inp.pos.cpu().numpy(), f64(inp.k_new),
+                                   f64(inp.v_new), P64)
+    G = wl.G
+    gi, go = idx.cpu().numpy(), f64(out)
+    q64 = f64(inp.q)
+    for b in range(wl.B):
+        for h in range(wl.Hkv):
+            qg = q64[b, h * G:(h + 1) * G]
+            oi, oo, ol, s = oracle.decode_step_unit(qg, K2[b, h], V2[b, h], kp2[b, h], P64[h],
+                                                    wl.N, wl.M, default_scale(wl.d))
+            check_topm_unit(gi[b, h], s, wl.M, wl.N)
+            if np.array_equal(gi[b, h], oi):
+                check_attention(go[b, h * G:(h + 1) * G], oo, "step")
+            if (b, h) in inp.plants and wl.plant_mode == "replace":
+                assert set(inp.plants[(b, h)].tolist()) <= set(gi[b, h].tolist())
+
+
+def test_determinism():
+    _say("case: determinism")
+    wl = scaled(WORKLOADS["gqa7_16k"], N=8192, M=1024, B=2)
+    sh = _shape_of(wl.B, wl.Hq, wl.Hkv, wl.d, wl.r, wl.N)
+    ws = sa.alloc_workspace(sh, wl.N, wl.M)
+    res = [_run_step(make_decode_inputs(wl, seed=1, device="cuda"), sh, wl.M, ws)
+           for _ in range(2)]
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ cross-layer reuse
+
+def test_cross_layer_reuse_equals_decode_with_source_indices():
+    _say("case: cross-layer reuse")
+    wl = scaled(WORKLOADS["reuse8_64k"], N=4096, B=2, M=256)
+    sh = _shape_of(wl.B, wl.Hq, wl.Hkv, wl.d, wl.r, wl.N)
+    ws = sa.alloc_workspace(sh, wl.N, wl.M)
+    idx_of = {}
+    for layer in range(wl.layers):
+        inp = make_decode_inputs(wl, seed=2, layer=layer, device="cuda")
+        src = oracle.reuse_source_layer(layer, wl.full_layers)
+        if layer == src:
+            kp, idx, out, lse = _run_step(inp, sh, wl.M, ws)
+            idx_of[layer] = idx
+        else:
+            idx = idx_of[src]
+            out = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.bfloat16, device="cuda")
+            sa.sparse_attn_append_kv(sh, inp.pos, inp.k_new, inp.v_new, inp.P, inp.k_cache,
+                                     inp.v_cache, torch.zeros(wl.B, wl.Hkv, wl.N, wl.r,
+                                                              dtype=torch.uint8, device="cuda"))
+            sa.sparse_attn_decode(sh, inp.q, inp.k_cache, inp.v_cache, idx, wl.M,
+                                  default_scale(wl.d), out, None, ws)
+        G = wl.G
+        gi = idx.cpu().numpy()
+        q64, K64, V64 = f64(inp.q), f64(inp.k_cache), f64(inp.v_cache)
+        for b in range(wl.B):
+            for h in range(wl.Hkv):
+                o, _ = oracle.sparse_attention(q64[b, h * G:(h + 1) * G], K64[b, h], V64[b, h],
+                                               gi[b, h], default_scale(wl.d))
+                check_attention(f64(out)[b, h * G:(h + 1) * G], o, "layer %d" % layer)

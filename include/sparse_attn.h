@@ -142,9 +142,9 @@ int sparse_attn_index_score(const sa_shape* shape, const void* q, const float* P
  *          fewer than M positions are valid, all of them followed by -1.
  * M        1 <= M <= n_max.
  * workspace device buffer of >= sparse_attn_workspace_size(shape, n_max, M)
- *          bytes whose first sparse_attn_workspace_counter_bytes(shape) bytes
- *          are zero before its first use (sparse_attn_workspace_init does
- *          that); every call that completes leaves them zero again.
+ *          bytes, 256-byte aligned; scratch for the per-chunk candidates.
+ *          Its contents need no initialisation and are not meaningful after
+ *          the call.
  * ------------------------------------------------------------------------- */
 int sparse_attn_topm(const sa_shape* shape, const float* scores,
                      const int32_t* seq_lens, int32_t n_max, int32_t M,
@@ -211,13 +211,6 @@ int sparse_attn_linear_gate(const sa_shape* shape, const void* q,
  * sparse_attn_decode need for this shape, n_max and M (host only, pure).
  * Returns 0 when the arguments are invalid. */
 size_t sparse_attn_workspace_size(const sa_shape* shape, int32_t n_max, int32_t M);
-
-/* Bytes at the start of the workspace that must be zero before first use. */
-size_t sparse_attn_workspace_counter_bytes(const sa_shape* shape);
-
-/* Zero the counter region of a workspace (enqueued on `stream`). */
-int sparse_attn_workspace_init(const sa_shape* shape, void* workspace,
-                               size_t ws_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* sparse_attn_status_string(int status);

@@ -65,13 +65,10 @@ _SIGS = {
                            _SZ, _VP],
     "sparse_attn_linear_gate": [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP],
     "sparse_attn_workspace_size": [_SP, _I32, _I32],
-    "sparse_attn_workspace_counter_bytes": [_SP],
-    "sparse_attn_workspace_init": [_SP, _VP, _SZ, _VP],
     "sparse_attn_status_string": [ctypes.c_int],
 }
 _RESTYPES = {
     "sparse_attn_workspace_size": _SZ,
-    "sparse_attn_workspace_counter_bytes": _SZ,
     "sparse_attn_status_string": ctypes.c_char_p,
 }
 
@@ -139,22 +136,12 @@ def sparse_attn_workspace_size(shape, n_max, M):
     return int(load().sparse_attn_workspace_size(_sh(shape), int(n_max), int(M)))
 
 
-def sparse_attn_workspace_counter_bytes(shape):
-    return int(load().sparse_attn_workspace_counter_bytes(_sh(shape)))
-
-
 def alloc_workspace(shape, n_max, M, device="cuda"):
-    """Zero-filled workspace for (n_max, M); its counter region starts at zero."""
+    """Workspace for calls with this (n_max, M) (contents need no initialisation)."""
     n = sparse_attn_workspace_size(shape, n_max, M)
     if n == 0:
         raise ValueError("invalid shape/n_max/M for a workspace: %r %d %d" % (shape, n_max, M))
-    return torch.zeros(n, dtype=torch.uint8, device=device)
-
-
-def sparse_attn_workspace_init(shape, workspace):
-    _call("sparse_attn_workspace_init", _sh(shape),
-          _dev_ptr(workspace, torch.uint8, name="workspace"), workspace.numel(),
-          _stream(workspace))
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def sparse_attn_append_kv(shape, pos, k_new, v_new, P, k_cache, v_cache, kp_cache):

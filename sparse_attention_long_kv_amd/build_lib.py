@@ -43,16 +43,20 @@ def _run(cmd):
     return r
 
 
-def build(jobs=None, verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs=None, verbose=False, out=None, defines=()):
+    """Compile and link; `out` overrides the library path, `defines` adds -D flags."""
+    tag = "_".join(d.replace("=", "-") for d in defines)
+    build_dir = BUILD if not defines else os.path.join(BUILD, "variant_" + tag)
+    os.makedirs(build_dir, exist_ok=True)
+    extra = ["-D" + d for d in defines]
     cmds = []
     objs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        cmds.append([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+        cmds.append([HIPCC] + HIP_FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in CXX_SOURCES:
-        obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
+        obj = os.path.join(build_dir, src.replace(".cpp", ".o"))
         cmds.append(["g++"] + CXX_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     jobs = jobs or min(len(cmds), os.cpu_count() or 4, 8)
@@ -61,18 +65,22 @@ def build(jobs=None, verbose=False):
             fut.result()
             if verbose:
                 print(" ".join(cmd))
-    tmp = LIB + ".tmp"
+    lib = out or LIB
+    tmp = lib + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--out", default=None, help="write the library here instead")
+    ap.add_argument("-D", dest="defines", action="append", default=[],
+                    help="extra preprocessor definition for the HIP sources")
     a = ap.parse_args(argv)
-    print(build(a.jobs, a.verbose))
+    print(build(a.jobs, a.verbose, a.out, tuple(a.defines)))
 
 
 if __name__ == "__main__":

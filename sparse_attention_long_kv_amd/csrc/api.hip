@@ -165,12 +165,3 @@ extern "C" int sparse_attn_linear_gate(const sa_shape* shape, const void* q, con
                 c.stream);
 }
 
-extern "C" int sparse_attn_workspace_init(const sa_shape* shape, void* workspace,
-                                          size_t ws_bytes, void* stream) {
-  int st = check_shape(shape);
-  if (st != SA_OK) return st;
-  const size_t need = counter_bytes(*shape);
-  if (!ptr_ok(workspace, kAlign) || ws_bytes < need) return SA_ERR_WORKSPACE;
-  return finish(run_zero_u32((uint32_t*)workspace, need / 4, (hipStream_t)stream),
-                (hipStream_t)stream);
-}

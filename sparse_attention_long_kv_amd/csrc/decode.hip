@@ -18,7 +18,7 @@
 // base-2 domain.  States merge across lane groups, waves and finally across
 // the S workgroups with the log-sum-exp rule
 //   m = max m_s,  l = sum l_s 2^(m_s - m),  o = sum o_s 2^(m_s - m) / l,
-// the last workgroup of a unit to finish doing the cross-workgroup merge.
+// the cross-workgroup merge being a small second launch (none when S = 1).
 #include "device_common.hpp"
 #include "kernels.h"
 
@@ -33,7 +33,6 @@ struct DecodeArgs {
   float qscale;        // softmax_scale * log2(e)
   uint16_t* out;
   float* lse;
-  uint32_t* counters;
   float* pm;
   float* pl;
   float* po;
@@ -51,7 +50,8 @@ struct DecodeGeom {
   static constexpr int kLanesPerRow = D / 8;              // 16 (d=128) or 8 (d=64)
   static constexpr int kGroupsPerWave = kWave / kLanesPerRow;
   static constexpr int kGroups = 4 * kGroupsPerWave;      // rows in flight per pass
-  static constexpr int kUnroll = G <= 8 ? 4 : 2;          // rows per group per pass
+  static constexpr int kUnroll = G <= 4 ? 8 : 4;          // rows per group per pass
+  static constexpr int kIdxTile = 1024;                   // selected rows staged in LDS
 };
 
 template <int D, int G>
@@ -61,8 +61,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   constexpr int U = Geo::kUnroll;
   __shared__ float sm[4][G], sl[4][G];
   __shared__ float so[4][G][D];
-  __shared__ float fm[G], fl[G];
-  __shared__ uint32_t flag;
+  __shared__ int32_t sidx[Geo::kIdxTile];
 
   const int u = blockIdx.x / a.S, split = blockIdx.x % a.S;
   const int b = u / a.Hkv, h = u % a.Hkv;
@@ -96,68 +95,72 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   const int r0 = split * a.rps;
   const int r1 = min(a.M, r0 + a.rps);
   const int32_t* idx_u = a.idx + (size_t)u * a.M;
-  const uint16_t* ku = a.k + (size_t)u * a.Ncap * D + sub * 8;
-  const uint16_t* vu = a.v + (size_t)u * a.Ncap * D + sub * 8;
+  // this unit's K and V rows; a padding entry maps to an offset past the end
+  // and loads zeros (masked out of the softmax below)
+  const uint32_t unit_bytes = (uint32_t)a.Ncap * D * 2;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + (size_t)u * a.Ncap * D, unit_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + (size_t)u * a.Ncap * D, unit_bytes);
+  const uint32_t lane_off = (uint32_t)(sub * 16);
 
-  // trip count is the same for every lane (rows past r1 are masked), so the
-  // DPP reductions below always run with the whole wave active
-  for (int j0 = r0; j0 < r1; j0 += Geo::kGroups * U) {
-    int n[U];
-    bool ok[U];
-    uint4 kr[U], vr[U];
-#pragma unroll
-    for (int x = 0; x < U; ++x) {
-      const int jj = j0 + gid + x * Geo::kGroups;
-      n[x] = jj < r1 ? idx_u[jj] : -1;
-      ok[x] = (unsigned)n[x] < (unsigned)a.Ncap;
-    }
-#pragma unroll
-    for (int x = 0; x < U; ++x) {
-      kr[x] = make_uint4(0, 0, 0, 0);
-      vr[x] = make_uint4(0, 0, 0, 0);
-      if (ok[x]) {
-        kr[x] = *reinterpret_cast<const uint4*>(ku + (size_t)n[x] * D);
-        vr[x] = *reinterpret_cast<const uint4*>(vu + (size_t)n[x] * D);
-      }
-    }
-    // logits (base 2), reduced over the row's lanes
-    float s[U][G];
-#pragma unroll
-    for (int x = 0; x < U; ++x) {
-      float kf[8];
-      bf16x8_to_f32(kr[x], kf);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float acc = qf[g][0] * kf[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) acc = __builtin_fmaf(qf[g][e], kf[e], acc);
-        s[x][g] = group_sum<LG>(acc);
-      }
-    }
-    // online softmax update of this lane group's state
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = m[g];
-#pragma unroll
-      for (int x = 0; x < U; ++x) mx = ok[x] ? fmaxf(mx, s[x][g]) : mx;
-      const float alpha = merge_scale(m[g], mx);
-      float p[U];
-#pragma unroll
-      for (int x = 0; x < U; ++x) p[x] = ok[x] ? fast_exp2(s[x][g] - mx) : 0.0f;
-      float lsum = l[g] * alpha;
-#pragma unroll
-      for (int x = 0; x < U; ++x) lsum += p[x];
-      l[g] = lsum;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[g][e] *= alpha;
+  for (int t0 = r0; t0 < r1; t0 += Geo::kIdxTile) {
+    const int t1 = min(r1, t0 + Geo::kIdxTile);
+    __syncthreads();
+    for (int j = t0 + tid; j < t1; j += kBlock) sidx[j - t0] = idx_u[j];
+    __syncthreads();
+    // Every lane runs the same trip count (rows past t1 are masked), so the
+    // DPP reductions always see the whole wave active.  Row loads are
+    // unconditional buffer loads.
+    for (int j0 = t0; j0 < t1; j0 += Geo::kGroups * U) {
+      bool ok[U];
+      uint4 kr[U], vr[U];
 #pragma unroll
       for (int x = 0; x < U; ++x) {
-        float vf[8];
-        bf16x8_to_f32(vr[x], vf);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[g][e] = __builtin_fmaf(p[x], vf[e], o[g][e]);
+        const int jj = j0 + gid + x * Geo::kGroups;
+        const int n = jj < t1 ? sidx[jj - t0] : -1;
+        ok[x] = (unsigned)n < (unsigned)a.Ncap;
+        const uint32_t off = ok[x] ? (uint32_t)n * (D * 2) + lane_off : 0xFFFFFFF0u;
+        kr[x] = buffer_load16(rk, off, 0);
+        vr[x] = buffer_load16(rv, off, 0);
       }
-      m[g] = mx;
+      // logits (base 2), reduced over the row's lanes
+      float s[U][G];
+#pragma unroll
+      for (int x = 0; x < U; ++x) {
+        float kf[8];
+        bf16x8_to_f32(kr[x], kf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float acc = qf[g][0] * kf[0];
+#pragma unroll
+          for (int e = 1; e < 8; ++e) acc = __builtin_fmaf(qf[g][e], kf[e], acc);
+          s[x][g] = group_sum<LG>(acc);
+        }
+      }
+      // online softmax update of this lane group's state
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float mx = m[g];
+#pragma unroll
+        for (int x = 0; x < U; ++x) mx = ok[x] ? fmaxf(mx, s[x][g]) : mx;
+        const float alpha = merge_scale(m[g], mx);
+        float p[U];
+#pragma unroll
+        for (int x = 0; x < U; ++x) p[x] = ok[x] ? fast_exp2(s[x][g] - mx) : 0.0f;
+        float lsum = l[g] * alpha;
+#pragma unroll
+        for (int x = 0; x < U; ++x) lsum += p[x];
+        l[g] = lsum;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[g][e] *= alpha;
+#pragma unroll
+        for (int x = 0; x < U; ++x) {
+          float vf[8];
+          bf16x8_to_f32(vr[x], vf);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[g][e] = __builtin_fmaf(p[x], vf[e], o[g][e]);
+        }
+        m[g] = mx;
+      }
     }
   }
 
@@ -213,16 +216,17 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       a.po[(part0 + g) * D + dd] = ot;
     }
   }
-  if (a.S == 1) return;
+}
 
-  // the last workgroup of the unit merges the S partial states
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) flag = (atomicAdd(&a.counters[u], 1u) == (uint32_t)(a.S - 1)) ? 1u : 0u;
-  __syncthreads();
-  if (!flag) return;
-  __threadfence();
-  if (tid == 0) atomicExch(&a.counters[u], 0u);
+// Merge the S partial states of one unit (one workgroup per unit).  A separate
+// launch orders the partial writes before these reads without device-scope
+// fences inside the attention kernel.
+template <int D, int G>
+__global__ __launch_bounds__(256) void combine_kernel(const DecodeArgs a) {
+  __shared__ float fm[G], fl[G];
+  const int u = blockIdx.x;
+  const int b = u / a.Hkv, h = u % a.Hkv;
+  const int tid = threadIdx.x;
   const size_t ubase = (size_t)u * a.S * G;
   if (tid < G) {
     const int g = tid;
@@ -253,11 +257,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 }
 
 template <int D>
-static void launch_decode_d(int G, const DecodeArgs& a, dim3 grid, hipStream_t st) {
+static void launch_decode_d(int G, const DecodeArgs& a, dim3 grid, int units, hipStream_t st) {
   switch (G) {
 #define SA_CASE(GG)                                                                    \
   case GG:                                                                             \
     hipLaunchKernelGGL((decode_kernel<D, GG>), grid, dim3(kBlock), 0, st, a);          \
+    if (a.S > 1)                                                                       \
+      hipLaunchKernelGGL((combine_kernel<D, GG>), dim3(units), dim3(kBlock), 0, st, a); \
     break;
     SA_CASE(1) SA_CASE(2) SA_CASE(3) SA_CASE(4) SA_CASE(5) SA_CASE(6) SA_CASE(7) SA_CASE(8)
     SA_CASE(9) SA_CASE(10) SA_CASE(11) SA_CASE(12) SA_CASE(13) SA_CASE(14) SA_CASE(15)
@@ -285,15 +291,14 @@ hipError_t run_decode(const LaunchCommon& c, const DecodePlan& plan, const void*
   a.out = (uint16_t*)out;
   a.lse = lse;
   char* ws = (char*)workspace;
-  a.counters = (uint32_t*)ws;
   a.pm = (float*)(ws + plan.off_m);
   a.pl = (float*)(ws + plan.off_l);
   a.po = (float*)(ws + plan.off_o);
   const long blocks = (long)plan.units * plan.splits;
   if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks);
-  if (c.D == 128) launch_decode_d<128>(c.G, a, grid, c.stream);
-  else launch_decode_d<64>(c.G, a, grid, c.stream);
+  if (c.D == 128) launch_decode_d<128>(c.G, a, grid, plan.units, c.stream);
+  else launch_decode_d<64>(c.G, a, grid, plan.units, c.stream);
   return hipGetLastError();
 }
 

@@ -62,6 +62,26 @@ __device__ __forceinline__ uint32_t f64_to_e4m3(double x) {
   return sign | (uint32_t)(biased << 3) | (uint32_t)q;
 }
 
+// ---------------------------------------------------------------- buffer loads
+
+// Raw buffer resource over [base, base + bytes): loads whose lane offset is at
+// or past `bytes` return zero (hardware range check over the vector and
+// immediate offsets; callers pass the whole offset in the lane offset and 0 as
+// the scalar one), so tails and padding need no clamping or branches.
+constexpr int kBufferWord3 = 0x00020000;   // raw (untyped) 32-bit element format
+typedef unsigned int sa_u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferWord3);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff) {
+  const sa_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---------------------------------------------------------------- DPP sums
 
 // DPP control words (gfx9 encoding)

@@ -24,10 +24,6 @@ bool ptr_ok(const void* p, size_t align) {
   return p != nullptr && (reinterpret_cast<uintptr_t>(p) % align) == 0;
 }
 
-size_t counter_bytes(const sa_shape& s) {
-  return align_up((size_t)s.batch * s.num_kv_heads * sizeof(uint32_t), kAlign);
-}
-
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int plan_topm(const sa_shape& s, int n_max, int M, TopmPlan* p) {
@@ -39,17 +35,18 @@ int plan_topm(const sa_shape& s, int n_max, int M, TopmPlan* p) {
   if (splits > kMaxSplits) return SA_ERR_UNSUPPORTED;
   p->units = (int)units;
   p->chunk = chunk;
-  p->kpt = chunk / kBlock;
+  p->kpt = chunk / kChunkBlock;
   p->splits = (int)splits;
   p->mc = std::min(M, chunk);
-  p->multi_tile = splits * p->mc > kMergeTile;
-  size_t off = counter_bytes(s);
+  p->ms = (int)align_up((size_t)p->mc, kBlock);
+  p->multi_tile = splits * p->ms > kMergeTile;
+  size_t off = 0;
   p->off_cnt = off;
   off = align_up(off + (size_t)units * splits * sizeof(int32_t), kAlign);
   p->off_key = off;
-  off = align_up(off + (size_t)units * splits * p->mc * sizeof(uint32_t), kAlign);
+  off = align_up(off + (size_t)units * splits * p->ms * sizeof(uint32_t), kAlign);
   p->off_pos = off;
-  off = align_up(off + (size_t)units * splits * p->mc * sizeof(int32_t), kAlign);
+  off = align_up(off + (size_t)units * splits * p->ms * sizeof(int32_t), kAlign);
   p->end = off;
   return SA_OK;
 }
@@ -64,7 +61,7 @@ int plan_decode(const sa_shape& s, int M, DecodePlan* p) {
   p->units = (int)units;
   p->splits = (int)splits;
   p->rows_per_split = (int)rps;
-  size_t off = counter_bytes(s);
+  size_t off = 0;
   const size_t parts = (size_t)units * splits * G;
   p->off_m = off;
   off = align_up(off + parts * sizeof(float), kAlign);
@@ -96,11 +93,6 @@ extern "C" size_t sparse_attn_workspace_size(const sa_shape* shape, int32_t n_ma
                                              int32_t M) {
   if (!shape) return 0;
   return sa::workspace_bytes(*shape, n_max, M);
-}
-
-extern "C" size_t sparse_attn_workspace_counter_bytes(const sa_shape* shape) {
-  if (sa::check_shape(shape) != SA_OK) return 0;
-  return sa::counter_bytes(*shape);
 }
 
 extern "C" const char* sparse_attn_status_string(int status) {

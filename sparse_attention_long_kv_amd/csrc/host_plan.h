@@ -11,9 +11,11 @@ namespace sa {
 
 // Fixed launch geometry shared with the kernels.
 constexpr int kBlock = 256;              // threads per workgroup (4 waves of 64)
-constexpr int kMaxKeysPerThread = 64;    // register-resident selection keys
-constexpr int kMaxChunk = kBlock * kMaxKeysPerThread;   // 16384 positions
-constexpr int kMinChunk = kBlock;                       // 256 positions
+constexpr int kChunkBlock = 512;         // chunk-select workgroups (8 waves)
+constexpr int kMaxKeysPerThread = 64;    // register-resident merge keys
+constexpr int kMaxChunkKeysPerThread = 32;
+constexpr int kMaxChunk = kChunkBlock * kMaxChunkKeysPerThread;   // 16384 positions
+constexpr int kMinChunk = kChunkBlock;                            // 512 positions
 constexpr int kMergeTile = kBlock * kMaxKeysPerThread;  // keys per merge tile
 constexpr int kMaxSplits = 1024;         // chunks per (b, KV head) unit
 constexpr int kTargetBlocks = 2048;      // enough workgroups for 256 CUs
@@ -22,10 +24,11 @@ constexpr size_t kAlign = 256;
 
 struct TopmPlan {
   int units;        // B * Hkv
-  int chunk;        // positions per chunk workgroup (multiple of 256)
-  int kpt;          // keys per thread = chunk / 256
+  int chunk;        // positions per chunk workgroup (multiple of 512)
+  int kpt;          // keys per thread = chunk / 512
   int splits;       // chunks per unit
-  int mc;           // candidate slots per chunk = min(M, chunk)
+  int mc;           // candidates per chunk at most = min(M, chunk)
+  int ms;           // candidate slots per chunk: mc rounded up to 256
   bool multi_tile;  // merge input exceeds one register tile
   size_t off_cnt, off_key, off_pos, end;   // byte offsets in the workspace
 };
@@ -44,7 +47,6 @@ int check_shape(const sa_shape* s);
 // Non-null and aligned to `align` bytes.
 bool ptr_ok(const void* p, size_t align);
 
-size_t counter_bytes(const sa_shape& s);
 int plan_topm(const sa_shape& s, int n_max, int M, TopmPlan* out);
 int plan_decode(const sa_shape& s, int M, DecodePlan* out);
 size_t workspace_bytes(const sa_shape& s, int n_max, int M);

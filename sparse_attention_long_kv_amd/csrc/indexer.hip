@@ -20,9 +20,9 @@
 // lowest-position keys == t, in ascending position order, with one ordered
 // prefix scan.  The fused path ("index_topm") splits a unit's positions into
 // chunks, selects the chunk-local top-M (exact for the union because the
-// order (score desc, position asc) is total), and the last chunk workgroup of
-// a unit to finish merges the candidates with the same machinery.  The
-// unfused path ("topm") does the same from scores stored in HBM.
+// order (score desc, position asc) is total), and a second launch merges
+// each unit's candidates with the same machinery.  The unfused path ("topm")
+// does the same from scores stored in HBM.
 #include "device_common.hpp"
 #include "kernels.h"
 
@@ -30,12 +30,12 @@ namespace sa {
 
 // ------------------------------------------------------------------ query
 
-// qt (R floats, LDS) for unit (b, h).  `part` is 256 doubles of LDS.
+// qt (R floats, LDS) for unit (b, h).  `part` is NT doubles of LDS.
 // Every thread of the block must call this (it synchronises).
-template <int D, int R>
+template <int D, int R, int NT = kBlock>
 __device__ void indexer_query(const uint16_t* __restrict__ q, const float* __restrict__ P,
                               int b, int h, int G, int Hq, float* qt, double* part) {
-  constexpr int kParts = kBlock / R;     // 8 (r=32) or 16 (r=16)
+  constexpr int kParts = NT / R;         // basis-row groups, one partial sum each
   constexpr int kPer = D / kParts;       // basis rows per part
   const int t = threadIdx.x;
   const int j = t % R, pi = t / R;
@@ -116,16 +116,26 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   const uint8_t* kpu = kp + (size_t)u * Ncap * R;
   float* su = scores + (size_t)u * n_max;
   const int pos_lane = (R == 32) ? (lane >> 1) : lane;
-  for (int it = 0; it < kIters; ++it) {
-    const int p0 = blk * kScorePositionsPerBlock + (it * 4 + w) * kPPW;
-    if (p0 >= n_max) break;                         // uniform per wave
-    const int p = p0 + pos_lane;
-    uint4 c = make_uint4(0, 0, 0, 0);
-    if (p < len) c = load16(kpu + (size_t)p0 * R + lane * 16);
-    float s = lane_score<R>(ql, c);
-    if (p >= len) s = -__builtin_inff();
-    const bool writer = (R == 32) ? ((lane & 1) == 0) : true;
-    if (writer && p < n_max) su[p] = s;
+  const int blk0 = blk * kScorePositionsPerBlock;
+  const int nv = min(max(len - blk0, 0), kScorePositionsPerBlock);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(kpu + (size_t)blk0 * R, (uint32_t)nv * R);
+  constexpr int kBatch = 8;
+  static_assert(kIters % kBatch == 0, "batches");
+  for (int it0 = 0; it0 < kIters; it0 += kBatch) {
+    if (blk0 + (it0 * 4 + w) * kPPW >= n_max) break;      // uniform per wave
+    uint4 c[kBatch];
+#pragma unroll
+    for (int x = 0; x < kBatch; ++x)
+      c[x] = buffer_load16(rs, (uint32_t)(lane * 16 + ((it0 + x) * 4 + w) * kPPW * R), 0);
+#pragma unroll
+    for (int x = 0; x < kBatch; ++x) {
+      const int p0 = blk0 + ((it0 + x) * 4 + w) * kPPW;
+      const int p = p0 + pos_lane;
+      float s = lane_score<R>(ql, c[x]);
+      if (p >= len) s = -__builtin_inff();
+      const bool writer = (R == 32) ? ((lane & 1) == 0) : true;
+      if (writer && p < n_max) su[p] = s;
+    }
   }
 }
 
@@ -156,42 +166,79 @@ struct SelectArgs {
   const uint8_t* kp;
   const float* scores;
   const int32_t* seq_lens;
-  int n_max, Ncap, Hq, Hkv, G, M, S, chunk, mc;
-  uint32_t* counters;
+  int n_max, Ncap, Hq, Hkv, G, M, S, chunk, ms;   // ms: candidate slots per chunk
   int32_t* cand_cnt;
   uint32_t* cand_key;
   int32_t* cand_pos;
   int32_t* idx;
 };
 
+// 16-byte loads each lane keeps in flight while scoring (tuning knob)
+#ifndef SA_CHUNK_LOADS_IN_FLIGHT
+#define SA_CHUNK_LOADS_IN_FLIGHT 16
+#endif
+
+constexpr int kDigitBits = 12;
+constexpr int kBins = 1 << kDigitBits;      // radix-select histogram bins
+constexpr int kChunkThreads = kChunkBlock;  // chunk workgroups: 8 waves
+constexpr int kMergeThreads = 1024;         // merge workgroups: 16 waves
+
+template <int NT>
 struct SelectShared {
+  static constexpr int W = NT / kWave;
   float qt[32];
-  double part[kBlock];
-  uint32_t red[8];
-  uint32_t seg[kBlock];
-  uint32_t wtot[4];
-  uint32_t flag;
-  int32_t cnt[kMaxSplits];
+  double part[NT];
+  uint32_t red[2][W];
+  uint32_t mnmx[2][W];
+  uint32_t seg[NT];
+  uint32_t wtot[W];
+  uint32_t pick[2];
+  uint32_t hist[kBins + kWave];   // + one private dummy bin per lane
 };
 
+
+// Inclusive prefix sum over the block in thread order; `total` gets the sum.
+template <int NT>
+__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, SelectShared<NT>& sh,
+                                                         uint32_t& total) {
+  constexpr int W = NT / kWave;
+  const int w = threadIdx.x / kWave;
+  const uint32_t inc = wave_inclusive_scan(v);
+  __syncthreads();
+  if (lane_id() == kWave - 1) sh.wtot[w] = inc;
+  __syncthreads();
+  uint32_t wb = 0, tot = 0;
+#pragma unroll
+  for (int ww = 0; ww < W; ++ww) {
+    wb += ww < w ? sh.wtot[ww] : 0u;
+    tot += sh.wtot[ww];
+  }
+  total = tot;
+  return wb + inc;
+}
+
 // Number of keys >= t over the block (every thread receives it).
-template <int K>
+template <int NT, int K>
 __device__ __forceinline__ uint32_t count_ge(const uint32_t (&key)[K], uint32_t t,
-                                             SelectShared& sh, int& ph) {
+                                             SelectShared<NT>& sh, int& ph) {
+  constexpr int W = NT / kWave;
   uint32_t c = 0;
 #pragma unroll
   for (int i = 0; i < K; ++i) c += (uint32_t)popc64(ballot(key[i] >= t));
-  const int w = threadIdx.x / kWave;
-  if (lane_id() == 0) sh.red[ph * 4 + w] = c;
+  sh.red[ph][threadIdx.x / kWave] = c;
   __syncthreads();
-  const uint32_t tot = sh.red[ph * 4] + sh.red[ph * 4 + 1] + sh.red[ph * 4 + 2] + sh.red[ph * 4 + 3];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int ww = 0; ww < W; ++ww) tot += sh.red[ph][ww];
   ph ^= 1;
   return tot;
 }
 
 // Block-wide min over nonzero keys and max over all keys.
-__device__ __forceinline__ void block_key_range(uint32_t mn, uint32_t mx, SelectShared& sh,
+template <int NT>
+__device__ __forceinline__ void block_key_range(uint32_t mn, uint32_t mx, SelectShared<NT>& sh,
                                                 uint32_t& omn, uint32_t& omx) {
+  constexpr int W = NT / kWave;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, kWave));
@@ -199,11 +246,17 @@ __device__ __forceinline__ void block_key_range(uint32_t mn, uint32_t mx, Select
   }
   const int w = threadIdx.x / kWave;
   __syncthreads();
-  if (lane_id() == 0) { sh.seg[w] = mn; sh.seg[4 + w] = mx; }
+  sh.mnmx[0][w] = mn;
+  sh.mnmx[1][w] = mx;
   __syncthreads();
-  omn = min(min(sh.seg[0], sh.seg[1]), min(sh.seg[2], sh.seg[3]));
-  omx = max(max(sh.seg[4], sh.seg[5]), max(sh.seg[6], sh.seg[7]));
-  __syncthreads();
+  uint32_t a = 0xFFFFFFFFu, b = 0u;
+#pragma unroll
+  for (int ww = 0; ww < W; ++ww) {
+    a = min(a, sh.mnmx[0][ww]);
+    b = max(b, sh.mnmx[1][ww]);
+  }
+  omn = a;
+  omx = b;
 }
 
 template <int K>
@@ -233,27 +286,25 @@ __device__ __forceinline__ uint32_t find_threshold(CountFn cnt, uint32_t lo, uin
 // position order -- every key > t and the first `need` keys == t (counting
 // from eq_base already emitted).  emit(i, slot) receives the output slot.
 // Returns this tile's (gt, eq) totals packed as gt | eq << 16.
-template <int K, class EmitFn>
+template <int NT, int K, class EmitFn>
 __device__ __forceinline__ uint32_t emit_in_order(const uint32_t (&key)[K], uint32_t t,
                                                   uint32_t need, uint32_t gt_base,
-                                                  uint32_t eq_base, SelectShared& sh,
+                                                  uint32_t eq_base, SelectShared<NT>& sh,
                                                   EmitFn emit) {
-  static_assert(K * 4 <= kBlock, "segments");
+  constexpr int W = NT / kWave;
+  static_assert(K * W <= NT, "segments");
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
 #pragma unroll
   for (int i = 0; i < K; ++i) {
     const uint64_t mg = ballot(key[i] > t), me = ballot(key[i] == t);
-    if (lane == 0) sh.seg[i * 4 + w] = (uint32_t)popc64(mg) | ((uint32_t)popc64(me) << 16);
+    // every lane stores the same (wave-uniform) value: no per-key branch
+    sh.seg[i * W + w] = (uint32_t)popc64(mg) | ((uint32_t)popc64(me) << 16);
   }
   __syncthreads();
-  const uint32_t v = tid < K * 4 ? sh.seg[tid] : 0u;
-  const uint32_t inc = wave_inclusive_scan(v);
-  if (lane == kWave - 1) sh.wtot[w] = inc;
-  __syncthreads();
-  uint32_t wb = 0;
-  for (int ww = 0; ww < w; ++ww) wb += sh.wtot[ww];
-  const uint32_t total = sh.wtot[0] + sh.wtot[1] + sh.wtot[2] + sh.wtot[3];
-  if (tid < K * 4) sh.seg[tid] = wb + inc - v;
+  const uint32_t v = tid < K * W ? sh.seg[tid] : 0u;
+  uint32_t total;
+  const uint32_t incl = block_inclusive_scan(v, sh, total);
+  if (tid < K * W) sh.seg[tid] = incl - v;
   __syncthreads();
   const uint64_t lt = lanemask_lt();
   // An opaque copy of t keeps the compiler from carrying the first pass's
@@ -263,7 +314,7 @@ __device__ __forceinline__ uint32_t emit_in_order(const uint32_t (&key)[K], uint
 #pragma unroll
   for (int i = 0; i < K; ++i) {
     const uint64_t mg = ballot(key[i] > t2), me = ballot(key[i] == t2);
-    const uint32_t pre = sh.seg[i * 4 + w];
+    const uint32_t pre = sh.seg[i * W + w];
     const uint32_t gtb = gt_base + (pre & 0xFFFFu) + (uint32_t)popc64(mg & lt);
     const uint32_t eqb = eq_base + (pre >> 16) + (uint32_t)popc64(me & lt);
     if (key[i] > t2) emit(i, gtb + min(eqb, need));
@@ -273,105 +324,358 @@ __device__ __forceinline__ uint32_t emit_in_order(const uint32_t (&key)[K], uint
   return total;
 }
 
-// Candidate key of flat slot f in a unit's [S][mc] candidate array (0 if empty).
-__device__ __forceinline__ uint32_t cand_key_at(const uint32_t* ck, const SelectShared& sh,
-                                                int f, int flat_n, int mc) {
-  if (f >= flat_n) return 0u;
-  const int s = f / mc, k = f - s * mc;
-  return k < sh.cnt[s] ? ck[f] : 0u;
+// Exact selection threshold by radix select on register keys.
+//
+// Keys are the block's nonzero register keys (0 = empty) and 1 <= target <=
+// their number.  Returns t = the target-th largest key and need = how many
+// keys equal to t belong to the selection (target - #keys > t).  Offsets
+// d = key - min are resolved 12 bits at a time from the top of the occupied
+// range (at most three levels for 32-bit keys): histogram the digit of the
+// keys still on the chosen path in LDS, then pick the bin where the count
+// from the top reaches the target.  Exact for any key distribution.
+template <int NT, int K>
+__device__ void radix_threshold(const uint32_t (&key)[K], uint32_t target, SelectShared<NT>& sh,
+                                uint32_t& t_out, uint32_t& need_out) {
+  const int tid = threadIdx.x;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  thread_key_range(key, mn, mx);
+  block_key_range(mn, mx, sh, mn, mx);
+  const uint32_t range = mx - mn;
+  const int bitlen = range == 0u ? 0 : 32 - __clz((int)range);
+  int lo = max(0, bitlen - kDigitBits);   // lowest bit of the current digit
+  int top = lo + kDigitBits;              // bits >= top are fixed by `path`
+  uint32_t path = 0;                      // chosen high part of d (d >> top)
+  uint32_t above = 0;                     // keys strictly above the chosen bins
+  for (;;) {
+    const int width = top - lo;
+    for (int b = tid; b < kBins + kWave; b += NT) sh.hist[b] = 0u;
+    __syncthreads();
+    // Offsets are re-derived per level from an opaque copy of the minimum so
+    // the compiler keeps no per-key masks alive across levels; keys off the
+    // path (and empty keys, whose offset wraps above the range) count into
+    // this lane's private dummy bin, so the atomics need no branch.
+    uint32_t base = mn;
+    asm volatile("" : "+v"(base));
+    const uint32_t dummy = (uint32_t)(kBins + lane_id());
+    const uint32_t digit_mask = (1u << width) - 1u;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const uint32_t d = key[i] - base;
+      const bool on_path = d <= range && (top >= 32 || (d >> top) == path);
+      atomicAdd(&sh.hist[on_path ? ((d >> lo) & digit_mask) : dummy], 1u);
+    }
+    __syncthreads();
+    // thread t owns bins [kPer*t, kPer*(t+1)); counts run from the top
+    constexpr int kPer = kBins / NT;
+    uint32_t c[kPer];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      c[j] = sh.hist[tid * kPer + j];
+      mine += c[j];
+    }
+    uint32_t total;
+    const uint32_t incl = block_inclusive_scan(mine, sh, total);
+    const uint32_t above_mine = total - incl;          // bins owned by higher threads
+    const uint32_t rank = target - above;               // 1-based rank on this path
+    if (above_mine < rank && rank <= above_mine + mine) {
+      uint32_t cum = above_mine;
+#pragma unroll
+      for (int j = kPer - 1; j >= 0; --j) {
+        if (cum + c[j] >= rank) {
+          sh.pick[0] = (uint32_t)(tid * kPer + j);
+          sh.pick[1] = cum;
+          break;
+        }
+        cum += c[j];
+      }
+    }
+    __syncthreads();
+    const uint32_t b = sh.pick[0];
+    above += sh.pick[1];
+    __syncthreads();
+    path = (path << width) | b;
+    top = lo;
+    if (lo == 0) break;
+    lo = max(0, lo - kDigitBits);
+  }
+  t_out = mn + path;
+  need_out = target - above;
 }
 
-// Merge the chunk candidates of unit u into idx (last workgroup of the unit).
-template <bool MULTI>
-__device__ void merge_unit(const SelectArgs& a, int u, SelectShared& sh) {
-  const int tid = threadIdx.x;
-  const int S = a.S, mc = a.mc, M = a.M;
-  const int flat_n = S * mc;
-  uint32_t my = 0;
-  for (int s = tid; s < S; s += kBlock) {
-    const int c = a.cand_cnt[(size_t)u * S + s];
-    sh.cnt[s] = c;
-    my += (uint32_t)c;
+// ------------------------------------------------------------------ merge
+
+// A unit's valid chunk candidates are compacted, in chunk order, into a dense
+// LDS tile of up to kMergeTile (key, position) pairs -- 128 KB of gfx950's
+// 160 KB -- so every pass below is a short rolled loop over LDS (the merge
+// runs once per unit, so compact code matters more than unrolling).  Dense
+// index order equals ascending position order.  Units with more valid
+// candidates than one tile re-stage each tile per pass.
+struct MergeLds {
+  uint32_t key[kMergeTile];
+  int32_t pos[kMergeTile];
+  uint32_t hist[kBins + kWave];
+  int32_t off[kMaxSplits + 1];   // dense offset of each chunk's candidates
+  uint32_t seg[kMergeThreads];
+  uint32_t wtot[kMergeThreads / kWave];
+  uint32_t mnmx[2][kMergeThreads / kWave];
+  uint32_t pick[2];
+};
+
+__device__ __forceinline__ uint32_t merge_scan(uint32_t v, MergeLds& sh, uint32_t& total) {
+  constexpr int W = kMergeThreads / kWave;
+  const int w = threadIdx.x / kWave;
+  const uint32_t inc = wave_inclusive_scan(v);
+  __syncthreads();
+  if (lane_id() == kWave - 1) sh.wtot[w] = inc;
+  __syncthreads();
+  uint32_t wb = 0, tot = 0;
+#pragma unroll
+  for (int ww = 0; ww < W; ++ww) {
+    wb += ww < w ? sh.wtot[ww] : 0u;
+    tot += sh.wtot[ww];
   }
-  const uint32_t total = wave_sum_u32(my);
+  total = tot;
+  return wb + inc;
+}
+
+// Copy dense candidates [d0, d0 + n) of unit u into the LDS tile.
+__device__ void stage_tile(const SelectArgs& a, int u, MergeLds& sh, int d0, int n) {
+  constexpr int NT = kMergeThreads;
+  const uint32_t* ck = a.cand_key + (size_t)u * a.S * a.ms;
+  const int32_t* cp = a.cand_pos + (size_t)u * a.S * a.ms;
   __syncthreads();
-  if (lane_id() == 0) sh.red[tid / kWave] = total;
+  // first chunk overlapping the tile (off[] is ascending)
+  int s = 0;
+  {
+    int lo = 0, hi = a.S;              // largest s with off[s] <= d0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sh.off[mid] <= d0) lo = mid; else hi = mid;
+    }
+    s = lo;
+  }
+  for (; s < a.S && sh.off[s] < d0 + n; ++s) {
+    const int b0 = max(sh.off[s], d0), b1 = min(sh.off[s + 1], d0 + n);
+    const int src = s * a.ms - sh.off[s];
+#pragma unroll 4
+    for (int d = b0 + threadIdx.x; d < b1; d += NT) {
+      sh.key[d - d0] = ck[src + d];
+      sh.pos[d - d0] = cp[src + d];
+    }
+  }
   __syncthreads();
-  const uint32_t nvalid = sh.red[0] + sh.red[1] + sh.red[2] + sh.red[3];
+}
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const SelectArgs a) {
+  constexpr int NT = kMergeThreads;
+  constexpr int W = NT / kWave;
+  __shared__ MergeLds sh;
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  const int S = a.S, M = a.M;
+
+  // dense offsets of the chunks' candidate lists (exclusive scan of counts)
+  const int spt = (S + NT - 1) / NT;    // chunks per thread, contiguous
+  uint32_t my = 0;
+  for (int j = 0; j < spt; ++j) {
+    const int s = tid * spt + j;
+    if (s < S) my += (uint32_t)a.cand_cnt[(size_t)u * S + s];
+  }
+  uint32_t nvalid;
+  uint32_t run = merge_scan(my, sh, nvalid) - my;
+  for (int j = 0; j < spt; ++j) {
+    const int s = tid * spt + j;
+    if (s < S) {
+      sh.off[s] = (int)run;
+      run += (uint32_t)a.cand_cnt[(size_t)u * S + s];
+    }
+  }
+  if (tid == 0) sh.off[S] = (int)nvalid;
   __syncthreads();
-  const uint32_t* ck = a.cand_key + (size_t)u * flat_n;
-  const int32_t* cp = a.cand_pos + (size_t)u * flat_n;
+
   int32_t* idx_u = a.idx + (size_t)u * M;
   const uint32_t target = min(nvalid, (uint32_t)M);
-  int ph = 0;
-  constexpr int K = kMaxKeysPerThread;
-
-  if (!MULTI) {
-    uint32_t key[K];
+  const int ntiles = ((int)nvalid + kMergeTile - 1) / kMergeTile;
+  auto tile_n = [&](int tile) { return min((int)nvalid - tile * kMergeTile, kMergeTile); };
+  if (ntiles == 1) {
+    const int flat_n = S * a.ms;
+    if (flat_n <= kMergeTile) {
+      // one batch of loads over the whole [S][ms] array (all in flight), then
+      // scatter the valid entries to their dense slots
+      constexpr int K = kMergeTile / NT;
+      const uint32_t* ck = a.cand_key + (size_t)u * flat_n;
+      const int32_t* cp = a.cand_pos + (size_t)u * flat_n;
+      uint32_t kv[K];
+      int32_t pv[K];
 #pragma unroll
-    for (int i = 0; i < K; ++i) key[i] = cand_key_at(ck, sh, i * kBlock + tid, flat_n, mc);
-    uint32_t t = 0, need = 0;
-    if (nvalid > (uint32_t)M) {
-      uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-      thread_key_range(key, mn, mx);
-      block_key_range(mn, mx, sh, mn, mx);
-      t = find_threshold([&](uint32_t x) { return count_ge(key, x, sh, ph); }, mn, mx, target);
-      const uint32_t gt = (t == 0xFFFFFFFFu) ? 0u : count_ge(key, t + 1, sh, ph);
-      need = target - gt;
-    }
-    emit_in_order(key, t, need, 0, 0, sh, [&](int i, uint32_t slot) {
-      idx_u[slot] = cp[i * kBlock + tid];
-    });
-  } else {
-    const int ntiles = (flat_n + kMergeTile - 1) / kMergeTile;
-    auto load_tile = [&](int tile, uint32_t (&key)[K]) {
-#pragma unroll
-      for (int i = 0; i < K; ++i)
-        key[i] = cand_key_at(ck, sh, tile * kMergeTile + i * kBlock + tid, flat_n, mc);
-    };
-    uint32_t t = 0, need = 0;
-    if (nvalid > (uint32_t)M) {
-      uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-      for (int tile = 0; tile < ntiles; ++tile) {
-        uint32_t key[K];
-        load_tile(tile, key);
-        thread_key_range(key, mn, mx);
+      for (int i = 0; i < K; ++i) {
+        const int f = min(i * NT + tid, flat_n - 1);
+        kv[i] = ck[f];
+        pv[i] = cp[f];
       }
-      block_key_range(mn, mx, sh, mn, mx);
-      auto cnt = [&](uint32_t x) {
-        uint32_t c = 0;
-        for (int tile = 0; tile < ntiles; ++tile) {
-          uint32_t key[K];
-          load_tile(tile, key);
-          c += count_ge(key, x, sh, ph);
+      const int ms = a.ms;
+      const float inv_ms = 1.0f / (float)ms;
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        // chunk of flat slot f: f / ms via a float reciprocal (f < 2^24, so
+        // the estimate is off by at most one) and an exact correction
+        const int f = i * NT + tid;
+        int sc = (int)((float)f * inv_ms);
+        sc -= (sc * ms > f) ? 1 : 0;
+        sc += ((sc + 1) * ms <= f) ? 1 : 0;
+        const int slot = f - sc * ms;
+        if (f < flat_n && sc < S && slot < sh.off[sc + 1] - sh.off[sc]) {
+          const int d = sh.off[sc] + slot;
+          sh.key[d] = kv[i];
+          sh.pos[d] = pv[i];
         }
-        return c;
-      };
-      t = find_threshold(cnt, mn, mx, target);
-      const uint32_t gt = (t == 0xFFFFFFFFu) ? 0u : cnt(t + 1);
-      need = target - gt;
-    }
-    uint32_t gt_base = 0, eq_base = 0;
-    for (int tile = 0; tile < ntiles; ++tile) {
-      uint32_t key[K];
-      load_tile(tile, key);
-      const int fbase = tile * kMergeTile;
-      const uint32_t tot = emit_in_order(key, t, need, gt_base, eq_base, sh,
-                                         [&](int i, uint32_t slot) {
-                                           idx_u[slot] = cp[fbase + i * kBlock + tid];
-                                         });
-      gt_base += tot & 0xFFFFu;
-      eq_base += tot >> 16;
+      }
+      __syncthreads();
+    } else {
+      stage_tile(a, u, sh, 0, (int)nvalid);
     }
   }
-  for (int slot = (int)target + tid; slot < M; slot += kBlock) idx_u[slot] = -1;
+
+  uint32_t t = 0, need = 0;
+  if (nvalid > (uint32_t)M) {
+    // key range
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int tile = 0; tile < ntiles; ++tile) {
+      if (ntiles > 1) stage_tile(a, u, sh, tile * kMergeTile, tile_n(tile));
+      const int n = tile_n(tile);
+#pragma unroll
+      for (int i = 0; i < kMergeTile / NT; ++i) {
+        const int j = i * NT + tid;
+        if (j < n) {
+          mn = min(mn, sh.key[j]);
+          mx = max(mx, sh.key[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+      mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+    }
+    __syncthreads();
+    sh.mnmx[0][w] = mn;
+    sh.mnmx[1][w] = mx;
+    __syncthreads();
+    mn = 0xFFFFFFFFu;
+    mx = 0u;
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww) {
+      mn = min(mn, sh.mnmx[0][ww]);
+      mx = max(mx, sh.mnmx[1][ww]);
+    }
+    // radix select, 12 bits per level, over (key - mn)
+    const uint32_t range = mx - mn;
+    const int bitlen = range == 0u ? 0 : 32 - __clz((int)range);
+    int lo = max(0, bitlen - kDigitBits), top = lo + kDigitBits;
+    uint32_t path = 0, above = 0;
+    for (;;) {
+      const int width = top - lo;
+      const uint32_t digit_mask = (1u << width) - 1u;
+      __syncthreads();
+      for (int b = tid; b < kBins; b += NT) sh.hist[b] = 0u;
+      __syncthreads();
+      for (int tile = 0; tile < ntiles; ++tile) {
+        if (ntiles > 1) stage_tile(a, u, sh, tile * kMergeTile, tile_n(tile));
+        const int n = tile_n(tile);
+#pragma unroll
+        for (int i = 0; i < kMergeTile / NT; ++i) {
+          const int j = i * NT + tid;
+          const uint32_t d = sh.key[min(j, n - 1)] - mn;
+          if (j < n && (top >= 32 || (d >> top) == path))
+            atomicAdd(&sh.hist[(d >> lo) & digit_mask], 1u);
+        }
+      }
+      __syncthreads();
+      constexpr int kPer = kBins / NT;
+      uint32_t cnt[kPer], mine = 0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        cnt[j] = sh.hist[tid * kPer + j];
+        mine += cnt[j];
+      }
+      uint32_t total;
+      const uint32_t above_mine = [&] {
+        const uint32_t incl = merge_scan(mine, sh, total);
+        return total - incl;
+      }();
+      const uint32_t rank = target - above;
+      if (above_mine < rank && rank <= above_mine + mine) {
+        uint32_t cum = above_mine;
+        for (int j = kPer - 1; j >= 0; --j) {
+          if (cum + cnt[j] >= rank) {
+            sh.pick[0] = (uint32_t)(tid * kPer + j);
+            sh.pick[1] = cum;
+            break;
+          }
+          cum += cnt[j];
+        }
+      }
+      __syncthreads();
+      const uint32_t bsel = sh.pick[0];
+      above += sh.pick[1];
+      path = (path << width) | bsel;
+      top = lo;
+      if (lo == 0) break;
+      lo = max(0, lo - kDigitBits);
+    }
+    t = mn + path;
+    need = target - above;
+  }
+
+  // ordered emission: register row i of thread (w, lane) is dense index
+  // i * NT + 64 w + lane, so (i, w, lane) order is ascending position order
+  uint32_t gt_base = 0, eq_base = 0;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    if (ntiles > 1) stage_tile(a, u, sh, tile * kMergeTile, tile_n(tile));
+    const int n = tile_n(tile);
+    constexpr int kRows = kMergeTile / NT;
+    const int rows = (n + NT - 1) / NT;             // <= kRows
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      const int j = i * NT + tid;
+      const uint32_t k = j < n ? sh.key[min(j, n - 1)] : 0u;
+      const uint64_t mg = ballot(k > t), me = ballot(j < n && k == t);
+      if (i < rows) sh.seg[i * W + w] = (uint32_t)popc64(mg) | ((uint32_t)popc64(me) << 16);
+    }
+    __syncthreads();
+    const uint32_t v = tid < rows * W ? sh.seg[tid] : 0u;
+    uint32_t total;
+    const uint32_t incl = merge_scan(v, sh, total);
+    if (tid < rows * W) sh.seg[tid] = incl - v;
+    __syncthreads();
+    const uint64_t lt = lanemask_lt();
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      if (i >= rows) break;                         // block-uniform
+      const int j = i * NT + tid;
+      const uint32_t k = j < n ? sh.key[min(j, n - 1)] : 0u;
+      const bool gt = k > t, eq = j < n && k == t;
+      const uint64_t mg = ballot(gt), me = ballot(eq);
+      const uint32_t pre = sh.seg[i * W + w];
+      const uint32_t gtb = gt_base + (pre & 0xFFFFu) + (uint32_t)popc64(mg & lt);
+      const uint32_t eqb = eq_base + (pre >> 16) + (uint32_t)popc64(me & lt);
+      if (gt) idx_u[gtb + min(eqb, need)] = sh.pos[j];
+      else if (eq && eqb < need) idx_u[gtb + eqb] = sh.pos[j];
+    }
+    gt_base += total & 0xFFFFu;
+    eq_base += total >> 16;
+    __syncthreads();
+  }
+  for (int slot = (int)target + tid; slot < M; slot += NT) idx_u[slot] = -1;
 }
 
-// One chunk of one unit: keys, chunk-local top-M, candidates, then the
-// last-arriving chunk workgroup of the unit merges.
-template <int D, int R, int KPT, bool FUSED, bool MULTI>
-__global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
-  __shared__ SelectShared sh;
+// One chunk of one unit: keys, chunk-local exact top-M, candidates out.
+// Key register i of thread (wave w, lane l) is position base + i*NT + 64w + l.
+template <int D, int R, int KPT, bool FUSED>
+__global__ __launch_bounds__(kChunkThreads, 4) void chunk_select_kernel(const SelectArgs a) {
+  constexpr int NT = kChunkThreads;
+  __shared__ SelectShared<NT> sh;
   const int u = blockIdx.x / a.S, c = blockIdx.x % a.S;
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
@@ -383,97 +687,103 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
   if (nv > 0) {                                   // block-uniform
     uint32_t key[KPT];
     if (FUSED) {
-      indexer_query<D, R>(a.q, a.P, b, h, a.G, a.Hq, sh.qt, sh.part);
+      // this chunk's rows only: loads past the valid positions return zero
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(a.kp + ((size_t)u * a.Ncap + base) * R, (uint32_t)nv * R);
+      // lane byte offset within one wave's 64 positions; r=32 lanes pair up
+      // on a position (first half of the wave's rows: +0, second: +1024)
+      const uint32_t voff = (uint32_t)(w * kWave * R + lane * 16);
+      constexpr int kLoadsPerIter = R / 16;
+      constexpr int kPerBatch = SA_CHUNK_LOADS_IN_FLIGHT / kLoadsPerIter;
+      constexpr int kBatch = (KPT < kPerBatch) ? KPT : kPerBatch;
+      uint4 ca[kBatch], cb[kBatch];
+      auto load_batch = [&](int i0) {
+#pragma unroll
+        for (int x = 0; x < kBatch; ++x) {
+          // the whole offset is in the lane offset: the hardware range check
+          // covers the vector and immediate offsets, not the scalar one
+          const uint32_t off = voff + (uint32_t)((i0 + x) * NT * R);
+          ca[x] = buffer_load16(rs, off, 0);
+          if (R == 32) cb[x] = buffer_load16(rs, off + 1024, 0);
+        }
+      };
+      // the first batch is in flight while the indexer query is formed
+      load_batch(0);
+      indexer_query<D, R, NT>(a.q, a.P, b, h, a.G, a.Hq, sh.qt, sh.part);
       float ql[16];
       lane_query<R>(sh.qt, ql);
-      const uint8_t* kpu = a.kp + (size_t)u * a.Ncap * R;
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int p = base + i * kBlock + w * kWave + lane;
-        if (R == 16) {
-          uint4 cc = make_uint4(0, 0, 0, 0);
-          if (p < len) cc = load16(kpu + (size_t)p * 16);
-          const float s = lane_score<R>(ql, cc);
-          key[i] = p < len ? score_key(s + 0.0f) : 0u;
-        } else {
-          const int p0 = base + i * kBlock + w * kWave;
-          const int pa = p0 + (lane >> 1), pb = pa + 32;
-          uint4 ca = make_uint4(0, 0, 0, 0), cb = make_uint4(0, 0, 0, 0);
-          if (pa < len) ca = load16(kpu + (size_t)p0 * 32 + lane * 16);
-          if (pb < len) cb = load16(kpu + (size_t)p0 * 32 + 1024 + lane * 16);
-          const float sa = lane_score<R>(ql, ca);
-          const float sb = lane_score<R>(ql, cb);
-          // lane l takes position p0 + l: from lane 2l of the first half
-          // (l < 32) or lane 2(l-32)+1 of the second
-          const float x = (lane & 1) ? sb : sa;
-          const int src = (lane < 32) ? 2 * lane : 2 * (lane - 32) + 1;
-          const float s = __shfl(x, src, kWave);
+      for (int i0 = 0; i0 < KPT; i0 += kBatch) {
+        if (i0 > 0) load_batch(i0);
+#pragma unroll
+        for (int x = 0; x < kBatch; ++x) {
+          const int i = i0 + x;
+          const int p = base + i * NT + w * kWave + lane;
+          float s;
+          if (R == 16) {
+            s = lane_score<R>(ql, ca[x]);
+          } else {
+            const float sa = lane_score<R>(ql, ca[x]);
+            const float sb = lane_score<R>(ql, cb[x]);
+            // lane l takes position p0 + l: from lane 2l of the first half
+            // (l < 32) or lane 2(l-32)+1 of the second
+            const float xv = (lane & 1) ? sb : sa;
+            const int src = (lane < 32) ? 2 * lane : 2 * (lane - 32) + 1;
+            s = __shfl(xv, src, kWave);
+          }
           key[i] = p < len ? score_key(s + 0.0f) : 0u;
         }
       }
     } else {
-      const float* su = a.scores + (size_t)u * a.n_max;
+      const float* su = a.scores + (size_t)u * a.n_max + base;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(su, (uint32_t)nv * 4u);
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
-        const int p = base + i * kBlock + w * kWave + lane;
-        key[i] = p < len ? score_key(su[p] + 0.0f) : 0u;
+        const int p = base + i * NT + w * kWave + lane;
+        const float sv = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rs, (i * NT + w * kWave + lane) * 4, 0, 0));
+        key[i] = p < len ? score_key(sv + 0.0f) : 0u;
       }
     }
 
     uint32_t t = 0, need = 0;
     if (nv > a.M) {
-      int ph = 0;
-      uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-      thread_key_range(key, mn, mx);
-      block_key_range(mn, mx, sh, mn, mx);
-      const uint32_t target = (uint32_t)a.M;
-      t = find_threshold([&](uint32_t x) { return count_ge(key, x, sh, ph); }, mn, mx, target);
-      const uint32_t gt = (t == 0xFFFFFFFFu) ? 0u : count_ge(key, t + 1, sh, ph);
-      need = target - gt;
+      radix_threshold(key, (uint32_t)a.M, sh, t, need);
       nsel = a.M;
     } else {
       nsel = nv;
     }
-    uint32_t* ck = a.cand_key + ((size_t)u * a.S + c) * a.mc;
-    int32_t* cp = a.cand_pos + ((size_t)u * a.S + c) * a.mc;
+    uint32_t* ck = a.cand_key + ((size_t)u * a.S + c) * a.ms;
+    int32_t* cp = a.cand_pos + ((size_t)u * a.S + c) * a.ms;
     emit_in_order(key, t, need, 0, 0, sh, [&](int i, uint32_t slot) {
       ck[slot] = key[i];
-      cp[slot] = base + i * kBlock + w * kWave + lane;
+      cp[slot] = base + i * NT + w * kWave + lane;
     });
   }
   if (tid == 0) a.cand_cnt[(size_t)u * a.S + c] = nsel;
-
-  // last workgroup of the unit to arrive merges
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) sh.flag = (atomicAdd(&a.counters[u], 1u) == (uint32_t)(a.S - 1)) ? 1u : 0u;
-  __syncthreads();
-  if (!sh.flag) return;
-  __threadfence();
-  if (tid == 0) atomicExch(&a.counters[u], 0u);
-  merge_unit<MULTI>(a, u, sh);
 }
 
-template <int D, int R, bool FUSED, bool MULTI>
-static void launch_select_kpt(const SelectArgs& a, int kpt, dim3 grid, hipStream_t st) {
+template <int D, int R, bool FUSED>
+static void launch_chunks_kpt(const SelectArgs& a, int kpt, dim3 grid, hipStream_t st) {
   switch (kpt) {
 #define SA_CASE(K)                                                                         \
   case K:                                                                                  \
-    hipLaunchKernelGGL((select_kernel<D, R, K, FUSED, MULTI>), grid, dim3(kBlock), 0, st, a); \
+    hipLaunchKernelGGL((chunk_select_kernel<D, R, K, FUSED>), grid, dim3(kChunkThreads), 0, \
+                       st, a);                                                             \
     break;
-    SA_CASE(1) SA_CASE(2) SA_CASE(4) SA_CASE(8) SA_CASE(16) SA_CASE(32) SA_CASE(64)
+    SA_CASE(1) SA_CASE(2) SA_CASE(4) SA_CASE(8) SA_CASE(16) SA_CASE(32)
 #undef SA_CASE
     default: break;
   }
 }
 
-template <bool FUSED, bool MULTI>
-static void launch_select_shape(const LaunchCommon& c, const SelectArgs& a, int kpt, dim3 grid) {
-  if (!FUSED) { launch_select_kpt<64, 16, false, MULTI>(a, kpt, grid, c.stream); return; }
-  if (c.D == 128 && c.R == 32) launch_select_kpt<128, 32, true, MULTI>(a, kpt, grid, c.stream);
-  else if (c.D == 128 && c.R == 16) launch_select_kpt<128, 16, true, MULTI>(a, kpt, grid, c.stream);
-  else if (c.D == 64 && c.R == 32) launch_select_kpt<64, 32, true, MULTI>(a, kpt, grid, c.stream);
-  else launch_select_kpt<64, 16, true, MULTI>(a, kpt, grid, c.stream);
+template <bool FUSED>
+static void launch_chunks(const LaunchCommon& c, const SelectArgs& a, int kpt, dim3 grid) {
+  if (!FUSED) { launch_chunks_kpt<64, 16, false>(a, kpt, grid, c.stream); return; }
+  if (c.D == 128 && c.R == 32) launch_chunks_kpt<128, 32, true>(a, kpt, grid, c.stream);
+  else if (c.D == 128 && c.R == 16) launch_chunks_kpt<128, 16, true>(a, kpt, grid, c.stream);
+  else if (c.D == 64 && c.R == 32) launch_chunks_kpt<64, 32, true>(a, kpt, grid, c.stream);
+  else launch_chunks_kpt<64, 16, true>(a, kpt, grid, c.stream);
 }
 
 hipError_t run_select(const LaunchCommon& c, const TopmPlan& plan, bool fused, const void* q,
@@ -494,23 +804,20 @@ hipError_t run_select(const LaunchCommon& c, const TopmPlan& plan, bool fused, c
   a.M = M;
   a.S = plan.splits;
   a.chunk = plan.chunk;
-  a.mc = plan.mc;
+  a.ms = plan.ms;
   char* ws = (char*)workspace;
-  a.counters = (uint32_t*)ws;
   a.cand_cnt = (int32_t*)(ws + plan.off_cnt);
   a.cand_key = (uint32_t*)(ws + plan.off_key);
   a.cand_pos = (int32_t*)(ws + plan.off_pos);
   a.idx = idx;
   const long blocks = (long)plan.units * plan.splits;
   if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)blocks);
-  if (fused) {
-    if (plan.multi_tile) launch_select_shape<true, true>(c, a, plan.kpt, grid);
-    else launch_select_shape<true, false>(c, a, plan.kpt, grid);
-  } else {
-    if (plan.multi_tile) launch_select_shape<false, true>(c, a, plan.kpt, grid);
-    else launch_select_shape<false, false>(c, a, plan.kpt, grid);
-  }
+  if (fused) launch_chunks<true>(c, a, plan.kpt, dim3((unsigned)blocks));
+  else launch_chunks<false>(c, a, plan.kpt, dim3((unsigned)blocks));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the kernel boundary orders the candidate writes before the merge's reads
+  hipLaunchKernelGGL(merge_kernel, dim3(plan.units), dim3(kMergeThreads), 0, c.stream, a);
   return hipGetLastError();
 }
 

@@ -32,6 +32,5 @@ hipError_t run_decode(const LaunchCommon& c, const DecodePlan& plan, const void*
 hipError_t run_linear_gate(const LaunchCommon& c, const void* q, const void* k_new,
                            const void* v_new, float* S, float* z, const float* w_gate,
                            const void* o_sparse, void* out, int update_state);
-hipError_t run_zero_u32(uint32_t* p, size_t n, hipStream_t stream);
 
 }  // namespace sa

@@ -130,17 +130,4 @@ hipError_t run_linear_gate(const LaunchCommon& c, const void* q, const void* k_n
   return hipGetLastError();
 }
 
-// Zero n uint32 words (a plain fill kernel, safe inside captured graphs).
-__global__ void zero_u32_kernel(uint32_t* p, size_t n) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
-
-hipError_t run_zero_u32(uint32_t* p, size_t n, hipStream_t stream) {
-  if (n == 0) return hipSuccess;
-  const size_t blocks = (n + kBlock - 1) / kBlock;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, p, n);
-  return hipGetLastError();
-}
-
 }  // namespace sa

@@ -191,9 +191,6 @@ def test_topm_fused_and_unfused_match_oracle(name):
     sa.sparse_attn_index_score(sh, qd, Pd, kpd, sl, n_max, scores)
     sa.sparse_attn_topm(sh, scores, sl, n_max, M, idx_u, ws)
     sa.sparse_attn_index_topm(sh, qd, Pd, kpd, sl, n_max, M, idx_f, ws)
-    # the workspace counters are back at zero after each call
-    nctr = sa.sparse_attn_workspace_counter_bytes(sh)
-    assert int(ws[:nctr].sum().item()) == 0
     gu, gf = idx_u.cpu().numpy(), idx_f.cpu().numpy()
     assert np.array_equal(gu, gf), "fused and unfused index sets differ"
     G = Hq // Hkv

@@ -175,11 +175,16 @@ struct SelectArgs {
 
 // 16-byte loads each lane keeps in flight while scoring (tuning knob)
 #ifndef SA_CHUNK_LOADS_IN_FLIGHT
-#define SA_CHUNK_LOADS_IN_FLIGHT 16
+#define SA_CHUNK_LOADS_IN_FLIGHT 8
 #endif
 
+// Radix digits of the 32-bit keys, most significant first: [20, 32) holds the
+// sign, exponent and top 3 mantissa bits of the score; then [8, 20), [0, 8).
 constexpr int kDigitBits = 12;
-constexpr int kBins = 1 << kDigitBits;      // radix-select histogram bins
+constexpr int kBins = 1 << kDigitBits;      // histogram bins per level
+constexpr int kTopShift = 32 - kDigitBits;  // first-level digit = key >> 20
+constexpr int kListCap = 4096;              // threshold-bin keys kept in LDS (chunks)
+constexpr int kMergeListCap = 1024;         // (merge: its LDS is nearly full)
 constexpr int kChunkThreads = kChunkBlock;  // chunk workgroups: 8 waves
 constexpr int kMergeThreads = 1024;         // merge workgroups: 16 waves
 
@@ -188,19 +193,18 @@ struct SelectShared {
   static constexpr int W = NT / kWave;
   float qt[32];
   double part[NT];
-  uint32_t red[2][W];
-  uint32_t mnmx[2][W];
   uint32_t seg[NT];
   uint32_t wtot[W];
   uint32_t pick[2];
+  uint32_t list_n;
   uint32_t hist[kBins + kWave];   // + one private dummy bin per lane
+  static constexpr int kCap = kListCap;
+  uint32_t list[kCap];
 };
 
-
 // Inclusive prefix sum over the block in thread order; `total` gets the sum.
-template <int NT>
-__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, SelectShared<NT>& sh,
-                                                         uint32_t& total) {
+template <int NT, class Sh>
+__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, Sh& sh, uint32_t& total) {
   constexpr int W = NT / kWave;
   const int w = threadIdx.x / kWave;
   const uint32_t inc = wave_inclusive_scan(v);
@@ -217,69 +221,105 @@ __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, SelectShare
   return wb + inc;
 }
 
-// Number of keys >= t over the block (every thread receives it).
-template <int NT, int K>
-__device__ __forceinline__ uint32_t count_ge(const uint32_t (&key)[K], uint32_t t,
-                                             SelectShared<NT>& sh, int& ph) {
-  constexpr int W = NT / kWave;
-  uint32_t c = 0;
+// With the current level's histogram in sh.hist (bins of keys on `path`),
+// find the bin holding the key of 1-based rank target - above counted from the
+// top; above += keys in higher bins; path gains the bin as its low digit.
+template <int NT, class Sh>
+__device__ void pick_bin(Sh& sh, int width, uint32_t target, uint32_t& path, uint32_t& above) {
+  constexpr int kPer = kBins / NT;
+  const int tid = threadIdx.x;
+  uint32_t c[kPer];
+  uint32_t mine = 0;
 #pragma unroll
-  for (int i = 0; i < K; ++i) c += (uint32_t)popc64(ballot(key[i] >= t));
-  sh.red[ph][threadIdx.x / kWave] = c;
+  for (int j = 0; j < kPer; ++j) {
+    c[j] = sh.hist[tid * kPer + j];
+    mine += c[j];
+  }
+  uint32_t total;
+  const uint32_t incl = block_inclusive_scan<NT>(mine, sh, total);
+  const uint32_t above_mine = total - incl;          // bins owned by higher threads
+  const uint32_t rank = target - above;
+  if (above_mine < rank && rank <= above_mine + mine) {
+    uint32_t cum = above_mine;
+#pragma unroll
+    for (int j = kPer - 1; j >= 0; --j) {
+      if (cum + c[j] >= rank) {
+        sh.pick[0] = (uint32_t)(tid * kPer + j);
+        sh.pick[1] = cum;
+        break;
+      }
+      cum += c[j];
+    }
+  }
   __syncthreads();
-  uint32_t tot = 0;
-#pragma unroll
-  for (int ww = 0; ww < W; ++ww) tot += sh.red[ph][ww];
-  ph ^= 1;
-  return tot;
+  const uint32_t b = sh.pick[0];
+  above += sh.pick[1];
+  __syncthreads();
+  path = (path << width) | b;
 }
 
-// Block-wide min over nonzero keys and max over all keys.
-template <int NT>
-__device__ __forceinline__ void block_key_range(uint32_t mn, uint32_t mx, SelectShared<NT>& sh,
-                                                uint32_t& omn, uint32_t& omx) {
-  constexpr int W = NT / kWave;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, kWave));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, kWave));
-  }
-  const int w = threadIdx.x / kWave;
+// One radix level over keys produced by `visit(f)`, which calls f(key, valid)
+// for each key this thread owns.  Keys off `path` (and invalid ones) count
+// into the lane's private dummy bin so the atomics need no branch.
+template <int NT, class Sh, class Visit>
+__device__ void radix_level(Sh& sh, int top, int lo, uint32_t target, uint32_t& path,
+                            uint32_t& above, Visit visit) {
+  const int width = top - lo;
+  const uint32_t digit_mask = (1u << width) - 1u;
+  for (int b = threadIdx.x; b < kBins + kWave; b += NT) sh.hist[b] = 0u;
   __syncthreads();
-  sh.mnmx[0][w] = mn;
-  sh.mnmx[1][w] = mx;
+  const uint32_t dummy = (uint32_t)(kBins + lane_id());
+  // an opaque copy stops the compiler from keeping per-key masks alive
+  uint32_t pth = path;
+  asm volatile("" : "+v"(pth));
+  visit([&](uint32_t k, bool valid) {
+    const bool on = valid && (top >= 32 || (k >> top) == pth);
+    atomicAdd(&sh.hist[on ? ((k >> lo) & digit_mask) : dummy], 1u);
+  });
   __syncthreads();
-  uint32_t a = 0xFFFFFFFFu, b = 0u;
-#pragma unroll
-  for (int ww = 0; ww < W; ++ww) {
-    a = min(a, sh.mnmx[0][ww]);
-    b = max(b, sh.mnmx[1][ww]);
-  }
-  omn = a;
-  omx = b;
+  pick_bin<NT>(sh, width, target, path, above);
 }
 
-template <int K>
-__device__ __forceinline__ void thread_key_range(const uint32_t (&key)[K], uint32_t& mn,
-                                                 uint32_t& mx) {
-#pragma unroll
-  for (int i = 0; i < K; ++i) {
-    mn = key[i] ? min(mn, key[i]) : mn;
-    mx = max(mx, key[i]);
+// Levels 2 and 3 of the exact threshold search.  The first-level histogram
+// (digit key >> 20) is already in sh.hist.  Keys of the chosen first-level bin
+// are compacted into an LDS list (usually ~1% of the keys) and resolved
+// there; if the bin is too large, the remaining levels run over `visit`.
+// Returns t (the target-th largest key) and need = target - #keys > t.
+template <int NT, class Sh, class Visit>
+__device__ void finish_threshold(Sh& sh, uint32_t target, uint32_t& t_out, uint32_t& need_out,
+                                 Visit visit) {
+  const int tid = threadIdx.x, lane = lane_id();
+  uint32_t path = 0, above = 0;
+  pick_bin<NT>(sh, kDigitBits, target, path, above);
+  const uint32_t b1 = path;
+  if (tid == 0) sh.list_n = 0u;
+  __syncthreads();
+  const uint64_t lt = lanemask_lt();
+  visit([&](uint32_t k, bool valid) {
+    const bool in = valid && (k >> kTopShift) == b1;
+    const uint64_t m = ballot(in);
+    if (m) {                                        // wave-uniform
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&sh.list_n, (uint32_t)popc64(m));
+      base = (uint32_t)__shfl((int)base, 0, kWave);
+      const uint32_t slot = base + (uint32_t)popc64(m & lt);
+      if (in && slot < (uint32_t)Sh::kCap) sh.list[slot] = k;
+    }
+  });
+  __syncthreads();
+  const uint32_t n = sh.list_n;
+  if (n <= (uint32_t)Sh::kCap) {
+    auto list_visit = [&](auto&& f) {
+      for (uint32_t j = tid; j < n; j += NT) f(sh.list[j], true);
+    };
+    radix_level<NT>(sh, kTopShift, 8, target, path, above, list_visit);
+    radix_level<NT>(sh, 8, 0, target, path, above, list_visit);
+  } else {
+    radix_level<NT>(sh, kTopShift, 8, target, path, above, visit);
+    radix_level<NT>(sh, 8, 0, target, path, above, visit);
   }
-}
-
-// Largest t with count(key >= t) >= target, given count(key >= lo) >= target
-// and hi = the largest key.  `cnt(t)` is a block-uniform count.
-template <class CountFn>
-__device__ __forceinline__ uint32_t find_threshold(CountFn cnt, uint32_t lo, uint32_t hi,
-                                                   uint32_t target) {
-  if (cnt(hi) >= target) return hi;
-  while (hi - lo > 1) {
-    const uint32_t mid = lo + ((hi - lo) >> 1);
-    if (cnt(mid) >= target) lo = mid; else hi = mid;
-  }
-  return lo;
+  t_out = path;
+  need_out = target - above;
 }
 
 // Emit, in register order (i, wave, lane) -- which callers make equal to
@@ -293,7 +333,7 @@ __device__ __forceinline__ uint32_t emit_in_order(const uint32_t (&key)[K], uint
                                                   EmitFn emit) {
   constexpr int W = NT / kWave;
   static_assert(K * W <= NT, "segments");
-  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  const int tid = threadIdx.x, w = tid / kWave;
 #pragma unroll
   for (int i = 0; i < K; ++i) {
     const uint64_t mg = ballot(key[i] > t), me = ballot(key[i] == t);
@@ -303,7 +343,7 @@ __device__ __forceinline__ uint32_t emit_in_order(const uint32_t (&key)[K], uint
   __syncthreads();
   const uint32_t v = tid < K * W ? sh.seg[tid] : 0u;
   uint32_t total;
-  const uint32_t incl = block_inclusive_scan(v, sh, total);
+  const uint32_t incl = block_inclusive_scan<NT>(v, sh, total);
   if (tid < K * W) sh.seg[tid] = incl - v;
   __syncthreads();
   const uint64_t lt = lanemask_lt();
@@ -324,120 +364,25 @@ __device__ __forceinline__ uint32_t emit_in_order(const uint32_t (&key)[K], uint
   return total;
 }
 
-// Exact selection threshold by radix select on register keys.
-//
-// Keys are the block's nonzero register keys (0 = empty) and 1 <= target <=
-// their number.  Returns t = the target-th largest key and need = how many
-// keys equal to t belong to the selection (target - #keys > t).  Offsets
-// d = key - min are resolved 12 bits at a time from the top of the occupied
-// range (at most three levels for 32-bit keys): histogram the digit of the
-// keys still on the chosen path in LDS, then pick the bin where the count
-// from the top reaches the target.  Exact for any key distribution.
-template <int NT, int K>
-__device__ void radix_threshold(const uint32_t (&key)[K], uint32_t target, SelectShared<NT>& sh,
-                                uint32_t& t_out, uint32_t& need_out) {
-  const int tid = threadIdx.x;
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  thread_key_range(key, mn, mx);
-  block_key_range(mn, mx, sh, mn, mx);
-  const uint32_t range = mx - mn;
-  const int bitlen = range == 0u ? 0 : 32 - __clz((int)range);
-  int lo = max(0, bitlen - kDigitBits);   // lowest bit of the current digit
-  int top = lo + kDigitBits;              // bits >= top are fixed by `path`
-  uint32_t path = 0;                      // chosen high part of d (d >> top)
-  uint32_t above = 0;                     // keys strictly above the chosen bins
-  for (;;) {
-    const int width = top - lo;
-    for (int b = tid; b < kBins + kWave; b += NT) sh.hist[b] = 0u;
-    __syncthreads();
-    // Offsets are re-derived per level from an opaque copy of the minimum so
-    // the compiler keeps no per-key masks alive across levels; keys off the
-    // path (and empty keys, whose offset wraps above the range) count into
-    // this lane's private dummy bin, so the atomics need no branch.
-    uint32_t base = mn;
-    asm volatile("" : "+v"(base));
-    const uint32_t dummy = (uint32_t)(kBins + lane_id());
-    const uint32_t digit_mask = (1u << width) - 1u;
-#pragma unroll
-    for (int i = 0; i < K; ++i) {
-      const uint32_t d = key[i] - base;
-      const bool on_path = d <= range && (top >= 32 || (d >> top) == path);
-      atomicAdd(&sh.hist[on_path ? ((d >> lo) & digit_mask) : dummy], 1u);
-    }
-    __syncthreads();
-    // thread t owns bins [kPer*t, kPer*(t+1)); counts run from the top
-    constexpr int kPer = kBins / NT;
-    uint32_t c[kPer];
-    uint32_t mine = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      c[j] = sh.hist[tid * kPer + j];
-      mine += c[j];
-    }
-    uint32_t total;
-    const uint32_t incl = block_inclusive_scan(mine, sh, total);
-    const uint32_t above_mine = total - incl;          // bins owned by higher threads
-    const uint32_t rank = target - above;               // 1-based rank on this path
-    if (above_mine < rank && rank <= above_mine + mine) {
-      uint32_t cum = above_mine;
-#pragma unroll
-      for (int j = kPer - 1; j >= 0; --j) {
-        if (cum + c[j] >= rank) {
-          sh.pick[0] = (uint32_t)(tid * kPer + j);
-          sh.pick[1] = cum;
-          break;
-        }
-        cum += c[j];
-      }
-    }
-    __syncthreads();
-    const uint32_t b = sh.pick[0];
-    above += sh.pick[1];
-    __syncthreads();
-    path = (path << width) | b;
-    top = lo;
-    if (lo == 0) break;
-    lo = max(0, lo - kDigitBits);
-  }
-  t_out = mn + path;
-  need_out = target - above;
-}
-
 // ------------------------------------------------------------------ merge
 
 // A unit's valid chunk candidates are compacted, in chunk order, into a dense
 // LDS tile of up to kMergeTile (key, position) pairs -- 128 KB of gfx950's
-// 160 KB -- so every pass below is a short rolled loop over LDS (the merge
-// runs once per unit, so compact code matters more than unrolling).  Dense
-// index order equals ascending position order.  Units with more valid
-// candidates than one tile re-stage each tile per pass.
+// 160 KB -- so every pass below is a short loop over LDS.  Dense index order
+// equals ascending position order.  Units with more valid candidates than one
+// tile re-stage each tile per pass.
 struct MergeLds {
   uint32_t key[kMergeTile];
   int32_t pos[kMergeTile];
   uint32_t hist[kBins + kWave];
+  static constexpr int kCap = kMergeListCap;
+  uint32_t list[kCap];
   int32_t off[kMaxSplits + 1];   // dense offset of each chunk's candidates
   uint32_t seg[kMergeThreads];
   uint32_t wtot[kMergeThreads / kWave];
-  uint32_t mnmx[2][kMergeThreads / kWave];
   uint32_t pick[2];
+  uint32_t list_n;
 };
-
-__device__ __forceinline__ uint32_t merge_scan(uint32_t v, MergeLds& sh, uint32_t& total) {
-  constexpr int W = kMergeThreads / kWave;
-  const int w = threadIdx.x / kWave;
-  const uint32_t inc = wave_inclusive_scan(v);
-  __syncthreads();
-  if (lane_id() == kWave - 1) sh.wtot[w] = inc;
-  __syncthreads();
-  uint32_t wb = 0, tot = 0;
-#pragma unroll
-  for (int ww = 0; ww < W; ++ww) {
-    wb += ww < w ? sh.wtot[ww] : 0u;
-    tot += sh.wtot[ww];
-  }
-  total = tot;
-  return wb + inc;
-}
 
 // Copy dense candidates [d0, d0 + n) of unit u into the LDS tile.
 __device__ void stage_tile(const SelectArgs& a, int u, MergeLds& sh, int d0, int n) {
@@ -445,7 +390,6 @@ __device__ void stage_tile(const SelectArgs& a, int u, MergeLds& sh, int d0, int
   const uint32_t* ck = a.cand_key + (size_t)u * a.S * a.ms;
   const int32_t* cp = a.cand_pos + (size_t)u * a.S * a.ms;
   __syncthreads();
-  // first chunk overlapping the tile (off[] is ascending)
   int s = 0;
   {
     int lo = 0, hi = a.S;              // largest s with off[s] <= d0
@@ -470,10 +414,13 @@ __device__ void stage_tile(const SelectArgs& a, int u, MergeLds& sh, int d0, int
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const SelectArgs a) {
   constexpr int NT = kMergeThreads;
   constexpr int W = NT / kWave;
+  constexpr int kRows = kMergeTile / NT;
   __shared__ MergeLds sh;
   const int u = blockIdx.x;
-  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  const int tid = threadIdx.x, w = tid / kWave;
   const int S = a.S, M = a.M;
+
+  for (int b = tid; b < kBins + kWave; b += NT) sh.hist[b] = 0u;
 
   // dense offsets of the chunks' candidate lists (exclusive scan of counts)
   const int spt = (S + NT - 1) / NT;    // chunks per thread, contiguous
@@ -483,7 +430,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const SelectArgs a
     if (s < S) my += (uint32_t)a.cand_cnt[(size_t)u * S + s];
   }
   uint32_t nvalid;
-  uint32_t run = merge_scan(my, sh, nvalid) - my;
+  uint32_t run = block_inclusive_scan<NT>(my, sh, nvalid) - my;
   for (int j = 0; j < spt; ++j) {
     const int s = tid * spt + j;
     if (s < S) {
@@ -498,6 +445,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const SelectArgs a
   const uint32_t target = min(nvalid, (uint32_t)M);
   const int ntiles = ((int)nvalid + kMergeTile - 1) / kMergeTile;
   auto tile_n = [&](int tile) { return min((int)nvalid - tile * kMergeTile, kMergeTile); };
+  const bool select = nvalid > (uint32_t)M;
+  const uint32_t dummy = (uint32_t)(kBins + lane_id());
+
+  // stage (single tile) and build the first-level histogram on the way
   if (ntiles == 1) {
     const int flat_n = S * a.ms;
     if (flat_n <= kMergeTile) {
@@ -525,116 +476,65 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const SelectArgs a
         sc -= (sc * ms > f) ? 1 : 0;
         sc += ((sc + 1) * ms <= f) ? 1 : 0;
         const int slot = f - sc * ms;
-        if (f < flat_n && sc < S && slot < sh.off[sc + 1] - sh.off[sc]) {
+        const bool valid = f < flat_n && sc < S && slot < sh.off[sc + 1] - sh.off[sc];
+        if (valid) {
           const int d = sh.off[sc] + slot;
           sh.key[d] = kv[i];
           sh.pos[d] = pv[i];
         }
+        if (select) atomicAdd(&sh.hist[valid ? (kv[i] >> kTopShift) : dummy], 1u);
       }
       __syncthreads();
     } else {
       stage_tile(a, u, sh, 0, (int)nvalid);
+      if (select) {
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+          const int j = i * NT + tid;
+          atomicAdd(&sh.hist[j < (int)nvalid ? (sh.key[j] >> kTopShift) : dummy], 1u);
+        }
+        __syncthreads();
+      }
     }
+  } else if (select) {
+    for (int tile = 0; tile < ntiles; ++tile) {
+      stage_tile(a, u, sh, tile * kMergeTile, tile_n(tile));
+      const int n = tile_n(tile);
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) {
+        const int j = i * NT + tid;
+        atomicAdd(&sh.hist[j < n ? (sh.key[j] >> kTopShift) : dummy], 1u);
+      }
+    }
+    __syncthreads();
   }
 
   uint32_t t = 0, need = 0;
-  if (nvalid > (uint32_t)M) {
-    // key range
-    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-    for (int tile = 0; tile < ntiles; ++tile) {
-      if (ntiles > 1) stage_tile(a, u, sh, tile * kMergeTile, tile_n(tile));
-      const int n = tile_n(tile);
-#pragma unroll
-      for (int i = 0; i < kMergeTile / NT; ++i) {
-        const int j = i * NT + tid;
-        if (j < n) {
-          mn = min(mn, sh.key[j]);
-          mx = max(mx, sh.key[j]);
-        }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
-      mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
-    }
-    __syncthreads();
-    sh.mnmx[0][w] = mn;
-    sh.mnmx[1][w] = mx;
-    __syncthreads();
-    mn = 0xFFFFFFFFu;
-    mx = 0u;
-#pragma unroll
-    for (int ww = 0; ww < W; ++ww) {
-      mn = min(mn, sh.mnmx[0][ww]);
-      mx = max(mx, sh.mnmx[1][ww]);
-    }
-    // radix select, 12 bits per level, over (key - mn)
-    const uint32_t range = mx - mn;
-    const int bitlen = range == 0u ? 0 : 32 - __clz((int)range);
-    int lo = max(0, bitlen - kDigitBits), top = lo + kDigitBits;
-    uint32_t path = 0, above = 0;
-    for (;;) {
-      const int width = top - lo;
-      const uint32_t digit_mask = (1u << width) - 1u;
-      __syncthreads();
-      for (int b = tid; b < kBins; b += NT) sh.hist[b] = 0u;
-      __syncthreads();
+  if (select) {
+    auto visit_all = [&](auto&& f) {
       for (int tile = 0; tile < ntiles; ++tile) {
         if (ntiles > 1) stage_tile(a, u, sh, tile * kMergeTile, tile_n(tile));
         const int n = tile_n(tile);
 #pragma unroll
-        for (int i = 0; i < kMergeTile / NT; ++i) {
+        for (int i = 0; i < kRows; ++i) {
           const int j = i * NT + tid;
-          const uint32_t d = sh.key[min(j, n - 1)] - mn;
-          if (j < n && (top >= 32 || (d >> top) == path))
-            atomicAdd(&sh.hist[(d >> lo) & digit_mask], 1u);
+          f(sh.key[min(j, n - 1)], j < n);
         }
       }
-      __syncthreads();
-      constexpr int kPer = kBins / NT;
-      uint32_t cnt[kPer], mine = 0;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        cnt[j] = sh.hist[tid * kPer + j];
-        mine += cnt[j];
-      }
-      uint32_t total;
-      const uint32_t above_mine = [&] {
-        const uint32_t incl = merge_scan(mine, sh, total);
-        return total - incl;
-      }();
-      const uint32_t rank = target - above;
-      if (above_mine < rank && rank <= above_mine + mine) {
-        uint32_t cum = above_mine;
-        for (int j = kPer - 1; j >= 0; --j) {
-          if (cum + cnt[j] >= rank) {
-            sh.pick[0] = (uint32_t)(tid * kPer + j);
-            sh.pick[1] = cum;
-            break;
-          }
-          cum += cnt[j];
-        }
-      }
-      __syncthreads();
-      const uint32_t bsel = sh.pick[0];
-      above += sh.pick[1];
-      path = (path << width) | bsel;
-      top = lo;
-      if (lo == 0) break;
-      lo = max(0, lo - kDigitBits);
-    }
-    t = mn + path;
-    need = target - above;
+    };
+    finish_threshold<NT>(sh, target, t, need, visit_all);
   }
 
-  // ordered emission: register row i of thread (w, lane) is dense index
-  // i * NT + 64 w + lane, so (i, w, lane) order is ascending position order
+  // ordered emission: row i of thread (w, lane) is dense index i*NT + 64w + lane.
+  // Output slots are staged in LDS (the histogram region is free now) when
+  // they fit, then written with contiguous stores.
+  const bool staged = target <= (uint32_t)(kBins + kWave);
+  int32_t* out = staged ? reinterpret_cast<int32_t*>(sh.hist) : idx_u;
+  __syncthreads();
   uint32_t gt_base = 0, eq_base = 0;
   for (int tile = 0; tile < ntiles; ++tile) {
     if (ntiles > 1) stage_tile(a, u, sh, tile * kMergeTile, tile_n(tile));
     const int n = tile_n(tile);
-    constexpr int kRows = kMergeTile / NT;
     const int rows = (n + NT - 1) / NT;             // <= kRows
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
@@ -646,7 +546,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const SelectArgs a
     __syncthreads();
     const uint32_t v = tid < rows * W ? sh.seg[tid] : 0u;
     uint32_t total;
-    const uint32_t incl = merge_scan(v, sh, total);
+    const uint32_t incl = block_inclusive_scan<NT>(v, sh, total);
     if (tid < rows * W) sh.seg[tid] = incl - v;
     __syncthreads();
     const uint64_t lt = lanemask_lt();
@@ -660,18 +560,24 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const SelectArgs a
       const uint32_t pre = sh.seg[i * W + w];
       const uint32_t gtb = gt_base + (pre & 0xFFFFu) + (uint32_t)popc64(mg & lt);
       const uint32_t eqb = eq_base + (pre >> 16) + (uint32_t)popc64(me & lt);
-      if (gt) idx_u[gtb + min(eqb, need)] = sh.pos[j];
-      else if (eq && eqb < need) idx_u[gtb + eqb] = sh.pos[j];
+      if (gt) out[gtb + min(eqb, need)] = sh.pos[j];
+      else if (eq && eqb < need) out[gtb + eqb] = sh.pos[j];
     }
     gt_base += total & 0xFFFFu;
     eq_base += total >> 16;
     __syncthreads();
   }
+  if (staged)
+    for (int slot = tid; slot < (int)target; slot += NT) idx_u[slot] = out[slot];
   for (int slot = (int)target + tid; slot < M; slot += NT) idx_u[slot] = -1;
 }
 
+// ------------------------------------------------------------------ chunks
+
 // One chunk of one unit: keys, chunk-local exact top-M, candidates out.
 // Key register i of thread (wave w, lane l) is position base + i*NT + 64w + l.
+// The first-level radix histogram is built while the keys are produced, so
+// it hides under the memory stream.
 template <int D, int R, int KPT, bool FUSED>
 __global__ __launch_bounds__(kChunkThreads, 4) void chunk_select_kernel(const SelectArgs a) {
   constexpr int NT = kChunkThreads;
@@ -682,9 +588,12 @@ __global__ __launch_bounds__(kChunkThreads, 4) void chunk_select_kernel(const Se
   const int len = a.seq_lens ? min(max(a.seq_lens[b], 0), a.n_max) : a.n_max;
   const int base = c * a.chunk;
   const int nv = min(max(len - base, 0), a.chunk);
+  const bool select = nv > a.M;
+  const uint32_t dummy = (uint32_t)(kBins + lane);
   int nsel = 0;
 
   if (nv > 0) {                                   // block-uniform
+    for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
     uint32_t key[KPT];
     if (FUSED) {
       // this chunk's rows only: loads past the valid positions return zero
@@ -707,7 +616,8 @@ __global__ __launch_bounds__(kChunkThreads, 4) void chunk_select_kernel(const Se
           if (R == 32) cb[x] = buffer_load16(rs, off + 1024, 0);
         }
       };
-      // the first batch is in flight while the indexer query is formed
+      // the first batch is in flight while the indexer query is formed (its
+      // barriers also order the histogram clearing above)
       load_batch(0);
       indexer_query<D, R, NT>(a.q, a.P, b, h, a.G, a.Hq, sh.qt, sh.part);
       float ql[16];
@@ -732,33 +642,55 @@ __global__ __launch_bounds__(kChunkThreads, 4) void chunk_select_kernel(const Se
             s = __shfl(xv, src, kWave);
           }
           key[i] = p < len ? score_key(s + 0.0f) : 0u;
+          if (select) atomicAdd(&sh.hist[p < len ? (key[i] >> kTopShift) : dummy], 1u);
         }
       }
     } else {
       const float* su = a.scores + (size_t)u * a.n_max + base;
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(su, (uint32_t)nv * 4u);
+      __syncthreads();                            // histogram cleared
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         const int p = base + i * NT + w * kWave + lane;
         const float sv = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(rs, (i * NT + w * kWave + lane) * 4, 0, 0));
         key[i] = p < len ? score_key(sv + 0.0f) : 0u;
+        if (select) atomicAdd(&sh.hist[p < len ? (key[i] >> kTopShift) : dummy], 1u);
       }
     }
 
     uint32_t t = 0, need = 0;
-    if (nv > a.M) {
-      radix_threshold(key, (uint32_t)a.M, sh, t, need);
+    if (select) {
+      __syncthreads();
+      finish_threshold<NT>(sh, (uint32_t)a.M, t, need, [&](auto&& f) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) f(key[i], key[i] != 0u);
+      });
       nsel = a.M;
     } else {
       nsel = nv;
     }
     uint32_t* ck = a.cand_key + ((size_t)u * a.S + c) * a.ms;
     int32_t* cp = a.cand_pos + ((size_t)u * a.S + c) * a.ms;
-    emit_in_order(key, t, need, 0, 0, sh, [&](int i, uint32_t slot) {
-      ck[slot] = key[i];
-      cp[slot] = base + i * NT + w * kWave + lane;
-    });
+    if (nsel <= SelectShared<NT>::kCap / 2) {
+      // compact in LDS (the list region is free now), then write out with
+      // whole-wave contiguous stores
+      uint32_t* lk = sh.list;
+      uint32_t* lp = sh.list + SelectShared<NT>::kCap / 2;
+      emit_in_order(key, t, need, 0, 0, sh, [&](int i, uint32_t slot) {
+        lk[slot] = key[i];
+        lp[slot] = (uint32_t)(base + i * NT + w * kWave + lane);
+      });
+      for (int j = tid; j < nsel; j += NT) {
+        ck[j] = lk[j];
+        cp[j] = (int32_t)lp[j];
+      }
+    } else {
+      emit_in_order(key, t, need, 0, 0, sh, [&](int i, uint32_t slot) {
+        ck[slot] = key[i];
+        cp[slot] = base + i * NT + w * kWave + lane;
+      });
+    }
   }
   if (tid == 0) a.cand_cnt[(size_t)u * a.S + c] = nsel;
 }

@@ -32,15 +32,19 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def algorithmic_bytes(wl):
-    """Bytes the method itself must move per step, by kernel."""
+    """Bytes the method itself must move per step, by call: every input read
+    once and every output written once (workspace traffic is not counted)."""
     units = wl.B * wl.Hkv
     q = wl.B * wl.Hq * wl.d * 2
     idx = units * wl.M * 4
     P = wl.Hkv * wl.d * wl.r * 4
-    append = units * (2 * wl.d * 2 + wl.r) * 2 + wl.B * 4 + P   # read new rows + write rows
-    index_topm = units * wl.N * wl.r + q + P + idx               # FP8 stream + q, P, idx out
+    # read the new K/V rows, write K/V rows + the FP8 projected key
+    append = units * (2 * wl.d * 2) + units * (2 * wl.d * 2 + wl.r) + wl.B * 4 + P
+    candidates = units * wl.N * wl.r + q + P       # the FP8 key stream, the queries, P
+    merge = idx                                     # the selected positions
     decode = units * wl.M * wl.d * 2 * 2 + idx + q + wl.B * wl.Hq * wl.d * 2
-    return {"append_kv": append, "index_topm": index_topm, "decode": decode}
+    return {"append_kv": append, "index_candidates": candidates, "merge_candidates": merge,
+            "decode": decode}
 
 
 def _source_hash(names):
@@ -65,8 +69,66 @@ def measured_traffic(kernel_key, src_hash):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(inp, wl, n_units, seed=0):
-    """Time the oracle on a bounded sample of (batch row, KV head) units."""
+CALIB_KERNEL_TAG = "neg"      # torch.neg on fp32: reads and writes exactly n*4 bytes
+
+
+def ingest_counters(fetch_csv, write_csv, calib_mib, kernel="chunk_select_kernel"):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE; both with --calibration-mib) into profiles/traffic.json: each
+    counter's per-dispatch mean for `kernel`, scaled by what the same counter
+    reads for the calibration kernel, whose true traffic is known."""
+    import csv
+
+    def per_dispatch(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        return vals
+
+    def mean_for(vals, pred):
+        xs = [v for (name, _), v in vals.items() if pred(name)]
+        if not xs:
+            raise SystemExit("no dispatch matched in the counter file")
+        return sum(xs) / len(xs), len(xs)
+
+    true_bytes = calib_mib * 2.0 ** 20
+    out = {}
+    for label, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"),
+                                 ("write", write_csv, "WRITE_SIZE")):
+        vals = per_dispatch(path, counter)
+        calib, _ = mean_for(vals, lambda n: CALIB_KERNEL_TAG in n and "elementwise" in n)
+        kern, n = mean_for(vals, lambda n: kernel in n)
+        scale = true_bytes / (calib * 1024.0)
+        out[label] = {"counter_kib_per_dispatch": kern, "dispatches": n,
+                      "calibration_kib": calib, "scale": scale,
+                      "bytes_per_launch": kern * 1024.0 * scale}
+    src_hash = _source_hash(["indexer.hip", "device_common.hpp"])
+    entry = {"source_hash": src_hash,
+             "bytes_per_launch": round(out["fetch"]["bytes_per_launch"]
+                                       + out["write"]["bytes_per_launch"]),
+             "fetch": out["fetch"], "write": out["write"],
+             "calibration": "torch.neg over %d MiB of fp32 (reads and writes %d MiB)"
+                            % (calib_mib, calib_mib)}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    table[kernel] = entry
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1)
+    print(json.dumps({kernel: entry}))
+
+
+def cpu_baseline(inp, wl, n_units, min_seconds=10.0, seed=0):
+    """Time the oracle on a bounded sample of (batch row, KV head) units: the
+    sampled units' decode steps are repeated until at least `min_seconds` of
+    oracle time has been measured (each unit's FP8 cache is prepared by the
+    oracle beforehand, untimed: it is cache state, not part of the step)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -78,27 +140,32 @@ def cpu_baseline(inp, wl, n_units, seed=0):
     G = wl.G
     P64 = inp.P.double().cpu().numpy()
     q64 = inp.q.double().cpu().numpy()
-    total = 0.0
+    total, count = 0.0, 0
     with threadpool_limits(limits=1):
+        prepared = []
         for u in units:
             b, h = divmod(int(u), wl.Hkv)
             K = inp.k_cache[b, h].double().cpu().numpy()
             V = inp.v_cache[b, h].double().cpu().numpy()
             kp = oracle.project_keys(K, P64[h])            # cache state: not timed
             kn = inp.k_new[b, h].double().cpu().numpy()
-            t0 = time.perf_counter()
-            kp[wl.N - 1] = oracle.project_keys(kn, P64[h])[0]
-            K[wl.N - 1] = kn[0]
-            oracle.decode_step_unit(q64[b, h * G:(h + 1) * G], K, V, kp, P64[h], wl.N, wl.M,
-                                    default_scale(wl.d))
-            total += time.perf_counter() - t0
-    per_unit = total / len(units)
+            prepared.append((b, h, K, V, kp, kn))
+        while total < min_seconds or count < len(prepared):
+            for b, h, K, V, kp, kn in prepared:
+                t0 = time.perf_counter()
+                kp[wl.N - 1] = oracle.project_keys(kn, P64[h])[0]
+                K[wl.N - 1] = kn[0]
+                oracle.decode_step_unit(q64[b, h * G:(h + 1) * G], K, V, kp, P64[h], wl.N,
+                                        wl.M, default_scale(wl.d))
+                total += time.perf_counter() - t0
+                count += 1
+    per_unit = total / count
     step_s = per_unit * wl.B * wl.Hkv
-    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": "%d of %d (batch row, KV head) units of one step, scaled to the "
-                      "whole step (%.3f s per unit, numpy fp64, BLAS pinned to 1 thread)"
-                      % (len(units), wl.B * wl.Hkv, per_unit),
-            "seconds_measured": total}
+    return {"value": round(1.0 / step_s, 4), "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": "%d unit-steps over %d sampled of the %d (batch row, KV head) units of "
+                      "one step, scaled to the whole step (%.4f s per unit, numpy fp64, BLAS "
+                      "pinned to 1 thread)" % (count, len(units), wl.B * wl.Hkv, per_unit),
+            "seconds_measured": round(total, 2)}
 
 
 def main(argv=None):
@@ -107,10 +174,20 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="longctx_128k")
-    ap.add_argument("--cpu-units", type=int, default=12,
+    ap.add_argument("--cpu-units", type=int, default=16,
                     help="units of the step timed for the oracle baseline (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calibration-mib", type=int, default=0,
+                    help="before the timed region, run one torch.neg over this many MiB "
+                         "(a kernel of known traffic for scaling rocprofv3 byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: write profiles/traffic.json from two rocprofv3 "
+                         "--pmc counter files of a --calibration-mib run")
     a = ap.parse_args(argv)
+
+    if a.traffic_from:
+        ingest_counters(a.traffic_from[0], a.traffic_from[1], a.calibration_mib or 1024)
+        return
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every step of this path is independent per "
@@ -139,30 +216,38 @@ def main(argv=None):
     scale = default_scale(wl.d)
     torch.cuda.synchronize()
 
-    ev = {k: [] for k in ("append_kv", "index_topm", "decode")}
+    names = ("append_kv", "index_candidates", "merge_candidates", "decode")
+    ev = {k: [] for k in names}
+    calls = (
+        lambda: sa.sparse_attn_append_kv(sh, inp.pos, inp.k_new, inp.v_new, inp.P, inp.k_cache,
+                                         inp.v_cache, kp),
+        lambda: sa.sparse_attn_index_candidates(sh, inp.q, inp.P, kp, inp.seq_lens, wl.N, wl.M,
+                                                ws),
+        lambda: sa.sparse_attn_merge_candidates(sh, wl.N, wl.M, idx, ws),
+        lambda: sa.sparse_attn_decode(sh, inp.q, inp.k_cache, inp.v_cache, idx, wl.M, scale,
+                                      out, None, ws),
+    )
 
     def step(record):
+        # HIP events between the calls go on the stream the library launches on
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] if record \
+            else None
+        for i, call in enumerate(calls):
+            if record:
+                e[i].record()
+            call()
         if record:
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            e[0].record()
-        sa.sparse_attn_append_kv(sh, inp.pos, inp.k_new, inp.v_new, inp.P, inp.k_cache,
-                                 inp.v_cache, kp)
-        if record:
-            e[1].record()
-        sa.sparse_attn_index_topm(sh, inp.q, inp.P, kp, inp.seq_lens, wl.N, wl.M, idx, ws)
-        if record:
-            e[2].record()
-        sa.sparse_attn_decode(sh, inp.q, inp.k_cache, inp.v_cache, idx, wl.M, scale, out,
-                              None, ws)
-        if record:
-            e[3].record()
-            ev["append_kv"].append((e[0], e[1]))
-            ev["index_topm"].append((e[1], e[2]))
-            ev["decode"].append((e[2], e[3]))
+            e[-1].record()
+            for i, k in enumerate(names):
+                ev[k].append((e[i], e[i + 1]))
 
     print("bench: warmup %d" % a.warmup, file=sys.stderr, flush=True)
     for _ in range(a.warmup):
         step(False)
+    if a.calibration_mib > 0:
+        x = torch.ones(a.calibration_mib * 2 ** 18, dtype=torch.float32, device=dev)
+        torch.neg(x, out=torch.empty_like(x))
+        del x
     torch.cuda.synchronize()
 
     # timed region: exactly K steps, back to back, synchronised on both sides
@@ -184,13 +269,15 @@ def main(argv=None):
     steps_per_s = 1e3 / ms_per_step
     hbm_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    dom = "index_topm"
+    # dominant kernel: chunk_select_kernel, the one launch of index_candidates
+    dom = "index_candidates"
     dom_gbps = bytes_k[dom] / (kern_us[dom] * 1e-6) / 1e9
     src_hash = _source_hash(["indexer.hip", "device_common.hpp"])
-    traffic = measured_traffic(dom, src_hash)
+    traffic = measured_traffic("chunk_select_kernel", src_hash)
     roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-                "traffic": traffic, "kernel": "select_kernel (sparse_attn_index_topm)",
+                "traffic": traffic,
+                "kernel": "chunk_select_kernel (sparse_attn_index_candidates)",
                 "bytes_per_launch": bytes_k[dom], "avg_launch_us": round(kern_us[dom], 2),
                 "source_hash": src_hash}
 

@@ -163,6 +163,28 @@ int sparse_attn_index_topm(const sa_shape* shape, const void* q, const float* P,
                            void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * sparse_attn_index_candidates + sparse_attn_merge_candidates -- the two
+ * launches of sparse_attn_index_topm as separate calls (same selection as
+ * above; useful to time, overlap or schedule the scoring stream apart from
+ * the per-head merge).
+ *
+ * index_candidates scores every position in [0, min(seq_lens[b], n_max)) and
+ * leaves, in `workspace`, each position chunk's own top-M (an exact superset
+ * of the head's top-M).  merge_candidates reads them back and writes idx
+ * exactly as sparse_attn_index_topm does.  Between the two calls the
+ * workspace belongs to them: both must see the same shape, n_max and M, be
+ * ordered on one stream, and nothing else may use the workspace in between.
+ * Arguments as in sparse_attn_index_topm.
+ * ------------------------------------------------------------------------- */
+int sparse_attn_index_candidates(const sa_shape* shape, const void* q, const float* P,
+                                 const uint8_t* kp_cache, const int32_t* seq_lens,
+                                 int32_t n_max, int32_t M,
+                                 void* workspace, size_t ws_bytes, void* stream);
+int sparse_attn_merge_candidates(const sa_shape* shape, int32_t n_max, int32_t M,
+                                 int32_t* idx, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
+/* ---------------------------------------------------------------------------
  * sparse_attn_decode -- gather-free sparse attention (step 4).
  *
  * JSSA article, "How JSSA preserves token order": final attention uses the

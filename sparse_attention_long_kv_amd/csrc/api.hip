@@ -45,9 +45,9 @@ constexpr size_t A16 = 16, A4 = 4;
 
 int check_topm_common(const sa_shape* shape, const int32_t* seq_lens, int32_t n_max,
                       int32_t M, const int32_t* idx, const void* ws, size_t ws_bytes,
-                      TopmPlan* plan) {
+                      TopmPlan* plan, bool need_idx = true) {
   if (seq_lens && !ptr_ok(seq_lens, A4)) return SA_ERR_INVALID;
-  if (!ptr_ok(idx, A4)) return SA_ERR_INVALID;
+  if (need_idx && !ptr_ok(idx, A4)) return SA_ERR_INVALID;
   if (n_max < 1 || n_max > shape->capacity) return SA_ERR_INVALID;
   if (M < 1 || M > n_max) return SA_ERR_INVALID;
   const int st = plan_topm(*shape, n_max, M, plan);
@@ -109,8 +109,8 @@ extern "C" int sparse_attn_topm(const sa_shape* shape, const float* scores,
   st = check_topm_common(shape, seq_lens, n_max, M, idx, workspace, ws_bytes, &plan);
   if (st != SA_OK) return st;
   const LaunchCommon c = common(*shape, stream);
-  return finish(run_select(c, plan, false, nullptr, nullptr, nullptr, scores, seq_lens, n_max, M,
-                           idx, workspace),
+  return finish(run_select(c, plan, kSelectChunks | kSelectMerge, false, nullptr, nullptr, nullptr,
+                           scores, seq_lens, n_max, M, idx, workspace),
                 c.stream);
 }
 
@@ -125,8 +125,39 @@ extern "C" int sparse_attn_index_topm(const sa_shape* shape, const void* q, cons
   st = check_topm_common(shape, seq_lens, n_max, M, idx, workspace, ws_bytes, &plan);
   if (st != SA_OK) return st;
   const LaunchCommon c = common(*shape, stream);
-  return finish(run_select(c, plan, true, q, P, kp_cache, nullptr, seq_lens, n_max, M, idx,
-                           workspace),
+  return finish(run_select(c, plan, kSelectChunks | kSelectMerge, true, q, P, kp_cache, nullptr,
+                           seq_lens, n_max, M, idx, workspace),
+                c.stream);
+}
+
+extern "C" int sparse_attn_index_candidates(const sa_shape* shape, const void* q, const float* P,
+                                            const uint8_t* kp_cache, const int32_t* seq_lens,
+                                            int32_t n_max, int32_t M, void* workspace,
+                                            size_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  if (!ptr_ok(q, A16) || !ptr_ok(P, A4) || !ptr_ok(kp_cache, A16)) return SA_ERR_INVALID;
+  TopmPlan plan;
+  st = check_topm_common(shape, seq_lens, n_max, M, nullptr, workspace, ws_bytes, &plan,
+                         /*need_idx=*/false);
+  if (st != SA_OK) return st;
+  const LaunchCommon c = common(*shape, stream);
+  return finish(run_select(c, plan, kSelectChunks, true, q, P, kp_cache, nullptr, seq_lens, n_max,
+                           M, nullptr, workspace),
+                c.stream);
+}
+
+extern "C" int sparse_attn_merge_candidates(const sa_shape* shape, int32_t n_max, int32_t M,
+                                            int32_t* idx, void* workspace, size_t ws_bytes,
+                                            void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  TopmPlan plan;
+  st = check_topm_common(shape, nullptr, n_max, M, idx, workspace, ws_bytes, &plan);
+  if (st != SA_OK) return st;
+  const LaunchCommon c = common(*shape, stream);
+  return finish(run_select(c, plan, kSelectMerge, true, nullptr, nullptr, nullptr, nullptr,
+                           nullptr, n_max, M, idx, workspace),
                 c.stream);
 }
 

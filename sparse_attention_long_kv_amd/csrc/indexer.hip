@@ -718,8 +718,8 @@ static void launch_chunks(const LaunchCommon& c, const SelectArgs& a, int kpt, d
   else launch_chunks_kpt<64, 16, true>(a, kpt, grid, c.stream);
 }
 
-hipError_t run_select(const LaunchCommon& c, const TopmPlan& plan, bool fused, const void* q,
-                      const float* P, const uint8_t* kp, const float* scores,
+hipError_t run_select(const LaunchCommon& c, const TopmPlan& plan, int stages, bool fused,
+                      const void* q, const float* P, const uint8_t* kp, const float* scores,
                       const int32_t* seq_lens, int n_max, int M, int32_t* idx,
                       void* workspace) {
   SelectArgs a;
@@ -744,13 +744,18 @@ hipError_t run_select(const LaunchCommon& c, const TopmPlan& plan, bool fused, c
   a.idx = idx;
   const long blocks = (long)plan.units * plan.splits;
   if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-  if (fused) launch_chunks<true>(c, a, plan.kpt, dim3((unsigned)blocks));
-  else launch_chunks<false>(c, a, plan.kpt, dim3((unsigned)blocks));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // the kernel boundary orders the candidate writes before the merge's reads
-  hipLaunchKernelGGL(merge_kernel, dim3(plan.units), dim3(kMergeThreads), 0, c.stream, a);
-  return hipGetLastError();
+  if (stages & kSelectChunks) {
+    if (fused) launch_chunks<true>(c, a, plan.kpt, dim3((unsigned)blocks));
+    else launch_chunks<false>(c, a, plan.kpt, dim3((unsigned)blocks));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & kSelectMerge) {
+    // the kernel boundary orders the candidate writes before the merge's reads
+    hipLaunchKernelGGL(merge_kernel, dim3(plan.units), dim3(kMergeThreads), 0, c.stream, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace sa

@@ -21,9 +21,12 @@ hipError_t run_project_keys(const LaunchCommon& c, const void* k_cache, const fl
 hipError_t run_index_score(const LaunchCommon& c, const void* q, const float* P,
                            const uint8_t* kp, const int32_t* seq_lens, int n_max,
                            float* scores);
-// fused == true: scores computed from (q, P, kp); otherwise read from `scores`.
-hipError_t run_select(const LaunchCommon& c, const TopmPlan& plan, bool fused, const void* q,
-                      const float* P, const uint8_t* kp, const float* scores,
+// Selection runs as two launches: per-chunk candidates (kSelectChunks; fused
+// == true computes the scores from (q, P, kp), otherwise reads `scores`), then
+// the per-unit merge into idx (kSelectMerge).  `stages` picks either or both.
+constexpr int kSelectChunks = 1, kSelectMerge = 2;
+hipError_t run_select(const LaunchCommon& c, const TopmPlan& plan, int stages, bool fused,
+                      const void* q, const float* P, const uint8_t* kp, const float* scores,
                       const int32_t* seq_lens, int n_max, int M, int32_t* idx,
                       void* workspace);
 hipError_t run_decode(const LaunchCommon& c, const DecodePlan& plan, const void* q,

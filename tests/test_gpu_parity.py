@@ -191,8 +191,12 @@ def test_topm_fused_and_unfused_match_oracle(name):
     sa.sparse_attn_index_score(sh, qd, Pd, kpd, sl, n_max, scores)
     sa.sparse_attn_topm(sh, scores, sl, n_max, M, idx_u, ws)
     sa.sparse_attn_index_topm(sh, qd, Pd, kpd, sl, n_max, M, idx_f, ws)
+    idx_s = torch.full_like(idx_f, -7)
+    sa.sparse_attn_index_candidates(sh, qd, Pd, kpd, sl, n_max, M, ws)
+    sa.sparse_attn_merge_candidates(sh, n_max, M, idx_s, ws)
     gu, gf = idx_u.cpu().numpy(), idx_f.cpu().numpy()
     assert np.array_equal(gu, gf), "fused and unfused index sets differ"
+    assert np.array_equal(idx_s.cpu().numpy(), gf), "two-call selection differs"
     G = Hq // Hkv
     swaps = 0
     for b in range(B):
@@ -443,3 +447,77 @@ def test_cross_layer_reuse_equals_decode_with_source_indices():
                 o, _ = oracle.sparse_attention(q64[b, h * G:(h + 1) * G], K64[b, h], V64[b, h],
                                                gi[b, h], default_scale(wl.d))
                 check_attention(f64(out)[b, h * G:(h + 1) * G], o, "layer %d" % layer)
+
+
+# ------------------------------------------------------------------ full size
+
+def _bench_sequence(inp, sh, M, ws):
+    """The calls, in the order and launch configuration bench.py times."""
+    wl = inp.wl
+    kp = torch.empty(wl.B, wl.Hkv, wl.N, wl.r, dtype=torch.uint8, device="cuda")
+    sa.sparse_attn_project_keys(sh, inp.k_cache, inp.P, 0, wl.N, kp)
+    sa.sparse_attn_append_kv(sh, inp.pos, inp.k_new, inp.v_new, inp.P, inp.k_cache,
+                             inp.v_cache, kp)
+    idx = torch.empty(wl.B, wl.Hkv, M, dtype=torch.int32, device="cuda")
+    sa.sparse_attn_index_candidates(sh, inp.q, inp.P, kp, inp.seq_lens, wl.N, M, ws)
+    sa.sparse_attn_merge_candidates(sh, wl.N, M, idx, ws)
+    out = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(wl.B, wl.Hq, dtype=torch.float32, device="cuda")
+    sa.sparse_attn_decode(sh, inp.q, inp.k_cache, inp.v_cache, idx, M, default_scale(wl.d),
+                          out, lse, ws)
+    return kp, idx, out, lse
+
+
+@pytest.mark.parametrize("name", ["longctx_128k", "gqa7_16k"])
+def test_full_size_step_on_sampled_units(name):
+    """Whole workload at its real size; the oracle checks a sample of units
+    (first, last, and two seeded ones), and every unit is checked for
+    properties that hold at any size: idx ascending, distinct, in range and
+    -1-padded only past the valid count; the two-call selection equals the
+    one-call selection; nearly all planted rows are selected."""
+    wl = WORKLOADS[name]
+    _say("case: full size", wl.name, "B=%d Hkv=%d N=%d M=%d" % (wl.B, wl.Hkv, wl.N, wl.M))
+    inp = make_decode_inputs(wl, seed=7, device="cuda")
+    rng = np.random.default_rng(11)
+    picks = sorted({(0, 0), (wl.B - 1, wl.Hkv - 1)}
+                   | {(int(rng.integers(wl.B)), int(rng.integers(wl.Hkv))) for _ in range(2)})
+    # the generator's cache rows for the sampled units, before the HIP append
+    saved = {(b, h): (f64(inp.k_cache[b, h]), f64(inp.v_cache[b, h])) for b, h in picks}
+    sh = _shape_of(wl.B, wl.Hq, wl.Hkv, wl.d, wl.r, wl.N)
+    ws = sa.alloc_workspace(sh, wl.N, wl.M)
+    kp, idx, out, lse = _bench_sequence(inp, sh, wl.M, ws)
+    idx1 = torch.empty_like(idx)
+    sa.sparse_attn_index_topm(sh, inp.q, inp.P, kp, inp.seq_lens, wl.N, wl.M, idx1, ws)
+    assert torch.equal(idx, idx1)
+    gi = idx.cpu().numpy()
+    assert np.all(gi >= 0) and np.all(gi < wl.N)
+    assert np.all(np.diff(gi, axis=-1) > 0), "indices must ascend strictly"
+    # sanity of the input recipe: planted rows (k += 2 * group-mean query) rank
+    # high, so nearly all of them are selected (their random part can still
+    # push a few below the M-th score; the sampled units below are exact)
+    hit = sum(np.intersect1d(rows, gi[b, h]).size for (b, h), rows in inp.plants.items())
+    tot = sum(rows.size for rows in inp.plants.values())
+    assert hit >= 0.9 * tot, (hit, tot)
+    assert np.all(np.isfinite(lse.cpu().numpy()))
+    P64 = inp.P.double().cpu().numpy()
+    q64, go, gl = f64(inp.q), f64(out), lse.cpu().double().numpy()
+    G, pos = wl.G, inp.pos.cpu().numpy()
+    kn, vn = f64(inp.k_new), f64(inp.v_new)
+    for b, h in picks:
+        K0, V0 = saved[(b, h)]
+        kp0 = oracle.project_keys(K0, P64[h])[None, None]
+        K2, V2, kp2 = oracle.append_kv(K0[None, None], V0[None, None], kp0, pos[b:b + 1],
+                                       kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1],
+                                       P64[h:h + 1])
+        qg = q64[b, h * G:(h + 1) * G]
+        oi, oo, ol, s = oracle.decode_step_unit(qg, K2[0, 0], V2[0, 0], kp2[0, 0], P64[h],
+                                                wl.N, wl.M, default_scale(wl.d))
+        swaps = check_topm_unit(gi[b, h], s, wl.M, wl.N)
+        _say("  unit", (b, h), "band swaps", swaps)
+        if np.array_equal(gi[b, h], oi):
+            check_attention(go[b, h * G:(h + 1) * G], oo, "full-size unit %s" % ((b, h),))
+            assert np.all(np.abs(gl[b, h * G:(h + 1) * G] - ol) <= 1e-3 * (1 + np.abs(ol)))
+        else:
+            o2, l2 = oracle.sparse_attention(qg, K2[0, 0], V2[0, 0], gi[b, h],
+                                             default_scale(wl.d))
+            check_attention(go[b, h * G:(h + 1) * G], o2, "full-size unit %s" % ((b, h),))

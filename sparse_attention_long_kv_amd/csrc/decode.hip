@@ -9,15 +9,25 @@
 // the remaining sparse-attention time at large batch.
 //
 // Layout.  A (batch row, KV head) unit's M selected rows are split over S
-// workgroups ("split-K").  Inside a workgroup, a group of d/8 lanes owns one
-// row at a time: each lane loads 16 bytes (8 bf16) of the K row and of the V
-// row straight from the cache, so one wave instruction fetches whole 256-byte
-// (d=128) rows.  The G queries of the GQA group stay in registers, pre-scaled
-// by softmax_scale * log2(e).  Logits are reduced across the row's lanes with
-// DPP; each lane group keeps its own online-softmax state (m, l, o) in the
-// base-2 domain.  States merge across lane groups, waves and finally across
-// the S workgroups with the log-sum-exp rule
-//   m = max m_s,  l = sum l_s 2^(m_s - m),  o = sum o_s 2^(m_s - m) / l,
+// workgroups ("split-K"); each wave of a workgroup takes tiles of 16 selected
+// rows.  Both products of a tile run on the matrix cores:
+//
+//  * logits: one 16x16x32 bf16 MFMA per 32 dims, A = the 16 K rows (each
+//    lane loads 16 bytes of one row straight from the cache), B = the GQA
+//    group's queries (heads as columns, zero past G).  Lane (q4, n) receives
+//    the logits of head n for rows 4v + q4, v = 0..3, because the lane that
+//    supplies A row m loads tile row 4(m % 4) + m / 4.
+//  * values: 16x16x4 fp32 MFMAs, A = the softmax weights exactly as the logit
+//    product left them (head n, row 4v + q4), B = fp32 V rows (lane (q4, n)
+//    loads d/16 dims, n*d/16 onward, of row 4v + q4; one MFMA per dim).  The
+//    output tile holds heads as rows, so lane (q4, n) accumulates heads
+//    4 q4 + v for dims n*d/16 + j.
+//
+// The online softmax runs in base 2 per head; each tile's maximum is shared
+// by the four lanes of a head with two cross-lane steps, and the accumulated
+// outputs are rescaled only when some head's running maximum moves.  States
+// merge across waves in LDS and across the S workgroups with the log-sum-exp
+// rule  m = max m_s,  l = sum l_s 2^(m_s - m),  o = sum o_s 2^(m_s - m) / l,
 // the cross-workgroup merge being a small second launch (none when S = 1).
 #include "device_common.hpp"
 #include "kernels.h"
@@ -29,7 +39,7 @@ struct DecodeArgs {
   const uint16_t* k;
   const uint16_t* v;
   const int32_t* idx;
-  int M, Ncap, Hq, Hkv, S, rps;
+  int M, Ncap, Hq, Hkv, G, S, rps;
   float qscale;        // softmax_scale * log2(e)
   uint16_t* out;
   float* lse;
@@ -38,6 +48,15 @@ struct DecodeArgs {
   float* po;
 };
 
+typedef __bf16 sa_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float sa_f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int sa_u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxHeads = 16;      // MFMA tile width: G <= 16
+constexpr int kDecodeWaves = kBlock / kWave;
+constexpr int kDecodeIdxTile = 1024;
+constexpr uint32_t kOffNone = 0x80000000u;   // past any unit's range: loads return zero
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // (m, l) merge weights of two base-2 states; -inf states weigh 0.
@@ -45,161 +64,149 @@ __device__ __forceinline__ float merge_scale(float m_part, float m_tot) {
   return m_part == -__builtin_inff() ? 0.0f : fast_exp2(m_part - m_tot);
 }
 
-template <int D, int G>
-struct DecodeGeom {
-  static constexpr int kLanesPerRow = D / 8;              // 16 (d=128) or 8 (d=64)
-  static constexpr int kGroupsPerWave = kWave / kLanesPerRow;
-  static constexpr int kGroups = 4 * kGroupsPerWave;      // rows in flight per pass
-  static constexpr int kUnroll = G <= 4 ? 8 : 4;          // rows per group per pass
-  static constexpr int kIdxTile = 1024;                   // selected rows staged in LDS
-};
+template <int DL>
+__device__ __forceinline__ void load_v_dims(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&f)[DL]) {
+  if constexpr (DL == 8) {
+    bf16x8_to_f32(buffer_load16(r, off, 0), f);
+  } else {
+    const sa_u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    f[0] = bf16_lo(x.x); f[1] = bf16_hi(x.x);
+    f[2] = bf16_lo(x.y); f[3] = bf16_hi(x.y);
+  }
+}
 
-template <int D, int G>
-__global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
-  using Geo = DecodeGeom<D, G>;
-  constexpr int LG = Geo::kLanesPerRow;
-  constexpr int U = Geo::kUnroll;
-  __shared__ float sm[4][G], sl[4][G];
-  __shared__ float so[4][G][D];
-  __shared__ int32_t sidx[Geo::kIdxTile];
+template <int D>
+__global__ __launch_bounds__(kBlock) void decode_kernel(const DecodeArgs a) {
+  constexpr int KS = D / 32;          // logit MFMAs per tile
+  constexpr int DL = D / 16;          // value dims per lane (one MFMA each)
+  constexpr int W = kDecodeWaves;
+  __shared__ float sm[W][kMaxHeads], sl[W][kMaxHeads];
+  __shared__ float so[W][kMaxHeads][D];
+  __shared__ int32_t sidx[kDecodeIdxTile];
 
+  const int G = a.G;
   const int u = blockIdx.x / a.S, split = blockIdx.x % a.S;
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
-  const int gid = w * Geo::kGroupsPerWave + lane / LG;
-  const int sub = lane % LG;
+  const int q4 = lane >> 4, n16 = lane & 15;
+  const bool head_ok = n16 < G;
 
-  // queries of the group, this lane's 8 dims, pre-scaled
-  float qf[G][8];
+  // B operand of the logit product: head n16's dims 32i + 8 q4 .. + 8
+  sa_bf16x8 qb[KS];
   {
-    const uint16_t* qb = a.q + ((size_t)b * a.Hq + (size_t)h * G) * D + sub * 8;
+    const uint16_t* qp =
+        a.q + ((size_t)b * a.Hq + (size_t)h * G + min(n16, G - 1)) * D + 8 * q4;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(qb + (size_t)g * D);
-      float f[8];
-      bf16x8_to_f32(raw, f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[g][e] = f[e] * a.qscale;
+    for (int i = 0; i < KS; ++i) {
+      uint4 raw = *reinterpret_cast<const uint4*>(qp + 32 * i);
+      if (!head_ok) raw = make_uint4(0u, 0u, 0u, 0u);
+      qb[i] = __builtin_bit_cast(sa_bf16x8, raw);
     }
   }
 
-  float m[G], l[G], o[G][8];
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+  sa_f32x4 o[DL];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -__builtin_inff();
-    l[g] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[g][e] = 0.0f;
-  }
+  for (int j = 0; j < DL; ++j) o[j] = sa_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int r0 = split * a.rps;
   const int r1 = min(a.M, r0 + a.rps);
   const int32_t* idx_u = a.idx + (size_t)u * a.M;
-  // this unit's K and V rows; a padding entry maps to an offset past the end
-  // and loads zeros (masked out of the softmax below)
   const uint32_t unit_bytes = (uint32_t)a.Ncap * D * 2;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + (size_t)u * a.Ncap * D, unit_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + (size_t)u * a.Ncap * D, unit_bytes);
-  const uint32_t lane_off = (uint32_t)(sub * 16);
+  const int tk = 4 * (n16 & 3) + (n16 >> 2);          // tile row whose K this lane loads
+  const uint32_t koff = (uint32_t)(8 * q4) * 2;       // bytes of dims 8 q4
+  const uint32_t voff = (uint32_t)(DL * n16) * 2;     // bytes of dims DL n16
 
-  for (int t0 = r0; t0 < r1; t0 += Geo::kIdxTile) {
-    const int t1 = min(r1, t0 + Geo::kIdxTile);
+  for (int t0 = r0; t0 < r1; t0 += kDecodeIdxTile) {
+    const int cnt = min(r1 - t0, kDecodeIdxTile);
+    const int ntile = (cnt + 15) >> 4;
     __syncthreads();
-    for (int j = t0 + tid; j < t1; j += kBlock) sidx[j - t0] = idx_u[j];
+    for (int j = tid; j < ntile * 16; j += kBlock) sidx[j] = j < cnt ? idx_u[t0 + j] : -1;
     __syncthreads();
-    // Every lane runs the same trip count (rows past t1 are masked), so the
-    // DPP reductions always see the whole wave active.  Row loads are
-    // unconditional buffer loads.
-    for (int j0 = t0; j0 < t1; j0 += Geo::kGroups * U) {
-      bool ok[U];
-      uint4 kr[U], vr[U];
+    for (int tt = w; tt < ntile; tt += W) {           // wave-uniform trip count
+      const int rb = tt * 16;
+      const int nk = sidx[rb + tk];
+      int nr[4];
 #pragma unroll
-      for (int x = 0; x < U; ++x) {
-        const int jj = j0 + gid + x * Geo::kGroups;
-        const int n = jj < t1 ? sidx[jj - t0] : -1;
-        ok[x] = (unsigned)n < (unsigned)a.Ncap;
-        const uint32_t off = ok[x] ? (uint32_t)n * (D * 2) + lane_off : 0xFFFFFFF0u;
-        kr[x] = buffer_load16(rk, off, 0);
-        vr[x] = buffer_load16(rv, off, 0);
+      for (int v = 0; v < 4; ++v) nr[v] = sidx[rb + 4 * v + q4];
+      const uint32_t kb = (unsigned)nk < (unsigned)a.Ncap ? (uint32_t)nk * (D * 2) + koff : kOffNone;
+      uint4 kr[KS];
+#pragma unroll
+      for (int i = 0; i < KS; ++i) kr[i] = buffer_load16(rk, kb + 64u * i, 0);
+      float vf[4][DL];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t vb =
+            (unsigned)nr[v] < (unsigned)a.Ncap ? (uint32_t)nr[v] * (D * 2) + voff : kOffNone;
+        load_v_dims<DL>(rv, vb, vf[v]);
       }
-      // logits (base 2), reduced over the row's lanes
-      float s[U][G];
+      sa_f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int x = 0; x < U; ++x) {
-        float kf[8];
-        bf16x8_to_f32(kr[x], kf);
+      for (int i = 0; i < KS; ++i)
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sa_bf16x8, kr[i]), qb[i], c,
+                                                    0, 0, 0);
+      float s[4];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float acc = qf[g][0] * kf[0];
+      for (int v = 0; v < 4; ++v)
+        s[v] = (head_ok && (unsigned)nr[v] < (unsigned)a.Ncap) ? c[v] * a.qscale : -__builtin_inff();
+      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_run, mx);
+      if (ballot(m_new != m_run)) {                   // wave-uniform
+        const float alpha = merge_scale(m_run, m_new);
+        l_run *= alpha;
+        float al[4];
 #pragma unroll
-          for (int e = 1; e < 8; ++e) acc = __builtin_fmaf(qf[g][e], kf[e], acc);
-          s[x][g] = group_sum<LG>(acc);
-        }
+        for (int v = 0; v < 4; ++v) al[v] = __shfl(alpha, 4 * q4 + v, kWave);
+#pragma unroll
+        for (int j = 0; j < DL; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[j][v] *= al[v];
+        m_run = m_new;
       }
-      // online softmax update of this lane group's state
+      const float mref = m_run == -__builtin_inff() ? 0.0f : m_run;
+      float p[4];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float mx = m[g];
+      for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[v] - mref);
+      l_run += (p[0] + p[1]) + (p[2] + p[3]);
 #pragma unroll
-        for (int x = 0; x < U; ++x) mx = ok[x] ? fmaxf(mx, s[x][g]) : mx;
-        const float alpha = merge_scale(m[g], mx);
-        float p[U];
+      for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int x = 0; x < U; ++x) p[x] = ok[x] ? fast_exp2(s[x][g] - mx) : 0.0f;
-        float lsum = l[g] * alpha;
-#pragma unroll
-        for (int x = 0; x < U; ++x) lsum += p[x];
-        l[g] = lsum;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[g][e] *= alpha;
-#pragma unroll
-        for (int x = 0; x < U; ++x) {
-          float vf[8];
-          bf16x8_to_f32(vr[x], vf);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[g][e] = __builtin_fmaf(p[x], vf[e], o[g][e]);
-        }
-        m[g] = mx;
-      }
+        for (int j = 0; j < DL; ++j)
+          o[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[v], vf[v][j], o[j], 0, 0, 0);
     }
   }
 
-  // merge the lane groups of this wave (lanes with equal `sub`)
-#pragma unroll
-  for (int off = LG; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(m[g], off, kWave);
-      const float lo = __shfl_xor(l[g], off, kWave);
-      const float mt = fmaxf(m[g], mo);
-      const float as = merge_scale(m[g], mt), ao = merge_scale(mo, mt);
-      l[g] = l[g] * as + lo * ao;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float oo = __shfl_xor(o[g][e], off, kWave);
-        o[g][e] = o[g][e] * as + oo * ao;
-      }
-      m[g] = mt;
-    }
+  // per-wave state -> LDS: head h's (m, l) from lane h, outputs from the tile
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
+  if (lane < kMaxHeads) {
+    sm[w][lane] = m_run;
+    sl[w][lane] = l_run;
   }
-  if (lane < LG) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (lane == 0) { sm[w][g] = m[g]; sl[w][g] = l[g]; }
+  for (int v = 0; v < 4; ++v) {
+    const int hd = 4 * q4 + v;
+    if (hd < G) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) so[w][g][sub * 8 + e] = o[g][e];
+      for (int j = 0; j < DL; ++j) so[w][hd][DL * n16 + j] = o[j][v];
     }
   }
   __syncthreads();
 
-  // merge the 4 waves: thread -> (g, dim)
+  // merge the waves: thread -> (g, dim)
   const size_t part0 = ((size_t)u * a.S + split) * G;
   for (int t = tid; t < G * D; t += kBlock) {
     const int g = t / D, dd = t % D;
-    const float mt = fmaxf(fmaxf(sm[0][g], sm[1][g]), fmaxf(sm[2][g], sm[3][g]));
+    float mt = sm[0][g];
+#pragma unroll
+    for (int ww = 1; ww < W; ++ww) mt = fmaxf(mt, sm[ww][g]);
     float lt = 0.0f, ot = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    for (int ww = 0; ww < W; ++ww) {
       const float sc = merge_scale(sm[ww][g], mt);
       lt += sl[ww][g] * sc;
       ot += so[ww][g][dd] * sc;
@@ -221,9 +228,10 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 // Merge the S partial states of one unit (one workgroup per unit).  A separate
 // launch orders the partial writes before these reads without device-scope
 // fences inside the attention kernel.
-template <int D, int G>
-__global__ __launch_bounds__(256) void combine_kernel(const DecodeArgs a) {
-  __shared__ float fm[G], fl[G];
+template <int D>
+__global__ __launch_bounds__(kBlock) void combine_kernel(const DecodeArgs a) {
+  __shared__ float fm[kMaxHeads], fl[kMaxHeads];
+  const int G = a.G;
   const int u = blockIdx.x;
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int tid = threadIdx.x;
@@ -257,20 +265,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const DecodeArgs a) {
 }
 
 template <int D>
-static void launch_decode_d(int G, const DecodeArgs& a, dim3 grid, int units, hipStream_t st) {
-  switch (G) {
-#define SA_CASE(GG)                                                                    \
-  case GG:                                                                             \
-    hipLaunchKernelGGL((decode_kernel<D, GG>), grid, dim3(kBlock), 0, st, a);          \
-    if (a.S > 1)                                                                       \
-      hipLaunchKernelGGL((combine_kernel<D, GG>), dim3(units), dim3(kBlock), 0, st, a); \
-    break;
-    SA_CASE(1) SA_CASE(2) SA_CASE(3) SA_CASE(4) SA_CASE(5) SA_CASE(6) SA_CASE(7) SA_CASE(8)
-    SA_CASE(9) SA_CASE(10) SA_CASE(11) SA_CASE(12) SA_CASE(13) SA_CASE(14) SA_CASE(15)
-    SA_CASE(16)
-#undef SA_CASE
-    default: break;
-  }
+static void launch_decode_d(const DecodeArgs& a, dim3 grid, int units, hipStream_t st) {
+  hipLaunchKernelGGL((decode_kernel<D>), grid, dim3(kBlock), 0, st, a);
+  if (a.S > 1) hipLaunchKernelGGL((combine_kernel<D>), dim3(units), dim3(kBlock), 0, st, a);
 }
 
 hipError_t run_decode(const LaunchCommon& c, const DecodePlan& plan, const void* q,
@@ -285,6 +282,7 @@ hipError_t run_decode(const LaunchCommon& c, const DecodePlan& plan, const void*
   a.Ncap = c.Ncap;
   a.Hq = c.Hq;
   a.Hkv = c.Hkv;
+  a.G = c.G;
   a.S = plan.splits;
   a.rps = plan.rows_per_split;
   a.qscale = scale * 1.4426950408889634f;
@@ -296,9 +294,10 @@ hipError_t run_decode(const LaunchCommon& c, const DecodePlan& plan, const void*
   a.po = (float*)(ws + plan.off_o);
   const long blocks = (long)plan.units * plan.splits;
   if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  if (c.G < 1 || c.G > kMaxHeads) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks);
-  if (c.D == 128) launch_decode_d<128>(c.G, a, grid, plan.units, c.stream);
-  else launch_decode_d<64>(c.G, a, grid, plan.units, c.stream);
+  if (c.D == 128) launch_decode_d<128>(a, grid, plan.units, c.stream);
+  else launch_decode_d<64>(a, grid, plan.units, c.stream);
   return hipGetLastError();
 }
 

@@ -183,8 +183,10 @@ struct SelectArgs {
 constexpr int kDigitBits = 12;
 constexpr int kBins = 1 << kDigitBits;      // histogram bins per level
 constexpr int kTopShift = 32 - kDigitBits;  // first-level digit = key >> 20
-constexpr int kListCap = 4096;              // threshold-bin keys kept in LDS (chunks)
+constexpr int kListCap = 4224;              // threshold-bin keys kept in LDS (chunks)
+constexpr int kStageSlots = kListCap / 2 - kWave;   // candidates staged in the list region
 constexpr int kMergeListCap = 1024;         // (merge: its LDS is nearly full)
+constexpr int kRankMax = 256;               // lists up to this size are ranked directly
 constexpr int kChunkThreads = kChunkBlock;  // chunk workgroups: 8 waves
 constexpr int kMergeThreads = 1024;         // merge workgroups: 16 waves
 
@@ -195,11 +197,10 @@ struct SelectShared {
   double part[NT];
   uint32_t seg[NT];
   uint32_t wtot[W];
-  uint32_t pick[2];
-  uint32_t list_n;
+  uint32_t pick[3];
   uint32_t hist[kBins + kWave];   // + one private dummy bin per lane
   static constexpr int kCap = kListCap;
-  uint32_t list[kCap];
+  alignas(16) uint32_t list[kCap];
 };
 
 // Inclusive prefix sum over the block in thread order; `total` gets the sum.
@@ -224,6 +225,7 @@ __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, Sh& sh, uin
 // With the current level's histogram in sh.hist (bins of keys on `path`),
 // find the bin holding the key of 1-based rank target - above counted from the
 // top; above += keys in higher bins; path gains the bin as its low digit.
+// sh.pick[2] is left holding the chosen bin's count.
 template <int NT, class Sh>
 __device__ void pick_bin(Sh& sh, int width, uint32_t target, uint32_t& path, uint32_t& above) {
   constexpr int kPer = kBins / NT;
@@ -246,6 +248,7 @@ __device__ void pick_bin(Sh& sh, int width, uint32_t target, uint32_t& path, uin
       if (cum + c[j] >= rank) {
         sh.pick[0] = (uint32_t)(tid * kPer + j);
         sh.pick[1] = cum;
+        sh.pick[2] = c[j];
         break;
       }
       cum += c[j];
@@ -280,34 +283,72 @@ __device__ void radix_level(Sh& sh, int top, int lo, uint32_t target, uint32_t& 
   pick_bin<NT>(sh, width, target, path, above);
 }
 
-// Levels 2 and 3 of the exact threshold search.  The first-level histogram
+// Exact threshold among the n keys of the LDS list (n <= NT, list padded with
+// zero keys to a multiple of 4): each thread ranks its own key against the
+// whole list (broadcast LDS reads), and the thread holding the key of
+// 1-based rank `rank` publishes it.  Returns t, gt = #list keys > t and
+// eq = #list keys == t.
+template <int NT, class Sh>
+__device__ void rank_in_list(Sh& sh, uint32_t n, uint32_t rank, uint32_t& t, uint32_t& gt_out,
+                             uint32_t& eq_out) {
+  const int tid = threadIdx.x;
+  if ((tid & ~(kWave - 1)) < (int)n) {             // waves holding no list key skip
+    const uint32_t k = tid < (int)n ? sh.list[tid] : 0u;
+    uint32_t gt = 0, ge = 0;
+    const uint32_t n4 = (n + 3u) & ~3u;
+    for (uint32_t j = 0; j < n4; j += 4) {
+      const uint4 x = *reinterpret_cast<const uint4*>(&sh.list[j]);
+      gt += (x.x > k) + (x.y > k) + (x.z > k) + (x.w > k);
+      ge += (x.x >= k) + (x.y >= k) + (x.z >= k) + (x.w >= k);
+    }
+    // threads holding equal keys write equal values
+    if (tid < (int)n && gt < rank && rank <= ge) {
+      sh.pick[0] = k;
+      sh.pick[1] = gt;
+      sh.pick[2] = ge - gt;
+    }
+  }
+  __syncthreads();
+  t = sh.pick[0];
+  gt_out = sh.pick[1];
+  eq_out = sh.pick[2];
+  __syncthreads();
+}
+
+// Remaining levels of the exact threshold search.  The first-level histogram
 // (digit key >> 20) is already in sh.hist.  Keys of the chosen first-level bin
-// are compacted into an LDS list (usually ~1% of the keys) and resolved
-// there; if the bin is too large, the remaining levels run over `visit`.
-// Returns t (the target-th largest key) and need = target - #keys > t.
+// (usually ~1% of the keys) are compacted into an LDS list -- counted per
+// thread, offsets from one block scan, then written -- and the threshold is
+// found there: by direct ranking when the list is short, else by two more
+// radix levels; if the bin overflows the list, those levels run over `visit`.
+// Returns t (the target-th largest key), need = target - #keys > t (how many
+// keys equal to t are selected) and eq = #keys == t.
 template <int NT, class Sh, class Visit>
 __device__ void finish_threshold(Sh& sh, uint32_t target, uint32_t& t_out, uint32_t& need_out,
-                                 Visit visit) {
-  const int tid = threadIdx.x, lane = lane_id();
+                                 uint32_t& eq_out, Visit visit) {
+  const int tid = threadIdx.x;
   uint32_t path = 0, above = 0;
   pick_bin<NT>(sh, kDigitBits, target, path, above);
   const uint32_t b1 = path;
-  if (tid == 0) sh.list_n = 0u;
+  uint32_t cnt = 0;
+  visit([&](uint32_t k, bool valid) { cnt += (valid && (k >> kTopShift) == b1) ? 1u : 0u; });
+  uint32_t n;
+  uint32_t off = block_inclusive_scan<NT>(cnt, sh, n) - cnt;
+  if (n <= (uint32_t)Sh::kCap) {
+    visit([&](uint32_t k, bool valid) {
+      if (valid && (k >> kTopShift) == b1) sh.list[off++] = k;
+    });
+    if (tid < 4 && n + tid < (uint32_t)Sh::kCap) sh.list[n + tid] = 0u;   // pad for rank_in_list
+  }
   __syncthreads();
-  const uint64_t lt = lanemask_lt();
-  visit([&](uint32_t k, bool valid) {
-    const bool in = valid && (k >> kTopShift) == b1;
-    const uint64_t m = ballot(in);
-    if (m) {                                        // wave-uniform
-      uint32_t base = 0;
-      if (lane == 0) base = atomicAdd(&sh.list_n, (uint32_t)popc64(m));
-      base = (uint32_t)__shfl((int)base, 0, kWave);
-      const uint32_t slot = base + (uint32_t)popc64(m & lt);
-      if (in && slot < (uint32_t)Sh::kCap) sh.list[slot] = k;
-    }
-  });
-  __syncthreads();
-  const uint32_t n = sh.list_n;
+  if (n <= (uint32_t)kRankMax && n <= (uint32_t)NT) {
+    uint32_t t, gt, eq;
+    rank_in_list<NT>(sh, n, target - above, t, gt, eq);
+    t_out = t;
+    need_out = target - above - gt;
+    eq_out = eq;
+    return;
+  }
   if (n <= (uint32_t)Sh::kCap) {
     auto list_visit = [&](auto&& f) {
       for (uint32_t j = tid; j < n; j += NT) f(sh.list[j], true);
@@ -320,48 +361,68 @@ __device__ void finish_threshold(Sh& sh, uint32_t target, uint32_t& t_out, uint3
   }
   t_out = path;
   need_out = target - above;
+  eq_out = sh.pick[2];
+  __syncthreads();
 }
 
 // Emit, in register order (i, wave, lane) -- which callers make equal to
-// position order -- every key > t and the first `need` keys == t (counting
-// from eq_base already emitted).  emit(i, slot) receives the output slot.
-// Returns this tile's (gt, eq) totals packed as gt | eq << 16.
+// position order -- the selected keys: every key > t and the first `need`
+// keys == t.  emit(i, sel, slot) is called for every key (branch-free callers
+// write unselected keys to a scratch slot); slot = number of selected keys
+// before this one.  When every key == t is selected (need == eq, the usual
+// case) selection is the single predicate key >= t, one ballot per row.
 template <int NT, int K, class EmitFn>
-__device__ __forceinline__ uint32_t emit_in_order(const uint32_t (&key)[K], uint32_t t,
-                                                  uint32_t need, uint32_t gt_base,
-                                                  uint32_t eq_base, SelectShared<NT>& sh,
-                                                  EmitFn emit) {
+__device__ __forceinline__ void emit_in_order(const uint32_t (&key)[K], uint32_t t, uint32_t need,
+                                              uint32_t eq, SelectShared<NT>& sh, EmitFn emit) {
   constexpr int W = NT / kWave;
   static_assert(K * W <= NT, "segments");
   const int tid = threadIdx.x, w = tid / kWave;
+  const bool single = need == eq;                 // block-uniform
+  // pass 1: per (row, wave) counts, wave-major so pass 2 reads them at once
 #pragma unroll
   for (int i = 0; i < K; ++i) {
-    const uint64_t mg = ballot(key[i] > t), me = ballot(key[i] == t);
-    // every lane stores the same (wave-uniform) value: no per-key branch
-    sh.seg[i * W + w] = (uint32_t)popc64(mg) | ((uint32_t)popc64(me) << 16);
+    uint32_t v;
+    if (single) {
+      v = (uint32_t)popc64(ballot(key[i] >= t));
+    } else {
+      v = (uint32_t)popc64(ballot(key[i] > t)) | ((uint32_t)popc64(ballot(key[i] == t)) << 16);
+    }
+    sh.seg[w * K + i] = v;                        // same value from every lane
   }
   __syncthreads();
-  const uint32_t v = tid < K * W ? sh.seg[tid] : 0u;
+  // exclusive scan in (row, wave) order
+  const int sr = tid / W, sw = tid % W;
+  const uint32_t v = tid < K * W ? sh.seg[sw * K + sr] : 0u;
   uint32_t total;
   const uint32_t incl = block_inclusive_scan<NT>(v, sh, total);
-  if (tid < K * W) sh.seg[tid] = incl - v;
   __syncthreads();
-  const uint64_t lt = lanemask_lt();
-  // An opaque copy of t keeps the compiler from carrying the first pass's
-  // 2*K ballot masks (scalar register pairs) across the scan.
+  if (tid < K * W) sh.seg[sw * K + sr] = incl - v;
+  __syncthreads();
+  uint32_t pre[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) pre[i] = sh.seg[w * K + i];
+  // an opaque copy of t keeps the compiler from carrying pass 1's ballot
+  // masks (scalar register pairs) into this pass
   uint32_t t2 = t;
   asm volatile("" : "+v"(t2));
 #pragma unroll
   for (int i = 0; i < K; ++i) {
-    const uint64_t mg = ballot(key[i] > t2), me = ballot(key[i] == t2);
-    const uint32_t pre = sh.seg[i * W + w];
-    const uint32_t gtb = gt_base + (pre & 0xFFFFu) + (uint32_t)popc64(mg & lt);
-    const uint32_t eqb = eq_base + (pre >> 16) + (uint32_t)popc64(me & lt);
-    if (key[i] > t2) emit(i, gtb + min(eqb, need));
-    else if (key[i] == t2 && eqb < need) emit(i, gtb + eqb);
+    if (single) {
+      const bool sel = key[i] >= t2;
+      const uint32_t slot = pre[i] + (uint32_t)__builtin_amdgcn_mbcnt_hi(
+          (uint32_t)(ballot(sel) >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ballot(sel), 0u));
+      emit(i, sel, slot);
+    } else {
+      const bool gt = key[i] > t2, eqk = key[i] == t2;
+      const uint64_t mg = ballot(gt), me = ballot(eqk);
+      const uint32_t gtb = (pre[i] & 0xFFFFu) +
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(mg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mg, 0u));
+      const uint32_t eqb = (pre[i] >> 16) +
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u));
+      emit(i, gt || (eqk && eqb < need), gtb + min(eqb, need));
+    }
   }
   __syncthreads();
-  return total;
 }
 
 // ------------------------------------------------------------------ merge
@@ -376,12 +437,11 @@ struct MergeLds {
   int32_t pos[kMergeTile];
   uint32_t hist[kBins + kWave];
   static constexpr int kCap = kMergeListCap;
-  uint32_t list[kCap];
+  alignas(16) uint32_t list[kCap];
   int32_t off[kMaxSplits + 1];   // dense offset of each chunk's candidates
   uint32_t seg[kMergeThreads];
   uint32_t wtot[kMergeThreads / kWave];
-  uint32_t pick[2];
-  uint32_t list_n;
+  uint32_t pick[3];
 };
 
 // Copy dense candidates [d0, d0 + n) of unit u into the LDS tile.
@@ -509,7 +569,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const SelectArgs a
     __syncthreads();
   }
 
-  uint32_t t = 0, need = 0;
+  // without selection every staged candidate (key >= 1) is emitted
+  uint32_t t = 1, need = 0, eq = 0;
   if (select) {
     auto visit_all = [&](auto&& f) {
       for (int tile = 0; tile < ntiles; ++tile) {
@@ -522,14 +583,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const SelectArgs a
         }
       }
     };
-    finish_threshold<NT>(sh, target, t, need, visit_all);
+    finish_threshold<NT>(sh, target, t, need, eq, visit_all);
   }
 
-  // ordered emission: row i of thread (w, lane) is dense index i*NT + 64w + lane.
-  // Output slots are staged in LDS (the histogram region is free now) when
-  // they fit, then written with contiguous stores.
-  const bool staged = target <= (uint32_t)(kBins + kWave);
+  // Ordered emission: row i of thread (w, lane) is dense index i*NT + 64w + lane,
+  // so (row, wave, lane) order is ascending position order.  Output slots are
+  // staged in LDS (the histogram region is free now; unselected entries go to
+  // a per-lane scratch slot past the real ones) when they fit, then written
+  // with contiguous stores.
+  const bool single = need == eq;                 // selection is key >= t
+  const bool staged = target <= (uint32_t)kBins;
   int32_t* out = staged ? reinterpret_cast<int32_t*>(sh.hist) : idx_u;
+  const int lane = lane_id();
   __syncthreads();
   uint32_t gt_base = 0, eq_base = 0;
   for (int tile = 0; tile < ntiles; ++tile) {
@@ -539,32 +604,61 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const SelectArgs a
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
       const int j = i * NT + tid;
-      const uint32_t k = j < n ? sh.key[min(j, n - 1)] : 0u;
-      const uint64_t mg = ballot(k > t), me = ballot(j < n && k == t);
-      if (i < rows) sh.seg[i * W + w] = (uint32_t)popc64(mg) | ((uint32_t)popc64(me) << 16);
+      const uint32_t k = sh.key[min(j, n - 1)];
+      uint32_t v;
+      if (single) {
+        v = (uint32_t)popc64(ballot(j < n && k >= t));
+      } else {
+        v = (uint32_t)popc64(ballot(j < n && k > t)) |
+            ((uint32_t)popc64(ballot(j < n && k == t)) << 16);
+      }
+      if (i < rows) sh.seg[w * kRows + i] = v;      // same value from every lane
     }
     __syncthreads();
-    const uint32_t v = tid < rows * W ? sh.seg[tid] : 0u;
+    const int sr = tid / W, sw = tid % W;
+    const uint32_t v = tid < rows * W ? sh.seg[sw * kRows + sr] : 0u;
     uint32_t total;
     const uint32_t incl = block_inclusive_scan<NT>(v, sh, total);
-    if (tid < rows * W) sh.seg[tid] = incl - v;
     __syncthreads();
-    const uint64_t lt = lanemask_lt();
+    if (tid < rows * W) sh.seg[sw * kRows + sr] = incl - v;
+    __syncthreads();
+    uint32_t pre[kRows];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) pre[i] = sh.seg[w * kRows + i];
+    uint32_t t2 = t;
+    asm volatile("" : "+v"(t2));
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
       if (i >= rows) break;                         // block-uniform
       const int j = i * NT + tid;
-      const uint32_t k = j < n ? sh.key[min(j, n - 1)] : 0u;
-      const bool gt = k > t, eq = j < n && k == t;
-      const uint64_t mg = ballot(gt), me = ballot(eq);
-      const uint32_t pre = sh.seg[i * W + w];
-      const uint32_t gtb = gt_base + (pre & 0xFFFFu) + (uint32_t)popc64(mg & lt);
-      const uint32_t eqb = eq_base + (pre >> 16) + (uint32_t)popc64(me & lt);
-      if (gt) out[gtb + min(eqb, need)] = sh.pos[j];
-      else if (eq && eqb < need) out[gtb + eqb] = sh.pos[j];
+      const uint32_t k = sh.key[min(j, n - 1)];
+      const int32_t p = sh.pos[min(j, n - 1)];
+      bool sel;
+      uint32_t slot;
+      if (single) {
+        sel = j < n && k >= t2;
+        const uint64_t m = ballot(sel);
+        slot = gt_base + pre[i] +
+               __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      } else {
+        const bool gt = j < n && k > t2, eqk = j < n && k == t2;
+        const uint64_t mg = ballot(gt), me = ballot(eqk);
+        const uint32_t gtb = gt_base + (pre[i] & 0xFFFFu) +
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(mg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mg, 0u));
+        const uint32_t eqb = eq_base + (pre[i] >> 16) +
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u));
+        sel = gt || (eqk && eqb < need);
+        slot = gtb + min(eqb, need);
+      }
+      if (staged) out[sel ? slot : (uint32_t)(kBins + lane)] = p;
+      else if (sel) out[slot] = p;
     }
-    gt_base += total & 0xFFFFu;
-    eq_base += total >> 16;
+    if (single) {
+      gt_base += total;
+    } else {
+      gt_base += total & 0xFFFFu;
+      eq_base += total >> 16;
+    }
     __syncthreads();
   }
   if (staged)
@@ -659,10 +753,11 @@ __global__ __launch_bounds__(kChunkThreads, 4) void chunk_select_kernel(const Se
       }
     }
 
-    uint32_t t = 0, need = 0;
+    // without selection every valid key (key >= 1) is emitted
+    uint32_t t = 1, need = 0, eq = 0;
     if (select) {
       __syncthreads();
-      finish_threshold<NT>(sh, (uint32_t)a.M, t, need, [&](auto&& f) {
+      finish_threshold<NT>(sh, (uint32_t)a.M, t, need, eq, [&](auto&& f) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) f(key[i], key[i] != 0u);
       });
@@ -672,23 +767,27 @@ __global__ __launch_bounds__(kChunkThreads, 4) void chunk_select_kernel(const Se
     }
     uint32_t* ck = a.cand_key + ((size_t)u * a.S + c) * a.ms;
     int32_t* cp = a.cand_pos + ((size_t)u * a.S + c) * a.ms;
-    if (nsel <= SelectShared<NT>::kCap / 2) {
-      // compact in LDS (the list region is free now), then write out with
+    if (nsel <= kStageSlots) {
+      // compact in LDS (the list region is free now; unselected keys go to a
+      // per-lane scratch slot past the real ones), then write out with
       // whole-wave contiguous stores
       uint32_t* lk = sh.list;
-      uint32_t* lp = sh.list + SelectShared<NT>::kCap / 2;
-      emit_in_order(key, t, need, 0, 0, sh, [&](int i, uint32_t slot) {
-        lk[slot] = key[i];
-        lp[slot] = (uint32_t)(base + i * NT + w * kWave + lane);
+      uint32_t* lp = sh.list + kListCap / 2;
+      emit_in_order(key, t, need, eq, sh, [&](int i, bool sel, uint32_t slot) {
+        const uint32_t d = sel ? slot : (uint32_t)(kStageSlots + lane);
+        lk[d] = key[i];
+        lp[d] = (uint32_t)(base + i * NT + w * kWave + lane);
       });
       for (int j = tid; j < nsel; j += NT) {
         ck[j] = lk[j];
         cp[j] = (int32_t)lp[j];
       }
     } else {
-      emit_in_order(key, t, need, 0, 0, sh, [&](int i, uint32_t slot) {
-        ck[slot] = key[i];
-        cp[slot] = base + i * NT + w * kWave + lane;
+      emit_in_order(key, t, need, eq, sh, [&](int i, bool sel, uint32_t slot) {
+        if (sel) {
+          ck[slot] = key[i];
+          cp[slot] = base + i * NT + w * kWave + lane;
+        }
       });
     }
   }

@@ -53,8 +53,9 @@ typedef float sa_f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int sa_u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxHeads = 16;      // MFMA tile width: G <= 16
-constexpr int kDecodeWaves = kBlock / kWave;
-constexpr int kDecodeIdxTile = 1024;
+constexpr int kDecodeWaves = 12;   // waves per workgroup: 3 per SIMD fill a CU
+constexpr int kDecodeThreads = kDecodeWaves * kWave;
+constexpr int kDecodeIdxTile = 2048;
 constexpr uint32_t kOffNone = 0x80000000u;   // past any unit's range: loads return zero
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -64,25 +65,45 @@ __device__ __forceinline__ float merge_scale(float m_part, float m_tot) {
   return m_part == -__builtin_inff() ? 0.0f : fast_exp2(m_part - m_tot);
 }
 
-template <int DL>
-__device__ __forceinline__ void load_v_dims(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&f)[DL]) {
-  if constexpr (DL == 8) {
-    bf16x8_to_f32(buffer_load16(r, off, 0), f);
+// One lane's share of a V row: 8 bf16 (d = 128) or 4 bf16 (d = 64).
+template <int D> struct VRaw { using type = uint4; };
+template <> struct VRaw<64> { using type = sa_u32x2; };
+
+template <int D>
+__device__ __forceinline__ typename VRaw<D>::type load_v_raw(__amdgpu_buffer_rsrc_t r,
+                                                             uint32_t off) {
+  if constexpr (D == 128) return buffer_load16(r, off, 0);
+  else return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void v_raw_to_f32(const typename VRaw<D>::type& x, float* f) {
+  if constexpr (D == 128) {
+    bf16x8_to_f32(x, f);
   } else {
-    const sa_u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
     f[0] = bf16_lo(x.x); f[1] = bf16_hi(x.x);
     f[2] = bf16_lo(x.y); f[3] = bf16_hi(x.y);
   }
 }
 
+// Registers of one loaded 16-row tile.
 template <int D>
-__global__ __launch_bounds__(kBlock) void decode_kernel(const DecodeArgs a) {
+struct TileRaw {
+  uint4 k[D / 32];
+  typename VRaw<D>::type v[4];
+  int nr[4];
+};
+
+// Dynamic LDS: the waves' output tiles, [waves][G][D] floats.
+template <int D>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs a) {
   constexpr int KS = D / 32;          // logit MFMAs per tile
   constexpr int DL = D / 16;          // value dims per lane (one MFMA each)
   constexpr int W = kDecodeWaves;
+  constexpr int NT = kDecodeThreads;
   __shared__ float sm[W][kMaxHeads], sl[W][kMaxHeads];
-  __shared__ float so[W][kMaxHeads][D];
   __shared__ int32_t sidx[kDecodeIdxTile];
+  extern __shared__ float so[];       // [W][G][D]
 
   const int G = a.G;
   const int u = blockIdx.x / a.S, split = blockIdx.x % a.S;
@@ -119,64 +140,81 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DecodeArgs a) {
   const uint32_t koff = (uint32_t)(8 * q4) * 2;       // bytes of dims 8 q4
   const uint32_t voff = (uint32_t)(DL * n16) * 2;     // bytes of dims DL n16
 
+  // row loads of one 16-row tile (tile rows come from the staged indices)
+  auto issue = [&](int tt, TileRaw<D>& t) {
+    const int rb = tt * 16;
+    const int nk = sidx[rb + tk];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) t.nr[v] = sidx[rb + 4 * v + q4];
+    const uint32_t kb =
+        (unsigned)nk < (unsigned)a.Ncap ? (uint32_t)nk * (D * 2) + koff : kOffNone;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) t.k[i] = buffer_load16(rk, kb + 64u * i, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint32_t vb =
+          (unsigned)t.nr[v] < (unsigned)a.Ncap ? (uint32_t)t.nr[v] * (D * 2) + voff : kOffNone;
+      t.v[v] = load_v_raw<D>(rv, vb);
+    }
+  };
+  // logits, online softmax and value products of one loaded tile
+  auto consume = [&](const TileRaw<D>& t) {
+    sa_f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < KS; ++i)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sa_bf16x8, t.k[i]), qb[i], c,
+                                                  0, 0, 0);
+    float s[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      s[v] = (head_ok && (unsigned)t.nr[v] < (unsigned)a.Ncap) ? c[v] * a.qscale
+                                                                : -__builtin_inff();
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m_run, mx);
+    if (ballot(m_new != m_run)) {                     // wave-uniform
+      const float alpha = merge_scale(m_run, m_new);
+      l_run *= alpha;
+      float al[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) al[v] = __shfl(alpha, 4 * q4 + v, kWave);
+#pragma unroll
+      for (int j = 0; j < DL; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[j][v] *= al[v];
+      m_run = m_new;
+    }
+    const float mref = m_run == -__builtin_inff() ? 0.0f : m_run;
+    float p[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[v] - mref);
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float vf[DL];
+      v_raw_to_f32<D>(t.v[v], vf);
+#pragma unroll
+      for (int j = 0; j < DL; ++j)
+        o[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[v], vf[j], o[j], 0, 0, 0);
+    }
+  };
+
   for (int t0 = r0; t0 < r1; t0 += kDecodeIdxTile) {
     const int cnt = min(r1 - t0, kDecodeIdxTile);
     const int ntile = (cnt + 15) >> 4;
     __syncthreads();
-    for (int j = tid; j < ntile * 16; j += kBlock) sidx[j] = j < cnt ? idx_u[t0 + j] : -1;
+    for (int j = tid; j < ntile * 16; j += NT) sidx[j] = j < cnt ? idx_u[t0 + j] : -1;
     __syncthreads();
-    for (int tt = w; tt < ntile; tt += W) {           // wave-uniform trip count
-      const int rb = tt * 16;
-      const int nk = sidx[rb + tk];
-      int nr[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) nr[v] = sidx[rb + 4 * v + q4];
-      const uint32_t kb = (unsigned)nk < (unsigned)a.Ncap ? (uint32_t)nk * (D * 2) + koff : kOffNone;
-      uint4 kr[KS];
-#pragma unroll
-      for (int i = 0; i < KS; ++i) kr[i] = buffer_load16(rk, kb + 64u * i, 0);
-      float vf[4][DL];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const uint32_t vb =
-            (unsigned)nr[v] < (unsigned)a.Ncap ? (uint32_t)nr[v] * (D * 2) + voff : kOffNone;
-        load_v_dims<DL>(rv, vb, vf[v]);
-      }
-      sa_f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int i = 0; i < KS; ++i)
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sa_bf16x8, kr[i]), qb[i], c,
-                                                    0, 0, 0);
-      float s[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        s[v] = (head_ok && (unsigned)nr[v] < (unsigned)a.Ncap) ? c[v] * a.qscale : -__builtin_inff();
-      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m_run, mx);
-      if (ballot(m_new != m_run)) {                   // wave-uniform
-        const float alpha = merge_scale(m_run, m_new);
-        l_run *= alpha;
-        float al[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) al[v] = __shfl(alpha, 4 * q4 + v, kWave);
-#pragma unroll
-        for (int j = 0; j < DL; ++j)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) o[j][v] *= al[v];
-        m_run = m_new;
-      }
-      const float mref = m_run == -__builtin_inff() ? 0.0f : m_run;
-      float p[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[v] - mref);
-      l_run += (p[0] + p[1]) + (p[2] + p[3]);
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int j = 0; j < DL; ++j)
-          o[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[v], vf[v][j], o[j], 0, 0, 0);
+    // Two tiles per iteration: both tiles' row loads are in flight before the
+    // first is consumed.  Trip counts are wave-uniform.
+    for (int tt = w; tt < ntile; tt += 2 * W) {
+      TileRaw<D> ra, rb;
+      issue(tt, ra);
+      const bool two = tt + W < ntile;
+      if (two) issue(tt + W, rb);
+      consume(ra);
+      if (two) consume(rb);
     }
   }
 
@@ -192,14 +230,14 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DecodeArgs a) {
     const int hd = 4 * q4 + v;
     if (hd < G) {
 #pragma unroll
-      for (int j = 0; j < DL; ++j) so[w][hd][DL * n16 + j] = o[j][v];
+      for (int j = 0; j < DL; ++j) so[((size_t)w * G + hd) * D + DL * n16 + j] = o[j][v];
     }
   }
   __syncthreads();
 
   // merge the waves: thread -> (g, dim)
   const size_t part0 = ((size_t)u * a.S + split) * G;
-  for (int t = tid; t < G * D; t += kBlock) {
+  for (int t = tid; t < G * D; t += NT) {
     const int g = t / D, dd = t % D;
     float mt = sm[0][g];
 #pragma unroll
@@ -209,7 +247,7 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(const DecodeArgs a) {
     for (int ww = 0; ww < W; ++ww) {
       const float sc = merge_scale(sm[ww][g], mt);
       lt += sl[ww][g] * sc;
-      ot += so[ww][g][dd] * sc;
+      ot += so[((size_t)ww * G + g) * D + dd] * sc;
     }
     if (a.S == 1) {
       const int hq = h * G + g;
@@ -266,7 +304,8 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const DecodeArgs a) {
 
 template <int D>
 static void launch_decode_d(const DecodeArgs& a, dim3 grid, int units, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<D>), grid, dim3(kBlock), 0, st, a);
+  const size_t lds = (size_t)kDecodeWaves * a.G * D * sizeof(float);
+  hipLaunchKernelGGL((decode_kernel<D>), grid, dim3(kDecodeThreads), lds, st, a);
   if (a.S > 1) hipLaunchKernelGGL((combine_kernel<D>), dim3(units), dim3(kBlock), 0, st, a);
 }
 

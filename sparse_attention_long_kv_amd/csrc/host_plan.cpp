@@ -54,7 +54,7 @@ int plan_topm(const sa_shape& s, int n_max, int M, TopmPlan* p) {
 int plan_decode(const sa_shape& s, int M, DecodePlan* p) {
   const int64_t units = (int64_t)s.batch * s.num_kv_heads;
   const int G = s.num_q_heads / s.num_kv_heads;
-  int64_t splits = std::max<int64_t>(1, ceil_div(kTargetBlocks, units));
+  int64_t splits = std::max<int64_t>(1, ceil_div(kDecodeTargetBlocks, units));
   splits = std::min<int64_t>(splits, std::max<int64_t>(1, ceil_div(M, kMinRowsPerSplit)));
   const int64_t rps = ceil_div(M, splits);
   splits = ceil_div(M, rps);          // no empty workgroups

@@ -20,6 +20,7 @@ constexpr int kMergeTile = kBlock * kMaxKeysPerThread;  // keys per merge tile
 constexpr int kMaxSplits = 1024;         // chunks per (b, KV head) unit
 constexpr int kTargetBlocks = 2048;      // enough workgroups for 256 CUs
 constexpr int kMinRowsPerSplit = 64;     // attention rows per workgroup (min)
+constexpr int kDecodeTargetBlocks = 256; // attention workgroups (12 waves) per launch: one per CU
 constexpr size_t kAlign = 256;
 
 struct TopmPlan {

@@ -38,8 +38,13 @@ int plan_topm(const sa_shape& s, int n_max, int M, TopmPlan* p) {
   p->kpt = chunk / kChunkBlock;
   p->splits = (int)splits;
   p->mc = std::min(M, chunk);
-  p->ms = (int)align_up((size_t)p->mc, kBlock);
-  p->multi_tile = splits * p->ms > kMergeTile;
+  // Slots beyond mc let a chunk hand over a superset (every key of the radix
+  // bin holding its M-th largest key, and all higher ones) instead of its
+  // exact top-M; multiples of the merge width map slots to whole merge rows.
+  p->ms = (int)align_up((size_t)std::min(chunk, p->mc + kSupersetSlack), kMergeThreadsHost);
+  const int64_t rows = splits * (p->ms / kMergeThreadsHost);
+  p->merge_kpt = rows <= kMaxMergeKeysPerThread ? (int)align_up((size_t)rows, 4) : 0;
+  if (p->merge_kpt > kMaxMergeKeysPerThread) p->merge_kpt = 0;
   size_t off = 0;
   p->off_cnt = off;
   off = align_up(off + (size_t)units * splits * sizeof(int32_t), kAlign);

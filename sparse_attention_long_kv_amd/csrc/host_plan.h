@@ -21,6 +21,9 @@ constexpr int kMaxSplits = 1024;         // chunks per (b, KV head) unit
 constexpr int kTargetBlocks = 2048;      // enough workgroups for 256 CUs
 constexpr int kMinRowsPerSplit = 64;     // attention rows per workgroup (min)
 constexpr int kDecodeTargetBlocks = 256; // attention workgroups (12 waves) per launch: one per CU
+constexpr int kSupersetSlack = 1024;     // extra candidate slots per chunk (see plan_topm)
+constexpr int kMergeThreadsHost = 1024;  // merge workgroup size
+constexpr int kMaxMergeKeysPerThread = 24;   // register-resident merge (else LDS tiles)
 constexpr size_t kAlign = 256;
 
 struct TopmPlan {
@@ -28,9 +31,9 @@ struct TopmPlan {
   int chunk;        // positions per chunk workgroup (multiple of 512)
   int kpt;          // keys per thread = chunk / 512
   int splits;       // chunks per unit
-  int mc;           // candidates per chunk at most = min(M, chunk)
-  int ms;           // candidate slots per chunk: mc rounded up to 256
-  bool multi_tile;  // merge input exceeds one register tile
+  int mc;           // exact candidates per chunk at most = min(M, chunk)
+  int ms;           // candidate slots per chunk (multiple of 1024, >= mc)
+  int merge_kpt;    // merge keys per thread when registers hold them all, else 0
   size_t off_cnt, off_key, off_pos, end;   // byte offsets in the workspace
 };
 

@@ -183,7 +183,7 @@ struct SelectArgs {
 constexpr int kDigitBits = 12;
 constexpr int kBins = 1 << kDigitBits;      // histogram bins per level
 constexpr int kTopShift = 32 - kDigitBits;  // first-level digit = key >> 20
-constexpr int kListCap = 4224;              // threshold-bin keys kept in LDS (chunks)
+constexpr int kListCap = 6272;              // threshold-bin keys kept in LDS (chunks)
 constexpr int kStageSlots = kListCap / 2 - kWave;   // candidates staged in the list region
 constexpr int kMergeListCap = 1024;         // (merge: its LDS is nearly full)
 constexpr int kRankMax = 256;               // lists up to this size are ranked directly
@@ -315,20 +315,18 @@ __device__ void rank_in_list(Sh& sh, uint32_t n, uint32_t rank, uint32_t& t, uin
   __syncthreads();
 }
 
-// Remaining levels of the exact threshold search.  The first-level histogram
-// (digit key >> 20) is already in sh.hist.  Keys of the chosen first-level bin
-// (usually ~1% of the keys) are compacted into an LDS list -- counted per
+// Remaining levels of the exact threshold search, given the first-level bin
+// `path` (digit key >> 20) and `above` = #keys in higher bins.  Keys of that
+// bin (usually ~1% of the keys) are compacted into an LDS list -- counted per
 // thread, offsets from one block scan, then written -- and the threshold is
 // found there: by direct ranking when the list is short, else by two more
 // radix levels; if the bin overflows the list, those levels run over `visit`.
 // Returns t (the target-th largest key), need = target - #keys > t (how many
 // keys equal to t are selected) and eq = #keys == t.
 template <int NT, class Sh, class Visit>
-__device__ void finish_threshold(Sh& sh, uint32_t target, uint32_t& t_out, uint32_t& need_out,
-                                 uint32_t& eq_out, Visit visit) {
+__device__ void resolve_bin(Sh& sh, uint32_t target, uint32_t path, uint32_t above,
+                            uint32_t& t_out, uint32_t& need_out, uint32_t& eq_out, Visit visit) {
   const int tid = threadIdx.x;
-  uint32_t path = 0, above = 0;
-  pick_bin<NT>(sh, kDigitBits, target, path, above);
   const uint32_t b1 = path;
   uint32_t cnt = 0;
   visit([&](uint32_t k, bool valid) { cnt += (valid && (k >> kTopShift) == b1) ? 1u : 0u; });
@@ -363,6 +361,15 @@ __device__ void finish_threshold(Sh& sh, uint32_t target, uint32_t& t_out, uint3
   need_out = target - above;
   eq_out = sh.pick[2];
   __syncthreads();
+}
+
+// Exact threshold search from the first-level histogram in sh.hist.
+template <int NT, class Sh, class Visit>
+__device__ void finish_threshold(Sh& sh, uint32_t target, uint32_t& t_out, uint32_t& need_out,
+                                 uint32_t& eq_out, Visit visit) {
+  uint32_t path = 0, above = 0;
+  pick_bin<NT>(sh, kDigitBits, target, path, above);
+  resolve_bin<NT>(sh, target, path, above, t_out, need_out, eq_out, visit);
 }
 
 // Emit, in register order (i, wave, lane) -- which callers make equal to
@@ -666,6 +673,68 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const SelectArgs a
   for (int slot = (int)target + tid; slot < M; slot += NT) idx_u[slot] = -1;
 }
 
+// Register-resident merge, used when a unit's candidate slots fit KPT rows of
+// the 1024-thread workgroup (S * ms <= 1024 * KPT, ms a multiple of 1024).
+// Slot f of the flat [S][ms] candidate array is key register f / 1024 of
+// thread f % 1024, so register order (i, wave, lane) is ascending position
+// order (chunks are in position order and so is each chunk's list); slots
+// past a chunk's count hold key 0 ("no position").  Selection then runs
+// exactly as in a chunk: first-level histogram, threshold, ordered emission.
+template <int KPT>
+__global__ __launch_bounds__(kMergeThreads) void merge_regs_kernel(const SelectArgs a) {
+  constexpr int NT = kMergeThreads;
+  __shared__ SelectShared<NT> sh;
+  __shared__ int32_t cnt_s[kMaxMergeKeysPerThread];
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int S = a.S, M = a.M;
+  const int rows_per_chunk = a.ms / NT;
+  for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
+  if (tid < S) cnt_s[tid] = a.cand_cnt[(size_t)u * S + tid];
+  __syncthreads();
+  uint32_t nvalid = 0;
+  for (int c = 0; c < S; ++c) nvalid += (uint32_t)cnt_s[c];
+  const uint32_t* ck = a.cand_key + (size_t)u * S * a.ms;
+  const int32_t* cp = a.cand_pos + (size_t)u * S * a.ms;
+  uint32_t key[KPT];
+  int32_t pos[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int c = i / rows_per_chunk;
+    const int slot = (i - c * rows_per_chunk) * NT + tid;
+    const bool valid = c < S && slot < cnt_s[min(c, S - 1)];
+    const size_t f = (size_t)i * NT + tid;
+    key[i] = valid ? ck[f] : 0u;
+    pos[i] = valid ? cp[f] : -1;
+  }
+  const bool select = nvalid > (uint32_t)M;
+  const uint32_t target = min(nvalid, (uint32_t)M);
+  if (select) {
+    const uint32_t dummy = (uint32_t)(kBins + lane);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) atomicAdd(&sh.hist[key[i] ? (key[i] >> kTopShift) : dummy], 1u);
+    __syncthreads();
+  }
+  // without selection every candidate (key >= 1) is emitted
+  uint32_t t = 1, need = 0, eq = 0;
+  if (select) {
+    finish_threshold<NT>(sh, target, t, need, eq, [&](auto&& f) {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) f(key[i], key[i] != 0u);
+    });
+  }
+  int32_t* idx_u = a.idx + (size_t)u * M;
+  const bool staged = target <= (uint32_t)(kListCap - kWave);
+  int32_t* out = reinterpret_cast<int32_t*>(sh.list);
+  emit_in_order(key, t, need, eq, sh, [&](int i, bool sel, uint32_t slot) {
+    if (staged) out[sel ? slot : (uint32_t)(kListCap - kWave + lane)] = pos[i];
+    else if (sel) idx_u[slot] = pos[i];
+  });
+  if (staged)
+    for (int j = tid; j < (int)target; j += NT) idx_u[j] = out[j];
+  for (int j = (int)target + tid; j < M; j += NT) idx_u[j] = -1;
+}
+
 // ------------------------------------------------------------------ chunks
 
 // One chunk of one unit: keys, chunk-local exact top-M, candidates out.
@@ -757,11 +826,22 @@ __global__ __launch_bounds__(kChunkThreads, 4) void chunk_select_kernel(const Se
     uint32_t t = 1, need = 0, eq = 0;
     if (select) {
       __syncthreads();
-      finish_threshold<NT>(sh, (uint32_t)a.M, t, need, eq, [&](auto&& f) {
+      uint32_t path = 0, above = 0;
+      pick_bin<NT>(sh, kDigitBits, (uint32_t)a.M, path, above);
+      const uint32_t in_bin = sh.pick[2];
+      if (above + in_bin <= (uint32_t)a.ms) {
+        // Superset: every key of the first-level bin holding the M-th largest
+        // key, and every higher key.  It contains the chunk's exact top-M; the
+        // merge selects exactly over the union.
+        t = max(path << kTopShift, 1u);           // key 0 marks no position
+        nsel = (int)(above + in_bin);
+      } else {
+        resolve_bin<NT>(sh, (uint32_t)a.M, path, above, t, need, eq, [&](auto&& f) {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) f(key[i], key[i] != 0u);
-      });
-      nsel = a.M;
+          for (int i = 0; i < KPT; ++i) f(key[i], key[i] != 0u);
+        });
+        nsel = a.M;
+      }
     } else {
       nsel = nv;
     }
@@ -851,7 +931,16 @@ hipError_t run_select(const LaunchCommon& c, const TopmPlan& plan, int stages, b
   }
   if (stages & kSelectMerge) {
     // the kernel boundary orders the candidate writes before the merge's reads
-    hipLaunchKernelGGL(merge_kernel, dim3(plan.units), dim3(kMergeThreads), 0, c.stream, a);
+    const dim3 grid(plan.units), block(kMergeThreads);
+    switch (plan.merge_kpt) {
+      case 4: hipLaunchKernelGGL(merge_regs_kernel<4>, grid, block, 0, c.stream, a); break;
+      case 8: hipLaunchKernelGGL(merge_regs_kernel<8>, grid, block, 0, c.stream, a); break;
+      case 12: hipLaunchKernelGGL(merge_regs_kernel<12>, grid, block, 0, c.stream, a); break;
+      case 16: hipLaunchKernelGGL(merge_regs_kernel<16>, grid, block, 0, c.stream, a); break;
+      case 20: hipLaunchKernelGGL(merge_regs_kernel<20>, grid, block, 0, c.stream, a); break;
+      case 24: hipLaunchKernelGGL(merge_regs_kernel<24>, grid, block, 0, c.stream, a); break;
+      default: hipLaunchKernelGGL(merge_kernel, grid, block, 0, c.stream, a); break;
+    }
     return hipGetLastError();
   }
   return hipSuccess;

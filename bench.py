@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode steps/sec and achieved HBM GB/s at N=128K, M=2048, r=32"
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+DOMINANT_KERNEL = "filter_kernel"
 
 
 def algorithmic_bytes(wl):
@@ -43,8 +44,9 @@ def algorithmic_bytes(wl):
     candidates = units * wl.N * wl.r + q + P       # the FP8 key stream, the queries, P
     merge = idx                                     # the selected positions
     decode = units * wl.M * wl.d * 2 * 2 + idx + q + wl.B * wl.Hq * wl.d * 2
-    return {"append_kv": append, "index_candidates": candidates, "merge_candidates": merge,
-            "decode": decode}
+    # the sampled bound reads a few rows again: no bytes of its own are required
+    return {"append_kv": append, "index_bound": 0, "index_candidates": candidates,
+            "merge_candidates": merge, "decode": decode}
 
 
 def _source_hash(names):
@@ -72,7 +74,7 @@ def measured_traffic(kernel_key, src_hash):
 CALIB_KERNEL_TAG = "neg"      # torch.neg on fp32: reads and writes exactly n*4 bytes
 
 
-def ingest_counters(fetch_csv, write_csv, calib_mib, kernel="chunk_select_kernel"):
+def ingest_counters(fetch_csv, write_csv, calib_mib, kernel=DOMINANT_KERNEL):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
     WRITE_SIZE; both with --calibration-mib) into profiles/traffic.json: each
     counter's per-dispatch mean for `kernel`, scaled by what the same counter
@@ -216,14 +218,18 @@ def main(argv=None):
     scale = default_scale(wl.d)
     torch.cuda.synchronize()
 
-    names = ("append_kv", "index_candidates", "merge_candidates", "decode")
+    names = ("append_kv", "index_bound", "index_candidates", "merge_candidates", "decode")
     ev = {k: [] for k in names}
+
+    def stage(st):
+        return lambda: sa.sparse_attn_index_topm_stage(sh, st, inp.q, inp.P, kp, inp.seq_lens,
+                                                       wl.N, wl.M, idx, ws)
     calls = (
         lambda: sa.sparse_attn_append_kv(sh, inp.pos, inp.k_new, inp.v_new, inp.P, inp.k_cache,
                                          inp.v_cache, kp),
-        lambda: sa.sparse_attn_index_candidates(sh, inp.q, inp.P, kp, inp.seq_lens, wl.N, wl.M,
-                                                ws),
-        lambda: sa.sparse_attn_merge_candidates(sh, wl.N, wl.M, idx, ws),
+        stage(sa.SA_STAGE_BOUND),
+        stage(sa.SA_STAGE_CANDIDATES),
+        stage(sa.SA_STAGE_MERGE),
         lambda: sa.sparse_attn_decode(sh, inp.q, inp.k_cache, inp.v_cache, idx, wl.M, scale,
                                       out, None, ws),
     )
@@ -269,15 +275,16 @@ def main(argv=None):
     steps_per_s = 1e3 / ms_per_step
     hbm_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # dominant kernel: chunk_select_kernel, the one launch of index_candidates
+    # dominant kernel: filter_kernel, the one launch of the candidates stage
     dom = "index_candidates"
     dom_gbps = bytes_k[dom] / (kern_us[dom] * 1e-6) / 1e9
     src_hash = _source_hash(["indexer.hip", "device_common.hpp"])
-    traffic = measured_traffic("chunk_select_kernel", src_hash)
+    traffic = measured_traffic(DOMINANT_KERNEL, src_hash)
     roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
                 "traffic": traffic,
-                "kernel": "chunk_select_kernel (sparse_attn_index_candidates)",
+                "kernel": "%s (sparse_attn_index_topm_stage, SA_STAGE_CANDIDATES)"
+                          % DOMINANT_KERNEL,
                 "bytes_per_launch": bytes_k[dom], "avg_launch_us": round(kern_us[dom], 2),
                 "source_hash": src_hash}
 
@@ -295,7 +302,8 @@ def main(argv=None):
         "tokens_per_s": round(steps_per_s * wl.B, 1),
         "step_bytes": step_bytes,
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
-        "kernel_gbps": {k: round(bytes_k[k] / (kern_us[k] * 1e-6) / 1e9, 1) for k in kern_us},
+        "kernel_gbps": {k: round(bytes_k[k] / (kern_us[k] * 1e-6) / 1e9, 1) for k in kern_us
+                        if bytes_k[k]},
         "roofline": roofline,
         "cpu_baseline": None,
     }

@@ -163,24 +163,29 @@ int sparse_attn_index_topm(const sa_shape* shape, const void* q, const float* P,
                            void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
- * sparse_attn_index_candidates + sparse_attn_merge_candidates -- the two
- * launches of sparse_attn_index_topm as separate calls (same selection as
- * above; useful to time, overlap or schedule the scoring stream apart from
- * the per-head merge).
+ * sparse_attn_index_topm_stage -- sparse_attn_index_topm as its three
+ * launches, one call each, for callers that time, overlap or schedule them
+ * separately.  Same selection and arguments as sparse_attn_index_topm; run
+ * the stages in order on one stream with the same shape, n_max, M and
+ * workspace, and let nothing else use the workspace in between.
  *
- * index_candidates scores every position in [0, min(seq_lens[b], n_max)) and
- * leaves, in `workspace`, each position chunk's own top-M (an exact superset
- * of the head's top-M).  merge_candidates reads them back and writes idx
- * exactly as sparse_attn_index_topm does.  Between the two calls the
- * workspace belongs to them: both must see the same shape, n_max and M, be
- * ordered on one stream, and nothing else may use the workspace in between.
- * Arguments as in sparse_attn_index_topm.
+ *   SA_STAGE_BOUND       per (b, KV head): a lower bound on the M-th largest
+ *                        score from a sample of the positions (a no-op for
+ *                        shapes that use the chunk-exact method below);
+ *   SA_STAGE_CANDIDATES  score every position; keep, per position chunk, the
+ *                        keys at or above the bound (or the chunk's exact
+ *                        top-M, chunk-exact method);
+ *   SA_STAGE_MERGE       exact top-M over the kept keys, written to idx (a
+ *                        head whose bound turned out too high is selected
+ *                        again exactly from the FP8 cache).
+ * idx is only written by SA_STAGE_MERGE (and may be NULL for the others).
+ * Returns SA_ERR_INVALID for an unknown stage.
  * ------------------------------------------------------------------------- */
-int sparse_attn_index_candidates(const sa_shape* shape, const void* q, const float* P,
-                                 const uint8_t* kp_cache, const int32_t* seq_lens,
-                                 int32_t n_max, int32_t M,
-                                 void* workspace, size_t ws_bytes, void* stream);
-int sparse_attn_merge_candidates(const sa_shape* shape, int32_t n_max, int32_t M,
+enum sa_stage { SA_STAGE_BOUND = 1, SA_STAGE_CANDIDATES = 2, SA_STAGE_MERGE = 3 };
+
+int sparse_attn_index_topm_stage(const sa_shape* shape, int32_t stage, const void* q,
+                                 const float* P, const uint8_t* kp_cache,
+                                 const int32_t* seq_lens, int32_t n_max, int32_t M,
                                  int32_t* idx, void* workspace, size_t ws_bytes,
                                  void* stream);
 

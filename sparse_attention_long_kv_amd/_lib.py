@@ -61,8 +61,8 @@ _SIGS = {
     "sparse_attn_index_score": [_SP, _VP, _VP, _VP, _VP, _I32, _VP, _VP],
     "sparse_attn_topm": [_SP, _VP, _VP, _I32, _I32, _VP, _VP, _SZ, _VP],
     "sparse_attn_index_topm": [_SP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _SZ, _VP],
-    "sparse_attn_index_candidates": [_SP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _SZ, _VP],
-    "sparse_attn_merge_candidates": [_SP, _I32, _I32, _VP, _VP, _SZ, _VP],
+    "sparse_attn_index_topm_stage": [_SP, _I32, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _SZ,
+                                     _VP],
     "sparse_attn_decode": [_SP, _VP, _VP, _VP, _VP, _I32, ctypes.c_float, _VP, _VP, _VP,
                            _SZ, _VP],
     "sparse_attn_linear_gate": [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP],
@@ -202,22 +202,20 @@ def sparse_attn_index_topm(shape, q, P, kp_cache, seq_lens, n_max, M, idx, works
           _dev_ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), _stream(q))
 
 
-def sparse_attn_index_candidates(shape, q, P, kp_cache, seq_lens, n_max, M, workspace):
+SA_STAGE_BOUND, SA_STAGE_CANDIDATES, SA_STAGE_MERGE = 1, 2, 3
+
+
+def sparse_attn_index_topm_stage(shape, stage, q, P, kp_cache, seq_lens, n_max, M, idx,
+                                 workspace):
     B, Hq, Hkv, d, r, Nc = (shape.batch, shape.num_q_heads, shape.num_kv_heads,
                             shape.head_dim, shape.rank, shape.capacity)
-    _call("sparse_attn_index_candidates", _sh(shape),
+    _call("sparse_attn_index_topm_stage", _sh(shape), int(stage),
           _dev_ptr(q, torch.bfloat16, (B, Hq, d), "q"),
           _dev_ptr(P, torch.float32, (Hkv, d, r), "P"),
           _dev_ptr(kp_cache, torch.uint8, (B, Hkv, Nc, r), "kp_cache"),
           _opt_ptr(seq_lens, torch.int32, (B,), "seq_lens"), int(n_max), int(M),
+          _opt_ptr(idx, torch.int32, (B, Hkv, M), "idx"),
           _dev_ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), _stream(q))
-
-
-def sparse_attn_merge_candidates(shape, n_max, M, idx, workspace):
-    B, Hkv = shape.batch, shape.num_kv_heads
-    _call("sparse_attn_merge_candidates", _sh(shape), int(n_max), int(M),
-          _dev_ptr(idx, torch.int32, (B, Hkv, M), "idx"),
-          _dev_ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), _stream(idx))
 
 
 def sparse_attn_decode(shape, q, k_cache, v_cache, idx, M, softmax_scale, out, lse, workspace):

@@ -114,51 +114,58 @@ extern "C" int sparse_attn_topm(const sa_shape* shape, const float* scores,
                 c.stream);
 }
 
+namespace {
+
+// Launches stage mask `stages` of the fused selection (all of it for
+// sparse_attn_index_topm).
+int index_topm_stages(const sa_shape* shape, int stages, const void* q, const float* P,
+                      const uint8_t* kp_cache, const int32_t* seq_lens, int32_t n_max, int32_t M,
+                      int32_t* idx, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  if (!ptr_ok(q, A16) || !ptr_ok(P, A4) || !ptr_ok(kp_cache, A16)) return SA_ERR_INVALID;
+  TopmPlan plan;
+  st = check_topm_common(shape, seq_lens, n_max, M, idx, workspace, ws_bytes, &plan,
+                         /*need_idx=*/(stages & kSelectMerge) != 0);
+  if (st != SA_OK) return st;
+  FilterPlan fplan;
+  st = plan_filter(*shape, n_max, M, &fplan);
+  if (st != SA_OK) return st;
+  const LaunchCommon c = common(*shape, stream);
+  if (fplan.enabled)
+    return finish(run_filter_select(c, fplan, stages, q, P, kp_cache, seq_lens, n_max, M, idx,
+                                    workspace),
+                  c.stream);
+  if ((stages & (kSelectChunks | kSelectMerge)) == 0) return SA_OK;
+  return finish(run_select(c, plan, stages & (kSelectChunks | kSelectMerge), true, q, P, kp_cache,
+                           nullptr, seq_lens, n_max, M, idx, workspace),
+                c.stream);
+}
+
+}  // namespace
+
 extern "C" int sparse_attn_index_topm(const sa_shape* shape, const void* q, const float* P,
                                       const uint8_t* kp_cache, const int32_t* seq_lens,
                                       int32_t n_max, int32_t M, int32_t* idx, void* workspace,
                                       size_t ws_bytes, void* stream) {
-  int st = check_shape(shape);
-  if (st != SA_OK) return st;
-  if (!ptr_ok(q, A16) || !ptr_ok(P, A4) || !ptr_ok(kp_cache, A16)) return SA_ERR_INVALID;
-  TopmPlan plan;
-  st = check_topm_common(shape, seq_lens, n_max, M, idx, workspace, ws_bytes, &plan);
-  if (st != SA_OK) return st;
-  const LaunchCommon c = common(*shape, stream);
-  return finish(run_select(c, plan, kSelectChunks | kSelectMerge, true, q, P, kp_cache, nullptr,
-                           seq_lens, n_max, M, idx, workspace),
-                c.stream);
+  return index_topm_stages(shape, kSelectBound | kSelectChunks | kSelectMerge, q, P, kp_cache,
+                           seq_lens, n_max, M, idx, workspace, ws_bytes, stream);
 }
 
-extern "C" int sparse_attn_index_candidates(const sa_shape* shape, const void* q, const float* P,
-                                            const uint8_t* kp_cache, const int32_t* seq_lens,
-                                            int32_t n_max, int32_t M, void* workspace,
-                                            size_t ws_bytes, void* stream) {
-  int st = check_shape(shape);
-  if (st != SA_OK) return st;
-  if (!ptr_ok(q, A16) || !ptr_ok(P, A4) || !ptr_ok(kp_cache, A16)) return SA_ERR_INVALID;
-  TopmPlan plan;
-  st = check_topm_common(shape, seq_lens, n_max, M, nullptr, workspace, ws_bytes, &plan,
-                         /*need_idx=*/false);
-  if (st != SA_OK) return st;
-  const LaunchCommon c = common(*shape, stream);
-  return finish(run_select(c, plan, kSelectChunks, true, q, P, kp_cache, nullptr, seq_lens, n_max,
-                           M, nullptr, workspace),
-                c.stream);
-}
-
-extern "C" int sparse_attn_merge_candidates(const sa_shape* shape, int32_t n_max, int32_t M,
+extern "C" int sparse_attn_index_topm_stage(const sa_shape* shape, int32_t stage, const void* q,
+                                            const float* P, const uint8_t* kp_cache,
+                                            const int32_t* seq_lens, int32_t n_max, int32_t M,
                                             int32_t* idx, void* workspace, size_t ws_bytes,
                                             void* stream) {
-  int st = check_shape(shape);
-  if (st != SA_OK) return st;
-  TopmPlan plan;
-  st = check_topm_common(shape, nullptr, n_max, M, idx, workspace, ws_bytes, &plan);
-  if (st != SA_OK) return st;
-  const LaunchCommon c = common(*shape, stream);
-  return finish(run_select(c, plan, kSelectMerge, true, nullptr, nullptr, nullptr, nullptr,
-                           nullptr, n_max, M, idx, workspace),
-                c.stream);
+  int mask;
+  switch (stage) {
+    case SA_STAGE_BOUND: mask = kSelectBound; break;
+    case SA_STAGE_CANDIDATES: mask = kSelectChunks; break;
+    case SA_STAGE_MERGE: mask = kSelectMerge; break;
+    default: return SA_ERR_INVALID;
+  }
+  return index_topm_stages(shape, mask, q, P, kp_cache, seq_lens, n_max, M, idx, workspace,
+                           ws_bytes, stream);
 }
 
 extern "C" int sparse_attn_decode(const sa_shape* shape, const void* q, const void* k_cache,

@@ -78,6 +78,46 @@ int plan_decode(const sa_shape& s, int M, DecodePlan* p) {
   return SA_OK;
 }
 
+int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* p) {
+  const int64_t units = (int64_t)s.batch * s.num_kv_heads;
+  *p = FilterPlan{};
+  p->units = (int)units;
+  if (n_max > kFilterMaxN || M > kFilterMaxM || M >= n_max) return SA_OK;
+  // chunks as large as 16384 positions, smaller while the grid is short of
+  // 1024 workgroups, but never more than 32 per unit (lists keep >= 128 slots)
+  int64_t chunk = kMaxChunk;
+  while (chunk > 2048 && units * ceil_div(n_max, chunk) < 1024) chunk >>= 1;
+  int64_t splits = ceil_div(n_max, chunk);
+  const int64_t max_splits = kFilterSlots / (kFilterWaves * kFilterMinCap);
+  if (splits > max_splits) {
+    chunk = align_up((size_t)ceil_div(n_max, max_splits), kChunkBlock);
+    splits = ceil_div(n_max, chunk);
+  }
+  const int64_t lists = splits * kFilterWaves;
+  int64_t cap = kFilterMinCap;
+  while (cap < kFilterMaxCap && cap * 2 * lists <= kFilterSlots) cap *= 2;
+  if (chunk > (int64_t)kFilterMaxRows * kChunkBlock) return SA_OK;
+  p->enabled = true;
+  p->chunk = (int)chunk;
+  p->splits = (int)splits;
+  p->cap = (int)cap;
+  p->cslots = (int)(cap * kFilterWaves);
+  p->rows = (int)ceil_div(splits * p->cslots, kMergeThreadsHost);
+  size_t off = 0;
+  p->off_thr = off;
+  off = align_up(off + (size_t)units * sizeof(uint32_t), kAlign);
+  p->off_qt = off;
+  off = align_up(off + (size_t)units * 32 * sizeof(float), kAlign);
+  p->off_cnt = off;
+  off = align_up(off + (size_t)units * splits * sizeof(int32_t), kAlign);
+  p->off_key = off;
+  off = align_up(off + (size_t)units * splits * p->cslots * sizeof(uint32_t), kAlign);
+  p->off_pos = off;
+  off = align_up(off + (size_t)units * splits * p->cslots * sizeof(int32_t), kAlign);
+  p->end = off;
+  return SA_OK;
+}
+
 size_t workspace_bytes(const sa_shape& s, int n_max, int M) {
   if (check_shape(&s) != SA_OK) return 0;
   if (n_max < 1 || n_max > s.capacity || M < 1) return 0;
@@ -88,6 +128,9 @@ size_t workspace_bytes(const sa_shape& s, int n_max, int M) {
     TopmPlan tp;
     if (plan_topm(s, n_max, M, &tp) != SA_OK) return 0;
     need = std::max(need, tp.end);
+    FilterPlan fp;
+    if (plan_filter(s, n_max, M, &fp) != SA_OK) return 0;
+    if (fp.enabled) need = std::max(need, fp.end);
   }
   return need;
 }

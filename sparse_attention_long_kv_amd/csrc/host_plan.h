@@ -37,6 +37,33 @@ struct TopmPlan {
   size_t off_cnt, off_key, off_pos, end;   // byte offsets in the workspace
 };
 
+// Filter path of the fused selection: a sampled per-unit lower bound on the
+// M-th score, chunks that keep only the keys at or above it (per-wave lists,
+// no per-chunk selection), and a merge that selects exactly over the lists
+// and falls back to an exact pass over the unit when the bound was too high
+// or a list overflowed.
+constexpr int kFilterMaxN = 1 << 19;     // merge marks selected positions in an LDS bitmap
+constexpr int kFilterMaxM = 6144;        // selected positions staged in LDS by the merge
+constexpr int kFilterSlots = 16384;      // candidate slots per unit (16 per merge thread)
+constexpr int kFilterMinCap = 128;       // slots per wave list, at least
+constexpr int kFilterMaxCap = 256;       // slots per wave list, at most (staged in LDS)
+constexpr int kFilterMaxRows = 64;       // 512-position rows per filter chunk, at most
+constexpr int kFilterWaves = 8;          // lists per chunk (one per wave of 512 threads)
+constexpr int kSampleBlocks = 512;       // sampled position blocks per unit
+constexpr int kSampleBlock = 8;          // positions per sampled block (256 B of FP8 rows)
+constexpr int kSampleSafety = 3;         // the bound aims at ~3 M keys per unit
+
+struct FilterPlan {
+  bool enabled;
+  int units;
+  int chunk;        // positions per filter workgroup (multiple of 512)
+  int splits;       // chunks per unit
+  int cap;          // slots per wave list (power of two)
+  int cslots;       // candidate slots per chunk = 8 * cap
+  int rows;         // merge rows per thread = splits * cslots / 1024
+  size_t off_thr, off_qt, off_cnt, off_key, off_pos, end;
+};
+
 struct DecodePlan {
   int units;
   int splits;           // workgroups per unit
@@ -53,6 +80,8 @@ bool ptr_ok(const void* p, size_t align);
 
 int plan_topm(const sa_shape& s, int n_max, int M, TopmPlan* out);
 int plan_decode(const sa_shape& s, int M, DecodePlan* out);
+// Fills `out`; out->enabled is false when the shape needs the chunk-exact path.
+int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* out);
 size_t workspace_bytes(const sa_shape& s, int n_max, int M);
 
 }  // namespace sa

@@ -30,25 +30,44 @@ namespace sa {
 
 // ------------------------------------------------------------------ query
 
-// qt (R floats, LDS) for unit (b, h).  `part` is NT doubles of LDS.
-// Every thread of the block must call this (it synchronises).
+// qt (R floats, LDS) for unit (b, h).  `part` is max(8R, D) doubles of LDS
+// (it first holds the group-mean query, then the partial sums).  The fp64 sums run
+// in the same order whatever the workgroup size (mean over the group in head
+// order; 8 parts of d/8 basis rows, then the parts in order), so every kernel
+// forms the same qt bits.  Every thread of the block must call this (it
+// synchronises).
 template <int D, int R, int NT = kBlock>
 __device__ void indexer_query(const uint16_t* __restrict__ q, const float* __restrict__ P,
                               int b, int h, int G, int Hq, float* qt, double* part) {
-  constexpr int kParts = NT / R;         // basis-row groups, one partial sum each
+  constexpr int kParts = 8;              // basis-row groups, one partial sum each
   constexpr int kPer = D / kParts;       // basis rows per part
+  static_assert(NT >= kParts * R && NT >= D, "workgroup too small for the query");
+  static_assert(kParts * R <= NT && D <= NT, "part holds NT doubles");
   const int t = threadIdx.x;
   const int j = t % R, pi = t / R;
   const uint16_t* qb = q + ((size_t)b * Hq + (size_t)h * G) * D;
   const float* Ph = P + (size_t)h * D * R;
-  double acc = 0.0;
-  for (int k = 0; k < kPer; ++k) {
-    const int i = pi * kPer + k;
-    double qs = 0.0;
-    for (int g = 0; g < G; ++g) qs += (double)__uint_as_float((uint32_t)qb[g * D + i] << 16);
-    acc = fma(qs / (double)G, (double)Ph[i * R + j], acc);
+  // this thread's basis entries, loaded before the mean is formed
+  float pv[kPer];
+  if (t < kParts * R) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) pv[k] = Ph[(pi * kPer + k) * R + j];
   }
-  part[t] = acc;
+  double mean = 0.0;
+  if (t < D) {
+    for (int g = 0; g < G; ++g) mean += (double)__uint_as_float((uint32_t)qb[g * D + t] << 16);
+    mean = mean / (double)G;
+  }
+  __syncthreads();                       // `part` may still be read by a previous call
+  if (t < D) part[t] = mean;
+  __syncthreads();
+  double acc = 0.0;
+  if (t < kParts * R) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) acc = fma(part[pi * kPer + k], (double)pv[k], acc);
+  }
+  __syncthreads();
+  if (t < kParts * R) part[t] = acc;
   __syncthreads();
   if (t < R) {
     double s = 0.0;
@@ -872,6 +891,496 @@ __global__ __launch_bounds__(kChunkThreads, 4) void chunk_select_kernel(const Se
     }
   }
   if (tid == 0) a.cand_cnt[(size_t)u * a.S + c] = nsel;
+}
+
+// ------------------------------------------------------------------ filter path
+//
+// The fused selection's main path for contexts up to 2^19 positions:
+//  1. sample_kernel: per unit, score 32 evenly spread blocks of 128 positions
+//     and take the k-th largest sample key, k ~ 2 M (sample size) / len, as a
+//     bound thr that about 2M keys of the unit reach (the whole unit when it
+//     has at most 4096 positions: then k = M and thr is the exact M-th key).
+//  2. filter_kernel: chunks of the unit stream their FP8 rows, score every
+//     position and append each key >= thr, with its position, to an LDS list
+//     of the wave that scored it (ballot + bit count, no key held in
+//     registers); at the end the wave lists are interleaved back into
+//     position order with one block scan over per-(row, wave) counts and
+//     written out as the chunk's candidates.
+//  3. filter_merge_kernel: if no list overflowed and at least M keys reached
+//     thr, then thr <= the M-th largest key of the unit, so the candidates
+//     hold every selected position; they are loaded into registers in
+//     position order, the exact M-th key is found among them and idx is
+//     emitted in order, as in the chunk-exact merge.  Otherwise the
+//     workgroup selects exactly by streaming the unit's rows again and
+//     marking the selection in an LDS bitmap (slow but rare).
+// Keys are bit-identical to the chunk-exact path's, so both give the same idx.
+
+// Inclusive prefix sum over the block in thread order (wtot: NT/64 words of LDS).
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan_small(uint32_t v, uint32_t* wtot, uint32_t& total) {
+  constexpr int W = NT / kWave;
+  const int w = threadIdx.x / kWave;
+  const uint32_t inc = wave_inclusive_scan(v);
+  __syncthreads();
+  if (lane_id() == kWave - 1) wtot[w] = inc;
+  __syncthreads();
+  uint32_t wb = 0, tot = 0;
+#pragma unroll
+  for (int ww = 0; ww < W; ++ww) {
+    wb += ww < w ? wtot[ww] : 0u;
+    tot += wtot[ww];
+  }
+  total = tot;
+  return wb + inc;
+}
+
+struct FilterArgs {
+  const uint16_t* q;
+  const float* P;
+  const uint8_t* kp;
+  const int32_t* seq_lens;
+  int n_max, Ncap, Hq, Hkv, G, M, S, chunk, cap, cslots, cslots_log2, rows;
+  uint32_t* thr;     // [units]
+  float* qt;         // [units][32] indexer queries (written by the bound stage)
+  int32_t* cnt;      // [units][S] kept keys per chunk, -1 when a wave list overflowed
+  uint32_t* ckey;    // [units][S][cslots] kept keys in position order (cslots = 8 cap)
+  int32_t* cpos;
+  int32_t* idx;
+};
+
+constexpr int kSampleThreads = kMergeThreads;
+constexpr int kSampleKeys = kSampleBlocks * kSampleBlock / kSampleThreads;
+constexpr int kBitmapWords = kFilterMaxN / 32;
+constexpr int kFilterMergeKeys = kFilterSlots / kMergeThreads;   // 16 per thread
+static_assert(kFilterMaxCap * kFilterWaves <= kFilterSlots, "a chunk's slots fit the merge");
+
+__device__ __forceinline__ int unit_len(const int32_t* seq_lens, int b, int n_max) {
+  return seq_lens ? min(max(seq_lens[b], 0), n_max) : n_max;
+}
+
+// Score of one whole position by one thread: the same 16-code chains, added
+// in the same order, as the paired-lane scoring, hence the same bits.
+template <int R>
+__device__ __forceinline__ float position_score(const float (&qlo)[16], const float (&qhi)[16],
+                                                const uint8_t* row) {
+  const uint4 c0 = load16(row);
+  float s = score16(qlo, c0);
+  if (R == 32) s = s + score16(qhi, load16(row + 16));
+  return s;
+}
+
+template <int R>
+__device__ __forceinline__ void query_halves(const float* qt, float (&qlo)[16], float (&qhi)[16]) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    qlo[k] = qt[k];
+    qhi[k] = R == 32 ? qt[16 + k] : 0.0f;
+  }
+}
+
+template <int D, int R>
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(const FilterArgs a) {
+  constexpr int NT = kSampleThreads;
+  __shared__ SelectShared<NT> sh;
+  const int u = blockIdx.x, b = u / a.Hkv, h = u % a.Hkv;
+  const int tid = threadIdx.x;
+  const int len = unit_len(a.seq_lens, b, a.n_max);
+  for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
+  indexer_query<D, R, NT>(a.q, a.P, b, h, a.G, a.Hq, sh.qt, sh.part);
+  if (tid < R) a.qt[(size_t)u * 32 + tid] = sh.qt[tid];
+  if (len <= a.M) {                                   // every valid position is selected
+    if (tid == 0) a.thr[u] = 1u;
+    return;
+  }
+  float qlo[16], qhi[16];
+  query_halves<R>(sh.qt, qlo, qhi);
+  // blocks of 8 consecutive positions, evenly spread over [0, len)
+  constexpr int kTotal = kSampleBlocks * kSampleBlock;
+  const bool all = len <= kTotal;
+  const uint8_t* kpu = a.kp + (size_t)u * a.Ncap * R;
+  uint32_t key[kSampleKeys];
+  uint4 c0[kSampleKeys], c1[kSampleKeys];
+  bool ok[kSampleKeys];
+#pragma unroll
+  for (int i = 0; i < kSampleKeys; ++i) {           // all row loads first
+    const int slot = i * NT + tid;
+    const int blk = slot / kSampleBlock, off = slot % kSampleBlock;
+    const int p = all ? slot
+                      : (int)(((int64_t)blk * (len - kSampleBlock)) / (kSampleBlocks - 1)) + off;
+    ok[i] = p < len;
+    const uint8_t* row = kpu + (size_t)(ok[i] ? p : 0) * R;
+    c0[i] = load16(row);
+    if (R == 32) c1[i] = load16(row + 16);
+  }
+#pragma unroll
+  for (int i = 0; i < kSampleKeys; ++i) {
+    float s = score16(qlo, c0[i]);
+    if (R == 32) s = s + score16(qhi, c1[i]);
+    key[i] = ok[i] ? score_key(s + 0.0f) : 0u;
+  }
+  // the k-th largest sample key, k ~ kSampleSafety * M * (sample size) / len;
+  // a sample of the whole unit gives the exact M-th key
+  const int ns = all ? len : kTotal;
+  uint32_t k = all ? (uint32_t)a.M
+                   : (uint32_t)min((int64_t)ns,
+                                   ((int64_t)kSampleSafety * a.M * ns + len - 1) / len);
+  k = max(k, 1u);
+  const uint32_t dummy = (uint32_t)(kBins + lane_id());
+#pragma unroll
+  for (int i = 0; i < kSampleKeys; ++i)
+    atomicAdd(&sh.hist[key[i] ? (key[i] >> kTopShift) : dummy], 1u);
+  __syncthreads();
+  uint32_t t, need, eq;
+  finish_threshold<NT>(sh, k, t, need, eq, [&](auto&& f) {
+#pragma unroll
+    for (int i = 0; i < kSampleKeys; ++i) f(key[i], key[i] != 0u);
+  });
+  if (tid == 0) a.thr[u] = t;
+}
+
+template <int D, int R>
+__global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs a) {
+  constexpr int NT = kChunkThreads;
+  __shared__ float qt[32];
+  // each wave's list is staged here, then interleaved into position order
+  __shared__ uint32_t sk[kFilterWaves][kFilterMaxCap];
+  __shared__ int32_t sp[kFilterWaves][kFilterMaxCap];
+  __shared__ uint32_t rowcnt[kFilterWaves][kFilterMaxRows];   // kept keys per (wave, row)
+  __shared__ uint32_t rowoff[kFilterWaves][kFilterMaxRows];   // output offset per (wave, row)
+  __shared__ uint32_t rowfirst[kFilterWaves][kFilterMaxRows]; // list index of a row's first key
+  __shared__ uint32_t wtot[NT / kWave];
+  __shared__ int ovf;
+  const int u = blockIdx.x / a.S, c = blockIdx.x % a.S;
+  const int b = u / a.Hkv, h = u % a.Hkv;
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int len = unit_len(a.seq_lens, b, a.n_max);
+  const int base = c * a.chunk;
+  const int nv = min(max(len - base, 0), a.chunk);
+  int32_t* cnt = a.cnt + (size_t)u * a.S + c;
+  if (len <= a.M || nv == 0) {                        // block-uniform
+    if (threadIdx.x == 0) *cnt = 0;
+    return;
+  }
+  const uint32_t thr = a.thr[u];
+  uint32_t* lk = a.ckey + ((size_t)u * a.S + c) * a.cslots;
+  int32_t* lp = a.cpos + ((size_t)u * a.S + c) * a.cslots;
+  // this chunk's rows only: loads past the valid positions return zero
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(a.kp + ((size_t)u * a.Ncap + base) * R, (uint32_t)nv * R);
+  const uint32_t voff = (uint32_t)(w * kWave * R + lane * 16);
+  constexpr int kLoadsPerIter = R / 16;
+  constexpr int kBatch = SA_CHUNK_LOADS_IN_FLIGHT / kLoadsPerIter;
+  // Two register sets: while one batch of rows is scored the next one is in
+  // flight (software pipelining keeps the memory queue full).
+  struct Batch {
+    uint4 a[kBatch], b[kBatch];
+  };
+  auto load_batch = [&](Batch& bt, int i0) {
+#pragma unroll
+    for (int x = 0; x < kBatch; ++x) {
+      const uint32_t off = voff + (uint32_t)((i0 + x) * NT * R);
+      bt.a[x] = buffer_load16(rs, off, 0);
+      if (R == 32) bt.b[x] = buffer_load16(rs, off + 1024, 0);
+    }
+  };
+  const int rows = (nv + NT - 1) / NT;
+  Batch b0, b1;
+  load_batch(b0, 0);
+  if (kBatch < rows) load_batch(b1, kBatch);
+  if (threadIdx.x < R) qt[threadIdx.x] = a.qt[(size_t)u * 32 + threadIdx.x];
+  __syncthreads();
+  float ql[16];
+  lane_query<R>(qt, ql);
+  uint32_t wc = 0;                                    // keys this wave appended so far
+  auto score_batch = [&](const Batch& bt, int i0) {
+#pragma unroll
+    for (int x = 0; x < kBatch; ++x) {
+      const int p = base + (i0 + x) * NT + w * kWave + lane;
+      float s;
+      if (R == 16) {
+        s = lane_score<R>(ql, bt.a[x]);
+      } else {
+        const float sa = lane_score<R>(ql, bt.a[x]);
+        const float sb = lane_score<R>(ql, bt.b[x]);
+        const float xv = (lane & 1) ? sb : sa;
+        const int src = (lane < 32) ? 2 * lane : 2 * (lane - 32) + 1;
+        s = __shfl(xv, src, kWave);
+      }
+      const uint32_t key = score_key(s + 0.0f);
+      const bool sel = p < len && key >= thr;
+      const uint64_t m = ballot(sel);
+      const uint32_t slot = wc + __builtin_amdgcn_mbcnt_hi(
+                                     (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (sel && slot < (uint32_t)a.cap) {
+        sk[w][slot] = key;
+        sp[w][slot] = p;
+      }
+      rowcnt[w][i0 + x] = (uint32_t)popc64(m);        // same value from every lane
+      wc += (uint32_t)popc64(m);
+    }
+  };
+  for (int i0 = 0; i0 < rows; i0 += 2 * kBatch) {    // block-uniform trip count
+    score_batch(b0, i0);
+    if (i0 + 2 * kBatch < rows) load_batch(b0, i0 + 2 * kBatch);
+    if (i0 + kBatch < rows) {
+      score_batch(b1, i0 + kBatch);
+      if (i0 + 3 * kBatch < rows) load_batch(b1, i0 + 3 * kBatch);
+    }
+  }
+  // Position order: key j of wave w's list sits in row i; it goes to
+  //   (keys of all (row, wave) before (i, w)) + (j - first index of row i).
+  if (threadIdx.x == 0) ovf = 0;
+  __syncthreads();
+  if (lane == 0 && wc > (uint32_t)a.cap) ovf = 1;
+  const int nrow = min(rows, kFilterMaxRows);
+  {
+    const uint32_t v = lane < nrow ? rowcnt[w][lane] : 0u;
+    const uint32_t incl = wave_inclusive_scan(v);
+    if (lane < nrow) rowfirst[w][lane] = incl - v;
+  }
+  const int tid = threadIdx.x;
+  const int gi = tid / kFilterWaves, gw = tid % kFilterWaves;     // (row, wave) order
+  const uint32_t v = gi < nrow ? rowcnt[gw][gi] : 0u;
+  uint32_t total;
+  const uint32_t incl = block_scan_small<NT>(v, wtot, total);
+  if (gi < nrow) rowoff[gw][gi] = incl - v;
+  __syncthreads();
+  const bool overflow = ovf != 0;
+  if (!overflow) {
+    const int n = (int)wc;
+    for (int j = lane; j < n; j += kWave) {
+      const int32_t p = sp[w][j];
+      const int i = (p - base) / NT;
+      const uint32_t o = rowoff[w][i] + ((uint32_t)j - rowfirst[w][i]);
+      lk[o] = sk[w][j];
+      lp[o] = p;
+    }
+  }
+  if (tid == 0) *cnt = overflow ? -1 : (int)total;
+}
+
+// Mark the selected positions of a unit in `bm` (bit p = position p) and
+// write them to idx in ascending order.  visit(f) calls f(key, pos, valid)
+// for every key of the unit that may be selected (every key >= t at least).
+// Selection: every key > t and, of the keys == t, the `need` lowest positions
+// (found as the top `need` of the keys ~pos).  Fills idx[0, M) completely.
+template <int NT, class Visit>
+__device__ void emit_bitmap(SelectShared<NT>& sh, uint32_t* bm, int len, uint32_t t,
+                            uint32_t need, uint32_t eq, int M, int32_t* idx_u, Visit visit) {
+  const int tid = threadIdx.x, lane = lane_id();
+  const int words = (len + 31) >> 5;
+  for (int j = tid; j < words; j += NT) bm[j] = 0u;
+  __syncthreads();
+  const bool single = need == eq;
+  visit([&](uint32_t k, int p, bool valid) {
+    if (valid && (k > t || (single && k == t))) atomicOr(&bm[p >> 5], 1u << (p & 31));
+  });
+  if (!single) {
+    // ties straddle the cut: rank the tied positions, lowest first
+    for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
+    __syncthreads();
+    const uint32_t dummy = (uint32_t)(kBins + lane);
+    visit([&](uint32_t k, int p, bool valid) {
+      const bool e = valid && k == t;
+      atomicAdd(&sh.hist[e ? (~(uint32_t)p >> kTopShift) : dummy], 1u);
+    });
+    __syncthreads();
+    uint32_t tp, np, ep;
+    finish_threshold<NT>(sh, need, tp, np, ep, [&](auto&& f) {
+      visit([&](uint32_t k, int p, bool valid) { f(~(uint32_t)p, valid && k == t); });
+    });
+    const int last = (int)~tp;                        // highest tied position selected
+    visit([&](uint32_t k, int p, bool valid) {
+      if (valid && k == t && p <= last) atomicOr(&bm[p >> 5], 1u << (p & 31));
+    });
+  }
+  __syncthreads();
+  // ascending positions: thread j owns a contiguous run of words
+  const int wpt = (words + NT - 1) / NT;
+  const int w0 = min(tid * wpt, words), w1 = min(w0 + wpt, words);
+  uint32_t mine = 0;
+  for (int j = w0; j < w1; ++j) mine += (uint32_t)__builtin_popcount(bm[j]);
+  uint32_t total;
+  uint32_t off = block_inclusive_scan<NT>(mine, sh, total) - mine;
+  int32_t* out = reinterpret_cast<int32_t*>(sh.list);   // free now; holds >= kFilterMaxM
+  const bool staged = M <= kListCap;
+  for (int j = w0; j < w1; ++j) {
+    uint32_t x = bm[j];
+    while (x) {
+      const int bit = __builtin_ctz(x);
+      x &= x - 1u;
+      const int32_t pos = j * 32 + bit;
+      if (off < (uint32_t)M) {
+        if (staged) out[off] = pos;
+        else idx_u[off] = pos;
+      }
+      ++off;
+    }
+  }
+  __syncthreads();
+  if (staged)
+    for (int j = tid; j < M; j += NT) idx_u[j] = j < (int)total ? out[j] : -1;
+  else
+    for (int j = (int)total + tid; j < M; j += NT) idx_u[j] = -1;
+}
+
+// Exact selection of one unit by streaming its rows again (the filter's
+// bound was above the M-th key, or a list overflowed).
+template <int D, int R>
+__device__ __forceinline__ void select_unit_streaming(const FilterArgs& a, SelectShared<kMergeThreads>& sh,
+                                                   uint32_t* bm, int u, int b, int h, int len,
+                                                   int32_t* idx_u) {
+  constexpr int NT = kMergeThreads;
+  const int tid = threadIdx.x;
+  for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
+  if (tid < R) sh.qt[tid] = a.qt[(size_t)u * 32 + tid];
+  __syncthreads();
+  float qlo[16], qhi[16];
+  query_halves<R>(sh.qt, qlo, qhi);
+  const uint8_t* kpu = a.kp + (size_t)u * a.Ncap * R;
+  auto visit3 = [&](auto&& f) {
+    for (int p0 = 0; p0 < len; p0 += NT) {
+      const int p = p0 + tid;
+      const bool ok = p < len;
+      const float s = position_score<R>(qlo, qhi, kpu + (size_t)(ok ? p : 0) * R);
+      f(ok ? score_key(s + 0.0f) : 0u, p, ok);
+    }
+  };
+  const uint32_t dummy = (uint32_t)(kBins + lane_id());
+  visit3([&](uint32_t k, int, bool ok) { atomicAdd(&sh.hist[ok ? (k >> kTopShift) : dummy], 1u); });
+  __syncthreads();
+  uint32_t t, need, eq;
+  finish_threshold<NT>(sh, (uint32_t)a.M, t, need, eq, [&](auto&& f) {
+    visit3([&](uint32_t k, int, bool ok) { f(k, ok); });
+  });
+  emit_bitmap<NT>(sh, bm, len, t, need, eq, a.M, idx_u, visit3);
+}
+
+template <int D, int R>
+__global__ __launch_bounds__(kMergeThreads) void filter_merge_kernel(const FilterArgs a) {
+  constexpr int NT = kMergeThreads;
+  constexpr int KPT = kFilterMergeKeys;
+  __shared__ SelectShared<NT> sh;
+  __shared__ uint32_t bm[kBitmapWords];           // used by the streaming fallback only
+  __shared__ int32_t cnt_s[kFilterSlots / (kFilterWaves * kFilterMinCap)];
+  __shared__ uint32_t red[NT / kWave];
+  const int u = blockIdx.x, b = u / a.Hkv, h = u % a.Hkv;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int len = unit_len(a.seq_lens, b, a.n_max);
+  const int M = a.M, S = a.S;
+  int32_t* idx_u = a.idx + (size_t)u * M;
+  if (len <= M) {                                     // every valid position, in order
+    for (int j = tid; j < M; j += NT) idx_u[j] = j < len ? j : -1;
+    return;
+  }
+  // Candidate keys, flat slot f = i * NT + tid of this unit's [S][cslots]
+  // array: register order is position order.  They are loaded before the
+  // counts arrive and masked afterwards.
+  const uint32_t* ck = a.ckey + (size_t)u * S * a.cslots;
+  const int32_t* cp = a.cpos + (size_t)u * S * a.cslots;
+  uint32_t key[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) key[i] = i < a.rows ? ck[i * NT + tid] : 0u;
+  const uint32_t thr = a.thr[u];
+  if (tid < S) cnt_s[tid] = a.cnt[(size_t)u * S + tid];
+  __syncthreads();
+  const bool over = tid < S && cnt_s[tid] < 0;
+  uint32_t total;
+  block_inclusive_scan<NT>(tid < S ? (uint32_t)max(cnt_s[tid], 0) : 0u, sh, total);
+  if (__syncthreads_or(over) || total < (uint32_t)M) {  // block-uniform
+    select_unit_streaming<D, R>(a, sh, bm, u, b, h, len, idx_u);
+    return;
+  }
+  uint32_t kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int f = i * NT + tid;
+    const bool valid = i < a.rows && (f & (a.cslots - 1)) < cnt_s[min(f >> a.cslots_log2, S - 1)];
+    key[i] = valid ? key[i] : 0u;
+    kmax = max(kmax, key[i]);
+  }
+  // Every candidate is >= thr >= 1.  Spread the candidates' range over the
+  // first radix digit: k' = ((key - thr) << lsh) + 1 (order-preserving, 0 is
+  // left for "no key", bit 31 of k' - 1 stays clear so k' cannot overflow).
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
+  if (lane == 0) red[w] = kmax;
+  for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
+  __syncthreads();
+  kmax = 0u;
+#pragma unroll
+  for (int ww = 0; ww < NT / kWave; ++ww) kmax = max(kmax, red[ww]);
+  const uint32_t span = kmax - thr;
+  const int lsh = span ? max(__clz((int)span) - 1, 0) : 0;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) key[i] = key[i] ? ((key[i] - thr) << lsh) + 1u : 0u;
+  const uint32_t dummy = (uint32_t)(kBins + lane);
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) atomicAdd(&sh.hist[key[i] ? (key[i] >> kTopShift) : dummy], 1u);
+  __syncthreads();
+  uint32_t t, need, eq;
+  finish_threshold<NT>(sh, (uint32_t)M, t, need, eq, [&](auto&& f) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) f(key[i], key[i] != 0u);
+  });
+  // ordered emission over the normalised keys; positions are read for the
+  // selected keys only
+  const bool staged = M <= kListCap - kWave;
+  int32_t* out = reinterpret_cast<int32_t*>(sh.list);
+  emit_in_order(key, t, need, eq, sh, [&](int i, bool sel, uint32_t slot) {
+    const int32_t p = sel ? cp[i * NT + tid] : 0;
+    if (staged) out[sel ? slot : (uint32_t)(kListCap - kWave + lane)] = p;
+    else if (sel) idx_u[slot] = p;
+  });
+  if (staged)
+    for (int j = tid; j < M; j += NT) idx_u[j] = out[j];
+}
+
+template <int D, int R>
+static void launch_filter_dr(const FilterArgs& a, int stages, int units, hipStream_t st) {
+  if (stages & kSelectBound)
+    hipLaunchKernelGGL((sample_kernel<D, R>), dim3(units), dim3(kSampleThreads), 0, st, a);
+  if (stages & kSelectChunks)
+    hipLaunchKernelGGL((filter_kernel<D, R>), dim3((unsigned)(units * a.S)), dim3(kChunkThreads),
+                       0, st, a);
+  if (stages & kSelectMerge)
+    hipLaunchKernelGGL((filter_merge_kernel<D, R>), dim3(units), dim3(kMergeThreads), 0, st, a);
+}
+
+hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int stages,
+                             const void* q, const float* P, const uint8_t* kp,
+                             const int32_t* seq_lens, int n_max, int M, int32_t* idx,
+                             void* workspace) {
+  FilterArgs a;
+  a.q = (const uint16_t*)q;
+  a.P = P;
+  a.kp = kp;
+  a.seq_lens = seq_lens;
+  a.n_max = n_max;
+  a.Ncap = c.Ncap;
+  a.Hq = c.Hq;
+  a.Hkv = c.Hkv;
+  a.G = c.G;
+  a.M = M;
+  a.S = plan.splits;
+  a.chunk = plan.chunk;
+  a.cap = plan.cap;
+  a.cslots = plan.cslots;
+  a.cslots_log2 = __builtin_ctz((unsigned)plan.cslots);
+  a.rows = plan.rows;
+  char* ws = (char*)workspace;
+  a.thr = (uint32_t*)(ws + plan.off_thr);
+  a.qt = (float*)(ws + plan.off_qt);
+  a.cnt = (int32_t*)(ws + plan.off_cnt);
+  a.ckey = (uint32_t*)(ws + plan.off_key);
+  a.cpos = (int32_t*)(ws + plan.off_pos);
+  a.idx = idx;
+  if ((long)plan.units * plan.splits > INT32_MAX) return hipErrorInvalidConfiguration;
+  if (c.D == 128 && c.R == 32) launch_filter_dr<128, 32>(a, stages, plan.units, c.stream);
+  else if (c.D == 128 && c.R == 16) launch_filter_dr<128, 16>(a, stages, plan.units, c.stream);
+  else if (c.D == 64 && c.R == 32) launch_filter_dr<64, 32>(a, stages, plan.units, c.stream);
+  else launch_filter_dr<64, 16>(a, stages, plan.units, c.stream);
+  return hipGetLastError();
 }
 
 template <int D, int R, bool FUSED>

@@ -24,11 +24,17 @@ hipError_t run_index_score(const LaunchCommon& c, const void* q, const float* P,
 // Selection runs as two launches: per-chunk candidates (kSelectChunks; fused
 // == true computes the scores from (q, P, kp), otherwise reads `scores`), then
 // the per-unit merge into idx (kSelectMerge).  `stages` picks either or both.
-constexpr int kSelectChunks = 1, kSelectMerge = 2;
+constexpr int kSelectChunks = 1, kSelectMerge = 2, kSelectBound = 4;
 hipError_t run_select(const LaunchCommon& c, const TopmPlan& plan, int stages, bool fused,
                       const void* q, const float* P, const uint8_t* kp, const float* scores,
                       const int32_t* seq_lens, int n_max, int M, int32_t* idx,
                       void* workspace);
+// Filter path of the fused selection (plan.enabled): stages kSelectBound
+// (sampled bound), kSelectChunks (filtering chunks), kSelectMerge.
+hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int stages,
+                             const void* q, const float* P, const uint8_t* kp,
+                             const int32_t* seq_lens, int n_max, int M, int32_t* idx,
+                             void* workspace);
 hipError_t run_decode(const LaunchCommon& c, const DecodePlan& plan, const void* q,
                       const void* k_cache, const void* v_cache, const int32_t* idx, int M,
                       float scale, void* out, float* lse, void* workspace);

@@ -126,12 +126,13 @@ def test_bad_arguments_are_rejected(lib):
     assert _st(lib, "sparse_attn_topm", by, P, None, wl.N, wl.M, P, P, need - 1, None) == -3
     assert _st(lib, "sparse_attn_index_topm", by, P, P, P, None, wl.N, wl.M, P, P, need - 1,
                None) == -3
-    assert _st(lib, "sparse_attn_index_candidates", by, P, P, P, None, wl.N, wl.M, None, need,
-               None) == -3
-    assert _st(lib, "sparse_attn_merge_candidates", by, wl.N, wl.M, P, P, need - 1, None) == -3
-    assert _st(lib, "sparse_attn_merge_candidates", by, wl.N, wl.M, None, P, need, None) == -1
-    assert _st(lib, "sparse_attn_index_candidates", by, P, P, P, None, wl.N, wl.N + 1, P, need,
-               None) == -1
+    stage = "sparse_attn_index_topm_stage"
+    assert _st(lib, stage, by, 2, P, P, P, None, wl.N, wl.M, None, None, need, None) == -3
+    assert _st(lib, stage, by, 3, P, P, P, None, wl.N, wl.M, P, P, need - 1, None) == -3
+    assert _st(lib, stage, by, 3, P, P, P, None, wl.N, wl.M, None, P, need, None) == -1
+    assert _st(lib, stage, by, 1, P, P, P, None, wl.N, wl.N + 1, None, P, need, None) == -1
+    assert _st(lib, stage, by, 0, P, P, P, None, wl.N, wl.M, P, P, need, None) == -1
+    assert _st(lib, stage, by, 4, P, P, P, None, wl.N, wl.M, P, P, need, None) == -1
     assert _st(lib, "sparse_attn_decode", by, P, P, P, P, wl.M, ctypes.c_float(1.0), P, None,
                P, 16, None) == -3
     # zero-size work is accepted without launching

@@ -192,8 +192,8 @@ def test_topm_fused_and_unfused_match_oracle(name):
     sa.sparse_attn_topm(sh, scores, sl, n_max, M, idx_u, ws)
     sa.sparse_attn_index_topm(sh, qd, Pd, kpd, sl, n_max, M, idx_f, ws)
     idx_s = torch.full_like(idx_f, -7)
-    sa.sparse_attn_index_candidates(sh, qd, Pd, kpd, sl, n_max, M, ws)
-    sa.sparse_attn_merge_candidates(sh, n_max, M, idx_s, ws)
+    for stage in (sa.SA_STAGE_BOUND, sa.SA_STAGE_CANDIDATES, sa.SA_STAGE_MERGE):
+        sa.sparse_attn_index_topm_stage(sh, stage, qd, Pd, kpd, sl, n_max, M, idx_s, ws)
     gu, gf = idx_u.cpu().numpy(), idx_f.cpu().numpy()
     assert np.array_equal(gu, gf), "fused and unfused index sets differ"
     assert np.array_equal(idx_s.cpu().numpy(), gf), "two-call selection differs"
@@ -459,8 +459,9 @@ def _bench_sequence(inp, sh, M, ws):
     sa.sparse_attn_append_kv(sh, inp.pos, inp.k_new, inp.v_new, inp.P, inp.k_cache,
                              inp.v_cache, kp)
     idx = torch.empty(wl.B, wl.Hkv, M, dtype=torch.int32, device="cuda")
-    sa.sparse_attn_index_candidates(sh, inp.q, inp.P, kp, inp.seq_lens, wl.N, M, ws)
-    sa.sparse_attn_merge_candidates(sh, wl.N, M, idx, ws)
+    for stage in (sa.SA_STAGE_BOUND, sa.SA_STAGE_CANDIDATES, sa.SA_STAGE_MERGE):
+        sa.sparse_attn_index_topm_stage(sh, stage, inp.q, inp.P, kp, inp.seq_lens, wl.N, M, idx,
+                                        ws)
     out = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(wl.B, wl.Hq, dtype=torch.float32, device="cuda")
     sa.sparse_attn_decode(sh, inp.q, inp.k_cache, inp.v_cache, idx, M, default_scale(wl.d),
@@ -521,3 +522,64 @@ def test_full_size_step_on_sampled_units(name):
             o2, l2 = oracle.sparse_attention(qg, K2[0, 0], V2[0, 0], gi[b, h],
                                              default_scale(wl.d))
             check_attention(go[b, h * G:(h + 1) * G], o2, "full-size unit %s" % ((b, h),))
+
+
+# ------------------------------------------------------------------ exact fallbacks
+
+def _topm_check_against_oracle(q, P, kp, M, n_max, lens=None):
+    B, Hkv = kp.shape[0], kp.shape[1]
+    Hq, d = q.shape[1], q.shape[2]
+    r, N = kp.shape[3], kp.shape[2]
+    G = Hq // Hkv
+    sh = _shape_of(B, Hq, Hkv, d, r, N)
+    ws = sa.alloc_workspace(sh, n_max, M)
+    idx = torch.empty(B, Hkv, M, dtype=torch.int32, device="cuda")
+    sl = None if lens is None else _dev(torch.tensor(lens, dtype=torch.int32))
+    sa.sparse_attn_index_topm(sh, _dev(q), _dev(P), _dev(kp), sl, n_max, M, idx, ws)
+    scores = torch.empty(B, Hkv, n_max, dtype=torch.float32, device="cuda")
+    sa.sparse_attn_index_score(sh, _dev(q), _dev(P), _dev(kp), sl, n_max, scores)
+    idx2 = torch.empty_like(idx)
+    sa.sparse_attn_topm(sh, scores, sl, n_max, M, idx2, ws)
+    assert torch.equal(idx, idx2), "index_topm and index_score + topm differ"
+    gi = idx.cpu().numpy()
+    P64 = P.double().numpy()
+    for b in range(B):
+        L = n_max if lens is None else min(lens[b], n_max)
+        for h in range(Hkv):
+            qt = oracle.indexer_query(f64(q)[b, h * G:(h + 1) * G], P64[h])
+            s = oracle.index_scores(qt, kp[b, h, :L])
+            check_topm_unit(gi[b, h], s, M, L)
+    return gi
+
+
+def test_topm_all_scores_equal_takes_lowest_positions():
+    """Every score equal: every candidate list overflows, so the exact
+    streaming selection of the unit runs; ties go to the lowest positions."""
+    _say("case: topm all equal")
+    B, Hq, Hkv, d, r, N, M = 1, 4, 1, 64, 16, 65536, 100
+    q = torch.zeros(B, Hq, d, dtype=torch.bfloat16)
+    q[0, :, 0] = 1.0
+    P = torch.zeros(Hkv, d, r, dtype=torch.float32)
+    P[0, :r, :r] = torch.eye(r)
+    kp = np.zeros((B, Hkv, N, r), dtype=np.uint8)
+    kp[..., 0] = 0x38                                      # 1.0 everywhere
+    gi = _topm_check_against_oracle(q, P, kp, M, N)
+    assert gi[0, 0].tolist() == list(range(M))
+
+
+def test_topm_sample_overestimate_falls_back_exactly():
+    """High scores planted exactly on the positions the bound's sample reads
+    (32 evenly spread blocks of 128 rows) push the sampled bound above the
+    M-th score; the merge must detect it and select exactly."""
+    _say("case: topm sample overestimate")
+    B, Hq, Hkv, d, r, N, M = 1, 4, 1, 128, 32, 65536, 2048
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, N, seed=21)
+    K64 = f64(K)
+    qbar = f64(q).reshape(B, Hkv, Hq // Hkv, d).mean(axis=2)
+    starts = [(j * (N - 128)) // 31 for j in range(32)]
+    rows = np.concatenate([np.arange(s0, s0 + 128) for s0 in starts[:8]])   # 1024 rows
+    K64[0, 0, rows] += 6.0 * qbar[0, 0]
+    P64 = P.double().numpy()
+    kp = oracle_kp(K64, P64)
+    gi = _topm_check_against_oracle(q, P, kp, M, N)
+    assert set(rows.tolist()) <= set(gi[0, 0].tolist())

@@ -89,8 +89,9 @@ typedef enum sa_status {
  * k_cache, v_cache [B][Hkv][Ncap][d] bf16 (row pos[b]+t <- token t).
  * kp_cache [B][Hkv][Ncap][r] uint8 FP8 codes:
  *          kp[n][j] = e4m3( sum_i k[i] * P[h][i][j] ), the sum formed in fp64
- *          starting from +0 and rounded once, to nearest-even, saturating at
- *          +-448.
+ *          (8 fused multiply-add chains from +0 over d/8 consecutive i each,
+ *          added in order to +0) and rounded once, to nearest-even,
+ *          saturating at +-448.
  * Rows pos[b]+t outside [0, Ncap) are skipped (device data is not checked on
  * the host).
  * ------------------------------------------------------------------------- */
@@ -123,8 +124,9 @@ int sparse_attn_project_keys(const sa_shape* shape, const void* k_cache,
  * scores   [B][Hkv][n_max] fp32 out:
  *          s[n] = sum_j qt[j] * dec(kp[n][j]) for n < len, -inf otherwise,
  *          where qt = P[h]^T * mean_g q[h*G+g] is formed in fp64 and rounded
- *          to fp32, and each score is accumulated in fp32 as two 16-term fused
- *          multiply-add chains (j < 16, then j >= 16) added together.
+ *          to fp32, and each score is accumulated in fp32 as one 16-term fused
+ *          multiply-add chain per 16 codes (r = 32: j < 16 and j >= 16, the
+ *          two chains then added).
  * ------------------------------------------------------------------------- */
 int sparse_attn_index_score(const sa_shape* shape, const void* q, const float* P,
                             const uint8_t* kp_cache, const int32_t* seq_lens,

@@ -5,15 +5,72 @@
 // preserves token order": each key has a low-rank projection onto its KV
 // head's basis, kept as FP8 next to the bf16 cache.
 //
-// Layout: one workgroup of 256 threads serves one (b, KV head) unit and a run
-// of rows.  A pass stages 64/r rows of keys into LDS as fp32, then lane
-// (row rr = lane / r, column j = lane % r) forms one projected value with a
-// d-long fp64 fused multiply-add chain (every product bf16 x fp32 is exact in
-// fp64) and writes its code byte.
+// Summation order (shared by both kernels, so a row's code is the same
+// whichever kernel wrote it): the d products of column j are split into 8
+// parts of d/8 consecutive rows of P; each part is a fused multiply-add chain
+// in fp64 starting from +0 (every product bf16 x fp32 is exact in fp64); the
+// parts are added in order to +0, and the total is rounded once to E4M3.
+//
+// Append (the decode hot path, one row per (b, KV head) per token) is latency
+// bound, so one workgroup serves one new row: 8 parts x r columns of threads
+// each form one partial sum straight from global memory, and the row's bf16
+// K/V copies go out in parallel.  The bulk projection stages key rows in LDS
+// and lets one lane form one code from all 8 parts.
 #include "device_common.hpp"
 #include "kernels.h"
 
 namespace sa {
+
+constexpr int kProjParts = 8;
+
+// ---------------------------------------------------------------- append
+
+template <int D, int R>
+__global__ __launch_bounds__(kBlock) void append_kv_kernel(
+    const int32_t* __restrict__ pos, int T, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, const float* __restrict__ P, int Hkv, int Ncap,
+    uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache, uint8_t* __restrict__ kp) {
+  constexpr int kPer = D / kProjParts;
+  static_assert(kProjParts * R <= kBlock, "one thread per (part, column)");
+  __shared__ double part[kProjParts * R];
+  const int u = blockIdx.x / T, tok = blockIdx.x % T;
+  const int b = u / Hkv, h = u % Hkv;
+  const long n = (long)pos[b] + tok;
+  if (n < 0 || n >= Ncap) return;                    // block-uniform
+  const int t = threadIdx.x;
+  const uint16_t* kr = k_new + ((size_t)u * T + tok) * D;
+  const uint16_t* vr = v_new + ((size_t)u * T + tok) * D;
+  // bf16 row copies: D/8 threads move 16 bytes of K and of V each
+  if (t < D / 8) {
+    const size_t off = ((size_t)u * Ncap + n) * D + t * 8;
+    *reinterpret_cast<uint4*>(k_cache + off) = *reinterpret_cast<const uint4*>(kr + t * 8);
+    *reinterpret_cast<uint4*>(v_cache + off) = *reinterpret_cast<const uint4*>(vr + t * 8);
+  }
+  // partial sum of part p for column j
+  const int p = t / R, j = t % R;
+  if (t < kProjParts * R) {
+    const float* Ph = P + (size_t)h * D * R + (size_t)p * kPer * R + j;
+    float pv[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) pv[k] = Ph[k * R];
+    float kv[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; k += 8) bf16x8_to_f32(*reinterpret_cast<const uint4*>(kr + p * kPer + k), kv + k);
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) acc = fma((double)kv[k], (double)pv[k], acc);
+    part[t] = acc;
+  }
+  __syncthreads();
+  if (t < R) {
+    double s = 0.0;
+#pragma unroll
+    for (int q = 0; q < kProjParts; ++q) s += part[q * R + t];
+    kp[((size_t)u * Ncap + n) * R + t] = (uint8_t)f64_to_e4m3(s);
+  }
+}
+
+// ---------------------------------------------------------------- bulk
 
 template <int D, int R>
 struct ProjGeom {
@@ -27,10 +84,9 @@ __device__ __forceinline__ void load_basis(const float* __restrict__ P, int h, f
   for (int i = threadIdx.x; i < D * R; i += blockDim.x) Ps[i] = src[i];
 }
 
-// Stage one bf16 key row (D values) into LDS as fp32; `lanes` lanes cooperate.
+// Stage one bf16 key row (D values) into LDS as fp32; D/8 lanes cooperate.
 template <int D>
 __device__ __forceinline__ void stage_row(const uint16_t* __restrict__ src, float* dst, int sub) {
-  // D bf16 = D/8 loads of 16 B
   if (sub < D / 8) {
     const uint4 v = *reinterpret_cast<const uint4*>(src + sub * 8);
     float f[8];
@@ -40,21 +96,28 @@ __device__ __forceinline__ void stage_row(const uint16_t* __restrict__ src, floa
   }
 }
 
+// One code from a staged row, in the shared summation order.
 template <int D, int R>
 __device__ __forceinline__ uint32_t project_one(const float* krow, const float* Ps, int j) {
-  double acc = 0.0;
-#pragma unroll 8
-  for (int i = 0; i < D; ++i) acc = fma((double)krow[i], (double)Ps[i * R + j], acc);
-  return f64_to_e4m3(acc);
+  constexpr int kPer = D / kProjParts;
+  double s = 0.0;
+#pragma unroll
+  for (int q = 0; q < kProjParts; ++q) {
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = q * kPer + k;
+      acc = fma((double)krow[i], (double)Ps[i * R + j], acc);
+    }
+    s += acc;
+  }
+  return f64_to_e4m3(s);
 }
 
-// Bulk: rows [n_begin, n_begin + n_count) of every unit.  Workgroup
-// blockIdx.x serves unit blockIdx.x / blocks_per_unit and a run of
-// kPassesPerBlock passes.
 constexpr int kPassesPerBlock = 8;
 
 template <int D, int R>
-__global__ __launch_bounds__(256) void project_keys_kernel(
+__global__ __launch_bounds__(kBlock) void project_keys_kernel(
     const uint16_t* __restrict__ k_cache, const float* __restrict__ P, int Hkv,
     int Ncap, int n_begin, int n_count, int blocks_per_unit, uint8_t* __restrict__ kp) {
   using Geo = ProjGeom<D, R>;
@@ -90,58 +153,6 @@ __global__ __launch_bounds__(256) void project_keys_kernel(
   }
 }
 
-// Append: token t of a unit goes to row pos[b] + t.  Copies the K and V rows
-// and writes the projection.  Same grid decomposition as the bulk kernel.
-template <int D, int R>
-__global__ __launch_bounds__(256) void append_kv_kernel(
-    const int32_t* __restrict__ pos, int T, const uint16_t* __restrict__ k_new,
-    const uint16_t* __restrict__ v_new, const float* __restrict__ P, int Hkv, int Ncap,
-    int blocks_per_unit, uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
-    uint8_t* __restrict__ kp) {
-  using Geo = ProjGeom<D, R>;
-  __shared__ float Ps[D * R];
-  __shared__ float Ks[Geo::kRowsPerPass][D];
-  const int u = blockIdx.x / blocks_per_unit;
-  const int rb = blockIdx.x % blocks_per_unit;
-  const int b = u / Hkv, h = u % Hkv;
-  load_basis<D, R>(P, h, Ps);
-  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int rr = lane / R, j = lane % R;
-  const int p0 = pos[b];
-  const uint16_t* kn = k_new + (size_t)u * T * D;
-  const uint16_t* vn = v_new + (size_t)u * T * D;
-  for (int pass = 0; pass < kPassesPerBlock; ++pass) {
-    const int t0 = (rb * kPassesPerBlock + pass) * Geo::kRowsPerPass;
-    if (t0 >= T) break;
-    __syncthreads();
-    {
-      constexpr int kPieces = D / 8;
-      const int t = threadIdx.x;
-      const int row = t / kPieces, piece = t % kPieces;
-      if (row < Geo::kRowsPerPass) {
-        const int tok = t0 + row;
-        if (tok < T) {
-          stage_row<D>(kn + (size_t)tok * D, Ks[row], piece);
-          const long n = (long)p0 + tok;
-          if (n >= 0 && n < Ncap) {
-            const size_t off = ((size_t)u * Ncap + n) * D + piece * 8;
-            *reinterpret_cast<uint4*>(k_cache + off) =
-                *reinterpret_cast<const uint4*>(kn + (size_t)tok * D + piece * 8);
-            *reinterpret_cast<uint4*>(v_cache + off) =
-                *reinterpret_cast<const uint4*>(vn + (size_t)tok * D + piece * 8);
-          }
-        }
-      }
-    }
-    __syncthreads();
-    const int row = w * Geo::kRowsPerWavePass + rr;
-    const int tok = t0 + row;
-    const long n = (long)p0 + tok;
-    if (tok < T && n >= 0 && n < Ncap)
-      kp[((size_t)u * Ncap + n) * R + j] = (uint8_t)project_one<D, R>(Ks[row], Ps, j);
-  }
-}
-
 template <int D, int R>
 static hipError_t launch_project(const LaunchCommon& c, const void* k_cache, const float* P,
                                  int n_begin, int n_count, uint8_t* kp) {
@@ -150,7 +161,7 @@ static hipError_t launch_project(const LaunchCommon& c, const void* k_cache, con
   const int bpu = (n_count + rows_per_block - 1) / rows_per_block;
   const long blocks = (long)bpu * c.units;
   if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((project_keys_kernel<D, R>), dim3((unsigned)blocks), dim3(256), 0,
+  hipLaunchKernelGGL((project_keys_kernel<D, R>), dim3((unsigned)blocks), dim3(kBlock), 0,
                      c.stream, (const uint16_t*)k_cache, P, c.Hkv, c.Ncap, n_begin, n_count,
                      bpu, kp);
   return hipGetLastError();
@@ -160,14 +171,11 @@ template <int D, int R>
 static hipError_t launch_append(const LaunchCommon& c, const int32_t* pos, int T,
                                 const void* k_new, const void* v_new, const float* P,
                                 void* k_cache, void* v_cache, uint8_t* kp) {
-  using Geo = ProjGeom<D, R>;
-  const int rows_per_block = Geo::kRowsPerPass * kPassesPerBlock;
-  const int bpu = (T + rows_per_block - 1) / rows_per_block;
-  const long blocks = (long)bpu * c.units;
+  const long blocks = (long)T * c.units;
   if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((append_kv_kernel<D, R>), dim3((unsigned)blocks), dim3(256), 0, c.stream,
+  hipLaunchKernelGGL((append_kv_kernel<D, R>), dim3((unsigned)blocks), dim3(kBlock), 0, c.stream,
                      pos, T, (const uint16_t*)k_new, (const uint16_t*)v_new, P, c.Hkv, c.Ncap,
-                     bpu, (uint16_t*)k_cache, (uint16_t*)v_cache, kp);
+                     (uint16_t*)k_cache, (uint16_t*)v_cache, kp);
   return hipGetLastError();
 }
 

@@ -49,7 +49,7 @@ constexpr int kFilterMinCap = 128;       // slots per wave list, at least
 constexpr int kFilterMaxCap = 256;       // slots per wave list, at most (staged in LDS)
 constexpr int kFilterMaxRows = 64;       // 512-position rows per filter chunk, at most
 constexpr int kFilterWaves = 8;          // lists per chunk (one per wave of 512 threads)
-constexpr int kSampleBlocks = 512;       // sampled position blocks per unit
+constexpr int kSampleBlocks = 128;       // sampled position blocks per unit
 constexpr int kSampleBlock = 8;          // positions per sampled block (256 B of FP8 rows)
 constexpr int kSampleSafety = 3;         // the bound aims at ~3 M keys per unit
 

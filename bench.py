@@ -74,6 +74,57 @@ def measured_traffic(kernel_key, src_hash):
 CALIB_KERNEL_TAG = "neg"      # torch.neg on fp32: reads and writes exactly n*4 bytes
 
 
+class HipTimer:
+    """HIP timing events recorded on a raw stream.  They are created with
+    hipEventDisableSystemFence: recording one then costs no cache write-back,
+    so timing every call of a step does not slow the step down (the default
+    events of torch.cuda.Event flush caches at each record)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        lib = None
+        for name in ("libamdhip64.so.7", "libamdhip64.so"):
+            try:
+                lib = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        if lib is None:
+            raise RuntimeError("HIP runtime library not found")
+        vp = ctypes.c_void_p
+        lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        lib.hipEventRecord.argtypes = [vp, vp]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        lib.hipEventDestroy.argtypes = [vp]
+        self.lib = lib
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = self.ct.c_void_p()
+            if self.lib.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            evs.append(e)
+        return evs
+
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ev, self.ct.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        if self.lib.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(e)
+
+
 def ingest_counters(fetch_csv, write_csv, calib_mib, kernel=DOMINANT_KERNEL):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
     WRITE_SIZE; both with --calibration-mib) into profiles/traffic.json: each
@@ -234,22 +285,29 @@ def main(argv=None):
                                       out, None, ws),
     )
 
-    def step(record):
-        # HIP events between the calls go on the stream the library launches on
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] if record \
-            else None
+    timer = HipTimer()
+    stream = torch.cuda.current_stream(dev).cuda_stream    # the stream every call launches on
+    dom_i = names.index("index_candidates")
+
+    def step(rec, every_call=False):
+        # rec: this step's events.  In the timed region only the dominant call
+        # is bracketed (two events); the breakdown pass brackets every call.
         for i, call in enumerate(calls):
-            if record:
-                e[i].record()
+            if rec is not None and (every_call or i == dom_i):
+                timer.record(rec[i if every_call else 0], stream)
             call()
-        if record:
-            e[-1].record()
+            if rec is not None and not every_call and i == dom_i:
+                timer.record(rec[1], stream)
+        if rec is not None and every_call:
+            timer.record(rec[-1], stream)
             for i, k in enumerate(names):
-                ev[k].append((e[i], e[i + 1]))
+                ev[k].append((rec[i], rec[i + 1]))
+        elif rec is not None:
+            dom_ev.append((rec[0], rec[1]))
 
     print("bench: warmup %d" % a.warmup, file=sys.stderr, flush=True)
     for _ in range(a.warmup):
-        step(False)
+        step(None)
     if a.calibration_mib > 0:
         x = torch.ones(a.calibration_mib * 2 ** 18, dtype=torch.float32, device=dev)
         torch.neg(x, out=torch.empty_like(x))
@@ -261,14 +319,28 @@ def main(argv=None):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    for _ in range(a.steps):
-        step(True)                  # HIP events between the calls, on the same stream
+    dom_ev = []
+    pool = timer.create(2 * a.steps)
+    for k in range(a.steps):
+        step(pool[2 * k:2 * k + 2])           # HIP events around the dominant call
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = start.elapsed_time(end)
     ms_per_step = 1e3 * wall / a.steps          # host clock around the K steps
-    kern_us = {k: 1e3 * sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in ev.items()}
+    dom_us = 1e3 * sum(timer.elapsed_ms(s0, s1) for s0, s1 in dom_ev) / len(dom_ev)
+    timer.destroy(pool)
+    # per-call breakdown (informational): a separate pass after the timed
+    # region, every call bracketed by events
+    n_ev = len(calls) + 1
+    bsteps = min(a.steps, 20)
+    pool = timer.create(n_ev * bsteps)
+    for k in range(bsteps):
+        step(pool[k * n_ev:(k + 1) * n_ev], every_call=True)
+    torch.cuda.synchronize()
+    kern_us = {k: 1e3 * sum(timer.elapsed_ms(s0, s1) for s0, s1 in v) / len(v)
+               for k, v in ev.items()}
+    timer.destroy(pool)
 
     bytes_k = algorithmic_bytes(wl)
     step_bytes = sum(bytes_k.values())
@@ -277,7 +349,7 @@ def main(argv=None):
 
     # dominant kernel: filter_kernel, the one launch of the candidates stage
     dom = "index_candidates"
-    dom_gbps = bytes_k[dom] / (kern_us[dom] * 1e-6) / 1e9
+    dom_gbps = bytes_k[dom] / (dom_us * 1e-6) / 1e9
     src_hash = _source_hash(["indexer.hip", "device_common.hpp"])
     traffic = measured_traffic(DOMINANT_KERNEL, src_hash)
     roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
@@ -285,7 +357,7 @@ def main(argv=None):
                 "traffic": traffic,
                 "kernel": "%s (sparse_attn_index_topm_stage, SA_STAGE_CANDIDATES)"
                           % DOMINANT_KERNEL,
-                "bytes_per_launch": bytes_k[dom], "avg_launch_us": round(kern_us[dom], 2),
+                "bytes_per_launch": bytes_k[dom], "avg_launch_us": round(dom_us, 2),
                 "source_hash": src_hash}
 
     res = {
@@ -301,8 +373,9 @@ def main(argv=None):
                    "head_dim": wl.d, "context_N": wl.N, "rank_r": wl.r, "budget_M": wl.M},
         "tokens_per_s": round(steps_per_s * wl.B, 1),
         "step_bytes": step_bytes,
-        "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
-        "kernel_gbps": {k: round(bytes_k[k] / (kern_us[k] * 1e-6) / 1e9, 1) for k in kern_us
+        "kernel_us_breakdown_pass": {k: round(v, 2) for k, v in kern_us.items()},
+        "kernel_gbps_breakdown_pass": {k: round(bytes_k[k] / (kern_us[k] * 1e-6) / 1e9, 1)
+                                       for k in kern_us
                         if bytes_k[k]},
         "roofline": roofline,
         "cpu_baseline": None,

@@ -1067,7 +1067,9 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
   // this chunk's rows only: loads past the valid positions return zero
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(a.kp + ((size_t)u * a.Ncap + base) * R, (uint32_t)nv * R);
-  const uint32_t voff = (uint32_t)(w * kWave * R + lane * 16);
+  // lane l scores position base + i*NT + 64w + l on its own (both 16-byte
+  // halves of an r = 32 row), so no cross-lane step is needed
+  const uint32_t voff = (uint32_t)((w * kWave + lane) * R);
   constexpr int kLoadsPerIter = R / 16;
   constexpr int kBatch = SA_CHUNK_LOADS_IN_FLIGHT / kLoadsPerIter;
   // Two register sets: while one batch of rows is scored the next one is in
@@ -1080,7 +1082,7 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
     for (int x = 0; x < kBatch; ++x) {
       const uint32_t off = voff + (uint32_t)((i0 + x) * NT * R);
       bt.a[x] = buffer_load16(rs, off, 0);
-      if (R == 32) bt.b[x] = buffer_load16(rs, off + 1024, 0);
+      if (R == 32) bt.b[x] = buffer_load16(rs, off + 16, 0);
     }
   };
   const int rows = (nv + NT - 1) / NT;
@@ -1089,23 +1091,17 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
   if (kBatch < rows) load_batch(b1, kBatch);
   if (threadIdx.x < R) qt[threadIdx.x] = a.qt[(size_t)u * 32 + threadIdx.x];
   __syncthreads();
-  float ql[16];
-  lane_query<R>(qt, ql);
+  float qlo[16], qhi[16];
+  query_halves<R>(qt, qlo, qhi);
   uint32_t wc = 0;                                    // keys this wave appended so far
   auto score_batch = [&](const Batch& bt, int i0) {
 #pragma unroll
     for (int x = 0; x < kBatch; ++x) {
       const int p = base + (i0 + x) * NT + w * kWave + lane;
-      float s;
-      if (R == 16) {
-        s = lane_score<R>(ql, bt.a[x]);
-      } else {
-        const float sa = lane_score<R>(ql, bt.a[x]);
-        const float sb = lane_score<R>(ql, bt.b[x]);
-        const float xv = (lane & 1) ? sb : sa;
-        const int src = (lane < 32) ? 2 * lane : 2 * (lane - 32) + 1;
-        s = __shfl(xv, src, kWave);
-      }
+      // the same two chains, added in the same order, as the paired-lane
+      // scoring of the other kernels: identical bits
+      float s = score16(qlo, bt.a[x]);
+      if (R == 32) s = s + score16(qhi, bt.b[x]);
       const uint32_t key = score_key(s + 0.0f);
       const bool sel = p < len && key >= thr;
       const uint64_t m = ballot(sel);

@@ -953,6 +953,7 @@ constexpr int kSampleKeys = kSampleBlocks * kSampleBlock / kSampleThreads;
 constexpr int kBitmapWords = kFilterMaxN / 32;
 constexpr int kFilterMergeKeys = kFilterSlots / kMergeThreads;   // 16 per thread
 static_assert(kFilterMaxCap * kFilterWaves <= kFilterSlots, "a chunk's slots fit the merge");
+static_assert(kFilterSlots / (kFilterWaves * kFilterMinCap) <= kWave, "one wave sums the chunk counts");
 
 __device__ __forceinline__ int unit_len(const int32_t* seq_lens, int b, int n_max) {
   return seq_lens ? min(max(seq_lens[b], 0), n_max) : n_max;
@@ -1041,7 +1042,6 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const FilterArgs
 template <int D, int R>
 __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs a) {
   constexpr int NT = kChunkThreads;
-  __shared__ float qt[32];
   // each wave's list is staged here, then interleaved into position order
   __shared__ uint32_t sk[kFilterWaves][kFilterMaxCap];
   __shared__ int32_t sp[kFilterWaves][kFilterMaxCap];
@@ -1089,10 +1089,10 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
   Batch b0, b1;
   load_batch(b0, 0);
   if (kBatch < rows) load_batch(b1, kBatch);
-  if (threadIdx.x < R) qt[threadIdx.x] = a.qt[(size_t)u * 32 + threadIdx.x];
-  __syncthreads();
+  // the query is the same for every lane: read with scalar loads it stays in
+  // scalar registers (an FMA takes one scalar operand), saving 32 VGPRs
   float qlo[16], qhi[16];
-  query_halves<R>(qt, qlo, qhi);
+  query_halves<R>(a.qt + (size_t)u * 32, qlo, qhi);
   uint32_t wc = 0;                                    // keys this wave appended so far
   auto score_batch = [&](const Batch& bt, int i0) {
 #pragma unroll
@@ -1111,7 +1111,7 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
         sk[w][slot] = key;
         sp[w][slot] = p;
       }
-      rowcnt[w][i0 + x] = (uint32_t)popc64(m);        // same value from every lane
+      if (i0 + x < rows) rowcnt[w][i0 + x] = (uint32_t)popc64(m);   // same value from every lane
       wc += (uint32_t)popc64(m);
     }
   };
@@ -1275,15 +1275,27 @@ __global__ __launch_bounds__(kMergeThreads) void filter_merge_kernel(const Filte
   const uint32_t* ck = a.ckey + (size_t)u * S * a.cslots;
   const int32_t* cp = a.cpos + (size_t)u * S * a.cslots;
   uint32_t key[KPT];
+  int32_t pos[KPT];
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) key[i] = i < a.rows ? ck[i * NT + tid] : 0u;
+  for (int i = 0; i < KPT; ++i) {
+    key[i] = i < a.rows ? ck[i * NT + tid] : 0u;
+    pos[i] = i < a.rows ? cp[i * NT + tid] : 0;
+  }
   const uint32_t thr = a.thr[u];
-  if (tid < S) cnt_s[tid] = a.cnt[(size_t)u * S + tid];
+  // per-chunk counts (S <= 64: one wave sums them); -1 marks an overflowed list
+  if (w == 0) {
+    const int c = lane < S ? a.cnt[(size_t)u * S + lane] : 0;
+    if (lane < S) cnt_s[lane] = c;
+    uint32_t tot = (uint32_t)max(c, 0);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tot += (uint32_t)__shfl_xor((int)tot, off, kWave);
+    const bool over = ballot(c < 0) != 0;
+    if (lane == 0) red[0] = over ? 0u : tot;
+  }
   __syncthreads();
-  const bool over = tid < S && cnt_s[tid] < 0;
-  uint32_t total;
-  block_inclusive_scan<NT>(tid < S ? (uint32_t)max(cnt_s[tid], 0) : 0u, sh, total);
-  if (__syncthreads_or(over) || total < (uint32_t)M) {  // block-uniform
+  const uint32_t total = red[0];
+  __syncthreads();                                    // red is reused below
+  if (total < (uint32_t)M) {                          // block-uniform (0 after an overflow)
     select_unit_streaming<D, R>(a, sh, bm, u, b, h, len, idx_u);
     return;
   }
@@ -1324,9 +1336,8 @@ __global__ __launch_bounds__(kMergeThreads) void filter_merge_kernel(const Filte
   const bool staged = M <= kListCap - kWave;
   int32_t* out = reinterpret_cast<int32_t*>(sh.list);
   emit_in_order(key, t, need, eq, sh, [&](int i, bool sel, uint32_t slot) {
-    const int32_t p = sel ? cp[i * NT + tid] : 0;
-    if (staged) out[sel ? slot : (uint32_t)(kListCap - kWave + lane)] = p;
-    else if (sel) idx_u[slot] = p;
+    if (staged) out[sel ? slot : (uint32_t)(kListCap - kWave + lane)] = pos[i];
+    else if (sel) idx_u[slot] = pos[i];
   });
   if (staged)
     for (int j = tid; j < M; j += NT) idx_u[j] = out[j];

@@ -83,9 +83,11 @@ int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* p) {
   *p = FilterPlan{};
   p->units = (int)units;
   if (n_max > kFilterMaxN || M > kFilterMaxM || M >= n_max) return SA_OK;
-  // chunks as large as 16384 positions, smaller while the grid is short of
-  // 1024 workgroups, but never more than 32 per unit (lists keep >= 128 slots)
-  int64_t chunk = kMaxChunk;
+  // Chunks as large as 32768 positions (fewer, longer workgroups stream
+  // better: about two rounds of the chip's slots), smaller while the grid is
+  // short of 1024 workgroups, but never more than 16 per unit (lists keep
+  // >= 128 slots).
+  int64_t chunk = kFilterMaxChunk;
   while (chunk > 2048 && units * ceil_div(n_max, chunk) < 1024) chunk >>= 1;
   int64_t splits = ceil_div(n_max, chunk);
   const int64_t max_splits = kFilterSlots / (kFilterWaves * kFilterMinCap);

@@ -46,7 +46,8 @@ constexpr int kFilterMaxN = 1 << 19;     // merge marks selected positions in an
 constexpr int kFilterMaxM = 6144;        // selected positions staged in LDS by the merge
 constexpr int kFilterSlots = 16384;      // candidate slots per unit (16 per merge thread)
 constexpr int kFilterMinCap = 128;       // slots per wave list, at least
-constexpr int kFilterMaxCap = 256;       // slots per wave list, at most (staged in LDS)
+constexpr int kFilterMaxCap = 512;       // slots per wave list, at most (staged in LDS)
+constexpr int kFilterMaxChunk = 32768;   // positions per filter workgroup, at most
 constexpr int kFilterMaxRows = 64;       // 512-position rows per filter chunk, at most
 constexpr int kFilterWaves = 8;          // lists per chunk (one per wave of 512 threads)
 constexpr int kSampleBlocks = 128;       // sampled position blocks per unit

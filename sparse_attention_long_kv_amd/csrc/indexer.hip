@@ -1130,16 +1130,38 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
   if (lane == 0 && wc > (uint32_t)a.cap) ovf = 1;
   const int nrow = min(rows, kFilterMaxRows);
   {
-    const uint32_t v = lane < nrow ? rowcnt[w][lane] : 0u;
-    const uint32_t incl = wave_inclusive_scan(v);
-    if (lane < nrow) rowfirst[w][lane] = incl - v;
+    // per-wave exclusive scan over its rows, 64 rows at a time
+    uint32_t carry = 0;
+    for (int r0 = 0; r0 < nrow; r0 += kWave) {       // wave-uniform
+      const int r = r0 + lane;
+      const uint32_t v = r < nrow ? rowcnt[w][r] : 0u;
+      const uint32_t incl = wave_inclusive_scan(v);
+      if (r < nrow) rowfirst[w][r] = carry + incl - v;
+      carry += (uint32_t)__shfl((int)incl, kWave - 1, kWave);
+    }
   }
+  // block exclusive scan in (row, wave) order, kEntries consecutive entries
+  // per thread
+  constexpr int kEntries = kFilterMaxRows * kFilterWaves / NT;
+  static_assert(kEntries * NT == kFilterMaxRows * kFilterWaves, "scan entries");
   const int tid = threadIdx.x;
-  const int gi = tid / kFilterWaves, gw = tid % kFilterWaves;     // (row, wave) order
-  const uint32_t v = gi < nrow ? rowcnt[gw][gi] : 0u;
+  uint32_t ev[kEntries], mine = 0;
+#pragma unroll
+  for (int e = 0; e < kEntries; ++e) {
+    const int g = tid * kEntries + e;
+    const int gi = g / kFilterWaves, gw = g % kFilterWaves;
+    ev[e] = gi < nrow ? rowcnt[gw][gi] : 0u;
+    mine += ev[e];
+  }
   uint32_t total;
-  const uint32_t incl = block_scan_small<NT>(v, wtot, total);
-  if (gi < nrow) rowoff[gw][gi] = incl - v;
+  uint32_t run = block_scan_small<NT>(mine, wtot, total) - mine;
+#pragma unroll
+  for (int e = 0; e < kEntries; ++e) {
+    const int g = tid * kEntries + e;
+    const int gi = g / kFilterWaves, gw = g % kFilterWaves;
+    if (gi < nrow) rowoff[gw][gi] = run;
+    run += ev[e];
+  }
   __syncthreads();
   const bool overflow = ovf != 0;
   if (!overflow) {

@@ -1,16 +1,17 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the indexer-selected sparse attention library.
 
-One step = the whole hot path for one layer over the whole batch:
-append the new token (K/V rows + FP8 projected key), fused index scoring +
-exact top-M per KV head, and gather-free sparse attention over the selected
-rows.  Inputs are synthetic (``workloads``) and resident in HBM before the
-timed region starts.
+One step = the whole hot path for one layer over the whole batch, i.e. one
+sparse_attn_decode_step called as its four launches: append the new token
+(K/V rows + FP8 projected key) with the sampled selection bound, score every
+position and keep the candidates, exact top-M per KV head, and gather-free
+sparse attention over the selected rows.  Inputs are synthetic
+(``workloads``) and resident in HBM before the timed region starts.
 
 Prints ONE JSON line:
   value         decode steps/s (N=1 GPU; whole-job throughput)
   hbm_gbps      algorithmic bytes per step / step time
-  roofline      the dominant kernel (fused score + top-M) against 8 TB/s
+  roofline      the dominant kernel (scoring + candidate filter) against 8 TB/s
   cpu_baseline  the fp64 oracle on the host, on a bounded sample of units
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -45,8 +46,7 @@ def algorithmic_bytes(wl):
     merge = idx                                     # the selected positions
     decode = units * wl.M * wl.d * 2 * 2 + idx + q + wl.B * wl.Hq * wl.d * 2
     # the sampled bound reads a few rows again: no bytes of its own are required
-    return {"append_kv": append, "index_bound": 0, "index_candidates": candidates,
-            "merge_candidates": merge, "decode": decode}
+    return {"append_bound": append, "candidates": candidates, "merge": merge, "attend": decode}
 
 
 def _source_hash(names):
@@ -269,25 +269,21 @@ def main(argv=None):
     scale = default_scale(wl.d)
     torch.cuda.synchronize()
 
-    names = ("append_kv", "index_bound", "index_candidates", "merge_candidates", "decode")
+    # the four launches of sparse_attn_decode_step, one call each
+    names = ("append_bound", "candidates", "merge", "attend")
     ev = {k: [] for k in names}
+    lse = None
 
     def stage(st):
-        return lambda: sa.sparse_attn_index_topm_stage(sh, st, inp.q, inp.P, kp, inp.seq_lens,
-                                                       wl.N, wl.M, idx, ws)
-    calls = (
-        lambda: sa.sparse_attn_append_kv(sh, inp.pos, inp.k_new, inp.v_new, inp.P, inp.k_cache,
-                                         inp.v_cache, kp),
-        stage(sa.SA_STAGE_BOUND),
-        stage(sa.SA_STAGE_CANDIDATES),
-        stage(sa.SA_STAGE_MERGE),
-        lambda: sa.sparse_attn_decode(sh, inp.q, inp.k_cache, inp.v_cache, idx, wl.M, scale,
-                                      out, None, ws),
-    )
+        return lambda: sa.sparse_attn_decode_step_stage(
+            sh, st, inp.pos, inp.k_new, inp.v_new, inp.q, inp.P, inp.k_cache, inp.v_cache, kp,
+            inp.seq_lens, wl.N, wl.M, scale, idx, out, lse, ws)
+    calls = tuple(stage(st) for st in (sa.SA_STEP_APPEND_BOUND, sa.SA_STEP_CANDIDATES,
+                                       sa.SA_STEP_MERGE, sa.SA_STEP_ATTEND))
 
     timer = HipTimer()
     stream = torch.cuda.current_stream(dev).cuda_stream    # the stream every call launches on
-    dom_i = names.index("index_candidates")
+    dom_i = names.index("candidates")
 
     def step(rec, every_call=False):
         # rec: this step's events.  In the timed region only the dominant call
@@ -348,14 +344,14 @@ def main(argv=None):
     hbm_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # dominant kernel: filter_kernel, the one launch of the candidates stage
-    dom = "index_candidates"
+    dom = "candidates"
     dom_gbps = bytes_k[dom] / (dom_us * 1e-6) / 1e9
     src_hash = _source_hash(["indexer.hip", "device_common.hpp"])
     traffic = measured_traffic(DOMINANT_KERNEL, src_hash)
     roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
                 "traffic": traffic,
-                "kernel": "%s (sparse_attn_index_topm_stage, SA_STAGE_CANDIDATES)"
+                "kernel": "%s (sparse_attn_decode_step_stage, SA_STEP_CANDIDATES)"
                           % DOMINANT_KERNEL,
                 "bytes_per_launch": bytes_k[dom], "avg_launch_us": round(dom_us, 2),
                 "source_hash": src_hash}

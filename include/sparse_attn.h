@@ -216,6 +216,48 @@ int sparse_attn_decode(const sa_shape* shape, const void* q, const void* k_cache
                        void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * sparse_attn_decode_step -- one whole decode step of one layer: exactly
+ * sparse_attn_append_kv (T new tokens), then sparse_attn_index_topm, then
+ * sparse_attn_decode, with the same arguments, but with fewer launches (the
+ * append shares a launch with the bound stage of the selection).
+ *
+ * JSSA article, "How JSSA preserves token order": append with projection,
+ * indexer scoring and top-M selection per KV head, then gather-free
+ * attention over the selected rows.
+ *
+ * idx is written (the step's selection, e.g. for IndexCache reuse by later
+ * layers), then out and lse as sparse_attn_decode writes them.  Arguments
+ * and checks are those of the three calls; the workspace is sized by
+ * sparse_attn_workspace_size(shape, n_max, M).
+ * ------------------------------------------------------------------------- */
+int sparse_attn_decode_step(const sa_shape* shape, const int32_t* pos, int32_t T,
+                            const void* k_new, const void* v_new, const void* q,
+                            const float* P, void* k_cache, void* v_cache,
+                            uint8_t* kp_cache, const int32_t* seq_lens, int32_t n_max,
+                            int32_t M, float softmax_scale, int32_t* idx, void* out,
+                            float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/* sparse_attn_decode_step_stage -- the launches of sparse_attn_decode_step,
+ * one call each (for timing or scheduling): SA_STEP_APPEND_BOUND, then
+ * SA_STEP_CANDIDATES, SA_STEP_MERGE (writes idx), SA_STEP_ATTEND (writes
+ * out, lse).  Run them in order on one stream with identical arguments.
+ * Returns SA_ERR_INVALID for an unknown stage. */
+enum sa_step_stage {
+  SA_STEP_APPEND_BOUND = 1,
+  SA_STEP_CANDIDATES = 2,
+  SA_STEP_MERGE = 3,
+  SA_STEP_ATTEND = 4
+};
+
+int sparse_attn_decode_step_stage(const sa_shape* shape, int32_t stage, const int32_t* pos,
+                                  int32_t T, const void* k_new, const void* v_new,
+                                  const void* q, const float* P, void* k_cache,
+                                  void* v_cache, uint8_t* kp_cache, const int32_t* seq_lens,
+                                  int32_t n_max, int32_t M, float softmax_scale, int32_t* idx,
+                                  void* out, float* lse, void* workspace, size_t ws_bytes,
+                                  void* stream);
+
+/* ---------------------------------------------------------------------------
  * sparse_attn_linear_gate -- LISA-style gated linear branch.
  *
  * LISA news items (aikraft.ru "LISA architecture"; opennieuws.be "Hybrid
@@ -236,8 +278,9 @@ int sparse_attn_linear_gate(const sa_shape* shape, const void* q,
                             float* z, const float* w_gate, const void* o_sparse,
                             void* out, int32_t update_state, void* stream);
 
-/* Bytes of workspace that sparse_attn_topm, sparse_attn_index_topm and
- * sparse_attn_decode need for this shape, n_max and M (host only, pure).
+/* Bytes of workspace that sparse_attn_topm, sparse_attn_index_topm(_stage),
+ * sparse_attn_decode and sparse_attn_decode_step(_stage) need for this shape,
+ * n_max and M (host only, pure).
  * Returns 0 when the arguments are invalid. */
 size_t sparse_attn_workspace_size(const sa_shape* shape, int32_t n_max, int32_t M);
 

@@ -65,6 +65,11 @@ _SIGS = {
                                      _VP],
     "sparse_attn_decode": [_SP, _VP, _VP, _VP, _VP, _I32, ctypes.c_float, _VP, _VP, _VP,
                            _SZ, _VP],
+    "sparse_attn_decode_step": [_SP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                _I32, _I32, ctypes.c_float, _VP, _VP, _VP, _VP, _SZ, _VP],
+    "sparse_attn_decode_step_stage": [_SP, _I32, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                      _VP, _I32, _I32, ctypes.c_float, _VP, _VP, _VP, _VP, _SZ,
+                                      _VP],
     "sparse_attn_linear_gate": [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP],
     "sparse_attn_workspace_size": [_SP, _I32, _I32],
     "sparse_attn_status_string": [ctypes.c_int],
@@ -216,6 +221,47 @@ def sparse_attn_index_topm_stage(shape, stage, q, P, kp_cache, seq_lens, n_max, 
           _opt_ptr(seq_lens, torch.int32, (B,), "seq_lens"), int(n_max), int(M),
           _opt_ptr(idx, torch.int32, (B, Hkv, M), "idx"),
           _dev_ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), _stream(q))
+
+
+SA_STEP_APPEND_BOUND, SA_STEP_CANDIDATES, SA_STEP_MERGE, SA_STEP_ATTEND = 1, 2, 3, 4
+
+
+def _step_args(shape, pos, k_new, v_new, q, P, k_cache, v_cache, kp_cache, seq_lens, n_max, M,
+               softmax_scale, idx, out, lse, workspace):
+    B, Hq, Hkv, d, r, Nc = (shape.batch, shape.num_q_heads, shape.num_kv_heads,
+                            shape.head_dim, shape.rank, shape.capacity)
+    if k_new.dim() != 4 or k_new.shape[:2] != (B, Hkv) or k_new.shape[3] != d:
+        raise ValueError("k_new must have shape (B, Hkv, T, d)")
+    T = k_new.shape[2]
+    return (_dev_ptr(pos, torch.int32, (B,), "pos"), int(T),
+            _dev_ptr(k_new, torch.bfloat16, (B, Hkv, T, d), "k_new"),
+            _dev_ptr(v_new, torch.bfloat16, (B, Hkv, T, d), "v_new"),
+            _dev_ptr(q, torch.bfloat16, (B, Hq, d), "q"),
+            _dev_ptr(P, torch.float32, (Hkv, d, r), "P"),
+            _dev_ptr(k_cache, torch.bfloat16, (B, Hkv, Nc, d), "k_cache"),
+            _dev_ptr(v_cache, torch.bfloat16, (B, Hkv, Nc, d), "v_cache"),
+            _dev_ptr(kp_cache, torch.uint8, (B, Hkv, Nc, r), "kp_cache"),
+            _opt_ptr(seq_lens, torch.int32, (B,), "seq_lens"), int(n_max), int(M),
+            float(softmax_scale),
+            _dev_ptr(idx, torch.int32, (B, Hkv, M), "idx"),
+            _dev_ptr(out, torch.bfloat16, (B, Hq, d), "out"),
+            _opt_ptr(lse, torch.float32, (B, Hq), "lse"),
+            _dev_ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), _stream(q))
+
+
+def sparse_attn_decode_step(shape, pos, k_new, v_new, q, P, k_cache, v_cache, kp_cache,
+                            seq_lens, n_max, M, softmax_scale, idx, out, lse, workspace):
+    _call("sparse_attn_decode_step", _sh(shape),
+          *_step_args(shape, pos, k_new, v_new, q, P, k_cache, v_cache, kp_cache, seq_lens,
+                      n_max, M, softmax_scale, idx, out, lse, workspace))
+
+
+def sparse_attn_decode_step_stage(shape, stage, pos, k_new, v_new, q, P, k_cache, v_cache,
+                                  kp_cache, seq_lens, n_max, M, softmax_scale, idx, out, lse,
+                                  workspace):
+    _call("sparse_attn_decode_step_stage", _sh(shape), int(stage),
+          *_step_args(shape, pos, k_new, v_new, q, P, k_cache, v_cache, kp_cache, seq_lens,
+                      n_max, M, softmax_scale, idx, out, lse, workspace))
 
 
 def sparse_attn_decode(shape, q, k_cache, v_cache, idx, M, softmax_scale, out, lse, workspace):

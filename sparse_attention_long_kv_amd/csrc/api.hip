@@ -168,6 +168,94 @@ extern "C" int sparse_attn_index_topm_stage(const sa_shape* shape, int32_t stage
                            ws_bytes, stream);
 }
 
+namespace {
+
+constexpr int kStepAppend = 1, kStepCandidates = 2, kStepMerge = 4, kStepAttend = 8;
+
+int decode_step_stages(const sa_shape* shape, int stages, const int32_t* pos, int32_t T,
+                       const void* k_new, const void* v_new, const void* q, const float* P,
+                       void* k_cache, void* v_cache, uint8_t* kp_cache, const int32_t* seq_lens,
+                       int32_t n_max, int32_t M, float softmax_scale, int32_t* idx, void* out,
+                       float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  if (T < 0 || T > shape->capacity) return SA_ERR_INVALID;
+  if (!ptr_ok(pos, A4) || !ptr_ok(k_new, A16) || !ptr_ok(v_new, A16) || !ptr_ok(q, A16) ||
+      !ptr_ok(P, A4) || !ptr_ok(k_cache, A16) || !ptr_ok(v_cache, A16) ||
+      !ptr_ok(kp_cache, A16) || !ptr_ok(out, A16))
+    return SA_ERR_INVALID;
+  if (lse && !ptr_ok(lse, A4)) return SA_ERR_INVALID;
+  if (!std::isfinite(softmax_scale)) return SA_ERR_INVALID;
+  TopmPlan tplan;
+  st = check_topm_common(shape, seq_lens, n_max, M, idx, workspace, ws_bytes, &tplan);
+  if (st != SA_OK) return st;
+  FilterPlan fplan;
+  st = plan_filter(*shape, n_max, M, &fplan);
+  if (st != SA_OK) return st;
+  DecodePlan dplan;
+  st = plan_decode(*shape, M, &dplan);
+  if (st != SA_OK) return st;
+  const LaunchCommon c = common(*shape, stream);
+  hipError_t e = hipSuccess;
+  if (stages & kStepAppend) {
+    if (fplan.enabled) {
+      const AppendRows rows{pos, T, k_new, v_new, k_cache, v_cache};
+      e = run_filter_select(c, fplan, kSelectBound, q, P, kp_cache, seq_lens, n_max, M, idx,
+                            workspace, &rows);
+    } else if (T > 0) {
+      e = run_append_kv(c, pos, T, k_new, v_new, P, k_cache, v_cache, kp_cache);
+    }
+    if (e != hipSuccess) return finish(e, c.stream);
+  }
+  for (int sel : {kStepCandidates, kStepMerge}) {
+    if (!(stages & sel)) continue;
+    const int mask = sel == kStepCandidates ? kSelectChunks : kSelectMerge;
+    e = fplan.enabled ? run_filter_select(c, fplan, mask, q, P, kp_cache, seq_lens, n_max, M,
+                                          idx, workspace)
+                      : run_select(c, tplan, mask, true, q, P, kp_cache, nullptr, seq_lens, n_max,
+                                   M, idx, workspace);
+    if (e != hipSuccess) return finish(e, c.stream);
+  }
+  if (stages & kStepAttend)
+    e = run_decode(c, dplan, q, k_cache, v_cache, idx, M, softmax_scale, out, lse, workspace);
+  return finish(e, c.stream);
+}
+
+}  // namespace
+
+extern "C" int sparse_attn_decode_step(const sa_shape* shape, const int32_t* pos, int32_t T,
+                                       const void* k_new, const void* v_new, const void* q,
+                                       const float* P, void* k_cache, void* v_cache,
+                                       uint8_t* kp_cache, const int32_t* seq_lens, int32_t n_max,
+                                       int32_t M, float softmax_scale, int32_t* idx, void* out,
+                                       float* lse, void* workspace, size_t ws_bytes,
+                                       void* stream) {
+  return decode_step_stages(shape, kStepAppend | kStepCandidates | kStepMerge | kStepAttend, pos,
+                            T, k_new, v_new, q, P, k_cache, v_cache, kp_cache, seq_lens, n_max,
+                            M, softmax_scale, idx, out, lse, workspace, ws_bytes, stream);
+}
+
+extern "C" int sparse_attn_decode_step_stage(const sa_shape* shape, int32_t stage,
+                                             const int32_t* pos, int32_t T, const void* k_new,
+                                             const void* v_new, const void* q, const float* P,
+                                             void* k_cache, void* v_cache, uint8_t* kp_cache,
+                                             const int32_t* seq_lens, int32_t n_max, int32_t M,
+                                             float softmax_scale, int32_t* idx, void* out,
+                                             float* lse, void* workspace, size_t ws_bytes,
+                                             void* stream) {
+  int mask;
+  switch (stage) {
+    case SA_STEP_APPEND_BOUND: mask = kStepAppend; break;
+    case SA_STEP_CANDIDATES: mask = kStepCandidates; break;
+    case SA_STEP_MERGE: mask = kStepMerge; break;
+    case SA_STEP_ATTEND: mask = kStepAttend; break;
+    default: return SA_ERR_INVALID;
+  }
+  return decode_step_stages(shape, mask, pos, T, k_new, v_new, q, P, k_cache, v_cache, kp_cache,
+                            seq_lens, n_max, M, softmax_scale, idx, out, lse, workspace, ws_bytes,
+                            stream);
+}
+
 extern "C" int sparse_attn_decode(const sa_shape* shape, const void* q, const void* k_cache,
                                   const void* v_cache, const int32_t* idx, int32_t M,
                                   float softmax_scale, void* out, float* lse, void* workspace,

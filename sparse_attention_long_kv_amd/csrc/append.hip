@@ -16,12 +16,10 @@
 // each form one partial sum straight from global memory, and the row's bf16
 // K/V copies go out in parallel.  The bulk projection stages key rows in LDS
 // and lets one lane form one code from all 8 parts.
-#include "device_common.hpp"
+#include "append_common.hpp"
 #include "kernels.h"
 
 namespace sa {
-
-constexpr int kProjParts = 8;
 
 // ---------------------------------------------------------------- append
 
@@ -30,44 +28,15 @@ __global__ __launch_bounds__(kBlock) void append_kv_kernel(
     const int32_t* __restrict__ pos, int T, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, const float* __restrict__ P, int Hkv, int Ncap,
     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache, uint8_t* __restrict__ kp) {
-  constexpr int kPer = D / kProjParts;
   static_assert(kProjParts * R <= kBlock, "one thread per (part, column)");
   __shared__ double part[kProjParts * R];
   const int u = blockIdx.x / T, tok = blockIdx.x % T;
   const int b = u / Hkv, h = u % Hkv;
   const long n = (long)pos[b] + tok;
   if (n < 0 || n >= Ncap) return;                    // block-uniform
-  const int t = threadIdx.x;
-  const uint16_t* kr = k_new + ((size_t)u * T + tok) * D;
-  const uint16_t* vr = v_new + ((size_t)u * T + tok) * D;
-  // bf16 row copies: D/8 threads move 16 bytes of K and of V each
-  if (t < D / 8) {
-    const size_t off = ((size_t)u * Ncap + n) * D + t * 8;
-    *reinterpret_cast<uint4*>(k_cache + off) = *reinterpret_cast<const uint4*>(kr + t * 8);
-    *reinterpret_cast<uint4*>(v_cache + off) = *reinterpret_cast<const uint4*>(vr + t * 8);
-  }
-  // partial sum of part p for column j
-  const int p = t / R, j = t % R;
-  if (t < kProjParts * R) {
-    const float* Ph = P + (size_t)h * D * R + (size_t)p * kPer * R + j;
-    float pv[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) pv[k] = Ph[k * R];
-    float kv[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; k += 8) bf16x8_to_f32(*reinterpret_cast<const uint4*>(kr + p * kPer + k), kv + k);
-    double acc = 0.0;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) acc = fma((double)kv[k], (double)pv[k], acc);
-    part[t] = acc;
-  }
-  __syncthreads();
-  if (t < R) {
-    double s = 0.0;
-#pragma unroll
-    for (int q = 0; q < kProjParts; ++q) s += part[q * R + t];
-    kp[((size_t)u * Ncap + n) * R + t] = (uint8_t)f64_to_e4m3(s);
-  }
+  const size_t row = (size_t)u * Ncap + n;
+  append_row<D, R>(k_new + ((size_t)u * T + tok) * D, v_new + ((size_t)u * T + tok) * D,
+                   P + (size_t)h * D * R, row, k_cache, v_cache, kp + row * R, part);
 }
 
 // ---------------------------------------------------------------- bulk

@@ -23,7 +23,7 @@
 // order (score desc, position asc) is total), and a second launch merges
 // each unit's candidates with the same machinery.  The unfused path ("topm")
 // does the same from scores stored in HBM.
-#include "device_common.hpp"
+#include "append_common.hpp"
 #include "kernels.h"
 
 namespace sa {
@@ -979,11 +979,12 @@ __device__ __forceinline__ void query_halves(const float* qt, float (&qlo)[16], 
   }
 }
 
+// The bound stage for unit u (the whole workgroup; it synchronises).
 template <int D, int R>
-__global__ __launch_bounds__(kSampleThreads) void sample_kernel(const FilterArgs a) {
+__device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<kSampleThreads>& sh,
+                                             int u) {
   constexpr int NT = kSampleThreads;
-  __shared__ SelectShared<NT> sh;
-  const int u = blockIdx.x, b = u / a.Hkv, h = u % a.Hkv;
+  const int b = u / a.Hkv, h = u % a.Hkv;
   const int tid = threadIdx.x;
   const int len = unit_len(a.seq_lens, b, a.n_max);
   for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
@@ -1037,6 +1038,42 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const FilterArgs
     for (int i = 0; i < kSampleKeys; ++i) f(key[i], key[i] != 0u);
   });
   if (tid == 0) a.thr[u] = t;
+}
+
+template <int D, int R>
+__global__ __launch_bounds__(kSampleThreads) void sample_kernel(const FilterArgs a) {
+  __shared__ SelectShared<kSampleThreads> sh;
+  sample_bound<D, R>(a, sh, blockIdx.x);
+}
+
+// Decode-step prologue: append the unit's new rows, then the bound stage, in
+// one workgroup (the bound is an estimate: whether its sample sees the new
+// rows does not matter; the filter and merge that follow do see them).
+struct AppendArgs {
+  const int32_t* pos;
+  int T;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+};
+
+template <int D, int R>
+__global__ __launch_bounds__(kSampleThreads) void append_bound_kernel(const FilterArgs a,
+                                                                       const AppendArgs ap) {
+  __shared__ SelectShared<kSampleThreads> sh;
+  const int u = blockIdx.x, b = u / a.Hkv, h = u % a.Hkv;
+  const int p0 = ap.pos[b];
+  for (int tok = 0; tok < ap.T; ++tok) {
+    const long n = (long)p0 + tok;
+    if (n < 0 || n >= a.Ncap) continue;               // block-uniform
+    const size_t row = (size_t)u * a.Ncap + n;
+    append_row<D, R>(ap.k_new + ((size_t)u * ap.T + tok) * D,
+                     ap.v_new + ((size_t)u * ap.T + tok) * D, a.P + (size_t)h * D * R, row,
+                     ap.k_cache, ap.v_cache, const_cast<uint8_t*>(a.kp) + row * R, sh.part);
+    __syncthreads();                                  // `part` is reused
+  }
+  sample_bound<D, R>(a, sh, u);
 }
 
 template <int D, int R>
@@ -1366,8 +1403,12 @@ __global__ __launch_bounds__(kMergeThreads) void filter_merge_kernel(const Filte
 }
 
 template <int D, int R>
-static void launch_filter_dr(const FilterArgs& a, int stages, int units, hipStream_t st) {
-  if (stages & kSelectBound)
+static void launch_filter_dr(const FilterArgs& a, const AppendArgs* ap, int stages, int units,
+                             hipStream_t st) {
+  if ((stages & kSelectBound) && ap)
+    hipLaunchKernelGGL((append_bound_kernel<D, R>), dim3(units), dim3(kSampleThreads), 0, st, a,
+                       *ap);
+  else if (stages & kSelectBound)
     hipLaunchKernelGGL((sample_kernel<D, R>), dim3(units), dim3(kSampleThreads), 0, st, a);
   if (stages & kSelectChunks)
     hipLaunchKernelGGL((filter_kernel<D, R>), dim3((unsigned)(units * a.S)), dim3(kChunkThreads),
@@ -1379,7 +1420,7 @@ static void launch_filter_dr(const FilterArgs& a, int stages, int units, hipStre
 hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int stages,
                              const void* q, const float* P, const uint8_t* kp,
                              const int32_t* seq_lens, int n_max, int M, int32_t* idx,
-                             void* workspace) {
+                             void* workspace, const AppendRows* rows) {
   FilterArgs a;
   a.q = (const uint16_t*)q;
   a.P = P;
@@ -1405,10 +1446,20 @@ hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int 
   a.cpos = (int32_t*)(ws + plan.off_pos);
   a.idx = idx;
   if ((long)plan.units * plan.splits > INT32_MAX) return hipErrorInvalidConfiguration;
-  if (c.D == 128 && c.R == 32) launch_filter_dr<128, 32>(a, stages, plan.units, c.stream);
-  else if (c.D == 128 && c.R == 16) launch_filter_dr<128, 16>(a, stages, plan.units, c.stream);
-  else if (c.D == 64 && c.R == 32) launch_filter_dr<64, 32>(a, stages, plan.units, c.stream);
-  else launch_filter_dr<64, 16>(a, stages, plan.units, c.stream);
+  AppendArgs ap;
+  if (rows) {
+    ap.pos = rows->pos;
+    ap.T = rows->T;
+    ap.k_new = (const uint16_t*)rows->k_new;
+    ap.v_new = (const uint16_t*)rows->v_new;
+    ap.k_cache = (uint16_t*)rows->k_cache;
+    ap.v_cache = (uint16_t*)rows->v_cache;
+  }
+  const AppendArgs* app = rows ? &ap : nullptr;
+  if (c.D == 128 && c.R == 32) launch_filter_dr<128, 32>(a, app, stages, plan.units, c.stream);
+  else if (c.D == 128 && c.R == 16) launch_filter_dr<128, 16>(a, app, stages, plan.units, c.stream);
+  else if (c.D == 64 && c.R == 32) launch_filter_dr<64, 32>(a, app, stages, plan.units, c.stream);
+  else launch_filter_dr<64, 16>(a, app, stages, plan.units, c.stream);
   return hipGetLastError();
 }
 

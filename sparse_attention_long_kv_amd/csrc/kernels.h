@@ -29,12 +29,23 @@ hipError_t run_select(const LaunchCommon& c, const TopmPlan& plan, int stages, b
                       const void* q, const float* P, const uint8_t* kp, const float* scores,
                       const int32_t* seq_lens, int n_max, int M, int32_t* idx,
                       void* workspace);
+// New rows appended by the decode-step prologue (see run_filter_select).
+struct AppendRows {
+  const int32_t* pos;
+  int T;
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+};
+
 // Filter path of the fused selection (plan.enabled): stages kSelectBound
-// (sampled bound), kSelectChunks (filtering chunks), kSelectMerge.
+// (sampled bound; with `rows`, the same launch first appends those rows),
+// kSelectChunks (filtering chunks), kSelectMerge.
 hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int stages,
                              const void* q, const float* P, const uint8_t* kp,
                              const int32_t* seq_lens, int n_max, int M, int32_t* idx,
-                             void* workspace);
+                             void* workspace, const AppendRows* rows = nullptr);
 hipError_t run_decode(const LaunchCommon& c, const DecodePlan& plan, const void* q,
                       const void* k_cache, const void* v_cache, const int32_t* idx, int M,
                       float scale, void* out, float* lse, void* workspace);

@@ -126,6 +126,18 @@ def test_bad_arguments_are_rejected(lib):
     assert _st(lib, "sparse_attn_topm", by, P, None, wl.N, wl.M, P, P, need - 1, None) == -3
     assert _st(lib, "sparse_attn_index_topm", by, P, P, P, None, wl.N, wl.M, P, P, need - 1,
                None) == -3
+    step = "sparse_attn_decode_step_stage"
+    f1 = ctypes.c_float(1.0)
+    assert _st(lib, step, by, 0, P, 1, P, P, P, P, P, P, P, None, wl.N, wl.M, f1, P, P, None, P,
+               need, None) == -1
+    assert _st(lib, step, by, 5, P, 1, P, P, P, P, P, P, P, None, wl.N, wl.M, f1, P, P, None, P,
+               need, None) == -1
+    assert _st(lib, step, by, 1, P, 1, P, P, P, P, P, P, P, None, wl.N, wl.M, f1, P, P, None, P,
+               need - 1, None) == -3
+    assert _st(lib, "sparse_attn_decode_step", by, P, -1, P, P, P, P, P, P, P, None, wl.N, wl.M,
+               f1, P, P, None, P, need, None) == -1
+    assert _st(lib, "sparse_attn_decode_step", by, P, 1, P, P, P, P, P, P, P, None, wl.N, wl.M,
+               ctypes.c_float(float("nan")), P, P, None, P, need, None) == -1
     stage = "sparse_attn_index_topm_stage"
     assert _st(lib, stage, by, 2, P, P, P, None, wl.N, wl.M, None, None, need, None) == -3
     assert _st(lib, stage, by, 3, P, P, P, None, wl.N, wl.M, P, P, need - 1, None) == -3

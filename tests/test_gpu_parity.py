@@ -452,20 +452,19 @@ def test_cross_layer_reuse_equals_decode_with_source_indices():
 # ------------------------------------------------------------------ full size
 
 def _bench_sequence(inp, sh, M, ws):
-    """The calls, in the order and launch configuration bench.py times."""
+    """The calls, in the order and launch configuration bench.py times: the
+    four stages of sparse_attn_decode_step."""
     wl = inp.wl
     kp = torch.empty(wl.B, wl.Hkv, wl.N, wl.r, dtype=torch.uint8, device="cuda")
     sa.sparse_attn_project_keys(sh, inp.k_cache, inp.P, 0, wl.N, kp)
-    sa.sparse_attn_append_kv(sh, inp.pos, inp.k_new, inp.v_new, inp.P, inp.k_cache,
-                             inp.v_cache, kp)
     idx = torch.empty(wl.B, wl.Hkv, M, dtype=torch.int32, device="cuda")
-    for stage in (sa.SA_STAGE_BOUND, sa.SA_STAGE_CANDIDATES, sa.SA_STAGE_MERGE):
-        sa.sparse_attn_index_topm_stage(sh, stage, inp.q, inp.P, kp, inp.seq_lens, wl.N, M, idx,
-                                        ws)
     out = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(wl.B, wl.Hq, dtype=torch.float32, device="cuda")
-    sa.sparse_attn_decode(sh, inp.q, inp.k_cache, inp.v_cache, idx, M, default_scale(wl.d),
-                          out, lse, ws)
+    for stage in (sa.SA_STEP_APPEND_BOUND, sa.SA_STEP_CANDIDATES, sa.SA_STEP_MERGE,
+                  sa.SA_STEP_ATTEND):
+        sa.sparse_attn_decode_step_stage(sh, stage, inp.pos, inp.k_new, inp.v_new, inp.q,
+                                         inp.P, inp.k_cache, inp.v_cache, kp, inp.seq_lens,
+                                         wl.N, M, default_scale(wl.d), idx, out, lse, ws)
     return kp, idx, out, lse
 
 
@@ -583,3 +582,45 @@ def test_topm_sample_overestimate_falls_back_exactly():
     kp = oracle_kp(K64, P64)
     gi = _topm_check_against_oracle(q, P, kp, M, N)
     assert set(rows.tolist()) <= set(gi[0, 0].tolist())
+
+
+# ------------------------------------------------------------------ decode step
+
+@pytest.mark.parametrize("name,N,T,lens", [("tiny", None, 1, None),
+                                           ("gqa7_16k", 8192, 1, [8192, 5000, 1, 0, 8192, 300,
+                                                                  8100, 7000]),
+                                           ("longctx_128k", 16384, 2, None)])
+def test_decode_step_equals_the_three_calls(name, N, T, lens):
+    """sparse_attn_decode_step (fused prologue) writes the same caches, idx,
+    out and lse, bit for bit, as append_kv + index_topm + decode."""
+    wl = WORKLOADS[name] if N is None else scaled(WORKLOADS[name], N=N, B=min(8, WORKLOADS[name].B))
+    _say("case: decode step", wl.name, wl.N, "T=%d" % T)
+    sh = _shape_of(wl.B, wl.Hq, wl.Hkv, wl.d, wl.r, wl.N)
+    res = []
+    for fused in (False, True):
+        inp = make_decode_inputs(wl, seed=13, device="cuda", seq_lens=lens)
+        g = torch.Generator(device="cuda").manual_seed(5)
+        k_new = torch.randn(wl.B, wl.Hkv, T, wl.d, generator=g, device="cuda").to(torch.bfloat16)
+        v_new = torch.randn(wl.B, wl.Hkv, T, wl.d, generator=g, device="cuda").to(torch.bfloat16)
+        pos = (inp.seq_lens - T).clamp(min=0).to(torch.int32)
+        kp = torch.empty(wl.B, wl.Hkv, wl.N, wl.r, dtype=torch.uint8, device="cuda")
+        sa.sparse_attn_project_keys(sh, inp.k_cache, inp.P, 0, wl.N, kp)
+        ws = sa.alloc_workspace(sh, wl.N, wl.M)
+        idx = torch.full((wl.B, wl.Hkv, wl.M), -9, dtype=torch.int32, device="cuda")
+        out = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(wl.B, wl.Hq, dtype=torch.float32, device="cuda")
+        scale = default_scale(wl.d)
+        if fused:
+            sa.sparse_attn_decode_step(sh, pos, k_new, v_new, inp.q, inp.P, inp.k_cache,
+                                       inp.v_cache, kp, inp.seq_lens, wl.N, wl.M, scale, idx, out,
+                                       lse, ws)
+        else:
+            sa.sparse_attn_append_kv(sh, pos, k_new, v_new, inp.P, inp.k_cache, inp.v_cache, kp)
+            sa.sparse_attn_index_topm(sh, inp.q, inp.P, kp, inp.seq_lens, wl.N, wl.M, idx, ws)
+            sa.sparse_attn_decode(sh, inp.q, inp.k_cache, inp.v_cache, idx, wl.M, scale, out,
+                                  lse, ws)
+        torch.cuda.synchronize()
+        res.append((inp.k_cache.clone(), inp.v_cache.clone(), kp, idx, out, lse))
+        del inp
+    for x, y in zip(res[0], res[1]):
+        assert torch.equal(x, y)

@@ -980,14 +980,35 @@ __device__ __forceinline__ void query_halves(const float* qt, float (&qlo)[16], 
 }
 
 // The bound stage for unit u (the whole workgroup; it synchronises).
-template <int D, int R>
+// between() runs while the sampled rows are in flight (every thread calls it).
+template <int D, int R, class Between>
 __device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<kSampleThreads>& sh,
-                                             int u) {
+                                             int u, Between between) {
   constexpr int NT = kSampleThreads;
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int tid = threadIdx.x;
   const int len = unit_len(a.seq_lens, b, a.n_max);
   for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
+  // blocks of 8 consecutive positions, evenly spread over [0, len); the row
+  // loads go out first
+  constexpr int kTotal = kSampleBlocks * kSampleBlock;
+  const bool all = len <= kTotal;
+  const uint8_t* kpu = a.kp + (size_t)u * a.Ncap * R;
+  uint32_t key[kSampleKeys];
+  uint4 c0[kSampleKeys], c1[kSampleKeys];
+  bool ok[kSampleKeys];
+#pragma unroll
+  for (int i = 0; i < kSampleKeys; ++i) {
+    const int slot = i * NT + tid;
+    const int blk = slot / kSampleBlock, off = slot % kSampleBlock;
+    const int p = all ? slot
+                      : (int)(((int64_t)blk * (len - kSampleBlock)) / (kSampleBlocks - 1)) + off;
+    ok[i] = p < len && len > a.M;
+    const uint8_t* row = kpu + (size_t)(ok[i] ? p : 0) * R;
+    c0[i] = load16(row);
+    if (R == 32) c1[i] = load16(row + 16);
+  }
+  between();
   indexer_query<D, R, NT>(a.q, a.P, b, h, a.G, a.Hq, sh.qt, sh.part);
   if (tid < R) a.qt[(size_t)u * 32 + tid] = sh.qt[tid];
   if (len <= a.M) {                                   // every valid position is selected
@@ -996,24 +1017,6 @@ __device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<k
   }
   float qlo[16], qhi[16];
   query_halves<R>(sh.qt, qlo, qhi);
-  // blocks of 8 consecutive positions, evenly spread over [0, len)
-  constexpr int kTotal = kSampleBlocks * kSampleBlock;
-  const bool all = len <= kTotal;
-  const uint8_t* kpu = a.kp + (size_t)u * a.Ncap * R;
-  uint32_t key[kSampleKeys];
-  uint4 c0[kSampleKeys], c1[kSampleKeys];
-  bool ok[kSampleKeys];
-#pragma unroll
-  for (int i = 0; i < kSampleKeys; ++i) {           // all row loads first
-    const int slot = i * NT + tid;
-    const int blk = slot / kSampleBlock, off = slot % kSampleBlock;
-    const int p = all ? slot
-                      : (int)(((int64_t)blk * (len - kSampleBlock)) / (kSampleBlocks - 1)) + off;
-    ok[i] = p < len;
-    const uint8_t* row = kpu + (size_t)(ok[i] ? p : 0) * R;
-    c0[i] = load16(row);
-    if (R == 32) c1[i] = load16(row + 16);
-  }
 #pragma unroll
   for (int i = 0; i < kSampleKeys; ++i) {
     float s = score16(qlo, c0[i]);
@@ -1043,7 +1046,7 @@ __device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<k
 template <int D, int R>
 __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const FilterArgs a) {
   __shared__ SelectShared<kSampleThreads> sh;
-  sample_bound<D, R>(a, sh, blockIdx.x);
+  sample_bound<D, R>(a, sh, blockIdx.x, [] {});
 }
 
 // Decode-step prologue: append the unit's new rows, then the bound stage, in
@@ -1064,16 +1067,17 @@ __global__ __launch_bounds__(kSampleThreads) void append_bound_kernel(const Filt
   __shared__ SelectShared<kSampleThreads> sh;
   const int u = blockIdx.x, b = u / a.Hkv, h = u % a.Hkv;
   const int p0 = ap.pos[b];
-  for (int tok = 0; tok < ap.T; ++tok) {
-    const long n = (long)p0 + tok;
-    if (n < 0 || n >= a.Ncap) continue;               // block-uniform
-    const size_t row = (size_t)u * a.Ncap + n;
-    append_row<D, R>(ap.k_new + ((size_t)u * ap.T + tok) * D,
-                     ap.v_new + ((size_t)u * ap.T + tok) * D, a.P + (size_t)h * D * R, row,
-                     ap.k_cache, ap.v_cache, const_cast<uint8_t*>(a.kp) + row * R, sh.part);
-    __syncthreads();                                  // `part` is reused
-  }
-  sample_bound<D, R>(a, sh, u);
+  sample_bound<D, R>(a, sh, u, [&] {
+    for (int tok = 0; tok < ap.T; ++tok) {
+      const long n = (long)p0 + tok;
+      if (n < 0 || n >= a.Ncap) continue;             // block-uniform
+      const size_t row = (size_t)u * a.Ncap + n;
+      append_row<D, R>(ap.k_new + ((size_t)u * ap.T + tok) * D,
+                       ap.v_new + ((size_t)u * ap.T + tok) * D, a.P + (size_t)h * D * R, row,
+                       ap.k_cache, ap.v_cache, const_cast<uint8_t*>(a.kp) + row * R, sh.part);
+      __syncthreads();                                // `part` is reused
+    }
+  });
 }
 
 template <int D, int R>

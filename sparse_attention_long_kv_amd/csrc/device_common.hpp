@@ -118,6 +118,11 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return k == 0u ? 1u : k;
 }
 
+// The score a key stands for (inverse of score_key on keys >= 2).
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // ---------------------------------------------------------------- lanes
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }

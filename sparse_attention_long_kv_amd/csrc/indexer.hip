@@ -397,9 +397,11 @@ __device__ void finish_threshold(Sh& sh, uint32_t target, uint32_t& t_out, uint3
 // write unselected keys to a scratch slot); slot = number of selected keys
 // before this one.  When every key == t is selected (need == eq, the usual
 // case) selection is the single predicate key >= t, one ballot per row.
+// Rows i >= nk (block-uniform) hold no selectable key and are skipped.
 template <int NT, int K, class EmitFn>
 __device__ __forceinline__ void emit_in_order(const uint32_t (&key)[K], uint32_t t, uint32_t need,
-                                              uint32_t eq, SelectShared<NT>& sh, EmitFn emit) {
+                                              uint32_t eq, SelectShared<NT>& sh, EmitFn emit,
+                                              int nk = K) {
   constexpr int W = NT / kWave;
   static_assert(K * W <= NT, "segments");
   const int tid = threadIdx.x, w = tid / kWave;
@@ -407,8 +409,9 @@ __device__ __forceinline__ void emit_in_order(const uint32_t (&key)[K], uint32_t
   // pass 1: per (row, wave) counts, wave-major so pass 2 reads them at once
 #pragma unroll
   for (int i = 0; i < K; ++i) {
-    uint32_t v;
-    if (single) {
+    uint32_t v = 0u;
+    if (i >= nk) {
+    } else if (single) {
       v = (uint32_t)popc64(ballot(key[i] >= t));
     } else {
       v = (uint32_t)popc64(ballot(key[i] > t)) | ((uint32_t)popc64(ballot(key[i] == t)) << 16);
@@ -433,7 +436,8 @@ __device__ __forceinline__ void emit_in_order(const uint32_t (&key)[K], uint32_t
   asm volatile("" : "+v"(t2));
 #pragma unroll
   for (int i = 0; i < K; ++i) {
-    if (single) {
+    if (i >= nk) {
+    } else if (single) {
       const bool sel = key[i] >= t2;
       const uint32_t slot = pre[i] + (uint32_t)__builtin_amdgcn_mbcnt_hi(
           (uint32_t)(ballot(sel) >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ballot(sel), 0u));
@@ -953,7 +957,9 @@ constexpr int kSampleKeys = kSampleBlocks * kSampleBlock / kSampleThreads;
 constexpr int kBitmapWords = kFilterMaxN / 32;
 constexpr int kFilterMergeKeys = kFilterSlots / kMergeThreads;   // 16 per thread
 static_assert(kFilterMaxCap * kFilterWaves <= kFilterSlots, "a chunk's slots fit the merge");
-static_assert(kFilterSlots / (kFilterWaves * kFilterMinCap) <= kWave, "one wave sums the chunk counts");
+constexpr int kFilterMaxSplits = kFilterSlots / (kFilterWaves * kFilterMinCap);   // 16
+static_assert(kFilterMaxSplits <= kWave && (kFilterMaxSplits & (kFilterMaxSplits - 1)) == 0,
+              "one wave scans the chunk counts; chunks are found by bisection");
 
 __device__ __forceinline__ int unit_len(const int32_t* seq_lens, int b, int n_max) {
   return seq_lens ? min(max(seq_lens[b], 0), n_max) : n_max;
@@ -980,10 +986,11 @@ __device__ __forceinline__ void query_halves(const float* qt, float (&qlo)[16], 
 }
 
 // The bound stage for unit u (the whole workgroup; it synchronises).
-// between() runs while the sampled rows are in flight (every thread calls it).
-template <int D, int R, class Between>
+// prologue() runs while the sampled rows are in flight (every thread calls
+// it) and leaves the unit's indexer query in sh.qt.
+template <int D, int R, class Prologue>
 __device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<kSampleThreads>& sh,
-                                             int u, Between between) {
+                                             int u, Prologue prologue) {
   constexpr int NT = kSampleThreads;
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int tid = threadIdx.x;
@@ -1008,8 +1015,7 @@ __device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<k
     c0[i] = load16(row);
     if (R == 32) c1[i] = load16(row + 16);
   }
-  between();
-  indexer_query<D, R, NT>(a.q, a.P, b, h, a.G, a.Hq, sh.qt, sh.part);
+  prologue();
   if (tid < R) a.qt[(size_t)u * 32 + tid] = sh.qt[tid];
   if (len <= a.M) {                                   // every valid position is selected
     if (tid == 0) a.thr[u] = 1u;
@@ -1046,7 +1052,11 @@ __device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<k
 template <int D, int R>
 __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const FilterArgs a) {
   __shared__ SelectShared<kSampleThreads> sh;
-  sample_bound<D, R>(a, sh, blockIdx.x, [] {});
+  const int u = blockIdx.x;
+  sample_bound<D, R>(a, sh, u, [&] {
+    indexer_query<D, R, kSampleThreads>(a.q, a.P, u / a.Hkv, u % a.Hkv, a.G, a.Hq, sh.qt,
+                                        sh.part);
+  });
 }
 
 // Decode-step prologue: append the unit's new rows, then the bound stage, in
@@ -1061,22 +1071,101 @@ struct AppendArgs {
   uint16_t* v_cache;
 };
 
+// The unit's first new row is appended (append_row's arithmetic) while its
+// indexer query is formed (indexer_query's arithmetic); both projections
+// share one load of the basis, and every global load of both goes out before
+// the first barrier.  Further new rows (T > 1) follow one at a time.  Leaves
+// the query in qt; part holds NT >= 512 + d doubles of LDS.
+template <int D, int R, int NT>
+__device__ __forceinline__ void append_rows_and_query(const FilterArgs& a, const AppendArgs& ap,
+                                                      int u, float* qt, double* part) {
+  constexpr int kPer = D / kProjParts;
+  constexpr int kMeanT = 512;                       // threads [512, 512 + d) form the mean
+  static_assert(kProjParts * 32 <= 256 && kMeanT + D <= NT, "thread roles");
+  double* part_a = part;                            // [8r] partial sums of the new row's code
+  double* part_m = part + 256;                      // [d]  group-mean query
+  double* part_q = part + kMeanT;                   // [8r] partial sums of the query
+  const int t = threadIdx.x;
+  const int b = u / a.Hkv, h = u % a.Hkv;
+  const int pi = t / R, j = t % R;
+  const bool proj = t < kProjParts * R;
+  const float* Ph = a.P + (size_t)h * D * R;
+  float pv[kPer];
+  if (proj) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) pv[k] = Ph[(pi * kPer + k) * R + j];
+  }
+  if (t >= kMeanT && t < kMeanT + D) {
+    const int i = t - kMeanT;
+    const uint16_t* qb = a.q + ((size_t)b * a.Hq + (size_t)h * a.G) * D;
+    double mean = 0.0;
+    for (int g = 0; g < a.G; ++g) mean += (double)__uint_as_float((uint32_t)qb[g * D + i] << 16);
+    part_m[i] = mean / (double)a.G;
+  }
+  const int p0 = ap.pos[b];
+  auto row_of = [&](int tok, size_t& row) {
+    const long n = (long)p0 + tok;
+    row = (size_t)u * a.Ncap + (size_t)n;
+    return n >= 0 && n < a.Ncap;                    // block-uniform
+  };
+  size_t row0 = 0;
+  const bool ok0 = ap.T > 0 && row_of(0, row0);
+  if (ok0) {
+    const uint16_t* kr = ap.k_new + (size_t)u * ap.T * D;
+    const uint16_t* vr = ap.v_new + (size_t)u * ap.T * D;
+    if (t < D / 8) {
+      const size_t off = row0 * D + t * 8;
+      *reinterpret_cast<uint4*>(ap.k_cache + off) = *reinterpret_cast<const uint4*>(kr + t * 8);
+      *reinterpret_cast<uint4*>(ap.v_cache + off) = *reinterpret_cast<const uint4*>(vr + t * 8);
+    }
+    if (proj) {
+      float kv[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; k += 8)
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(kr + pi * kPer + k), kv + k);
+      double acc = 0.0;
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) acc = fma((double)kv[k], (double)pv[k], acc);
+      part_a[t] = acc;
+    }
+  }
+  __syncthreads();
+  if (ok0 && t < R) {
+    double sum = 0.0;
+#pragma unroll
+    for (int q = 0; q < kProjParts; ++q) sum += part_a[q * R + t];
+    const_cast<uint8_t*>(a.kp)[row0 * R + t] = (uint8_t)f64_to_e4m3(sum);
+  }
+  if (proj) {
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) acc = fma(part_m[pi * kPer + k], (double)pv[k], acc);
+    part_q[t] = acc;
+  }
+  __syncthreads();
+  if (t < R) {
+    double sum = 0.0;
+    for (int q = 0; q < kProjParts; ++q) sum += part_q[q * R + t];
+    qt[t] = (float)sum;
+  }
+  for (int tok = 1; tok < ap.T; ++tok) {
+    size_t row;
+    if (!row_of(tok, row)) continue;
+    append_row<D, R>(ap.k_new + ((size_t)u * ap.T + tok) * D,
+                     ap.v_new + ((size_t)u * ap.T + tok) * D, Ph, row, ap.k_cache, ap.v_cache,
+                     const_cast<uint8_t*>(a.kp) + row * R, part_a);
+    __syncthreads();                                // part_a is reused
+  }
+  __syncthreads();
+}
+
 template <int D, int R>
 __global__ __launch_bounds__(kSampleThreads) void append_bound_kernel(const FilterArgs a,
                                                                        const AppendArgs ap) {
   __shared__ SelectShared<kSampleThreads> sh;
-  const int u = blockIdx.x, b = u / a.Hkv, h = u % a.Hkv;
-  const int p0 = ap.pos[b];
+  const int u = blockIdx.x;
   sample_bound<D, R>(a, sh, u, [&] {
-    for (int tok = 0; tok < ap.T; ++tok) {
-      const long n = (long)p0 + tok;
-      if (n < 0 || n >= a.Ncap) continue;             // block-uniform
-      const size_t row = (size_t)u * a.Ncap + n;
-      append_row<D, R>(ap.k_new + ((size_t)u * ap.T + tok) * D,
-                       ap.v_new + ((size_t)u * ap.T + tok) * D, a.P + (size_t)h * D * R, row,
-                       ap.k_cache, ap.v_cache, const_cast<uint8_t*>(a.kp) + row * R, sh.part);
-      __syncthreads();                                // `part` is reused
-    }
+    append_rows_and_query<D, R, kSampleThreads>(a, ap, u, sh.qt, sh.part);
   });
 }
 
@@ -1102,7 +1191,9 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
     if (threadIdx.x == 0) *cnt = 0;
     return;
   }
-  const uint32_t thr = a.thr[u];
+  // key >= thr  <=>  score >= thrf for every score the chains can produce
+  // (no NaN; -0 and +0 share the key of +0, and -0 >= +0 holds)
+  const float thrf = key_score(a.thr[u]);
   uint32_t* lk = a.ckey + ((size_t)u * a.S + c) * a.cslots;
   int32_t* lp = a.cpos + ((size_t)u * a.S + c) * a.cslots;
   // this chunk's rows only: loads past the valid positions return zero
@@ -1143,13 +1234,13 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
       // scoring of the other kernels: identical bits
       float s = score16(qlo, bt.a[x]);
       if (R == 32) s = s + score16(qhi, bt.b[x]);
-      const uint32_t key = score_key(s + 0.0f);
-      const bool sel = p < len && key >= thr;
-      const uint64_t m = ballot(sel);
+      const bool ge = s >= thrf, in = p < len;
+      const bool sel = ge && in;
+      const uint64_t m = ballot(ge) & ballot(in);     // (two compares, no select)
       const uint32_t slot = wc + __builtin_amdgcn_mbcnt_hi(
                                      (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
       if (sel && slot < (uint32_t)a.cap) {
-        sk[w][slot] = key;
+        sk[w][slot] = __float_as_uint(s);               // keyed when written out
         sp[w][slot] = p;
       }
       if (i0 + x < rows) rowcnt[w][i0 + x] = (uint32_t)popc64(m);   // same value from every lane
@@ -1211,7 +1302,7 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
       const int32_t p = sp[w][j];
       const int i = (p - base) / NT;
       const uint32_t o = rowoff[w][i] + ((uint32_t)j - rowfirst[w][i]);
-      lk[o] = sk[w][j];
+      lk[o] = score_key(__uint_as_float(sk[w][j]) + 0.0f);
       lp[o] = p;
     }
   }
@@ -1321,7 +1412,7 @@ __global__ __launch_bounds__(kMergeThreads) void filter_merge_kernel(const Filte
   constexpr int KPT = kFilterMergeKeys;
   __shared__ SelectShared<NT> sh;
   __shared__ uint32_t bm[kBitmapWords];           // used by the streaming fallback only
-  __shared__ int32_t cnt_s[kFilterSlots / (kFilterWaves * kFilterMinCap)];
+  __shared__ uint32_t start_s[kFilterMaxSplits];
   __shared__ uint32_t red[NT / kWave];
   const int u = blockIdx.x, b = u / a.Hkv, h = u % a.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
@@ -1332,28 +1423,15 @@ __global__ __launch_bounds__(kMergeThreads) void filter_merge_kernel(const Filte
     for (int j = tid; j < M; j += NT) idx_u[j] = j < len ? j : -1;
     return;
   }
-  // Candidate keys, flat slot f = i * NT + tid of this unit's [S][cslots]
-  // array: register order is position order.  They are loaded before the
-  // counts arrive and masked afterwards.
-  const uint32_t* ck = a.ckey + (size_t)u * S * a.cslots;
-  const int32_t* cp = a.cpos + (size_t)u * S * a.cslots;
-  uint32_t key[KPT];
-  int32_t pos[KPT];
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    key[i] = i < a.rows ? ck[i * NT + tid] : 0u;
-    pos[i] = i < a.rows ? cp[i * NT + tid] : 0;
-  }
-  const uint32_t thr = a.thr[u];
-  // per-chunk counts (S <= 64: one wave sums them); -1 marks an overflowed list
+  // Per-chunk counts (S <= 16): one wave forms their exclusive prefix; -1
+  // marks an overflowed list.
   if (w == 0) {
     const int c = lane < S ? a.cnt[(size_t)u * S + lane] : 0;
-    if (lane < S) cnt_s[lane] = c;
-    uint32_t tot = (uint32_t)max(c, 0);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) tot += (uint32_t)__shfl_xor((int)tot, off, kWave);
     const bool over = ballot(c < 0) != 0;
-    if (lane == 0) red[0] = over ? 0u : tot;
+    const uint32_t v = (uint32_t)max(c, 0);
+    const uint32_t incl = wave_inclusive_scan(v);
+    if (lane < kFilterMaxSplits) start_s[lane] = lane < S ? incl - v : 0xFFFFFFFFu;
+    if (lane == kWave - 1) red[0] = over ? 0u : incl;
   }
   __syncthreads();
   const uint32_t total = red[0];
@@ -1362,14 +1440,33 @@ __global__ __launch_bounds__(kMergeThreads) void filter_merge_kernel(const Filte
     select_unit_streaming<D, R>(a, sh, bm, u, b, h, len, idx_u);
     return;
   }
-  uint32_t kmax = 0u;
+  // The unit's candidates, numbered g = 0 .. total-1 in chunk order (hence in
+  // position order); key g sits in register i = g / NT of thread g % NT.
+  // Only the kept slots are read: chunk c holds g in [start_c, start_c+1).
+  const uint32_t* ck = a.ckey + (size_t)u * S * a.cslots;
+  const int32_t* cp = a.cpos + (size_t)u * S * a.cslots;
+  const int nk = (int)((total + NT - 1) / NT);        // rows in use, <= KPT
+  uint32_t key[KPT];
+  int32_t pos[KPT];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    const int f = i * NT + tid;
-    const bool valid = i < a.rows && (f & (a.cslots - 1)) < cnt_s[min(f >> a.cslots_log2, S - 1)];
-    key[i] = valid ? key[i] : 0u;
-    kmax = max(kmax, key[i]);
+    key[i] = 0u;
+    pos[i] = 0;
+    const uint32_t g = (uint32_t)(i * NT + tid);
+    if (i < nk && g < total) {
+      uint32_t c = 0;                                 // last chunk with start_c <= g
+#pragma unroll
+      for (int step = kFilterMaxSplits / 2; step >= 1; step >>= 1)
+        if (start_s[c + step] <= g) c += step;
+      const size_t f = (size_t)c * a.cslots + (g - start_s[c]);
+      key[i] = ck[f];
+      pos[i] = cp[f];
+    }
   }
+  const uint32_t thr = a.thr[u];
+  uint32_t kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) kmax = max(kmax, key[i]);
   // Every candidate is >= thr >= 1.  Spread the candidates' range over the
   // first radix digit: k' = ((key - thr) << lsh) + 1 (order-preserving, 0 is
   // left for "no key", bit 31 of k' - 1 stays clear so k' cannot overflow).
@@ -1387,12 +1484,14 @@ __global__ __launch_bounds__(kMergeThreads) void filter_merge_kernel(const Filte
   for (int i = 0; i < KPT; ++i) key[i] = key[i] ? ((key[i] - thr) << lsh) + 1u : 0u;
   const uint32_t dummy = (uint32_t)(kBins + lane);
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) atomicAdd(&sh.hist[key[i] ? (key[i] >> kTopShift) : dummy], 1u);
+  for (int i = 0; i < KPT; ++i)
+    if (i < nk) atomicAdd(&sh.hist[key[i] ? (key[i] >> kTopShift) : dummy], 1u);
   __syncthreads();
   uint32_t t, need, eq;
   finish_threshold<NT>(sh, (uint32_t)M, t, need, eq, [&](auto&& f) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) f(key[i], key[i] != 0u);
+    for (int i = 0; i < KPT; ++i)
+      if (i < nk) f(key[i], key[i] != 0u);
   });
   // ordered emission over the normalised keys; positions are read for the
   // selected keys only
@@ -1401,7 +1500,7 @@ __global__ __launch_bounds__(kMergeThreads) void filter_merge_kernel(const Filte
   emit_in_order(key, t, need, eq, sh, [&](int i, bool sel, uint32_t slot) {
     if (staged) out[sel ? slot : (uint32_t)(kListCap - kWave + lane)] = pos[i];
     else if (sel) idx_u[slot] = pos[i];
-  });
+  }, nk);
   if (staged)
     for (int j = tid; j < M; j += NT) idx_u[j] = out[j];
 }

@@ -2,10 +2,10 @@
 """Decode-step benchmark of the indexer-selected sparse attention library.
 
 One step = the whole hot path for one layer over the whole batch, i.e. one
-sparse_attn_decode_step called as its four launches: append the new token
-(K/V rows + FP8 projected key) with the sampled selection bound, score every
-position and keep the candidates, exact top-M per KV head, and gather-free
-sparse attention over the selected rows.  Inputs are synthetic
+sparse_attn_decode_step called as its three launches: append the new token
+(K/V rows + FP8 projected key) with the sampled selection bound; score every
+position and keep the candidates; exact top-M per KV head followed, in the
+same workgroups, by gather-free sparse attention over the selected rows.  Inputs are synthetic
 (``workloads``) and resident in HBM before the timed region starts.
 
 Prints ONE JSON line:
@@ -43,10 +43,11 @@ def algorithmic_bytes(wl):
     # read the new K/V rows, write K/V rows + the FP8 projected key
     append = units * (2 * wl.d * 2) + units * (2 * wl.d * 2 + wl.r) + wl.B * 4 + P
     candidates = units * wl.N * wl.r + q + P       # the FP8 key stream, the queries, P
-    merge = idx                                     # the selected positions
-    decode = units * wl.M * wl.d * 2 * 2 + idx + q + wl.B * wl.Hq * wl.d * 2
+    # write the selected positions; read the selected K/V rows and the
+    # queries, write the outputs
+    select_attend = idx + units * wl.M * wl.d * 2 * 2 + q + wl.B * wl.Hq * wl.d * 2
     # the sampled bound reads a few rows again: no bytes of its own are required
-    return {"append_bound": append, "candidates": candidates, "merge": merge, "attend": decode}
+    return {"append_bound": append, "candidates": candidates, "select_attend": select_attend}
 
 
 def _source_hash(names):
@@ -269,8 +270,8 @@ def main(argv=None):
     scale = default_scale(wl.d)
     torch.cuda.synchronize()
 
-    # the four launches of sparse_attn_decode_step, one call each
-    names = ("append_bound", "candidates", "merge", "attend")
+    # the three launches of sparse_attn_decode_step, one call each
+    names = ("append_bound", "candidates", "select_attend")
     ev = {k: [] for k in names}
     lse = None
 
@@ -279,7 +280,7 @@ def main(argv=None):
             sh, st, inp.pos, inp.k_new, inp.v_new, inp.q, inp.P, inp.k_cache, inp.v_cache, kp,
             inp.seq_lens, wl.N, wl.M, scale, idx, out, lse, ws)
     calls = tuple(stage(st) for st in (sa.SA_STEP_APPEND_BOUND, sa.SA_STEP_CANDIDATES,
-                                       sa.SA_STEP_MERGE, sa.SA_STEP_ATTEND))
+                                       sa.SA_STEP_SELECT_ATTEND))
 
     timer = HipTimer()
     stream = torch.cuda.current_stream(dev).cuda_stream    # the stream every call launches on

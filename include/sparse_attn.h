@@ -239,14 +239,20 @@ int sparse_attn_decode_step(const sa_shape* shape, const int32_t* pos, int32_t T
 
 /* sparse_attn_decode_step_stage -- the launches of sparse_attn_decode_step,
  * one call each (for timing or scheduling): SA_STEP_APPEND_BOUND, then
- * SA_STEP_CANDIDATES, SA_STEP_MERGE (writes idx), SA_STEP_ATTEND (writes
- * out, lse).  Run them in order on one stream with identical arguments.
+ * SA_STEP_CANDIDATES, then either SA_STEP_SELECT_ATTEND (writes idx, out,
+ * lse; what sparse_attn_decode_step itself runs) or SA_STEP_MERGE (writes
+ * idx) followed by SA_STEP_ATTEND (writes out, lse).  Both endings give the
+ * same bits.  SA_STEP_SELECT_ATTEND is one launch (plus the split merge when
+ * the attention is split) when the filter path serves the shape and
+ * G * head_dim <= 1024, else the two stages' launches.  Run the stages in
+ * order on one stream with identical arguments.
  * Returns SA_ERR_INVALID for an unknown stage. */
 enum sa_step_stage {
   SA_STEP_APPEND_BOUND = 1,
   SA_STEP_CANDIDATES = 2,
   SA_STEP_MERGE = 3,
-  SA_STEP_ATTEND = 4
+  SA_STEP_ATTEND = 4,
+  SA_STEP_SELECT_ATTEND = 5
 };
 
 int sparse_attn_decode_step_stage(const sa_shape* shape, int32_t stage, const int32_t* pos,

@@ -224,6 +224,7 @@ def sparse_attn_index_topm_stage(shape, stage, q, P, kp_cache, seq_lens, n_max, 
 
 
 SA_STEP_APPEND_BOUND, SA_STEP_CANDIDATES, SA_STEP_MERGE, SA_STEP_ATTEND = 1, 2, 3, 4
+SA_STEP_SELECT_ATTEND = 5
 
 
 def _step_args(shape, pos, k_new, v_new, q, P, k_cache, v_cache, kp_cache, seq_lens, n_max, M,

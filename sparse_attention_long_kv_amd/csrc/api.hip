@@ -207,11 +207,17 @@ int decode_step_stages(const sa_shape* shape, int stages, const int32_t* pos, in
     }
     if (e != hipSuccess) return finish(e, c.stream);
   }
+  // merge and attention in one launch where the filter path allows it
+  const bool fuse = (stages & kStepMerge) && (stages & kStepAttend) && fused_attend_ok(*shape, fplan);
+  if (fuse) stages &= ~kStepAttend;
+  const AttendFused att{&dplan, k_cache, v_cache, softmax_scale, out, lse,
+                        (char*)workspace + fused_partials_offset(fplan)};
   for (int sel : {kStepCandidates, kStepMerge}) {
     if (!(stages & sel)) continue;
     const int mask = sel == kStepCandidates ? kSelectChunks : kSelectMerge;
     e = fplan.enabled ? run_filter_select(c, fplan, mask, q, P, kp_cache, seq_lens, n_max, M,
-                                          idx, workspace)
+                                          idx, workspace, nullptr,
+                                          fuse && sel == kStepMerge ? &att : nullptr)
                       : run_select(c, tplan, mask, true, q, P, kp_cache, nullptr, seq_lens, n_max,
                                    M, idx, workspace);
     if (e != hipSuccess) return finish(e, c.stream);
@@ -249,6 +255,7 @@ extern "C" int sparse_attn_decode_step_stage(const sa_shape* shape, int32_t stag
     case SA_STEP_CANDIDATES: mask = kStepCandidates; break;
     case SA_STEP_MERGE: mask = kStepMerge; break;
     case SA_STEP_ATTEND: mask = kStepAttend; break;
+    case SA_STEP_SELECT_ATTEND: mask = kStepMerge | kStepAttend; break;
     default: return SA_ERR_INVALID;
   }
   return decode_step_stages(shape, mask, pos, T, k_new, v_new, q, P, k_cache, v_cache, kp_cache,

@@ -133,6 +133,7 @@ size_t workspace_bytes(const sa_shape& s, int n_max, int M) {
     FilterPlan fp;
     if (plan_filter(s, n_max, M, &fp) != SA_OK) return 0;
     if (fp.enabled) need = std::max(need, fp.end);
+    if (fused_attend_ok(s, fp)) need = std::max(need, fused_partials_offset(fp) + dp.end);
   }
   return need;
 }

@@ -54,6 +54,10 @@ constexpr int kSampleBlocks = 128;       // sampled position blocks per unit
 constexpr int kSampleBlock = 8;          // positions per sampled block (256 B of FP8 rows)
 constexpr int kSampleSafety = 3;         // the bound aims at ~3 M keys per unit
 
+// The filter path's merge workgroup can go on to attend over its selection
+// when the 16 waves' G x d output tiles fit the merge's 64 KB bitmap.
+constexpr int kFusedAttendMaxGD = (kFilterMaxN / 8) / (16 * 4);   // G d <= 1024
+
 struct FilterPlan {
   bool enabled;
   int units;
@@ -83,6 +87,12 @@ int plan_topm(const sa_shape& s, int n_max, int M, TopmPlan* out);
 int plan_decode(const sa_shape& s, int M, DecodePlan* out);
 // Fills `out`; out->enabled is false when the shape needs the chunk-exact path.
 int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* out);
+// Where the fused merge + attention keeps its split states: past the filter
+// path's workspace.
+inline size_t fused_partials_offset(const FilterPlan& fp) { return align_up(fp.end, kAlign); }
+inline bool fused_attend_ok(const sa_shape& s, const FilterPlan& fp) {
+  return fp.enabled && (s.num_q_heads / s.num_kv_heads) * s.head_dim <= kFusedAttendMaxGD;
+}
 size_t workspace_bytes(const sa_shape& s, int n_max, int M);
 
 }  // namespace sa

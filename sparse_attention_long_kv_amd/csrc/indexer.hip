@@ -24,6 +24,7 @@
 // each unit's candidates with the same machinery.  The unfused path ("topm")
 // does the same from scores stored in HBM.
 #include "append_common.hpp"
+#include "attend_common.hpp"
 #include "kernels.h"
 
 namespace sa {
@@ -1310,7 +1311,8 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
 }
 
 // Mark the selected positions of a unit in `bm` (bit p = position p) and
-// write them to idx in ascending order.  visit(f) calls f(key, pos, valid)
+// write them to idx in ascending order (idx_u may be null when M <= the list
+// capacity: the -1-padded selection is then left in sh.list).  visit(f) calls f(key, pos, valid)
 // for every key of the unit that may be selected (every key >= t at least).
 // Selection: every key > t and, of the keys == t, the `need` lowest positions
 // (found as the top `need` of the keys ~pos).  Fills idx[0, M) completely.
@@ -1368,10 +1370,15 @@ __device__ void emit_bitmap(SelectShared<NT>& sh, uint32_t* bm, int len, uint32_
     }
   }
   __syncthreads();
-  if (staged)
-    for (int j = tid; j < M; j += NT) idx_u[j] = j < (int)total ? out[j] : -1;
-  else
+  if (staged) {
+    for (int j = tid; j < M; j += NT) {
+      const int32_t v = j < (int)total ? out[j] : -1;
+      if (j >= (int)total) out[j] = -1;
+      if (idx_u) idx_u[j] = v;
+    }
+  } else {
     for (int j = (int)total + tid; j < M; j += NT) idx_u[j] = -1;
+  }
 }
 
 // Exact selection of one unit by streaming its rows again (the filter's
@@ -1406,21 +1413,38 @@ __device__ __forceinline__ void select_unit_streaming(const FilterArgs& a, Selec
   emit_bitmap<NT>(sh, bm, len, t, need, eq, a.M, idx_u, visit3);
 }
 
+// LDS of the merge workgroup.
+struct MergeShared {
+  SelectShared<kMergeThreads> sh;
+  uint32_t bm[kBitmapWords];        // used by the streaming fallback only
+  uint32_t start_s[kFilterMaxSplits];
+  uint32_t red[kMergeThreads / kWave];
+};
+
+// The merge of unit u by the whole workgroup (it synchronises).  Leaves the
+// unit's M selected positions, ascending and -1 padded, in ms.sh.list (as
+// int32) and, when write_idx, also in idx.
 template <int D, int R>
-__global__ __launch_bounds__(kMergeThreads) void filter_merge_kernel(const FilterArgs a) {
+__device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShared& ms, int u,
+                                                  bool write_idx) {
   constexpr int NT = kMergeThreads;
   constexpr int KPT = kFilterMergeKeys;
-  __shared__ SelectShared<NT> sh;
-  __shared__ uint32_t bm[kBitmapWords];           // used by the streaming fallback only
-  __shared__ uint32_t start_s[kFilterMaxSplits];
-  __shared__ uint32_t red[NT / kWave];
-  const int u = blockIdx.x, b = u / a.Hkv, h = u % a.Hkv;
+  static_assert(kFilterMaxM <= kListCap - kWave, "the selection is staged in LDS");
+  SelectShared<NT>& sh = ms.sh;
+  uint32_t* start_s = ms.start_s;
+  uint32_t* red = ms.red;
+  const int b = u / a.Hkv, h = u % a.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int len = unit_len(a.seq_lens, b, a.n_max);
   const int M = a.M, S = a.S;
-  int32_t* idx_u = a.idx + (size_t)u * M;
+  int32_t* idx_u = write_idx ? a.idx + (size_t)u * M : nullptr;
+  int32_t* out = reinterpret_cast<int32_t*>(sh.list);
   if (len <= M) {                                     // every valid position, in order
-    for (int j = tid; j < M; j += NT) idx_u[j] = j < len ? j : -1;
+    for (int j = tid; j < M; j += NT) {
+      out[j] = j < len ? j : -1;
+      if (idx_u) idx_u[j] = out[j];
+    }
+    __syncthreads();
     return;
   }
   // Per-chunk counts (S <= 16): one wave forms their exclusive prefix; -1
@@ -1437,7 +1461,8 @@ __global__ __launch_bounds__(kMergeThreads) void filter_merge_kernel(const Filte
   const uint32_t total = red[0];
   __syncthreads();                                    // red is reused below
   if (total < (uint32_t)M) {                          // block-uniform (0 after an overflow)
-    select_unit_streaming<D, R>(a, sh, bm, u, b, h, len, idx_u);
+    select_unit_streaming<D, R>(a, sh, ms.bm, u, b, h, len, idx_u);
+    __syncthreads();
     return;
   }
   // The unit's candidates, numbered g = 0 .. total-1 in chunk order (hence in
@@ -1493,21 +1518,46 @@ __global__ __launch_bounds__(kMergeThreads) void filter_merge_kernel(const Filte
     for (int i = 0; i < KPT; ++i)
       if (i < nk) f(key[i], key[i] != 0u);
   });
-  // ordered emission over the normalised keys; positions are read for the
-  // selected keys only
-  const bool staged = M <= kListCap - kWave;
-  int32_t* out = reinterpret_cast<int32_t*>(sh.list);
+  // ordered emission over the normalised keys (positions were loaded with
+  // the keys); unselected keys go to a scratch slot past the list
   emit_in_order(key, t, need, eq, sh, [&](int i, bool sel, uint32_t slot) {
-    if (staged) out[sel ? slot : (uint32_t)(kListCap - kWave + lane)] = pos[i];
-    else if (sel) idx_u[slot] = pos[i];
+    out[sel ? slot : (uint32_t)(kListCap - kWave + lane)] = pos[i];
   }, nk);
-  if (staged)
+  if (idx_u)
     for (int j = tid; j < M; j += NT) idx_u[j] = out[j];
 }
 
 template <int D, int R>
-static void launch_filter_dr(const FilterArgs& a, const AppendArgs* ap, int stages, int units,
-                             hipStream_t st) {
+__global__ __launch_bounds__(kMergeThreads) void filter_merge_kernel(const FilterArgs a) {
+  __shared__ MergeShared ms;
+  filter_merge_unit<D, R>(a, ms, blockIdx.x, true);
+}
+
+// The merge followed, in the same workgroup, by the attention of split
+// `split` of the unit over the selection it just left in LDS (no reload of
+// idx, no second launch; every split's workgroup merges, split 0 writes idx).
+// The waves' output tiles reuse the fallback's bitmap: 16 G d floats fit its
+// 64 KB when G d <= 1024.
+template <int D, int R>
+__global__ __launch_bounds__(kMergeThreads) void select_attend_kernel(const FilterArgs a,
+                                                                      const DecodeArgs d) {
+  static_assert(kAttendThreads == kMergeThreads, "one workgroup shape for both");
+  __shared__ MergeShared ms;
+  __shared__ float sm[kAttendWaves][kMaxHeads], sl[kAttendWaves][kMaxHeads];
+  const int u = blockIdx.x / d.S, split = blockIdx.x % d.S;
+  filter_merge_unit<D, R>(a, ms, u, split == 0);
+  AttendWave<D, kAttendWaves> aw;
+  aw.init(d, u);
+  const int r0 = split * d.rps;
+  const int r1 = min(d.M, r0 + d.rps);
+  aw.rows(d, reinterpret_cast<const int32_t*>(ms.sh.list) + r0, r1 - r0);
+  aw.finish(d, u, split, sm, sl, reinterpret_cast<float*>(ms.bm));
+}
+
+
+template <int D, int R>
+static void launch_filter_dr(const FilterArgs& a, const AppendArgs* ap, const DecodeArgs* da,
+                             int stages, int units, hipStream_t st) {
   if ((stages & kSelectBound) && ap)
     hipLaunchKernelGGL((append_bound_kernel<D, R>), dim3(units), dim3(kSampleThreads), 0, st, a,
                        *ap);
@@ -1516,14 +1566,17 @@ static void launch_filter_dr(const FilterArgs& a, const AppendArgs* ap, int stag
   if (stages & kSelectChunks)
     hipLaunchKernelGGL((filter_kernel<D, R>), dim3((unsigned)(units * a.S)), dim3(kChunkThreads),
                        0, st, a);
-  if (stages & kSelectMerge)
+  if ((stages & kSelectMerge) && da)
+    hipLaunchKernelGGL((select_attend_kernel<D, R>), dim3((unsigned)(units * da->S)),
+                       dim3(kMergeThreads), 0, st, a, *da);
+  else if (stages & kSelectMerge)
     hipLaunchKernelGGL((filter_merge_kernel<D, R>), dim3(units), dim3(kMergeThreads), 0, st, a);
 }
 
 hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int stages,
                              const void* q, const float* P, const uint8_t* kp,
                              const int32_t* seq_lens, int n_max, int M, int32_t* idx,
-                             void* workspace, const AppendRows* rows) {
+                             void* workspace, const AppendRows* rows, const AttendFused* att) {
   FilterArgs a;
   a.q = (const uint16_t*)q;
   a.P = P;
@@ -1559,11 +1612,39 @@ hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int 
     ap.v_cache = (uint16_t*)rows->v_cache;
   }
   const AppendArgs* app = rows ? &ap : nullptr;
-  if (c.D == 128 && c.R == 32) launch_filter_dr<128, 32>(a, app, stages, plan.units, c.stream);
-  else if (c.D == 128 && c.R == 16) launch_filter_dr<128, 16>(a, app, stages, plan.units, c.stream);
-  else if (c.D == 64 && c.R == 32) launch_filter_dr<64, 32>(a, app, stages, plan.units, c.stream);
-  else launch_filter_dr<64, 16>(a, app, stages, plan.units, c.stream);
-  return hipGetLastError();
+  DecodeArgs da;
+  if (att) {
+    const DecodePlan& dp = *att->plan;
+    if (c.G < 1 || c.G > kMaxHeads || (long)c.G * c.D > kBitmapWords / kAttendWaves ||
+        (long)plan.units * dp.splits > INT32_MAX)
+      return hipErrorInvalidConfiguration;
+    da.q = (const uint16_t*)q;
+    da.k = (const uint16_t*)att->k_cache;
+    da.v = (const uint16_t*)att->v_cache;
+    da.idx = idx;
+    da.M = M;
+    da.Ncap = c.Ncap;
+    da.Hq = c.Hq;
+    da.Hkv = c.Hkv;
+    da.G = c.G;
+    da.S = dp.splits;
+    da.rps = dp.rows_per_split;
+    da.qscale = att->scale * 1.4426950408889634f;
+    da.out = (uint16_t*)att->out;
+    da.lse = att->lse;
+    char* pw = (char*)att->partials;
+    da.pm = (float*)(pw + dp.off_m);
+    da.pl = (float*)(pw + dp.off_l);
+    da.po = (float*)(pw + dp.off_o);
+  }
+  const DecodeArgs* dap = att ? &da : nullptr;
+  if (c.D == 128 && c.R == 32) launch_filter_dr<128, 32>(a, app, dap, stages, plan.units, c.stream);
+  else if (c.D == 128 && c.R == 16) launch_filter_dr<128, 16>(a, app, dap, stages, plan.units, c.stream);
+  else if (c.D == 64 && c.R == 32) launch_filter_dr<64, 32>(a, app, dap, stages, plan.units, c.stream);
+  else launch_filter_dr<64, 16>(a, app, dap, stages, plan.units, c.stream);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && att && (stages & kSelectMerge)) e = run_combine(c, da);
+  return e;
 }
 
 template <int D, int R, bool FUSED>

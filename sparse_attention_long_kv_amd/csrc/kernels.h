@@ -39,16 +39,35 @@ struct AppendRows {
   void* v_cache;
 };
 
+// Attention run by the merge launch of the filter path, with run_decode's
+// plan and arguments; the split states (plan->splits > 1) go to `partials`,
+// which must not overlap the selection's workspace.
+struct AttendFused {
+  const DecodePlan* plan;
+  const void* k_cache;
+  const void* v_cache;
+  float scale;
+  void* out;
+  float* lse;
+  void* partials;
+};
+
 // Filter path of the fused selection (plan.enabled): stages kSelectBound
 // (sampled bound; with `rows`, the same launch first appends those rows),
-// kSelectChunks (filtering chunks), kSelectMerge.
+// kSelectChunks (filtering chunks), kSelectMerge (with `att`, each merge
+// workgroup then attends over the selection, followed by the split merge
+// when there are several splits; needs G d <= 1024).
 hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int stages,
                              const void* q, const float* P, const uint8_t* kp,
                              const int32_t* seq_lens, int n_max, int M, int32_t* idx,
-                             void* workspace, const AppendRows* rows = nullptr);
+                             void* workspace, const AppendRows* rows = nullptr,
+                             const AttendFused* att = nullptr);
 hipError_t run_decode(const LaunchCommon& c, const DecodePlan& plan, const void* q,
                       const void* k_cache, const void* v_cache, const int32_t* idx, int M,
                       float scale, void* out, float* lse, void* workspace);
+struct DecodeArgs;
+// Merge of the split states when DecodeArgs::S > 1 (no launch otherwise).
+hipError_t run_combine(const LaunchCommon& c, const DecodeArgs& a);
 hipError_t run_linear_gate(const LaunchCommon& c, const void* q, const void* k_new,
                            const void* v_new, float* S, float* z, const float* w_gate,
                            const void* o_sparse, void* out, int update_state);

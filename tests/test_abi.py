@@ -130,8 +130,9 @@ def test_bad_arguments_are_rejected(lib):
     f1 = ctypes.c_float(1.0)
     assert _st(lib, step, by, 0, P, 1, P, P, P, P, P, P, P, None, wl.N, wl.M, f1, P, P, None, P,
                need, None) == -1
-    assert _st(lib, step, by, 5, P, 1, P, P, P, P, P, P, P, None, wl.N, wl.M, f1, P, P, None, P,
-               need, None) == -1
+    for bad in (6, -1):                                       # unknown stages
+        assert _st(lib, step, by, bad, P, 1, P, P, P, P, P, P, P, None, wl.N, wl.M, f1, P, P,
+                   None, P, need, None) == -1
     assert _st(lib, step, by, 1, P, 1, P, P, P, P, P, P, P, None, wl.N, wl.M, f1, P, P, None, P,
                need - 1, None) == -3
     assert _st(lib, "sparse_attn_decode_step", by, P, -1, P, P, P, P, P, P, P, None, wl.N, wl.M,

@@ -453,15 +453,14 @@ def test_cross_layer_reuse_equals_decode_with_source_indices():
 
 def _bench_sequence(inp, sh, M, ws):
     """The calls, in the order and launch configuration bench.py times: the
-    four stages of sparse_attn_decode_step."""
+    three stages of sparse_attn_decode_step."""
     wl = inp.wl
     kp = torch.empty(wl.B, wl.Hkv, wl.N, wl.r, dtype=torch.uint8, device="cuda")
     sa.sparse_attn_project_keys(sh, inp.k_cache, inp.P, 0, wl.N, kp)
     idx = torch.empty(wl.B, wl.Hkv, M, dtype=torch.int32, device="cuda")
     out = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(wl.B, wl.Hq, dtype=torch.float32, device="cuda")
-    for stage in (sa.SA_STEP_APPEND_BOUND, sa.SA_STEP_CANDIDATES, sa.SA_STEP_MERGE,
-                  sa.SA_STEP_ATTEND):
+    for stage in (sa.SA_STEP_APPEND_BOUND, sa.SA_STEP_CANDIDATES, sa.SA_STEP_SELECT_ATTEND):
         sa.sparse_attn_decode_step_stage(sh, stage, inp.pos, inp.k_new, inp.v_new, inp.q,
                                          inp.P, inp.k_cache, inp.v_cache, kp, inp.seq_lens,
                                          wl.N, M, default_scale(wl.d), idx, out, lse, ws)
@@ -585,6 +584,52 @@ def test_topm_sample_overestimate_falls_back_exactly():
 
 
 # ------------------------------------------------------------------ decode step
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,r,N,M", [
+    (2, 8, 2, 128, 32, 8192, 512),     # G d = 512: one launch, then the split merge
+    (1, 16, 1, 128, 16, 4096, 256),    # G d = 2048: merge and attention launched apart
+    (3, 12, 1, 64, 16, 6000, 700),     # G d = 768, ragged tiles
+    (1, 4, 1, 128, 32, 20000, 6144),   # the largest M the merge stages in LDS
+])
+def test_select_attend_stage_equals_merge_then_attend(B, Hq, Hkv, d, r, N, M):
+    """SA_STEP_SELECT_ATTEND (the merge workgroups go on to attend over the
+    selection they hold) writes the same idx, out and lse, bit for bit, as
+    SA_STEP_MERGE followed by SA_STEP_ATTEND; the attention of two units is
+    checked against the oracle over the selected rows."""
+    _say("case: select+attend", B, Hq, Hkv, d, r, N, M)
+    sh = _shape_of(B, Hq, Hkv, d, r, N)
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, N, seed=41)
+    g = torch.Generator().manual_seed(42)
+    k_new = torch.randn(B, Hkv, 1, d, generator=g).to(torch.bfloat16)
+    v_new = torch.randn(B, Hkv, 1, d, generator=g).to(torch.bfloat16)
+    pos = torch.full((B,), N - 1, dtype=torch.int32)
+    res = []
+    for ending in ((sa.SA_STEP_MERGE, sa.SA_STEP_ATTEND), (sa.SA_STEP_SELECT_ATTEND,)):
+        Kd, Vd = _dev(K), _dev(V)
+        kp = torch.empty(B, Hkv, N, r, dtype=torch.uint8, device="cuda")
+        sa.sparse_attn_project_keys(sh, Kd, _dev(P), 0, N, kp)
+        ws = sa.alloc_workspace(sh, N, M)
+        idx = torch.full((B, Hkv, M), -9, dtype=torch.int32, device="cuda")
+        out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+        for stage in (sa.SA_STEP_APPEND_BOUND, sa.SA_STEP_CANDIDATES) + ending:
+            sa.sparse_attn_decode_step_stage(sh, stage, _dev(pos), _dev(k_new), _dev(v_new),
+                                             _dev(q), _dev(P), Kd, Vd, kp, None, N, M,
+                                             default_scale(d), idx, out, lse, ws)
+        torch.cuda.synchronize()
+        res.append((idx, out, lse, Kd, Vd))
+    for x, y in zip(res[0][:3], res[1][:3]):
+        assert torch.equal(x, y)
+    idx, out, _, Kd, Vd = res[1]
+    gi = idx.cpu().numpy()
+    assert np.all(np.diff(gi, axis=-1) > 0) and gi.min() >= 0 and gi.max() < N
+    G = Hq // Hkv
+    q64, K64, V64 = f64(q), f64(Kd), f64(Vd)
+    for b, h in {(0, 0), (B - 1, Hkv - 1)}:
+        o, _ = oracle.sparse_attention(q64[b, h * G:(h + 1) * G], K64[b, h], V64[b, h], gi[b, h],
+                                       default_scale(d))
+        check_attention(f64(out)[b, h * G:(h + 1) * G], o, "unit (%d, %d)" % (b, h))
+
 
 @pytest.mark.parametrize("name,N,T,lens", [("tiny", None, 1, None),
                                            ("gqa7_16k", 8192, 1, [8192, 5000, 1, 0, 8192, 300,

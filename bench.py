@@ -33,6 +33,78 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 DOMINANT_KERNEL = "filter_kernel"
 
 
+def measure_baselines(sa, torch, inp, wl, sh, kp, idx, ws, timer, stream, reps):
+    """The JSSA article's two comparisons, on this GPU, outside the timed
+    region: full attention over every cached row (its opening paragraph
+    compares decoding throughput against it) and gather-then-attend ("Why
+    token selection is not enough": the copy took more than half of the
+    sparse-attention time at large batch) against the gather-free attention.
+    Every timed call is preceded by an untimed candidates stage (a 1 GB
+    stream) so that no call finds its rows left in the caches by the last."""
+    from workloads import default_scale
+    scale = default_scale(wl.d)
+    dev = inp.q.device
+    out = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.bfloat16, device=dev)
+    dws = torch.empty(sa.sparse_attn_dense_workspace_size(sh, wl.N), dtype=torch.uint8,
+                      device=dev)
+    shg = sa.make_shape(wl.B, wl.Hq, wl.Hkv, wl.d, wl.r, wl.M)
+    gws = torch.empty(sa.sparse_attn_dense_workspace_size(shg, wl.M), dtype=torch.uint8,
+                      device=dev)
+    Kg = torch.empty(wl.B, wl.Hkv, wl.M, wl.d, dtype=torch.bfloat16, device=dev)
+    Vg = torch.empty_like(Kg)
+    glens = inp.seq_lens.clamp(max=wl.M).to(torch.int32)
+    flush = lambda: sa.sparse_attn_decode_step_stage(
+        sh, sa.SA_STEP_CANDIDATES, inp.pos, inp.k_new, inp.v_new, inp.q, inp.P, inp.k_cache,
+        inp.v_cache, kp, inp.seq_lens, wl.N, wl.M, scale, idx, out, None, ws)
+    calls = {
+        "dense": lambda: sa.sparse_attn_dense_decode(sh, inp.q, inp.k_cache, inp.v_cache,
+                                                     inp.seq_lens, wl.N, scale, out, None, dws),
+        "gather_free": lambda: sa.sparse_attn_decode(sh, inp.q, inp.k_cache, inp.v_cache, idx,
+                                                     wl.M, scale, out, None, ws),
+        "gather": lambda: sa.sparse_attn_gather_kv(sh, idx, wl.M, inp.k_cache, inp.v_cache,
+                                                   Kg, Vg),
+        "contiguous": lambda: sa.sparse_attn_dense_decode(shg, inp.q, Kg, Vg, glens, wl.M,
+                                                          scale, out, None, gws),
+    }
+    us = {}
+    for name, call in calls.items():
+        if name == "contiguous":                      # its input is the gathered copy
+            calls["gather"]()
+        call()
+        pool = timer.create(2 * reps)
+        for k in range(reps):
+            flush()
+            if name == "contiguous":
+                calls["gather"]()
+                flush()
+            timer.record(pool[2 * k], stream)
+            call()
+            timer.record(pool[2 * k + 1], stream)
+        torch.cuda.synchronize()
+        us[name] = 1e3 * sum(timer.elapsed_ms(pool[2 * k], pool[2 * k + 1])
+                             for k in range(reps)) / reps
+        timer.destroy(pool)
+    units = wl.B * wl.Hkv
+    rows = units * wl.N * wl.d * 2 * 2
+    sel = units * wl.M * wl.d * 2 * 2
+    gather_then_attend = us["gather"] + us["contiguous"]
+    return {
+        "what": "full attention over all cached rows, and gather-then-attend, against this "
+                "path (JSSA article: 6.43x over full attention at 128K / 2048 on B200; "
+                "the copy took > 50% of the sparse-attention time)",
+        "reps": reps,
+        "dense_attention_us": round(us["dense"], 1),
+        "dense_attention_gbps": round(rows / (us["dense"] * 1e-6) / 1e9, 1),
+        "gather_free_attention_us": round(us["gather_free"], 2),
+        "gather_us": round(us["gather"], 2),
+        "contiguous_attention_us": round(us["contiguous"], 2),
+        "gather_share_of_gather_then_attend": round(us["gather"] / gather_then_attend, 3),
+        "gather_free_speedup_over_gather_then_attend":
+            round(gather_then_attend / us["gather_free"], 2),
+        "gather_gbps": round(2 * sel / (us["gather"] * 1e-6) / 1e9, 1),
+    }
+
+
 def algorithmic_bytes(wl):
     """Bytes the method itself must move per step, by call: every input read
     once and every output written once (workspace traffic is not counted)."""
@@ -231,6 +303,8 @@ def main(argv=None):
     ap.add_argument("--cpu-units", type=int, default=16,
                     help="units of the step timed for the oracle baseline (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--baseline-reps", type=int, default=5,
+                    help="calls timed per comparison baseline (0: skip them)")
     ap.add_argument("--calibration-mib", type=int, default=0,
                     help="before the timed region, run one torch.neg over this many MiB "
                          "(a kernel of known traffic for scaling rocprofv3 byte counters)")
@@ -376,7 +450,14 @@ def main(argv=None):
                         if bytes_k[k]},
         "roofline": roofline,
         "cpu_baseline": None,
+        "baselines": None,
     }
+    if a.baseline_reps > 0:
+        print("bench: comparison baselines", file=sys.stderr, flush=True)
+        b = measure_baselines(sa, torch, inp, wl, sh, kp, idx, ws, timer, stream,
+                              a.baseline_reps)
+        b["dense_speedup_of_step"] = round(b["dense_attention_us"] / (1e3 * ms_per_step), 2)
+        res["baselines"] = b
     if a.cpu_units > 0:
         print("bench: cpu baseline (%d units)" % a.cpu_units, file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp, wl, a.cpu_units)

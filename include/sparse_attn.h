@@ -284,6 +284,42 @@ int sparse_attn_linear_gate(const sa_shape* shape, const void* q,
                             float* z, const float* w_gate, const void* o_sparse,
                             void* out, int32_t update_state, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Comparison baselines (not on the decode path).  The JSSA article (rit.work
+ * blog) measures its decoding throughput against full attention (opening
+ * paragraph: 6.43x at 128K context and a 2048-token budget on B200) and
+ * reports, in "Why token selection is not enough", that with the usual
+ * gather-then-attend scheme the copy into a contiguous buffer took more than
+ * half of the remaining sparse-attention time at large batch.  These two
+ * calls let both comparisons be measured on this GPU.
+ *
+ * sparse_attn_dense_decode -- exact attention of every query head over ALL
+ * valid rows n < len_b of its KV head (len_b = seq_lens[b] clamped to
+ * [0, n_max], or n_max when seq_lens is NULL), read as consecutive rows of
+ * the bf16 cache.  q, k_cache, v_cache, out, lse and softmax_scale as in
+ * sparse_attn_decode (len_b = 0 gives out = 0 and lse = -inf).  Workspace:
+ * sparse_attn_dense_workspace_size(shape, n_max) bytes, 256-byte aligned.
+ * Returns SA_ERR_INVALID for bad pointers or n_max outside [1, capacity],
+ * SA_ERR_WORKSPACE when the workspace is missing or too small.
+ * ------------------------------------------------------------------------- */
+int sparse_attn_dense_decode(const sa_shape* shape, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* seq_lens, int32_t n_max,
+                             float softmax_scale, void* out, float* lse, void* workspace,
+                             size_t ws_bytes, void* stream);
+size_t sparse_attn_dense_workspace_size(const sa_shape* shape, int32_t n_max);
+
+/* sparse_attn_gather_kv -- the copy of gather-then-attend: for every unit u
+ * and j < M, k_out[u][j] = k_cache[u][idx[u][j]] and v_out likewise (d bf16
+ * values per row), zero rows where idx[u][j] is -1 (or outside the cache).
+ * idx [B][Hkv][M] int32 (as sparse_attn_topm writes it); k_out, v_out
+ * [B][Hkv][M][d] bf16, caller-owned, 16-byte aligned.  Attending over the
+ * gathered rows is sparse_attn_dense_decode on a shape of capacity M with
+ * seq_lens min(len_b, M) and n_max = M.  Returns SA_ERR_INVALID for bad
+ * pointers or M outside [1, capacity]. */
+int sparse_attn_gather_kv(const sa_shape* shape, const int32_t* idx, int32_t M,
+                          const void* k_cache, const void* v_cache, void* k_out, void* v_out,
+                          void* stream);
+
 /* Bytes of workspace that sparse_attn_topm, sparse_attn_index_topm(_stage),
  * sparse_attn_decode and sparse_attn_decode_step(_stage) need for this shape,
  * n_max and M (host only, pure).

@@ -71,11 +71,16 @@ _SIGS = {
                                       _VP, _I32, _I32, ctypes.c_float, _VP, _VP, _VP, _VP, _SZ,
                                       _VP],
     "sparse_attn_linear_gate": [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP],
+    "sparse_attn_dense_decode": [_SP, _VP, _VP, _VP, _VP, _I32, ctypes.c_float, _VP, _VP, _VP,
+                                 _SZ, _VP],
+    "sparse_attn_gather_kv": [_SP, _VP, _I32, _VP, _VP, _VP, _VP, _VP],
     "sparse_attn_workspace_size": [_SP, _I32, _I32],
+    "sparse_attn_dense_workspace_size": [_SP, _I32],
     "sparse_attn_status_string": [ctypes.c_int],
 }
 _RESTYPES = {
     "sparse_attn_workspace_size": _SZ,
+    "sparse_attn_dense_workspace_size": _SZ,
     "sparse_attn_status_string": ctypes.c_char_p,
 }
 
@@ -276,6 +281,36 @@ def sparse_attn_decode(shape, q, k_cache, v_cache, idx, M, softmax_scale, out, l
           _dev_ptr(out, torch.bfloat16, (B, Hq, d), "out"),
           _opt_ptr(lse, torch.float32, (B, Hq), "lse"),
           _dev_ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), _stream(q))
+
+
+def sparse_attn_dense_decode(shape, q, k_cache, v_cache, seq_lens, n_max, softmax_scale, out,
+                             lse, workspace):
+    """Comparison baseline: attention over every valid row (M = N)."""
+    B, Hq, Hkv, d, Nc = (shape.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim,
+                         shape.capacity)
+    _call("sparse_attn_dense_decode", _sh(shape),
+          _dev_ptr(q, torch.bfloat16, (B, Hq, d), "q"),
+          _dev_ptr(k_cache, torch.bfloat16, (B, Hkv, Nc, d), "k_cache"),
+          _dev_ptr(v_cache, torch.bfloat16, (B, Hkv, Nc, d), "v_cache"),
+          _opt_ptr(seq_lens, torch.int32, (B,), "seq_lens"), int(n_max), float(softmax_scale),
+          _dev_ptr(out, torch.bfloat16, (B, Hq, d), "out"),
+          _opt_ptr(lse, torch.float32, (B, Hq), "lse"),
+          _dev_ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), _stream(q))
+
+
+def sparse_attn_dense_workspace_size(shape, n_max):
+    return int(load().sparse_attn_dense_workspace_size(_sh(shape), int(n_max)))
+
+
+def sparse_attn_gather_kv(shape, idx, M, k_cache, v_cache, k_out, v_out):
+    """Comparison baseline: copy the selected rows into contiguous buffers."""
+    B, Hkv, d, Nc = shape.batch, shape.num_kv_heads, shape.head_dim, shape.capacity
+    _call("sparse_attn_gather_kv", _sh(shape),
+          _dev_ptr(idx, torch.int32, (B, Hkv, M), "idx"), int(M),
+          _dev_ptr(k_cache, torch.bfloat16, (B, Hkv, Nc, d), "k_cache"),
+          _dev_ptr(v_cache, torch.bfloat16, (B, Hkv, Nc, d), "v_cache"),
+          _dev_ptr(k_out, torch.bfloat16, (B, Hkv, M, d), "k_out"),
+          _dev_ptr(v_out, torch.bfloat16, (B, Hkv, M, d), "v_out"), _stream(idx))
 
 
 def sparse_attn_linear_gate(shape, q, k_new, v_new, S, z, w_gate, o_sparse, out,

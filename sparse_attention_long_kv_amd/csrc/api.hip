@@ -284,6 +284,42 @@ extern "C" int sparse_attn_decode(const sa_shape* shape, const void* q, const vo
                 c.stream);
 }
 
+extern "C" int sparse_attn_dense_decode(const sa_shape* shape, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        const int32_t* seq_lens, int32_t n_max,
+                                        float softmax_scale, void* out, float* lse,
+                                        void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  if (!ptr_ok(q, A16) || !ptr_ok(k_cache, A16) || !ptr_ok(v_cache, A16) || !ptr_ok(out, A16))
+    return SA_ERR_INVALID;
+  if ((lse && !ptr_ok(lse, A4)) || (seq_lens && !ptr_ok(seq_lens, A4))) return SA_ERR_INVALID;
+  if (n_max < 1 || n_max > shape->capacity || !std::isfinite(softmax_scale))
+    return SA_ERR_INVALID;
+  DecodePlan plan;
+  st = plan_dense(*shape, n_max, &plan);
+  if (st != SA_OK) return st;
+  if (!ptr_ok(workspace, kAlign) || ws_bytes < dense_workspace_bytes(*shape, n_max))
+    return SA_ERR_WORKSPACE;
+  const LaunchCommon c = common(*shape, stream);
+  return finish(run_dense_decode(c, plan, q, k_cache, v_cache, seq_lens, n_max, softmax_scale,
+                                 out, lse, workspace),
+                c.stream);
+}
+
+extern "C" int sparse_attn_gather_kv(const sa_shape* shape, const int32_t* idx, int32_t M,
+                                     const void* k_cache, const void* v_cache, void* k_out,
+                                     void* v_out, void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  if (!ptr_ok(idx, A4) || !ptr_ok(k_cache, A16) || !ptr_ok(v_cache, A16) ||
+      !ptr_ok(k_out, A16) || !ptr_ok(v_out, A16))
+    return SA_ERR_INVALID;
+  if (M < 1 || M > shape->capacity) return SA_ERR_INVALID;
+  const LaunchCommon c = common(*shape, stream);
+  return finish(run_gather_kv(c, idx, M, k_cache, v_cache, k_out, v_out), c.stream);
+}
+
 extern "C" int sparse_attn_linear_gate(const sa_shape* shape, const void* q, const void* k_new,
                                        const void* v_new, float* S, float* z,
                                        const float* w_gate, const void* o_sparse, void* out,

@@ -50,6 +50,8 @@ struct DecodeArgs {
   float* pm;           // [units][S][G] partial states when S > 1
   float* pl;
   float* po;           // [units][S][G][d]
+  const int32_t* lens; // dense attention: valid rows per batch row (null = n_max)
+  int n_max;
 };
 
 typedef __bf16 sa_bf16x8 __attribute__((ext_vector_type(8)));
@@ -143,13 +145,15 @@ struct AttendWave {
     voff = (uint32_t)(DL * n16) * 2;          // bytes of dims DL n16
   }
 
-  // row loads of one 16-row tile (rows at or past cnt are none)
-  __device__ __forceinline__ void issue(const DecodeArgs& a, const int32_t* sidx, int cnt, int tt,
+  // row loads of one 16-row tile: run row j is cache row row_of(j), rows at
+  // or past cnt are none
+  template <class RowOf>
+  __device__ __forceinline__ void issue(const DecodeArgs& a, RowOf row_of, int cnt, int tt,
                                         TileRaw<D>& t) const {
     const int rb = tt * 16;
-    const int nk = rb + tk < cnt ? sidx[rb + tk] : -1;
+    const int nk = rb + tk < cnt ? row_of(rb + tk) : -1;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) t.nr[v] = rb + 4 * v + q4 < cnt ? sidx[rb + 4 * v + q4] : -1;
+    for (int v = 0; v < 4; ++v) t.nr[v] = rb + 4 * v + q4 < cnt ? row_of(rb + 4 * v + q4) : -1;
     const uint32_t kb =
         (unsigned)nk < (unsigned)a.Ncap ? (uint32_t)nk * (D * 2) + koff : kOffNone;
 #pragma unroll
@@ -210,7 +214,17 @@ struct AttendWave {
     const int ntile = (cnt + 15) >> 4;
     for (int tt = w; tt < ntile; tt += W) {
       TileRaw<D> t;
-      issue(a, sidx, cnt, tt, t);
+      issue(a, [&](int j) { return sidx[j]; }, cnt, tt, t);
+      consume(a, t);
+    }
+  }
+
+  // the cnt consecutive cache rows r0, r0 + 1, ... (dense attention)
+  __device__ __forceinline__ void rows_dense(const DecodeArgs& a, int r0, int cnt) {
+    const int ntile = (cnt + 15) >> 4;
+    for (int tt = w; tt < ntile; tt += W) {
+      TileRaw<D> t;
+      issue(a, [&](int j) { return r0 + j; }, cnt, tt, t);
       consume(a, t);
     }
   }

@@ -33,6 +33,66 @@ __global__ __launch_bounds__(kAttendThreads) void decode_kernel(const DecodeArgs
   aw.finish(a, u, split, sm, sl, so);
 }
 
+// ------------------------------------------------------------------ baselines
+//
+// Comparison baselines for the JSSA article's two measurements: full
+// attention (its opening paragraph compares decoding throughput against it)
+// and the gather-then-attend scheme ("Why token selection is not enough": the
+// copy into a contiguous buffer took more than half of the sparse-attention
+// time at large batch).  Neither is on the hot path.
+
+// Exact attention over every valid row n < len of the unit (consecutive
+// cache rows), split over S workgroups like the sparse kernel.
+template <int D>
+__global__ __launch_bounds__(kAttendThreads) void dense_decode_kernel(const DecodeArgs a) {
+  constexpr int W = kAttendWaves;
+  __shared__ float sm[W][kMaxHeads], sl[W][kMaxHeads];
+  extern __shared__ float so[];       // [W][G][D]
+  const int u = blockIdx.x / a.S, split = blockIdx.x % a.S;
+  const int b = u / a.Hkv;
+  const int len = a.lens ? min(max(a.lens[b], 0), a.n_max) : a.n_max;
+  AttendWave<D, W> aw;
+  aw.init(a, u);
+  const int r0 = split * a.rps;
+  const int r1 = min(len, r0 + a.rps);
+  if (r1 > r0) aw.rows_dense(a, r0, r1 - r0);       // block-uniform
+  aw.finish(a, u, split, sm, sl, so);
+}
+
+// Copy of the selected rows into contiguous [units][M][d] buffers (zero rows
+// for idx < 0): the "gather" of gather-then-attend.
+constexpr int kGatherPasses = 8;
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void gather_rows_kernel(const int32_t* __restrict__ idx,
+                                                             int M, int Ncap,
+                                                             const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v,
+                                                             uint16_t* __restrict__ ko,
+                                                             uint16_t* __restrict__ vo,
+                                                             int blocks_per_unit) {
+  constexpr int kPieces = D / 8;                      // 16-byte pieces per row
+  constexpr int kRowsPerPass = kBlock / kPieces;
+  const int u = blockIdx.x / blocks_per_unit, blk = blockIdx.x % blocks_per_unit;
+  const int piece = threadIdx.x % kPieces;
+#pragma unroll
+  for (int pass = 0; pass < kGatherPasses; ++pass) {
+    const int j = (blk * kGatherPasses + pass) * kRowsPerPass + threadIdx.x / kPieces;
+    if (j < M) {
+      const int n = idx[(size_t)u * M + j];
+      uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = kv;
+      if ((unsigned)n < (unsigned)Ncap) {
+        const size_t src = ((size_t)u * Ncap + n) * D + piece * 8;
+        kv = *reinterpret_cast<const uint4*>(k + src);
+        vv = *reinterpret_cast<const uint4*>(v + src);
+      }
+      const size_t dst = ((size_t)u * M + j) * D + piece * 8;
+      *reinterpret_cast<uint4*>(ko + dst) = kv;
+      *reinterpret_cast<uint4*>(vo + dst) = vv;
+    }
+  }
+}
+
 // Merge the S partial states of one unit (one workgroup per unit).  A separate
 // launch orders the partial writes before these reads without device-scope
 // fences inside the attention kernel.
@@ -88,10 +148,66 @@ hipError_t run_combine(const LaunchCommon& c, const DecodeArgs& a) {
   return hipGetLastError();
 }
 
+hipError_t run_dense_decode(const LaunchCommon& c, const DecodePlan& plan, const void* q,
+                            const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                            int n_max, float scale, void* out, float* lse, void* workspace) {
+  DecodeArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k_cache;
+  a.v = (const uint16_t*)v_cache;
+  a.idx = nullptr;
+  a.M = n_max;
+  a.Ncap = c.Ncap;
+  a.Hq = c.Hq;
+  a.Hkv = c.Hkv;
+  a.G = c.G;
+  a.S = plan.splits;
+  a.rps = plan.rows_per_split;
+  a.qscale = scale * 1.4426950408889634f;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  char* ws = (char*)workspace;
+  a.pm = (float*)(ws + plan.off_m);
+  a.pl = (float*)(ws + plan.off_l);
+  a.po = (float*)(ws + plan.off_o);
+  a.lens = seq_lens;
+  a.n_max = n_max;
+  const long blocks = (long)plan.units * plan.splits;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  if (c.G < 1 || c.G > kMaxHeads) return hipErrorInvalidConfiguration;
+  if (c.D == 128) {
+    hipLaunchKernelGGL((dense_decode_kernel<128>), dim3((unsigned)blocks), dim3(kAttendThreads),
+                       (size_t)kAttendWaves * c.G * 128 * sizeof(float), c.stream, a);
+  } else {
+    hipLaunchKernelGGL((dense_decode_kernel<64>), dim3((unsigned)blocks), dim3(kAttendThreads),
+                       (size_t)kAttendWaves * c.G * 64 * sizeof(float), c.stream, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = run_combine(c, a);
+  return e;
+}
+
+hipError_t run_gather_kv(const LaunchCommon& c, const int32_t* idx, int M, const void* k_cache,
+                         const void* v_cache, void* k_out, void* v_out) {
+  const int rows_per_block = kGatherPasses * (kBlock / (c.D / 8));
+  const long bpu = (M + rows_per_block - 1) / rows_per_block;
+  const long blocks = bpu * c.units;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  if (c.D == 128)
+    hipLaunchKernelGGL((gather_rows_kernel<128>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                       c.stream, idx, M, c.Ncap, (const uint16_t*)k_cache,
+                       (const uint16_t*)v_cache, (uint16_t*)k_out, (uint16_t*)v_out, (int)bpu);
+  else
+    hipLaunchKernelGGL((gather_rows_kernel<64>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                       c.stream, idx, M, c.Ncap, (const uint16_t*)k_cache,
+                       (const uint16_t*)v_cache, (uint16_t*)k_out, (uint16_t*)v_out, (int)bpu);
+  return hipGetLastError();
+}
+
 hipError_t run_decode(const LaunchCommon& c, const DecodePlan& plan, const void* q,
                       const void* k_cache, const void* v_cache, const int32_t* idx, int M,
                       float scale, void* out, float* lse, void* workspace) {
-  DecodeArgs a;
+  DecodeArgs a{};
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k_cache;
   a.v = (const uint16_t*)v_cache;

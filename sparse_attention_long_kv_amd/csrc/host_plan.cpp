@@ -78,6 +78,40 @@ int plan_decode(const sa_shape& s, int M, DecodePlan* p) {
   return SA_OK;
 }
 
+static void plan_partials(const sa_shape& s, DecodePlan* p) {
+  const int G = s.num_q_heads / s.num_kv_heads;
+  size_t off = 0;
+  const size_t parts = (size_t)p->units * p->splits * G;
+  p->off_m = off;
+  off = align_up(off + parts * sizeof(float), kAlign);
+  p->off_l = off;
+  off = align_up(off + parts * sizeof(float), kAlign);
+  p->off_o = off;
+  off = align_up(off + parts * s.head_dim * sizeof(float), kAlign);
+  p->end = off;
+}
+
+int plan_dense(const sa_shape& s, int n_max, DecodePlan* p) {
+  const int64_t units = (int64_t)s.batch * s.num_kv_heads;
+  int64_t splits = std::max<int64_t>(1, ceil_div(kDecodeTargetBlocks, units));
+  splits = std::min<int64_t>(splits, std::max<int64_t>(1, ceil_div(n_max, kDenseSplitRows)));
+  const int64_t rps = (int64_t)align_up((size_t)ceil_div(n_max, splits), kDenseSplitRows);
+  splits = ceil_div(n_max, rps);
+  p->units = (int)units;
+  p->splits = (int)splits;
+  p->rows_per_split = (int)rps;
+  plan_partials(s, p);
+  return SA_OK;
+}
+
+size_t dense_workspace_bytes(const sa_shape& s, int n_max) {
+  if (check_shape(&s) != SA_OK) return 0;
+  if (n_max < 1 || n_max > s.capacity) return 0;
+  DecodePlan dp;
+  if (plan_dense(s, n_max, &dp) != SA_OK) return 0;
+  return std::max<size_t>(dp.end, kAlign);
+}
+
 int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* p) {
   const int64_t units = (int64_t)s.batch * s.num_kv_heads;
   *p = FilterPlan{};
@@ -144,6 +178,11 @@ extern "C" size_t sparse_attn_workspace_size(const sa_shape* shape, int32_t n_ma
                                              int32_t M) {
   if (!shape) return 0;
   return sa::workspace_bytes(*shape, n_max, M);
+}
+
+extern "C" size_t sparse_attn_dense_workspace_size(const sa_shape* shape, int32_t n_max) {
+  if (!shape) return 0;
+  return sa::dense_workspace_bytes(*shape, n_max);
 }
 
 extern "C" const char* sparse_attn_status_string(int status) {

@@ -20,7 +20,8 @@ constexpr int kMergeTile = kBlock * kMaxKeysPerThread;  // keys per merge tile
 constexpr int kMaxSplits = 1024;         // chunks per (b, KV head) unit
 constexpr int kTargetBlocks = 2048;      // enough workgroups for 256 CUs
 constexpr int kMinRowsPerSplit = 64;     // attention rows per workgroup (min)
-constexpr int kDecodeTargetBlocks = 256; // attention workgroups (12 waves) per launch: one per CU
+constexpr int kDecodeTargetBlocks = 256; // attention workgroups (16 waves) per launch: one per CU
+constexpr int kDenseSplitRows = 256;     // dense baseline: rows per split, a multiple of this
 constexpr int kSupersetSlack = 1024;     // extra candidate slots per chunk (see plan_topm)
 constexpr int kMergeThreadsHost = 1024;  // merge workgroup size
 constexpr int kMaxMergeKeysPerThread = 24;   // register-resident merge (else LDS tiles)
@@ -85,6 +86,10 @@ bool ptr_ok(const void* p, size_t align);
 
 int plan_topm(const sa_shape& s, int n_max, int M, TopmPlan* out);
 int plan_decode(const sa_shape& s, int M, DecodePlan* out);
+// Dense attention baseline over n_max rows, split like the sparse attention
+// (splits of a multiple of kDenseSplitRows rows).
+int plan_dense(const sa_shape& s, int n_max, DecodePlan* out);
+size_t dense_workspace_bytes(const sa_shape& s, int n_max);
 // Fills `out`; out->enabled is false when the shape needs the chunk-exact path.
 int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* out);
 // Where the fused merge + attention keeps its split states: past the filter

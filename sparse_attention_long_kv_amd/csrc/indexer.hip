@@ -1612,7 +1612,7 @@ hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int 
     ap.v_cache = (uint16_t*)rows->v_cache;
   }
   const AppendArgs* app = rows ? &ap : nullptr;
-  DecodeArgs da;
+  DecodeArgs da{};
   if (att) {
     const DecodePlan& dp = *att->plan;
     if (c.G < 1 || c.G > kMaxHeads || (long)c.G * c.D > kBitmapWords / kAttendWaves ||

@@ -65,6 +65,13 @@ hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int 
 hipError_t run_decode(const LaunchCommon& c, const DecodePlan& plan, const void* q,
                       const void* k_cache, const void* v_cache, const int32_t* idx, int M,
                       float scale, void* out, float* lse, void* workspace);
+// Comparison baselines: dense attention over every valid row (plan from
+// plan_dense), and the copy of the selected rows into contiguous buffers.
+hipError_t run_dense_decode(const LaunchCommon& c, const DecodePlan& plan, const void* q,
+                            const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                            int n_max, float scale, void* out, float* lse, void* workspace);
+hipError_t run_gather_kv(const LaunchCommon& c, const int32_t* idx, int M, const void* k_cache,
+                         const void* v_cache, void* k_out, void* v_out);
 struct DecodeArgs;
 // Merge of the split states when DecodeArgs::S > 1 (no launch otherwise).
 hipError_t run_combine(const LaunchCommon& c, const DecodeArgs& a);

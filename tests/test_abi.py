@@ -130,6 +130,21 @@ def test_bad_arguments_are_rejected(lib):
     f1 = ctypes.c_float(1.0)
     assert _st(lib, step, by, 0, P, 1, P, P, P, P, P, P, P, None, wl.N, wl.M, f1, P, P, None, P,
                need, None) == -1
+    # baselines
+    dneed = sa.sparse_attn_dense_workspace_size(sh, wl.N)
+    assert dneed > 0 and sa.sparse_attn_dense_workspace_size(sh, wl.N + 1) == 0
+    dense = "sparse_attn_dense_decode"
+    assert _st(lib, dense, by, P, P, P, None, 0, f1, P, None, P, dneed, None) == -1
+    assert _st(lib, dense, by, P, P, odd, None, wl.N, f1, P, None, P, dneed, None) == -1
+    assert _st(lib, dense, by, P, P, P, None, wl.N, ctypes.c_float(float("nan")), P, None, P,
+               dneed, None) == -1
+    assert _st(lib, dense, by, P, P, P, None, wl.N, f1, P, None, P, dneed - 1, None) == -3
+    assert _st(lib, dense, by, P, P, P, None, wl.N, f1, P, None, None, dneed, None) == -3
+    gather = "sparse_attn_gather_kv"
+    assert _st(lib, gather, by, P, 0, P, P, P, P, None) == -1
+    assert _st(lib, gather, by, P, wl.N + 1, P, P, P, P, None) == -1
+    assert _st(lib, gather, by, None, wl.M, P, P, P, P, None) == -1
+    assert _st(lib, gather, by, P, wl.M, P, P, odd, P, None) == -1
     for bad in (6, -1):                                       # unknown stages
         assert _st(lib, step, by, bad, P, 1, P, P, P, P, P, P, P, None, wl.N, wl.M, f1, P, P,
                    None, P, need, None) == -1

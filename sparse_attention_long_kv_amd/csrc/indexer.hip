@@ -10,19 +10,21 @@
 // Scores.  qt = P[h]^T mean_g q[h*G+g] is formed in fp64 and rounded to fp32.
 // A position's r FP8 codes are decoded exactly (gfx950 packed conversion) and
 // dotted with qt in fp32: one 16-term fused multiply-add chain per 16 codes,
-// the two chains of r = 32 added together.  One lane reads 16 bytes, so a
-// wave reads 1 KB of contiguous cache per instruction.
+// the two chains of r = 32 added together, in the same order in every kernel
+// (so every kernel forms the same score bits).
 //
 // Selection is exact.  Scores map to order-preserving uint32 keys (0 = no
-// position).  A workgroup holds up to 16384 keys in registers (64 per
-// thread).  It finds the M-th largest key t by bisection over the key range,
-// counting keys >= t with wave ballots, then emits every key > t plus the
-// lowest-position keys == t, in ascending position order, with one ordered
-// prefix scan.  The fused path ("index_topm") splits a unit's positions into
-// chunks, selects the chunk-local top-M (exact for the union because the
-// order (score desc, position asc) is total), and a second launch merges
-// each unit's candidates with the same machinery.  The unfused path ("topm")
-// does the same from scores stored in HBM.
+// position).  The M-th largest key t is found by a radix select (a 4096-bin
+// LDS histogram of the first 12-bit digit, then the keys of the chosen bin
+// ranked directly or by two more digits); every key > t and the
+// lowest-position keys == t are emitted in ascending position order by one
+// ordered block scan over per-(row, wave) ballot counts.  Two paths:
+//  * the filter path (fused selection up to 2^19 positions, described before
+//    filter_kernel below): a sampled bound, chunks that keep only the keys at
+//    or above it, and one merge workgroup per unit;
+//  * the chunk-exact path (scores from HBM, or shapes outside the filter
+//    path): chunks hand over a superset of their top-M, merged per unit.
+// Both give the same idx (the order (score desc, position asc) is total).
 #include "append_common.hpp"
 #include "attend_common.hpp"
 #include "kernels.h"
@@ -901,23 +903,24 @@ __global__ __launch_bounds__(kChunkThreads, 4) void chunk_select_kernel(const Se
 // ------------------------------------------------------------------ filter path
 //
 // The fused selection's main path for contexts up to 2^19 positions:
-//  1. sample_kernel: per unit, score 32 evenly spread blocks of 128 positions
-//     and take the k-th largest sample key, k ~ 2 M (sample size) / len, as a
-//     bound thr that about 2M keys of the unit reach (the whole unit when it
-//     has at most 4096 positions: then k = M and thr is the exact M-th key).
+//  1. bound (sample_kernel, or append_bound_kernel in the decode step): per
+//     unit, score 128 evenly spread blocks of 8 positions and take the k-th
+//     largest sample key, k ~ 3 M (sample size) / len, as a bound thr that
+//     about 3M keys of the unit reach (the whole unit when it has at most
+//     1024 positions: then k = M and thr is the exact M-th key).
 //  2. filter_kernel: chunks of the unit stream their FP8 rows, score every
-//     position and append each key >= thr, with its position, to an LDS list
-//     of the wave that scored it (ballot + bit count, no key held in
+//     position and append each score >= thr, with its position, to an LDS
+//     list of the wave that scored it (ballot + bit count, no key held in
 //     registers); at the end the wave lists are interleaved back into
 //     position order with one block scan over per-(row, wave) counts and
-//     written out as the chunk's candidates.
-//  3. filter_merge_kernel: if no list overflowed and at least M keys reached
-//     thr, then thr <= the M-th largest key of the unit, so the candidates
-//     hold every selected position; they are loaded into registers in
-//     position order, the exact M-th key is found among them and idx is
-//     emitted in order, as in the chunk-exact merge.  Otherwise the
-//     workgroup selects exactly by streaming the unit's rows again and
-//     marking the selection in an LDS bitmap (slow but rare).
+//     written out, keyed, as the chunk's candidates.
+//  3. merge (filter_merge_kernel, or select_attend_kernel in the decode
+//     step): if no list overflowed and at least M keys reached thr, then
+//     thr <= the M-th largest key of the unit, so the candidates hold every
+//     selected position; they are loaded into registers in position order,
+//     the exact M-th key is found among them and idx is emitted in order.
+//     Otherwise the workgroup selects exactly by streaming the unit's rows
+//     again and marking the selection in an LDS bitmap (slow but rare).
 // Keys are bit-identical to the chunk-exact path's, so both give the same idx.
 
 // Inclusive prefix sum over the block in thread order (wtot: NT/64 words of LDS).

@@ -211,3 +211,58 @@ def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
 
 def default_scale(d):
     return 1.0 / math.sqrt(d)
+
+
+# ---------------------------------------------------------------- calibration
+
+@dataclass
+class AnisoInputs:
+    """Keys and queries with per-KV-head anisotropic second moments, for basis
+    calibration and selection recall.  Per KV head h a seeded orthonormal
+    d x d basis U_h; a key is U_h (sqrt(lk) * z), a query head U_h (sqrt(lq) *
+    z'), z, z' ~ N(0, I), lk and lq the spectra below.  Separate draws of the
+    same distributions serve as calibration data (cal_q: group-mean queries,
+    cal_k: keys) and as the decode step's cache and queries."""
+    q: torch.Tensor        # [B, Hq, d] bf16
+    K: torch.Tensor        # [B, Hkv, N, d] bf16
+    V: torch.Tensor        # [B, Hkv, N, d] bf16
+    cal_q: np.ndarray      # [Hkv, n_cal_q, d] float64 group means of calibration queries
+    cal_k: np.ndarray      # [Hkv, n_cal_k, d] float64 calibration keys (bf16 values)
+    P_random: torch.Tensor # [Hkv, d, r] fp32 seeded orthonormal basis (no calibration)
+
+
+def aniso_spectra(d):
+    """Key energy decays from direction 0; query energy peaks at direction
+    40: the directions that carry most key energy are not those the queries
+    weigh most, so key-only statistics are not enough."""
+    i = np.arange(d, dtype=np.float64)
+    return 1.0 / (1.0 + i / 4.0), 1.0 / (1.0 + np.abs(i - 40.0) / 4.0)
+
+
+def make_aniso_inputs(B=4, Hq=16, Hkv=4, d=128, N=32768, r=32, n_cal_q=512, n_cal_k=16384,
+                      seed=0, device="cpu"):
+    rng = np.random.default_rng(_seed("aniso", seed))
+    lk, lq = aniso_spectra(d)
+    G = Hq // Hkv
+    U = np.stack([orthonormal_basis(d, d, _seed("aniso-basis", seed, h)) for h in range(Hkv)])
+
+    def draw(shape, lam, h):
+        z = rng.standard_normal(shape + (d,)) * np.sqrt(lam)
+        return z @ U[h].T
+
+    q = np.zeros((B, Hq, d))
+    K = np.zeros((B, Hkv, N, d), dtype=np.float32)
+    for h in range(Hkv):
+        q[:, h * G:(h + 1) * G] = draw((B, G), lq, h)
+        for b in range(B):
+            K[b, h] = draw((N,), lk, h)
+    V = rng.standard_normal((B, Hkv, N, d)).astype(np.float32)
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    cal_q = np.stack([draw((n_cal_q, G), lq, h).mean(axis=1) for h in range(Hkv)])
+    cal_k = np.stack([bf(draw((n_cal_k,), lk, h)).to(torch.float64).numpy()
+                      for h in range(Hkv)])
+    P = np.stack([orthonormal_basis(d, r, _seed("aniso-P", seed, h)) for h in range(Hkv)])
+    return AnisoInputs(q=bf(q).to(device), K=bf(K).to(device), V=bf(V).to(device),
+                       cal_q=cal_q, cal_k=cal_k,
+                       P_random=torch.from_numpy(np.ascontiguousarray(P, dtype=np.float32))
+                       .to(device))

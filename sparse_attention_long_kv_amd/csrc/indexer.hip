@@ -199,6 +199,12 @@ struct SelectArgs {
 #ifndef SA_CHUNK_LOADS_IN_FLIGHT
 #define SA_CHUNK_LOADS_IN_FLIGHT 8
 #endif
+// ... and in the filter kernel, per batch (two batches alternate); 6 keeps it
+// under 85 VGPRs, so three 512-thread workgroups share a CU (measured: 6 ->
+// 192.0 us, 8 -> 194.2 us, 12 -> 195.3 us at 128K)
+#ifndef SA_FILTER_LOADS_IN_FLIGHT
+#define SA_FILTER_LOADS_IN_FLIGHT 6
+#endif
 
 // Radix digits of the 32-bit keys, most significant first: [20, 32) holds the
 // sign, exponent and top 3 mantissa bits of the score; then [8, 20), [0, 8).
@@ -1190,6 +1196,7 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
   const int len = unit_len(a.seq_lens, b, a.n_max);
   const int base = c * a.chunk;
   const int nv = min(max(len - base, 0), a.chunk);
+  const int pend = base + nv;                         // this chunk's valid positions end here
   int32_t* cnt = a.cnt + (size_t)u * a.S + c;
   if (len <= a.M || nv == 0) {                        // block-uniform
     if (threadIdx.x == 0) *cnt = 0;
@@ -1207,7 +1214,7 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
   // halves of an r = 32 row), so no cross-lane step is needed
   const uint32_t voff = (uint32_t)((w * kWave + lane) * R);
   constexpr int kLoadsPerIter = R / 16;
-  constexpr int kBatch = SA_CHUNK_LOADS_IN_FLIGHT / kLoadsPerIter;
+  constexpr int kBatch = SA_FILTER_LOADS_IN_FLIGHT / kLoadsPerIter;
   // Two register sets: while one batch of rows is scored the next one is in
   // flight (software pipelining keeps the memory queue full).
   struct Batch {
@@ -1238,7 +1245,7 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
       // scoring of the other kernels: identical bits
       float s = score16(qlo, bt.a[x]);
       if (R == 32) s = s + score16(qhi, bt.b[x]);
-      const bool ge = s >= thrf, in = p < len;
+      const bool ge = s >= thrf, in = p < pend;
       const bool sel = ge && in;
       const uint64_t m = ballot(ge) & ballot(in);     // (two compares, no select)
       const uint32_t slot = wc + __builtin_amdgcn_mbcnt_hi(
@@ -1251,6 +1258,9 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
       wc += (uint32_t)popc64(m);
     }
   };
+  // The last batch may reach past the chunk's rows (kBatch need not divide
+  // them): those loads fall outside the descriptor's range and read zero, and
+  // their positions are at or past pend, so nothing of them is kept.
   for (int i0 = 0; i0 < rows; i0 += 2 * kBatch) {    // block-uniform trip count
     score_batch(b0, i0);
     if (i0 + 2 * kBatch < rows) load_batch(b0, i0 + 2 * kBatch);

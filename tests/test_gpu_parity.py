@@ -156,6 +156,11 @@ TOPM_CASES = {
     "m_equals_n": (2, 4, 2, 64, 32, 700, 700, None, 700),
     "m_one": (2, 4, 2, 64, 16, 5000, 5000, [5000, 17], 1),
     "many_chunks": (2, 28, 4, 128, 32, 16384, 16384, [16384, 9000], 2048),
+    # M a quarter of N: the sampled bound is a negative score, and the filter
+    # chunks' last load batch reaches past their rows (positions of the next
+    # chunk, loaded as zero) -- none of those may be kept
+    "low_bound": (1, 4, 1, 128, 32, 16384, 16384, None, 4096),
+    "low_bound_r16": (2, 8, 2, 64, 16, 12288, 12288, [12288, 10000], 3000),
 }
 
 

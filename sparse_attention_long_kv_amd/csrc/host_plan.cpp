@@ -132,13 +132,11 @@ int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* p) {
   const int64_t lists = splits * kFilterWaves;
   int64_t cap = kFilterMinCap;
   while (cap < kFilterMaxCap && cap * 2 * lists <= kFilterSlots) cap *= 2;
-  if (chunk > (int64_t)kFilterMaxRows * kChunkBlock) return SA_OK;
   p->enabled = true;
   p->chunk = (int)chunk;
   p->splits = (int)splits;
   p->cap = (int)cap;
   p->cslots = (int)(cap * kFilterWaves);
-  p->rows = (int)ceil_div(splits * p->cslots, kMergeThreadsHost);
   size_t off = 0;
   p->off_thr = off;
   off = align_up(off + (size_t)units * sizeof(uint32_t), kAlign);
@@ -146,10 +144,8 @@ int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* p) {
   off = align_up(off + (size_t)units * 32 * sizeof(float), kAlign);
   p->off_cnt = off;
   off = align_up(off + (size_t)units * splits * sizeof(int32_t), kAlign);
-  p->off_key = off;
-  off = align_up(off + (size_t)units * splits * p->cslots * sizeof(uint32_t), kAlign);
-  p->off_pos = off;
-  off = align_up(off + (size_t)units * splits * p->cslots * sizeof(int32_t), kAlign);
+  p->off_cand = off;                       // (key, position) pairs
+  off = align_up(off + (size_t)units * splits * p->cslots * 2 * sizeof(uint32_t), kAlign);
   p->end = off;
   return SA_OK;
 }

@@ -49,7 +49,6 @@ constexpr int kFilterSlots = 16384;      // candidate slots per unit (16 per mer
 constexpr int kFilterMinCap = 128;       // slots per wave list, at least
 constexpr int kFilterMaxCap = 512;       // slots per wave list, at most (staged in LDS)
 constexpr int kFilterMaxChunk = 32768;   // positions per filter workgroup, at most
-constexpr int kFilterMaxRows = 64;       // 512-position rows per filter chunk, at most
 constexpr int kFilterWaves = 8;          // lists per chunk (one per wave of 512 threads)
 constexpr int kSampleBlocks = 128;       // sampled position blocks per unit
 constexpr int kSampleBlock = 8;          // positions per sampled block (256 B of FP8 rows)
@@ -65,9 +64,8 @@ struct FilterPlan {
   int chunk;        // positions per filter workgroup (multiple of 512)
   int splits;       // chunks per unit
   int cap;          // slots per wave list (power of two)
-  int cslots;       // candidate slots per chunk = 8 * cap
-  int rows;         // merge rows per thread = splits * cslots / 1024
-  size_t off_thr, off_qt, off_cnt, off_key, off_pos, end;
+  int cslots;       // candidate slots per chunk = 8 * cap (one list per wave)
+  size_t off_thr, off_qt, off_cnt, off_cand, end;
 };
 
 struct DecodePlan {

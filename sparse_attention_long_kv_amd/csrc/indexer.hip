@@ -406,11 +406,9 @@ __device__ void finish_threshold(Sh& sh, uint32_t target, uint32_t& t_out, uint3
 // write unselected keys to a scratch slot); slot = number of selected keys
 // before this one.  When every key == t is selected (need == eq, the usual
 // case) selection is the single predicate key >= t, one ballot per row.
-// Rows i >= nk (block-uniform) hold no selectable key and are skipped.
 template <int NT, int K, class EmitFn>
 __device__ __forceinline__ void emit_in_order(const uint32_t (&key)[K], uint32_t t, uint32_t need,
-                                              uint32_t eq, SelectShared<NT>& sh, EmitFn emit,
-                                              int nk = K) {
+                                              uint32_t eq, SelectShared<NT>& sh, EmitFn emit) {
   constexpr int W = NT / kWave;
   static_assert(K * W <= NT, "segments");
   const int tid = threadIdx.x, w = tid / kWave;
@@ -418,9 +416,8 @@ __device__ __forceinline__ void emit_in_order(const uint32_t (&key)[K], uint32_t
   // pass 1: per (row, wave) counts, wave-major so pass 2 reads them at once
 #pragma unroll
   for (int i = 0; i < K; ++i) {
-    uint32_t v = 0u;
-    if (i >= nk) {
-    } else if (single) {
+    uint32_t v;
+    if (single) {
       v = (uint32_t)popc64(ballot(key[i] >= t));
     } else {
       v = (uint32_t)popc64(ballot(key[i] > t)) | ((uint32_t)popc64(ballot(key[i] == t)) << 16);
@@ -445,8 +442,7 @@ __device__ __forceinline__ void emit_in_order(const uint32_t (&key)[K], uint32_t
   asm volatile("" : "+v"(t2));
 #pragma unroll
   for (int i = 0; i < K; ++i) {
-    if (i >= nk) {
-    } else if (single) {
+    if (single) {
       const bool sel = key[i] >= t2;
       const uint32_t slot = pre[i] + (uint32_t)__builtin_amdgcn_mbcnt_hi(
           (uint32_t)(ballot(sel) >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ballot(sel), 0u));
@@ -953,12 +949,11 @@ struct FilterArgs {
   const float* P;
   const uint8_t* kp;
   const int32_t* seq_lens;
-  int n_max, Ncap, Hq, Hkv, G, M, S, chunk, cap, cslots, cslots_log2, rows;
+  int n_max, Ncap, Hq, Hkv, G, M, S, chunk, cap, cslots;
   uint32_t* thr;     // [units]
   float* qt;         // [units][32] indexer queries (written by the bound stage)
-  int32_t* cnt;      // [units][S] kept keys per chunk, -1 when a wave list overflowed
-  uint32_t* ckey;    // [units][S][cslots] kept keys in position order (cslots = 8 cap)
-  int32_t* cpos;
+  int32_t* cnt;      // [units][S] kept positions per chunk, -1 when a wave list overflowed
+  uint2* cand;       // [units][S][cslots] (key, position) of the kept positions, any order
   int32_t* idx;
 };
 
@@ -1182,16 +1177,14 @@ __global__ __launch_bounds__(kSampleThreads) void append_bound_kernel(const Filt
 template <int D, int R>
 __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs a) {
   constexpr int NT = kChunkThreads;
-  // each wave's list is staged here, then interleaved into position order
+  // Each wave lists the positions it keeps in LDS; at the end the 8 lists go
+  // out back to back as the chunk's candidates, (key, position) pairs in no
+  // particular order (the merge emits through a bitmap of positions).
   __shared__ uint32_t sk[kFilterWaves][kFilterMaxCap];
   __shared__ int32_t sp[kFilterWaves][kFilterMaxCap];
-  __shared__ uint32_t rowcnt[kFilterWaves][kFilterMaxRows];   // kept keys per (wave, row)
-  __shared__ uint32_t rowoff[kFilterWaves][kFilterMaxRows];   // output offset per (wave, row)
-  __shared__ uint32_t rowfirst[kFilterWaves][kFilterMaxRows]; // list index of a row's first key
-  __shared__ uint32_t wtot[NT / kWave];
-  __shared__ int ovf;
+  __shared__ uint32_t wn[kFilterWaves];
   const int u = blockIdx.x / a.S, c = blockIdx.x % a.S;
-  const int b = u / a.Hkv, h = u % a.Hkv;
+  const int b = u / a.Hkv;
   const int w = threadIdx.x / kWave, lane = lane_id();
   const int len = unit_len(a.seq_lens, b, a.n_max);
   const int base = c * a.chunk;
@@ -1205,13 +1198,14 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
   // key >= thr  <=>  score >= thrf for every score the chains can produce
   // (no NaN; -0 and +0 share the key of +0, and -0 >= +0 holds)
   const float thrf = key_score(a.thr[u]);
-  uint32_t* lk = a.ckey + ((size_t)u * a.S + c) * a.cslots;
-  int32_t* lp = a.cpos + ((size_t)u * a.S + c) * a.cslots;
+  uint2* lc = a.cand + ((size_t)u * a.S + c) * a.cslots;
   // this chunk's rows only: loads past the valid positions return zero
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(a.kp + ((size_t)u * a.Ncap + base) * R, (uint32_t)nv * R);
-  // lane l scores position base + i*NT + 64w + l on its own (both 16-byte
-  // halves of an r = 32 row), so no cross-lane step is needed
+  // Lane l scores position base + i*NT + 64w + l on its own (both 16-byte
+  // halves of an r = 32 row), so no cross-lane step is needed; the workgroup's
+  // 8 waves read each 512-position row together (one contiguous stream per
+  // workgroup: measured 8-10 us faster than a contiguous range per wave).
   const uint32_t voff = (uint32_t)((w * kWave + lane) * R);
   constexpr int kLoadsPerIter = R / 16;
   constexpr int kBatch = SA_FILTER_LOADS_IN_FLIGHT / kLoadsPerIter;
@@ -1236,7 +1230,7 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
   // scalar registers (an FMA takes one scalar operand), saving 32 VGPRs
   float qlo[16], qhi[16];
   query_halves<R>(a.qt + (size_t)u * 32, qlo, qhi);
-  uint32_t wc = 0;                                    // keys this wave appended so far
+  uint32_t wc = 0;                                    // positions this wave kept so far
   auto score_batch = [&](const Batch& bt, int i0) {
 #pragma unroll
     for (int x = 0; x < kBatch; ++x) {
@@ -1254,7 +1248,6 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
         sk[w][slot] = __float_as_uint(s);               // keyed when written out
         sp[w][slot] = p;
       }
-      if (i0 + x < rows) rowcnt[w][i0 + x] = (uint32_t)popc64(m);   // same value from every lane
       wc += (uint32_t)popc64(m);
     }
   };
@@ -1269,58 +1262,26 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
       if (i0 + 3 * kBatch < rows) load_batch(b1, i0 + 3 * kBatch);
     }
   }
-  // Position order: key j of wave w's list sits in row i; it goes to
-  //   (keys of all (row, wave) before (i, w)) + (j - first index of row i).
-  if (threadIdx.x == 0) ovf = 0;
+  // The lists go out only once every wave has finished reading: stores mixed
+  // into the read stream cost far more (measured), and one 8-byte store per
+  // candidate costs less than two 4-byte ones.  A count past cap means the
+  // wave's list overflowed: the chunk is marked -1 and the merge falls back.
+  if (lane == 0) wn[w] = wc;
   __syncthreads();
-  if (lane == 0 && wc > (uint32_t)a.cap) ovf = 1;
-  const int nrow = min(rows, kFilterMaxRows);
-  {
-    // per-wave exclusive scan over its rows, 64 rows at a time
-    uint32_t carry = 0;
-    for (int r0 = 0; r0 < nrow; r0 += kWave) {       // wave-uniform
-      const int r = r0 + lane;
-      const uint32_t v = r < nrow ? rowcnt[w][r] : 0u;
-      const uint32_t incl = wave_inclusive_scan(v);
-      if (r < nrow) rowfirst[w][r] = carry + incl - v;
-      carry += (uint32_t)__shfl((int)incl, kWave - 1, kWave);
-    }
-  }
-  // block exclusive scan in (row, wave) order, kEntries consecutive entries
-  // per thread
-  constexpr int kEntries = kFilterMaxRows * kFilterWaves / NT;
-  static_assert(kEntries * NT == kFilterMaxRows * kFilterWaves, "scan entries");
-  const int tid = threadIdx.x;
-  uint32_t ev[kEntries], mine = 0;
+  uint32_t off = 0, total = 0;
+  bool over = false;
 #pragma unroll
-  for (int e = 0; e < kEntries; ++e) {
-    const int g = tid * kEntries + e;
-    const int gi = g / kFilterWaves, gw = g % kFilterWaves;
-    ev[e] = gi < nrow ? rowcnt[gw][gi] : 0u;
-    mine += ev[e];
+  for (int ww = 0; ww < kFilterWaves; ++ww) {
+    const uint32_t x = wn[ww];
+    over |= x > (uint32_t)a.cap;
+    off += ww < w ? x : 0u;
+    total += x;
   }
-  uint32_t total;
-  uint32_t run = block_scan_small<NT>(mine, wtot, total) - mine;
-#pragma unroll
-  for (int e = 0; e < kEntries; ++e) {
-    const int g = tid * kEntries + e;
-    const int gi = g / kFilterWaves, gw = g % kFilterWaves;
-    if (gi < nrow) rowoff[gw][gi] = run;
-    run += ev[e];
+  if (!over) {
+    for (int j = lane; j < (int)wc; j += kWave)
+      lc[off + j] = make_uint2(score_key(__uint_as_float(sk[w][j]) + 0.0f), (uint32_t)sp[w][j]);
   }
-  __syncthreads();
-  const bool overflow = ovf != 0;
-  if (!overflow) {
-    const int n = (int)wc;
-    for (int j = lane; j < n; j += kWave) {
-      const int32_t p = sp[w][j];
-      const int i = (p - base) / NT;
-      const uint32_t o = rowoff[w][i] + ((uint32_t)j - rowfirst[w][i]);
-      lk[o] = score_key(__uint_as_float(sk[w][j]) + 0.0f);
-      lp[o] = p;
-    }
-  }
-  if (tid == 0) *cnt = overflow ? -1 : (int)total;
+  if (threadIdx.x == 0) *cnt = over ? -1 : (int)total;
 }
 
 // Mark the selected positions of a unit in `bm` (bit p = position p) and
@@ -1394,6 +1355,88 @@ __device__ void emit_bitmap(SelectShared<NT>& sh, uint32_t* bm, int len, uint32_
   }
 }
 
+// Emit, in ascending order, the selected positions of a unit whose
+// candidates sit in registers in no particular order (key[i], pos[i] for
+// i < nk; key 0 = none): every key > t and, of the keys == t, the `need`
+// lowest positions.  The selection is marked in an LDS bitmap of positions;
+// a selected position's output slot is the number of marked positions below
+// it (one block scan over per-thread groups of words gives a count before
+// each word, then a bit count inside the word).  Leaves the M positions, -1 padded, in sh.list (as int32) and
+// copies them to idx_u when it is not null.
+template <int NT, int K>
+__device__ __forceinline__ void emit_selected(SelectShared<NT>& sh, uint32_t* bm, int len,
+                                              uint32_t t, uint32_t need, uint32_t eq, int M,
+                                              int nk, const uint32_t (&key)[K],
+                                              const int32_t (&pos)[K], int32_t* idx_u) {
+  const int tid = threadIdx.x, lane = lane_id();
+  const int words = (len + 31) >> 5;
+  const int wpt = (words + NT - 1) / NT;              // words per thread group
+  for (int j = tid; j < words; j += NT) bm[j] = 0u;
+  int last = 0x7FFFFFFF;                              // highest tied position taken
+  if (need != eq) {                                   // block-uniform: ties straddle the cut
+    // the need lowest tied positions = the need largest of ~position
+    for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
+    __syncthreads();
+    const uint32_t dummy = (uint32_t)(kBins + lane);
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+      if (i < nk) atomicAdd(&sh.hist[key[i] == t ? (~(uint32_t)pos[i] >> kTopShift) : dummy], 1u);
+    __syncthreads();
+    uint32_t tp, np, ep;
+    finish_threshold<NT>(sh, need, tp, np, ep, [&](auto&& f) {
+#pragma unroll
+      for (int i = 0; i < K; ++i)
+        if (i < nk) f(~(uint32_t)pos[i], key[i] == t);
+    });
+    last = (int)~tp;
+  }
+  __syncthreads();                                    // bm is clear
+  auto taken = [&](int i) { return key[i] > t || (key[i] == t && pos[i] <= last); };
+#pragma unroll
+  for (int i = 0; i < K; ++i)
+    if (i < nk && taken(i)) atomicOr(&bm[pos[i] >> 5], 1u << (pos[i] & 31));
+  __syncthreads();
+  const int w0 = min(tid * wpt, words), w1 = min(w0 + wpt, words);
+  uint32_t mine = 0;
+  for (int j = w0; j < w1; ++j) mine += (uint32_t)__builtin_popcount(bm[j]);
+  uint32_t total;
+  const uint32_t incl = block_inclusive_scan<NT>(mine, sh, total);
+  // marked positions before each word: a table in the (free) histogram when
+  // the bitmap is short enough, else per thread group
+  const bool table = words <= kBins + kWave;          // block-uniform
+  if (table) {
+    uint32_t run = incl - mine;
+    for (int j = w0; j < w1; ++j) {
+      sh.hist[j] = run;
+      run += (uint32_t)__builtin_popcount(bm[j]);
+    }
+  } else {
+    sh.seg[tid] = incl - mine;
+  }
+  __syncthreads();
+  int32_t* out = reinterpret_cast<int32_t*>(sh.list);
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    if (i < nk && taken(i)) {
+      const int p = pos[i], wj = p >> 5;
+      uint32_t slot;
+      if (table) {
+        slot = sh.hist[wj];
+      } else {
+        const int grp = wj / wpt;
+        slot = sh.seg[grp];
+        for (int j = grp * wpt; j < wj; ++j) slot += (uint32_t)__builtin_popcount(bm[j]);
+      }
+      slot += (uint32_t)__builtin_popcount(bm[wj] & ((1u << (p & 31)) - 1u));
+      if (slot < (uint32_t)M) out[slot] = p;
+    }
+  }
+  for (int j = (int)total + tid; j < M; j += NT) out[j] = -1;
+  __syncthreads();
+  if (idx_u)
+    for (int j = tid; j < M; j += NT) idx_u[j] = out[j];
+}
+
 // Exact selection of one unit by streaming its rows again (the filter's
 // bound was above the M-th key, or a list overflowed).
 template <int D, int R>
@@ -1461,7 +1504,7 @@ __device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShar
     return;
   }
   // Per-chunk counts (S <= 16): one wave forms their exclusive prefix; -1
-  // marks an overflowed list.
+  // marks a chunk whose lists overflowed.
   if (w == 0) {
     const int c = lane < S ? a.cnt[(size_t)u * S + lane] : 0;
     const bool over = ballot(c < 0) != 0;
@@ -1478,11 +1521,10 @@ __device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShar
     __syncthreads();
     return;
   }
-  // The unit's candidates, numbered g = 0 .. total-1 in chunk order (hence in
-  // position order); key g sits in register i = g / NT of thread g % NT.
-  // Only the kept slots are read: chunk c holds g in [start_c, start_c+1).
-  const uint32_t* ck = a.ckey + (size_t)u * S * a.cslots;
-  const int32_t* cp = a.cpos + (size_t)u * S * a.cslots;
+  // The unit's candidates, numbered g = 0 .. total-1 chunk after chunk; key g
+  // sits in register i = g / NT of thread g % NT.  Only the kept slots are
+  // read: chunk c holds g in [start_c, start_c+1).
+  const uint2* cu = a.cand + (size_t)u * S * a.cslots;
   const int nk = (int)((total + NT - 1) / NT);        // rows in use, <= KPT
   uint32_t key[KPT];
   int32_t pos[KPT];
@@ -1496,9 +1538,9 @@ __device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShar
 #pragma unroll
       for (int step = kFilterMaxSplits / 2; step >= 1; step >>= 1)
         if (start_s[c + step] <= g) c += step;
-      const size_t f = (size_t)c * a.cslots + (g - start_s[c]);
-      key[i] = ck[f];
-      pos[i] = cp[f];
+      const uint2 kv = cu[(size_t)c * a.cslots + (g - start_s[c])];
+      key[i] = kv.x;
+      pos[i] = (int32_t)kv.y;
     }
   }
   const uint32_t thr = a.thr[u];
@@ -1531,13 +1573,9 @@ __device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShar
     for (int i = 0; i < KPT; ++i)
       if (i < nk) f(key[i], key[i] != 0u);
   });
-  // ordered emission over the normalised keys (positions were loaded with
-  // the keys); unselected keys go to a scratch slot past the list
-  emit_in_order(key, t, need, eq, sh, [&](int i, bool sel, uint32_t slot) {
-    out[sel ? slot : (uint32_t)(kListCap - kWave + lane)] = pos[i];
-  }, nk);
-  if (idx_u)
-    for (int j = tid; j < M; j += NT) idx_u[j] = out[j];
+  // the candidates are in no particular order: emit through a bitmap of the
+  // unit's positions
+  emit_selected<NT>(sh, ms.bm, len, t, need, eq, M, nk, key, pos, idx_u);
 }
 
 template <int D, int R>
@@ -1605,14 +1643,12 @@ hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int 
   a.chunk = plan.chunk;
   a.cap = plan.cap;
   a.cslots = plan.cslots;
-  a.cslots_log2 = __builtin_ctz((unsigned)plan.cslots);
-  a.rows = plan.rows;
+
   char* ws = (char*)workspace;
   a.thr = (uint32_t*)(ws + plan.off_thr);
   a.qt = (float*)(ws + plan.off_qt);
   a.cnt = (int32_t*)(ws + plan.off_cnt);
-  a.ckey = (uint32_t*)(ws + plan.off_key);
-  a.cpos = (int32_t*)(ws + plan.off_pos);
+  a.cand = (uint2*)(ws + plan.off_cand);
   a.idx = idx;
   if ((long)plan.units * plan.splits > INT32_MAX) return hipErrorInvalidConfiguration;
   AppendArgs ap;

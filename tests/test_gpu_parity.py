@@ -570,17 +570,41 @@ def test_topm_all_scores_equal_takes_lowest_positions():
     assert gi[0, 0].tolist() == list(range(M))
 
 
+def test_topm_ties_cut_by_m_take_lowest_positions():
+    """97 distinct FP8 rows repeated along the context: scores come in tie
+    groups of ~169 and M cuts one; the filter path (no list can overflow
+    here) must take, of the tied group, exactly the lowest positions, as the
+    chunk-exact path and the oracle do."""
+    _say("case: topm ties cut by M")
+    B, Hq, Hkv, d, r, N, M = 1, 4, 1, 128, 32, 16384, 1000
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, 97, seed=23)
+    P64 = P.double().numpy()
+    base = oracle_kp(f64(K), P64)                           # [1, 1, 97, r]
+    kp = np.ascontiguousarray(base[:, :, np.arange(N) % 97, :])
+    gi = _topm_check_against_oracle(q, P, kp, M, N)
+    qt = oracle.indexer_query(f64(q)[0], P64[0])
+    s = oracle.index_scores(qt, kp[0, 0])
+    v = np.sort(s)[::-1][M - 1]
+    above = np.flatnonzero(s > v)
+    tied = np.flatnonzero(s == v)
+    need = M - above.size
+    assert 0 < need < tied.size, (need, tied.size)          # M really cuts a tie group
+    assert gi[0, 0].tolist() == sorted(above.tolist() + tied[:need].tolist())
+
+
 def test_topm_sample_overestimate_falls_back_exactly():
-    """High scores planted exactly on the positions the bound's sample reads
-    (32 evenly spread blocks of 128 rows) push the sampled bound above the
-    M-th score; the merge must detect it and select exactly."""
+    """High scores planted exactly on positions the bound's sample reads (its
+    128 evenly spread blocks of 8 rows; 16 of them here, 128 rows, more than
+    the k = 96 sample keys the bound ranks down to) push the sampled bound
+    above the M-th score, so fewer than M positions reach it; the merge must
+    detect it and select exactly."""
     _say("case: topm sample overestimate")
     B, Hq, Hkv, d, r, N, M = 1, 4, 1, 128, 32, 65536, 2048
     q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, N, seed=21)
     K64 = f64(K)
     qbar = f64(q).reshape(B, Hkv, Hq // Hkv, d).mean(axis=2)
-    starts = [(j * (N - 128)) // 31 for j in range(32)]
-    rows = np.concatenate([np.arange(s0, s0 + 128) for s0 in starts[:8]])   # 1024 rows
+    starts = [(j * (N - 8)) // 127 for j in range(128)]
+    rows = np.concatenate([np.arange(s0, s0 + 8) for s0 in starts[::8]])   # 128 rows
     K64[0, 0, rows] += 6.0 * qbar[0, 0]
     P64 = P.double().numpy()
     kp = oracle_kp(K64, P64)

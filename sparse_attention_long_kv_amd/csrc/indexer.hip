@@ -199,11 +199,12 @@ struct SelectArgs {
 #ifndef SA_CHUNK_LOADS_IN_FLIGHT
 #define SA_CHUNK_LOADS_IN_FLIGHT 8
 #endif
-// ... and in the filter kernel, per batch (two batches alternate); 6 keeps it
-// under 85 VGPRs, so three 512-thread workgroups share a CU (measured: 6 ->
-// 192.0 us, 8 -> 194.2 us, 12 -> 195.3 us at 128K)
+// ... and in the filter kernel, per batch (two batches alternate): 2 (one
+// 512-position row per batch at r = 32) keeps it near 40 VGPRs, so four
+// 512-thread workgroups share a CU and every chunk of a 128K step is resident
+// at once (measured at 128K: 2 -> 187.5 us, 4 -> 188.9, 6 -> 189.4, 8 -> 190.4)
 #ifndef SA_FILTER_LOADS_IN_FLIGHT
-#define SA_FILTER_LOADS_IN_FLIGHT 6
+#define SA_FILTER_LOADS_IN_FLIGHT 2
 #endif
 
 // Radix digits of the 32-bit keys, most significant first: [20, 32) holds the

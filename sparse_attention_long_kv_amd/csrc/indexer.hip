@@ -17,8 +17,10 @@
 // position).  The M-th largest key t is found by a radix select (a 4096-bin
 // LDS histogram of the first 12-bit digit, then the keys of the chosen bin
 // ranked directly or by two more digits); every key > t and the
-// lowest-position keys == t are emitted in ascending position order by one
-// ordered block scan over per-(row, wave) ballot counts.  Two paths:
+// lowest-position keys == t are emitted in ascending position order, by one
+// ordered block scan over per-(row, wave) ballot counts when the keys sit in
+// registers in position order, else through an LDS bitmap of positions.
+// Two paths:
 //  * the filter path (fused selection up to 2^19 positions, described before
 //    filter_kernel below): a sampled bound, chunks that keep only the keys at
 //    or above it, and one merge workgroup per unit;
@@ -914,16 +916,16 @@ __global__ __launch_bounds__(kChunkThreads, 4) void chunk_select_kernel(const Se
 //  2. filter_kernel: chunks of the unit stream their FP8 rows, score every
 //     position and append each score >= thr, with its position, to an LDS
 //     list of the wave that scored it (ballot + bit count, no key held in
-//     registers); at the end the wave lists are interleaved back into
-//     position order with one block scan over per-(row, wave) counts and
-//     written out, keyed, as the chunk's candidates.
+//     registers); once every wave has finished reading, the 8 lists go out
+//     back to back as the chunk's candidates, packed (key, position) pairs
+//     in no particular order.
 //  3. merge (filter_merge_kernel, or select_attend_kernel in the decode
 //     step): if no list overflowed and at least M keys reached thr, then
 //     thr <= the M-th largest key of the unit, so the candidates hold every
-//     selected position; they are loaded into registers in position order,
-//     the exact M-th key is found among them and idx is emitted in order.
+//     selected position; they are loaded into registers, the exact M-th key
+//     is found among them and idx is emitted through a bitmap of positions.
 //     Otherwise the workgroup selects exactly by streaming the unit's rows
-//     again and marking the selection in an LDS bitmap (slow but rare).
+//     again and marking the selection in the bitmap (slow but rare).
 // Keys are bit-identical to the chunk-exact path's, so both give the same idx.
 
 // Inclusive prefix sum over the block in thread order (wtot: NT/64 words of LDS).

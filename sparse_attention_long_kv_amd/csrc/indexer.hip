@@ -228,7 +228,7 @@ struct SelectShared {
   double part[NT];
   uint32_t seg[NT];
   uint32_t wtot[W];
-  uint32_t pick[3];
+  uint32_t pick[4];
   uint32_t hist[kBins + kWave];   // + one private dummy bin per lane
   static constexpr int kCap = kListCap;
   alignas(16) uint32_t list[kCap];
@@ -359,6 +359,25 @@ __device__ void resolve_bin(Sh& sh, uint32_t target, uint32_t path, uint32_t abo
                             uint32_t& t_out, uint32_t& need_out, uint32_t& eq_out, Visit visit) {
   const int tid = threadIdx.x;
   const uint32_t b1 = path;
+  const uint32_t nbin = sh.pick[2];                  // the bin's count, from pick_bin
+  if (nbin <= (uint32_t)kRankMax && nbin <= (uint32_t)NT && nbin + 4 <= (uint32_t)Sh::kCap) {
+    // A short bin (the usual case): its keys take list slots in any order
+    // (ranking does not need their order), one atomic slot each, and are
+    // ranked directly -- no count pass and no block scan.
+    if (tid == 0) sh.pick[3] = 0u;
+    if (tid < 4) sh.list[nbin + tid] = 0u;           // pad for rank_in_list
+    __syncthreads();
+    visit([&](uint32_t k, bool valid) {
+      if (valid && (k >> kTopShift) == b1) sh.list[atomicAdd(&sh.pick[3], 1u)] = k;
+    });
+    __syncthreads();
+    uint32_t t, gt, eq;
+    rank_in_list<NT>(sh, nbin, target - above, t, gt, eq);
+    t_out = t;
+    need_out = target - above - gt;
+    eq_out = eq;
+    return;
+  }
   uint32_t cnt = 0;
   visit([&](uint32_t k, bool valid) { cnt += (valid && (k >> kTopShift) == b1) ? 1u : 0u; });
   uint32_t n;

@@ -12,6 +12,8 @@ Prints ONE JSON line:
   value         decode steps/s (N=1 GPU; whole-job throughput)
   hbm_gbps      algorithmic bytes per step / step time
   roofline      the dominant kernel (scoring + candidate filter) against 8 TB/s
+  cold_step_us  steps timed one at a time after a cache-evicting read
+                (median, p10, p90, and per launch)
   cpu_baseline  the fp64 oracle on the host, on a bounded sample of units
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -23,6 +25,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -303,6 +307,9 @@ def main(argv=None):
     ap.add_argument("--cpu-units", type=int, default=16,
                     help="units of the step timed for the oracle baseline (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="steps timed one by one after a 2 GiB read flush, after the "
+                         "timed region (0: skip)")
     ap.add_argument("--baseline-reps", type=int, default=5,
                     help="calls timed per comparison baseline (0: skip them)")
     ap.add_argument("--calibration-mib", type=int, default=0,
@@ -413,6 +420,35 @@ def main(argv=None):
                for k, v in ev.items()}
     timer.destroy(pool)
 
+    # cold steps (informational): each step alone, bracketed by events, after
+    # a 2 GiB read that evicts the 256 MB last-level cache.  (A write flush
+    # would leave up to 256 MB of dirty lines whose write-back then lands in
+    # the step's filter launch: ~55 us there, measured.)
+    cold = None
+    if a.cold_steps > 0:
+        flush = torch.ones(2 ** 29, dtype=torch.float32, device=dev)
+        acc = torch.empty((), dtype=torch.float32, device=dev)
+        pool = timer.create(n_ev * a.cold_steps)
+        for k in range(a.cold_steps):
+            torch.sum(flush, dim=0, out=acc)
+            rec = pool[k * n_ev:(k + 1) * n_ev]
+            for i, call in enumerate(calls):
+                timer.record(rec[i], stream)
+                call()
+            timer.record(rec[-1], stream)
+        torch.cuda.synchronize()
+        per = [[1e3 * timer.elapsed_ms(pool[k * n_ev + i], pool[k * n_ev + i + 1])
+                for i in range(len(calls))] for k in range(a.cold_steps)]
+        us = [1e3 * timer.elapsed_ms(pool[k * n_ev], pool[k * n_ev + n_ev - 1])
+              for k in range(a.cold_steps)]
+        timer.destroy(pool)
+        del flush, acc
+        q10, q50, q90 = (float(np.percentile(us, p)) for p in (10, 50, 90))
+        cold = {"steps": a.cold_steps, "read_flush_mib": 2048, "median_us": round(q50, 2),
+                "p10_us": round(q10, 2), "p90_us": round(q90, 2),
+                "median_us_per_call": {k: round(float(np.median([r[i] for r in per])), 2)
+                                       for i, k in enumerate(names)}}
+
     bytes_k = algorithmic_bytes(wl)
     step_bytes = sum(bytes_k.values())
     steps_per_s = 1e3 / ms_per_step
@@ -449,6 +485,7 @@ def main(argv=None):
                                        for k in kern_us
                         if bytes_k[k]},
         "roofline": roofline,
+        "cold_step_us": cold,
         "cpu_baseline": None,
         "baselines": None,
     }

@@ -527,6 +527,131 @@ def test_full_size_step_on_sampled_units(name):
             check_attention(go[b, h * G:(h + 1) * G], o2, "full-size unit %s" % ((b, h),))
 
 
+def _picks(wl, rng, extra=1):
+    """First and last unit plus ``extra`` seeded ones."""
+    return sorted({(0, 0), (wl.B - 1, wl.Hkv - 1)}
+                  | {(int(rng.integers(wl.B)), int(rng.integers(wl.Hkv))) for _ in range(extra)})
+
+
+def _unit_after_append(inp, K0, V0, b, h):
+    """The oracle's rows and FP8 codes of unit (b, h) after the step's append,
+    from the generator's rows K0, V0 (before the HIP append)."""
+    P64 = inp.P.double().cpu().numpy()
+    pos = inp.pos.cpu().numpy()
+    kp0 = oracle.project_keys(K0, P64[h])[None, None]
+    K2, V2, kp2 = oracle.append_kv(K0[None, None], V0[None, None], kp0, pos[b:b + 1],
+                                   f64(inp.k_new[b:b + 1, h:h + 1]),
+                                   f64(inp.v_new[b:b + 1, h:h + 1]), P64[h:h + 1])
+    return K2[0, 0], V2[0, 0], kp2[0, 0], P64[h]
+
+
+def test_full_size_cross_layer_reuse_on_sampled_units():
+    """reuse8_64k at its real size (B16, Hkv8, N65536, M2048; eight layers with
+    their own caches and queries).  The full layers 0 and 4 run the decode
+    step as bench.py launches it; layers 1-3 and 5-7 append their token and
+    attend, with sparse_attn_decode, over the index sets of their full layer.
+    In every layer the first and last unit and a seeded one are checked: the
+    full layers' sets against the exact top-M contract, every layer's output
+    against the oracle's attention over that layer's rows at the indices it
+    used, and every layer's appended FP8 code row against the oracle's."""
+    wl = WORKLOADS["reuse8_64k"]
+    sh = _shape_of(wl.B, wl.Hq, wl.Hkv, wl.d, wl.r, wl.N)
+    ws = sa.alloc_workspace(sh, wl.N, wl.M)
+    rng = np.random.default_rng(17)
+    idx_of = {}
+    G = wl.G
+    for layer in range(wl.layers):
+        src = oracle.reuse_source_layer(layer, wl.full_layers)
+        _say("case: full-size reuse, layer", layer, "indices of layer", src)
+        inp = make_decode_inputs(wl, seed=9, layer=layer, device="cuda")
+        picks = _picks(wl, rng)
+        saved = {(b, h): (f64(inp.k_cache[b, h]), f64(inp.v_cache[b, h])) for b, h in picks}
+        if layer == src:
+            kp, idx, out, lse = _bench_sequence(inp, sh, wl.M, ws)
+            idx_of[layer] = idx
+        else:
+            idx = idx_of[src]
+            kp = torch.zeros(wl.B, wl.Hkv, wl.N, wl.r, dtype=torch.uint8, device="cuda")
+            sa.sparse_attn_append_kv(sh, inp.pos, inp.k_new, inp.v_new, inp.P, inp.k_cache,
+                                     inp.v_cache, kp)
+            out = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.bfloat16, device="cuda")
+            lse = torch.empty(wl.B, wl.Hq, dtype=torch.float32, device="cuda")
+            sa.sparse_attn_decode(sh, inp.q, inp.k_cache, inp.v_cache, idx, wl.M,
+                                  default_scale(wl.d), out, lse, ws)
+        torch.cuda.synchronize()
+        gi, go, gl = idx.cpu().numpy(), f64(out), lse.cpu().double().numpy()
+        pos = inp.pos.cpu().numpy()
+        q64 = f64(inp.q)
+        for b, h in picks:
+            K2, V2, kp2, P64h = _unit_after_append(inp, *saved[(b, h)], b, h)
+            qg = q64[b, h * G:(h + 1) * G]
+            row = kp[b, h, pos[b]].cpu().numpy()[None, None, None]
+            ok, _ = kp_codes_match(row, kp2[pos[b]][None, None, None],
+                                   K2[pos[b]][None, None, None], P64h[None])
+            assert ok, "layer %d unit %s: appended code row" % (layer, (b, h))
+            if layer == src:
+                s = oracle.index_scores(oracle.indexer_query(qg, P64h), kp2[:wl.N])
+                swaps = check_topm_unit(gi[b, h], s, wl.M, wl.N)
+                _say("  unit", (b, h), "band swaps", swaps)
+            o, l = oracle.sparse_attention(qg, K2, V2, gi[b, h], default_scale(wl.d))
+            check_attention(go[b, h * G:(h + 1) * G], o, "layer %d unit %s" % (layer, (b, h)))
+            assert np.all(np.abs(gl[b, h * G:(h + 1) * G] - l) <= 1e-3 * (1 + np.abs(l)))
+        del inp, kp, out, lse
+
+
+def test_full_size_gated_hybrid_on_sampled_units():
+    """lisa_32k at its real size (B16, Hq32, Hkv8, N32768, M1024): the sparse
+    branch is the decode step as bench.py launches it; the linear branch's
+    state is prefilled over the rows before the new token (fp32, torch, as a
+    serving stack would have carried it) and sparse_attn_linear_gate adds the
+    new token and mixes the two branches.  On the first and last unit and a
+    seeded one: the index set against the top-M contract, the updated state
+    against the oracle's sums over all N rows, and the mixed output against
+    the oracle's gate applied to its own sparse attention at the same
+    indices."""
+    wl = WORKLOADS["lisa_32k"]
+    B, Hq, Hkv, d, N, G = wl.B, wl.Hq, wl.Hkv, wl.d, wl.N, wl.G
+    _say("case: full-size gated hybrid", wl.name)
+    inp = make_decode_inputs(wl, seed=5, device="cuda")
+    picks = _picks(wl, np.random.default_rng(19))
+    saved = {(b, h): (f64(inp.k_cache[b, h]), f64(inp.v_cache[b, h])) for b, h in picks}
+    S = torch.empty(B, Hkv, d, d, dtype=torch.float32, device="cuda")
+    z = torch.empty(B, Hkv, d, dtype=torch.float32, device="cuda")
+    for b in range(B):
+        Kf = inp.k_cache[b, :, :N - 1].float()
+        phi = torch.where(Kf > 0, Kf + 1.0, torch.exp(torch.clamp(Kf, max=0.0)))
+        S[b] = torch.matmul(phi.transpose(1, 2).contiguous(), inp.v_cache[b, :, :N - 1].float())
+        z[b] = phi.sum(dim=1)
+    del Kf, phi
+    sh = _shape_of(B, Hq, Hkv, d, wl.r, N)
+    ws = sa.alloc_workspace(sh, N, wl.M)
+    kp, idx, o_sp, lse = _bench_sequence(inp, sh, wl.M, ws)
+    out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device="cuda")
+    sa.sparse_attn_linear_gate(sh, inp.q, inp.k_new.view(B, Hkv, d), inp.v_new.view(B, Hkv, d),
+                               S, z, inp.w_gate, o_sp, out, True)
+    torch.cuda.synchronize()
+    gi, go = idx.cpu().numpy(), f64(out)
+    q64, w64 = f64(inp.q), inp.w_gate.double().cpu().numpy()
+    for b, h in picks:
+        K2, V2, kp2, P64h = _unit_after_append(inp, *saved[(b, h)], b, h)
+        qg = q64[b, h * G:(h + 1) * G]
+        s = oracle.index_scores(oracle.indexer_query(qg, P64h), kp2[:N])
+        swaps = check_topm_unit(gi[b, h], s, wl.M, N)
+        _say("  unit", (b, h), "band swaps", swaps)
+        S64, z64 = oracle.linear_state(K2[:N], V2[:N])
+        # fp32 sums of N terms in blocks: error well inside 64 ulp of the sum
+        # of the terms' magnitudes
+        phi_abs = np.abs(oracle.elu_plus_one(K2[:N]))
+        tol_S = 64 * 2.0 ** -24 * (phi_abs.T @ np.abs(V2[:N]))
+        assert np.all(np.abs(S[b, h].cpu().double().numpy() - S64) <= tol_S + 1e-6)
+        tol_z = 64 * 2.0 ** -24 * phi_abs.sum(axis=0)
+        assert np.all(np.abs(z[b, h].cpu().double().numpy() - z64) <= tol_z)
+        o_sp64, _ = oracle.sparse_attention(qg, K2, V2, gi[b, h], default_scale(d))
+        want, _, g = oracle.linear_gate(qg, S64, z64, w64[h * G:(h + 1) * G], o_sp64)
+        assert np.all((g > 0.2) & (g < 0.8)), g      # both branches weigh in
+        check_attention(go[b, h * G:(h + 1) * G], want, "hybrid unit %s" % ((b, h),))
+
+
 # ------------------------------------------------------------------ exact fallbacks
 
 def _topm_check_against_oracle(q, P, kp, M, n_max, lens=None):

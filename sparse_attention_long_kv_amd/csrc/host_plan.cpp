@@ -30,7 +30,10 @@ int plan_topm(const sa_shape& s, int n_max, int M, TopmPlan* p) {
   const int64_t units = (int64_t)s.batch * s.num_kv_heads;
   int chunk = kMaxChunk;
   // shrink chunks until the grid fills the chip, but never below one block
-  while (chunk > kMinChunk && units * ceil_div(n_max, chunk) < kTargetBlocks) chunk >>= 1;
+  // nor into more than kMaxSplits chunks per unit
+  while (chunk > kMinChunk && units * ceil_div(n_max, chunk) < kTargetBlocks &&
+         ceil_div(n_max, chunk / 2) <= kMaxSplits)
+    chunk >>= 1;
   const int64_t splits = ceil_div(n_max, chunk);
   if (splits > kMaxSplits) return SA_ERR_UNSUPPORTED;
   p->units = (int)units;

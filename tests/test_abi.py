@@ -78,6 +78,24 @@ def test_workspace_size_rules():
     assert sa.sparse_attn_workspace_size(bad, 100, 10) == 0
 
 
+@pytest.mark.parametrize("units", [(1, 1), (2, 4), (32, 8)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_workspace_covers_every_context_the_shape_allows(units, d):
+    """Every n_max up to the largest capacity the shape admits (int32 byte
+    offsets within a unit's cache) has a workspace, whatever the number of
+    units: the chunk planning never asks for more chunks than a unit may have.
+    Past that capacity the shape itself is unsupported."""
+    B, Hkv = units
+    top = (2 ** 31 - 1) // (d * 2)
+    for n in (1, 2047, 524288, 524289, 600000, 1 << 22, top):
+        sh = sa.make_shape(B, 4 * Hkv, Hkv, d, 32, n)
+        for M in sorted({1, min(n, 2048), min(n, 6145)}):
+            ws = sa.sparse_attn_workspace_size(sh, n, M)
+            assert ws > 0 and ws % 256 == 0, (units, d, n, M)
+    assert sa.sparse_attn_workspace_size(sa.make_shape(B, 4 * Hkv, Hkv, d, 32, top + 1),
+                                         top + 1, 2048) == 0
+
+
 _FAKE = 1 << 20      # aligned, never dereferenced (every call below fails a check)
 
 

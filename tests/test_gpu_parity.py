@@ -161,6 +161,12 @@ TOPM_CASES = {
     # chunk, loaded as zero) -- none of those may be kept
     "low_bound": (1, 4, 1, 128, 32, 16384, 16384, None, 4096),
     "low_bound_r16": (2, 8, 2, 64, 16, 12288, 12288, [12288, 10000], 3000),
+    # the limits of the filter path (n_max <= 2^19, M <= 6144) and one past
+    # each, where the fused selection takes the chunk-exact path instead
+    "filter_max_n": (1, 4, 1, 128, 32, 524288, 524288, None, 2048),
+    "past_filter_n": (1, 4, 1, 64, 16, 600000, 600000, None, 2048),
+    "filter_max_m": (1, 8, 2, 128, 32, 65536, 65536, None, 6144),
+    "past_filter_m": (1, 8, 2, 128, 32, 65536, 65536, None, 6145),
 }
 
 
@@ -785,14 +791,22 @@ def test_select_attend_stage_equals_merge_then_attend(B, Hq, Hkv, d, r, N, M):
         check_attention(f64(out)[b, h * G:(h + 1) * G], o, "unit (%d, %d)" % (b, h))
 
 
-@pytest.mark.parametrize("name,N,T,lens", [("tiny", None, 1, None),
-                                           ("gqa7_16k", 8192, 1, [8192, 5000, 1, 0, 8192, 300,
-                                                                  8100, 7000]),
-                                           ("longctx_128k", 16384, 2, None)])
-def test_decode_step_equals_the_three_calls(name, N, T, lens):
+@pytest.mark.parametrize("name,N,T,lens,M", [
+    ("tiny", None, 1, None, None),
+    ("gqa7_16k", 8192, 1, [8192, 5000, 1, 0, 8192, 300, 8100, 7000], None),
+    ("longctx_128k", 16384, 2, None, None),
+    # at the filter path's limits (one fused select + attend launch) and past
+    # them (chunk-exact selection, then the attention launch)
+    ("tiny", 524288, 1, None, 6144),
+    ("tiny", 600000, 1, None, 2048),
+    ("tiny", 65536, 1, None, 6145),
+])
+def test_decode_step_equals_the_three_calls(name, N, T, lens, M):
     """sparse_attn_decode_step (fused prologue) writes the same caches, idx,
     out and lse, bit for bit, as append_kv + index_topm + decode."""
     wl = WORKLOADS[name] if N is None else scaled(WORKLOADS[name], N=N, B=min(8, WORKLOADS[name].B))
+    if M is not None:
+        wl = scaled(wl, M=M)
     _say("case: decode step", wl.name, wl.N, "T=%d" % T)
     sh = _shape_of(wl.B, wl.Hq, wl.Hkv, wl.d, wl.r, wl.N)
     res = []
@@ -804,6 +818,11 @@ def test_decode_step_equals_the_three_calls(name, N, T, lens):
         pos = (inp.seq_lens - T).clamp(min=0).to(torch.int32)
         kp = torch.empty(wl.B, wl.Hkv, wl.N, wl.r, dtype=torch.uint8, device="cuda")
         sa.sparse_attn_project_keys(sh, inp.k_cache, inp.P, 0, wl.N, kp)
+        if not fused:        # the generator's rows of the units the oracle checks
+            picks = sorted({(0, 0), (wl.B - 1, wl.Hkv - 1)})
+            saved = {(b, h): (f64(inp.k_cache[b, h]), f64(inp.v_cache[b, h])) for b, h in picks}
+            host = (f64(inp.q), inp.P.double().cpu().numpy(), inp.seq_lens.cpu().numpy(),
+                    pos.cpu().numpy(), f64(k_new), f64(v_new))
         ws = sa.alloc_workspace(sh, wl.N, wl.M)
         idx = torch.full((wl.B, wl.Hkv, wl.M), -9, dtype=torch.int32, device="cuda")
         out = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.bfloat16, device="cuda")
@@ -823,3 +842,24 @@ def test_decode_step_equals_the_three_calls(name, N, T, lens):
         del inp
     for x, y in zip(res[0], res[1]):
         assert torch.equal(x, y)
+    # and the oracle, on the first and last unit
+    q64, P64, lens_h, pos_h, kn, vn = host
+    gi, go = res[1][3].cpu().numpy(), f64(res[1][4])
+    G = wl.G
+    for b, h in picks:
+        K0, V0 = saved[(b, h)]
+        L = int(lens_h[b])
+        if L == 0:
+            continue
+        kp0 = oracle.project_keys(K0, P64[h])[None, None]
+        K2, V2, kp2 = oracle.append_kv(K0[None, None], V0[None, None], kp0, pos_h[b:b + 1],
+                                       kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1], P64[h:h + 1])
+        qg = q64[b, h * G:(h + 1) * G]
+        oi, oo, _, s = oracle.decode_step_unit(qg, K2[0, 0], V2[0, 0], kp2[0, 0], P64[h], L,
+                                               wl.M, default_scale(wl.d))
+        swaps = check_topm_unit(gi[b, h], s, wl.M, L)
+        _say("  unit", (b, h), "band swaps", swaps)
+        if not np.array_equal(gi[b, h], oi):
+            oo, _ = oracle.sparse_attention(qg, K2[0, 0], V2[0, 0], gi[b, h],
+                                            default_scale(wl.d))
+        check_attention(go[b, h * G:(h + 1) * G], oo, "unit %s" % ((b, h),))

@@ -109,6 +109,150 @@ def measure_baselines(sa, torch, inp, wl, sh, kp, idx, ws, timer, stream, reps):
     }
 
 
+def _host_timed(torch, fn, reps):
+    """Microseconds per call of fn on the host clock, synchronised on both
+    sides of `reps` back-to-back calls (after two untimed ones)."""
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    return 1e6 * (time.perf_counter() - t0) / reps
+
+
+def measure_extensions(sa, torch, dev, reps):
+    """The two extensions at their own workloads, outside the timed region.
+
+    Cross-layer index reuse (IndexCache pages: layers that reuse the indices
+    of an earlier layer skip its indexer): eight layers of reuse8_64k with
+    the indexer and top-M on layers 0 and 4 only, the other layers appending
+    their token and attending over their source layer's indices, against the
+    same eight layers each running the whole decode step.
+
+    Gated hybrid (LISA items: a linear-attention branch merged with the
+    sparse one through a gate): the decode step of lisa_32k followed by
+    sparse_attn_linear_gate (state update and mix), against the decode step
+    alone and against full attention over every cached row.  The linear state
+    holds arbitrary values here (its cost does not depend on them)."""
+    from workloads import WORKLOADS, make_decode_inputs, default_scale
+    res = {}
+
+    wl = WORKLOADS["reuse8_64k"]
+    B, Hq, Hkv, d, N, r, M = wl.B, wl.Hq, wl.Hkv, wl.d, wl.N, wl.r, wl.M
+    sh = sa.make_shape(B, Hq, Hkv, d, r, N)
+    layers = [make_decode_inputs(wl, seed=0, layer=l, device=dev) for l in range(wl.layers)]
+    kps = []
+    for inp in layers:
+        kp = torch.empty(B, Hkv, N, r, dtype=torch.uint8, device=dev)
+        sa.sparse_attn_project_keys(sh, inp.k_cache, inp.P, 0, N, kp)       # prefill
+        kps.append(kp)
+    ws = sa.alloc_workspace(sh, N, M, device=dev)
+    idx = [torch.empty(B, Hkv, M, dtype=torch.int32, device=dev) for _ in range(wl.layers)]
+    out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)
+    scale = default_scale(d)
+    stages = (sa.SA_STEP_APPEND_BOUND, sa.SA_STEP_CANDIDATES, sa.SA_STEP_SELECT_ATTEND)
+
+    def full(l):
+        x = layers[l]
+        for st in stages:
+            sa.sparse_attn_decode_step_stage(sh, st, x.pos, x.k_new, x.v_new, x.q, x.P,
+                                             x.k_cache, x.v_cache, kps[l], x.seq_lens, N, M,
+                                             scale, idx[l], out, None, ws)
+
+    def reused(l, src):
+        x = layers[l]
+        sa.sparse_attn_append_kv(sh, x.pos, x.k_new, x.v_new, x.P, x.k_cache, x.v_cache, kps[l])
+        sa.sparse_attn_decode(sh, x.q, x.k_cache, x.v_cache, idx[src], M, scale, out, None, ws)
+
+    def step_reuse():
+        for l in range(wl.layers):
+            src = max(f for f in wl.full_layers if f <= l)
+            if l == src:
+                full(l)
+            else:
+                reused(l, src)
+
+    def step_every_layer():
+        for l in range(wl.layers):
+            full(l)
+
+    t_reuse = _host_timed(torch, step_reuse, reps)
+    t_all = _host_timed(torch, step_every_layer, reps)
+    bk = algorithmic_bytes(wl)
+    units = B * Hkv
+    layer_full = sum(bk.values())
+    layer_reused = (bk["append_bound"] + units * M * 4 + units * M * d * 2 * 2
+                    + 2 * B * Hq * d * 2)                 # idx read, rows, q, out
+    n_full = len(wl.full_layers)
+    bytes_reuse = n_full * layer_full + (wl.layers - n_full) * layer_reused
+    bytes_all = wl.layers * layer_full
+    res["index_reuse"] = {
+        "workload": "reuse8_64k: 8 layers of B%d Hq%d Hkv%d d%d N%d r%d M%d, indexer on layers %s"
+                    % (B, Hq, Hkv, d, N, r, M, ",".join(map(str, wl.full_layers))),
+        "reps": reps,
+        "us_per_8_layer_step": round(t_reuse, 1),
+        "us_per_8_layer_step_every_layer_indexed": round(t_all, 1),
+        "speedup": round(t_all / t_reuse, 3),
+        "bytes_per_8_layer_step": bytes_reuse,
+        "bytes_per_8_layer_step_every_layer_indexed": bytes_all,
+        "hbm_gbps": round(bytes_reuse / (t_reuse * 1e-6) / 1e9, 1),
+    }
+    del layers, kps, ws, idx
+    torch.cuda.empty_cache()
+
+    wl = WORKLOADS["lisa_32k"]
+    B, Hq, Hkv, d, N, r, M = wl.B, wl.Hq, wl.Hkv, wl.d, wl.N, wl.r, wl.M
+    sh = sa.make_shape(B, Hq, Hkv, d, r, N)
+    x = make_decode_inputs(wl, seed=0, device=dev)
+    kp = torch.empty(B, Hkv, N, r, dtype=torch.uint8, device=dev)
+    sa.sparse_attn_project_keys(sh, x.k_cache, x.P, 0, N, kp)
+    ws = sa.alloc_workspace(sh, N, M, device=dev)
+    dws = torch.empty(sa.sparse_attn_dense_workspace_size(sh, N), dtype=torch.uint8, device=dev)
+    idx1 = torch.empty(B, Hkv, M, dtype=torch.int32, device=dev)
+    o_sp = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(o_sp)
+    S = torch.zeros(B, Hkv, d, d, dtype=torch.float32, device=dev)
+    z = torch.ones(B, Hkv, d, dtype=torch.float32, device=dev)
+    scale = default_scale(d)
+
+    def sparse_step():
+        for st in stages:
+            sa.sparse_attn_decode_step_stage(sh, st, x.pos, x.k_new, x.v_new, x.q, x.P,
+                                             x.k_cache, x.v_cache, kp, x.seq_lens, N, M, scale,
+                                             idx1, o_sp, None, ws)
+
+    def gate():
+        sa.sparse_attn_linear_gate(sh, x.q, x.k_new.view(B, Hkv, d), x.v_new.view(B, Hkv, d),
+                                   S, z, x.w_gate, o_sp, out, True)
+
+    def hybrid_step():
+        sparse_step()
+        gate()
+
+    t_sparse = _host_timed(torch, sparse_step, reps)
+    t_hybrid = _host_timed(torch, hybrid_step, reps)
+    t_dense = _host_timed(torch, lambda: sa.sparse_attn_dense_decode(
+        sh, x.q, x.k_cache, x.v_cache, x.seq_lens, N, scale, o_sp, None, dws), reps)
+    units = B * Hkv
+    gate_bytes = (units * d * d * 4 * 2 + units * d * 4 * 2 + 2 * B * Hq * d * 2
+                  + units * 2 * d * 2 + Hq * d * 4 + B * Hq * d * 2)
+    hybrid_bytes = sum(algorithmic_bytes(wl).values()) + gate_bytes
+    res["gated_hybrid"] = {
+        "workload": "lisa_32k: B%d Hq%d Hkv%d d%d N%d r%d M%d, fp32 linear state %dx%d per KV "
+                    "head" % (B, Hq, Hkv, d, N, r, M, d, d),
+        "reps": reps,
+        "us_per_hybrid_step": round(t_hybrid, 1),
+        "us_per_sparse_step": round(t_sparse, 1),
+        "us_full_attention": round(t_dense, 1),
+        "hybrid_speedup_over_full_attention": round(t_dense / t_hybrid, 2),
+        "bytes_per_hybrid_step": hybrid_bytes,
+        "hbm_gbps": round(hybrid_bytes / (t_hybrid * 1e-6) / 1e9, 1),
+    }
+    return res
+
+
 def algorithmic_bytes(wl):
     """Bytes the method itself must move per step, by call: every input read
     once and every output written once (workspace traffic is not counted)."""
@@ -336,6 +480,9 @@ def main(argv=None):
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="steps timed one by one after a 2 GiB read flush, after the "
                          "timed region (0: skip)")
+    ap.add_argument("--ext-reps", type=int, default=10,
+                    help="steps timed per extension workload (index reuse over eight "
+                         "layers, gated hybrid); 0: skip them")
     ap.add_argument("--baseline-reps", type=int, default=5,
                     help="calls timed per comparison baseline (0: skip them)")
     ap.add_argument("--calibration-mib", type=int, default=0,
@@ -524,6 +671,13 @@ def main(argv=None):
     if a.cpu_units > 0:
         print("bench: cpu baseline (%d units)" % a.cpu_units, file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp, wl, a.cpu_units)
+    if a.ext_reps > 0:
+        print("bench: extensions", file=sys.stderr, flush=True)
+        del inp, kp, ws, idx, out
+        torch.cuda.empty_cache()
+        res["extensions"] = measure_extensions(sa, torch, dev, a.ext_reps)
+    else:
+        res["extensions"] = None
     print(json.dumps(res), flush=True)
 
 

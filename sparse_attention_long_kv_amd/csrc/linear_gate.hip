@@ -7,9 +7,12 @@
 //   S += phi(k) v^T,  z += phi(k)                      (update_state != 0)
 //   o_lin = (phi(q)^T S) / (phi(q)^T z),  g = sigmoid(w . q)
 //   out = g * o_sparse + (1 - g) * o_lin
-// One workgroup per (batch row, KV head); thread (row block, column j) streams
-// its slice of S once (read, update, write back) and accumulates the G
-// numerators for column j.
+// One 1024-thread workgroup per (batch row, KV head).  Thread (row block rb,
+// column j) holds rows rb*RPT .. rb*RPT + RPT - 1 of column j of S: it issues
+// all of their loads first, then updates and writes them back and adds their
+// contributions to the G numerators of column j in row order; the row blocks'
+// partial numerators are then added in block order.  Denominators and gates
+// are fixed-order sums over d formed while the loads are in flight.
 #include "device_common.hpp"
 #include "kernels.h"
 
@@ -21,49 +24,65 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p, size_t i) {
   return __uint_as_float((uint32_t)p[i] << 16);
 }
 
+constexpr int kGateThreads = 1024;
+
 template <int D, int G>
-__global__ __launch_bounds__(256) void linear_gate_kernel(
+__global__ __launch_bounds__(kGateThreads) void linear_gate_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, float* __restrict__ S, float* __restrict__ z,
     const float* __restrict__ w_gate, const uint16_t* __restrict__ o_sparse,
     uint16_t* __restrict__ out, int Hq, int Hkv, int update) {
-  constexpr int kRowBlocks = kBlock / D;        // 2 (d=128) or 4 (d=64)
-  constexpr int kRows = D / kRowBlocks;
+  constexpr int NT = kGateThreads;
+  constexpr int RB = NT / D;                    // row blocks: 8 (d = 128) or 16 (d = 64)
+  constexpr int RPT = D / RB;                   // rows per thread: 16 or 4
   __shared__ float phk[D], vn[D], zs[D];
   __shared__ float phq[G][D];
-  __shared__ float num[kRowBlocks][G][D];
+  __shared__ float num[RB][G][D];
   __shared__ float den[G], gate[G];
 
   const int u = blockIdx.x;
   const int b = u / Hkv, h = u % Hkv;
   const int tid = threadIdx.x;
-  const uint16_t* qb = q + ((size_t)b * Hq + (size_t)h * G) * D;
-
-  for (int i = tid; i < D; i += kBlock) {
-    const float kf = bf16_at(k_new, (size_t)u * D + i);
-    phk[i] = phi(kf);
-    vn[i] = bf16_at(v_new, (size_t)u * D + i);
-  }
-  for (int t = tid; t < G * D; t += kBlock) phq[t / D][t % D] = phi(bf16_at(qb, t));
-  __syncthreads();
-  float* zu = z + (size_t)u * D;
-  for (int i = tid; i < D; i += kBlock) {
-    float zi = zu[i];
-    if (update) {
-      zi = zi + phk[i];
-      zu[i] = zi;
-    }
-    zs[i] = zi;
-  }
-
   const int j = tid % D, rb = tid / D;
+  const uint16_t* qb = q + ((size_t)b * Hq + (size_t)h * G) * D;
+  float* Su = S + (size_t)u * D * D;
+
+  float sv[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) sv[r] = Su[(size_t)(rb * RPT + r) * D + j];
+  float* zu = z + (size_t)u * D;
+  if (tid < D) {
+    const float pk = phi(bf16_at(k_new, (size_t)u * D + tid));
+    phk[tid] = pk;
+    vn[tid] = bf16_at(v_new, (size_t)u * D + tid);
+    float zi = zu[tid];
+    if (update) {
+      zi = zi + pk;
+      zu[tid] = zi;
+    }
+    zs[tid] = zi;
+  }
+  for (int t = tid; t < G * D; t += NT) phq[t / D][t % D] = phi(bf16_at(qb, t));
+  __syncthreads();
+
+  if (tid < G) {                                // denominators, one thread per head
+    float dsum = 0.0f;
+    for (int i = 0; i < D; ++i) dsum = __builtin_fmaf(phq[tid][i], zs[i], dsum);
+    den[tid] = dsum;
+  } else if (tid >= 64 && tid < 64 + G) {       // gates
+    const int g = tid - 64;
+    const float* wg = w_gate + (size_t)(h * G + g) * D;
+    float x = 0.0f;
+    for (int i = 0; i < D; ++i) x = __builtin_fmaf(wg[i], bf16_at(qb, (size_t)g * D + i), x);
+    gate[g] = 1.0f / (1.0f + expf(-x));
+  }
   float acc[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) acc[g] = 0.0f;
-  float* Su = S + (size_t)u * D * D;
-  for (int r = 0; r < kRows; ++r) {
-    const int i = rb * kRows + r;
-    float sij = Su[(size_t)i * D + j];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const int i = rb * RPT + r;
+    float sij = sv[r];
     if (update) {
       sij = __builtin_fmaf(phk[i], vn[j], sij);
       Su[(size_t)i * D + j] = sij;
@@ -75,25 +94,11 @@ __global__ __launch_bounds__(256) void linear_gate_kernel(
   for (int g = 0; g < G; ++g) num[rb][g][j] = acc[g];
   __syncthreads();
 
-  // denominators and gates: one thread per head, fixed order
-  if (tid < G) {
-    float dsum = 0.0f;
-    for (int i = 0; i < D; ++i) dsum = __builtin_fmaf(phq[tid][i], zs[i], dsum);
-    den[tid] = dsum;
-  } else if (tid >= 64 && tid < 64 + G) {
-    const int g = tid - 64;
-    const float* wg = w_gate + (size_t)(h * G + g) * D;
-    float x = 0.0f;
-    for (int i = 0; i < D; ++i) x = __builtin_fmaf(wg[i], bf16_at(qb, (size_t)g * D + i), x);
-    gate[g] = 1.0f / (1.0f + expf(-x));
-  }
-  __syncthreads();
-
-  for (int t = tid; t < G * D; t += kBlock) {
+  for (int t = tid; t < G * D; t += NT) {
     const int g = t / D, jj = t % D;
     float nsum = 0.0f;
 #pragma unroll
-    for (int r = 0; r < kRowBlocks; ++r) nsum += num[r][g][jj];
+    for (int r = 0; r < RB; ++r) nsum += num[r][g][jj];
     const float olin = nsum / den[g];
     const size_t oi = ((size_t)b * Hq + (size_t)h * G + g) * D + jj;
     const float osp = bf16_at(o_sparse, oi);
@@ -106,7 +111,7 @@ template <int D>
 static void launch_lin_d(const LaunchCommon& c, const void* q, const void* k_new,
                          const void* v_new, float* S, float* z, const float* w,
                          const void* o_sp, void* out, int update) {
-  const dim3 grid(c.units), block(kBlock);
+  const dim3 grid(c.units), block(kGateThreads);
   switch (c.G) {
 #define SA_CASE(GG)                                                                        \
   case GG:                                                                                 \

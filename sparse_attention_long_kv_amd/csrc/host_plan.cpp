@@ -145,10 +145,17 @@ int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* p) {
   off = align_up(off + (size_t)units * sizeof(uint32_t), kAlign);
   p->off_qt = off;
   off = align_up(off + (size_t)units * 32 * sizeof(float), kAlign);
+  // A wave list that fills up goes to the unit's spill pool (one atomic
+  // reservation per full list), which follows the unit's chunk slots; its
+  // count follows the unit's chunk counts.  Half of the merge's capacity:
+  // with the ~3M kept keys of a unit that leaves room for clusters of several
+  // thousand high-scoring positions.
+  p->spill_cap = kFilterSlots / 2;
+  p->ustride = splits * p->cslots + p->spill_cap;
   p->off_cnt = off;
-  off = align_up(off + (size_t)units * splits * sizeof(int32_t), kAlign);
+  off = align_up(off + (size_t)units * (splits + 1) * sizeof(int32_t), kAlign);
   p->off_cand = off;                       // (key, position) pairs
-  off = align_up(off + (size_t)units * splits * p->cslots * 2 * sizeof(uint32_t), kAlign);
+  off = align_up(off + (size_t)units * p->ustride * 2 * sizeof(uint32_t), kAlign);
   p->end = off;
   return SA_OK;
 }

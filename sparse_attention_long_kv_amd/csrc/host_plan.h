@@ -65,6 +65,8 @@ struct FilterPlan {
   int splits;       // chunks per unit
   int cap;          // slots per wave list (power of two)
   int cslots;       // candidate slots per chunk = 8 * cap (one list per wave)
+  int spill_cap;    // slots of the unit's spill pool (lists that filled up mid-chunk)
+  int64_t ustride;  // pairs per unit: splits * cslots chunk slots, then the spill pool
   size_t off_thr, off_qt, off_cnt, off_cand, end;
 };
 

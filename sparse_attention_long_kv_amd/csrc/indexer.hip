@@ -296,7 +296,7 @@ __device__ void pick_bin(Sh& sh, int width, uint32_t target, uint32_t& path, uin
 // for each key this thread owns.  Keys off `path` (and invalid ones) count
 // into the lane's private dummy bin so the atomics need no branch.
 template <int NT, class Sh, class Visit>
-__device__ void radix_level(Sh& sh, int top, int lo, uint32_t target, uint32_t& path,
+__device__ __forceinline__ void radix_level(Sh& sh, int top, int lo, uint32_t target, uint32_t& path,
                             uint32_t& above, Visit visit) {
   const int width = top - lo;
   const uint32_t digit_mask = (1u << width) - 1u;
@@ -355,7 +355,7 @@ __device__ void rank_in_list(Sh& sh, uint32_t n, uint32_t rank, uint32_t& t, uin
 // Returns t (the target-th largest key), need = target - #keys > t (how many
 // keys equal to t are selected) and eq = #keys == t.
 template <int NT, class Sh, class Visit>
-__device__ void resolve_bin(Sh& sh, uint32_t target, uint32_t path, uint32_t above,
+__device__ __forceinline__ void resolve_bin(Sh& sh, uint32_t target, uint32_t path, uint32_t above,
                             uint32_t& t_out, uint32_t& need_out, uint32_t& eq_out, Visit visit) {
   const int tid = threadIdx.x;
   const uint32_t b1 = path;
@@ -415,7 +415,7 @@ __device__ void resolve_bin(Sh& sh, uint32_t target, uint32_t path, uint32_t abo
 
 // Exact threshold search from the first-level histogram in sh.hist.
 template <int NT, class Sh, class Visit>
-__device__ void finish_threshold(Sh& sh, uint32_t target, uint32_t& t_out, uint32_t& need_out,
+__device__ __forceinline__ void finish_threshold(Sh& sh, uint32_t target, uint32_t& t_out, uint32_t& need_out,
                                  uint32_t& eq_out, Visit visit) {
   uint32_t path = 0, above = 0;
   pick_bin<NT>(sh, kDigitBits, target, path, above);
@@ -971,11 +971,15 @@ struct FilterArgs {
   const float* P;
   const uint8_t* kp;
   const int32_t* seq_lens;
-  int n_max, Ncap, Hq, Hkv, G, M, S, chunk, cap, cslots;
+  int n_max, Ncap, Hq, Hkv, G, M, S, chunk, cap, cslots, spill_cap;
+  int64_t ustride;   // pairs per unit in cand: S * cslots, then spill_cap
   uint32_t* thr;     // [units]
   float* qt;         // [units][32] indexer queries (written by the bound stage)
-  int32_t* cnt;      // [units][S] kept positions per chunk, -1 when a wave list overflowed
-  uint2* cand;       // [units][S][cslots] (key, position) of the kept positions, any order
+  int32_t* cnt;      // [units][S + 1] kept positions per chunk (-1 when a wave list
+                     // overflowed), then the pairs reserved in the spill pool (zeroed by
+                     // the bound stage)
+  uint2* cand;       // per unit: [S][cslots] (key, position) of the kept positions (any
+                     // order), then the spill pool [spill_cap] of lists that filled up
   int32_t* idx;
 };
 
@@ -987,6 +991,9 @@ static_assert(kFilterMaxCap * kFilterWaves <= kFilterSlots, "a chunk's slots fit
 constexpr int kFilterMaxSplits = kFilterSlots / (kFilterWaves * kFilterMinCap);   // 16
 static_assert(kFilterMaxSplits <= kWave && (kFilterMaxSplits & (kFilterMaxSplits - 1)) == 0,
               "one wave scans the chunk counts; chunks are found by bisection");
+// bisection table of the merge: the chunks' starts, then the spill pool's
+constexpr int kMergeStarts = 2 * kFilterMaxSplits;
+static_assert(kMergeStarts <= kWave, "one wave writes the table");
 
 __device__ __forceinline__ int unit_len(const int32_t* seq_lens, int b, int n_max) {
   return seq_lens ? min(max(seq_lens[b], 0), n_max) : n_max;
@@ -1022,6 +1029,7 @@ __device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<k
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int tid = threadIdx.x;
   const int len = unit_len(a.seq_lens, b, a.n_max);
+  if (tid == 0) a.cnt[(size_t)u * (a.S + 1) + a.S] = 0;   // the filter reserves spill from 0
   for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
   // blocks of 8 consecutive positions, evenly spread over [0, len); the row
   // loads go out first
@@ -1212,7 +1220,8 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
   const int base = c * a.chunk;
   const int nv = min(max(len - base, 0), a.chunk);
   const int pend = base + nv;                         // this chunk's valid positions end here
-  int32_t* cnt = a.cnt + (size_t)u * a.S + c;
+  int32_t* cnt = a.cnt + (size_t)u * (a.S + 1) + c;
+  uint32_t* spill_cnt = reinterpret_cast<uint32_t*>(a.cnt + (size_t)u * (a.S + 1) + a.S);
   if (len <= a.M || nv == 0) {                        // block-uniform
     if (threadIdx.x == 0) *cnt = 0;
     return;
@@ -1220,7 +1229,7 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
   // key >= thr  <=>  score >= thrf for every score the chains can produce
   // (no NaN; -0 and +0 share the key of +0, and -0 >= +0 holds)
   const float thrf = key_score(a.thr[u]);
-  uint2* lc = a.cand + ((size_t)u * a.S + c) * a.cslots;
+  uint2* lc = a.cand + (size_t)u * a.ustride + (size_t)c * a.cslots;
   // this chunk's rows only: loads past the valid positions return zero
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(a.kp + ((size_t)u * a.Ncap + base) * R, (uint32_t)nv * R);
@@ -1252,7 +1261,23 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
   // scalar registers (an FMA takes one scalar operand), saving 32 VGPRs
   float qlo[16], qhi[16];
   query_halves<R>(a.qt + (size_t)u * 32, qlo, qhi);
-  uint32_t wc = 0;                                    // positions this wave kept so far
+  uint32_t wc = 0;                                    // positions in this wave's list
+  // A full list goes to the unit's spill pool (clustered high scores): one
+  // lane reserves its slots with an atomic, the wave copies it out, and the
+  // list starts again.  A pool too small for it is left counting past its
+  // capacity, which sends the merge to the exact fallback.
+  uint2* spill_u = a.cand + (size_t)u * a.ustride + (size_t)a.S * a.cslots;
+  auto spill_list = [&]() {
+    uint32_t at = 0u;
+    if (lane == 0) at = atomicAdd(spill_cnt, wc);
+    at = (uint32_t)__shfl((int)at, 0, kWave);
+    if (at + wc <= (uint32_t)a.spill_cap) {
+      for (int j = lane; j < (int)wc; j += kWave)
+        spill_u[at + j] =
+            make_uint2(score_key(__uint_as_float(sk[w][j]) + 0.0f), (uint32_t)sp[w][j]);
+    }
+    wc = 0;
+  };
   auto score_batch = [&](const Batch& bt, int i0) {
 #pragma unroll
     for (int x = 0; x < kBatch; ++x) {
@@ -1264,13 +1289,15 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
       const bool ge = s >= thrf, in = p < pend;
       const bool sel = ge && in;
       const uint64_t m = ballot(ge) & ballot(in);     // (two compares, no select)
+      const uint32_t n = (uint32_t)popc64(m);
+      if (wc + n > (uint32_t)a.cap) spill_list();     // wave-uniform, rare
       const uint32_t slot = wc + __builtin_amdgcn_mbcnt_hi(
                                      (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
       if (sel && slot < (uint32_t)a.cap) {
         sk[w][slot] = __float_as_uint(s);               // keyed when written out
         sp[w][slot] = p;
       }
-      wc += (uint32_t)popc64(m);
+      wc += n;
     }
   };
   // The last batch may reach past the chunk's rows (kBatch need not divide
@@ -1313,7 +1340,7 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
 // Selection: every key > t and, of the keys == t, the `need` lowest positions
 // (found as the top `need` of the keys ~pos).  Fills idx[0, M) completely.
 template <int NT, class Visit>
-__device__ void emit_bitmap(SelectShared<NT>& sh, uint32_t* bm, int len, uint32_t t,
+__device__ __forceinline__ void emit_bitmap(SelectShared<NT>& sh, uint32_t* bm, int len, uint32_t t,
                             uint32_t need, uint32_t eq, int M, int32_t* idx_u, Visit visit) {
   const int tid = threadIdx.x, lane = lane_id();
   const int words = (len + 31) >> 5;
@@ -1495,7 +1522,7 @@ __device__ __forceinline__ void select_unit_streaming(const FilterArgs& a, Selec
 struct MergeShared {
   SelectShared<kMergeThreads> sh;
   uint32_t bm[kBitmapWords];        // used by the streaming fallback only
-  uint32_t start_s[kFilterMaxSplits];
+  uint32_t start_s[kMergeStarts];
   uint32_t red[kMergeThreads / kWave];
 };
 
@@ -1525,15 +1552,17 @@ __device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShar
     __syncthreads();
     return;
   }
-  // Per-chunk counts (S <= 16): one wave forms their exclusive prefix; -1
-  // marks a chunk whose lists overflowed.
+  // Per-chunk counts (S <= 16), with the spill pool as chunk S: one wave
+  // forms their exclusive prefix; a chunk whose lists overflowed (-1), a pool
+  // that ran out, or more candidates than the registers hold send the unit
+  // to the exact fallback.
   if (w == 0) {
-    const int c = lane < S ? a.cnt[(size_t)u * S + lane] : 0;
-    const bool over = ballot(c < 0) != 0;
+    const int c = lane <= S ? a.cnt[(size_t)u * (S + 1) + lane] : 0;
+    const bool over = ballot(c < 0 || (lane == S && c > a.spill_cap)) != 0;
     const uint32_t v = (uint32_t)max(c, 0);
     const uint32_t incl = wave_inclusive_scan(v);
-    if (lane < kFilterMaxSplits) start_s[lane] = lane < S ? incl - v : 0xFFFFFFFFu;
-    if (lane == kWave - 1) red[0] = over ? 0u : incl;
+    if (lane < kMergeStarts) start_s[lane] = lane <= S ? incl - v : 0xFFFFFFFFu;
+    if (lane == kWave - 1) red[0] = (over || incl > (uint32_t)(NT * KPT)) ? 0u : incl;
   }
   __syncthreads();
   const uint32_t total = red[0];
@@ -1543,10 +1572,11 @@ __device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShar
     __syncthreads();
     return;
   }
-  // The unit's candidates, numbered g = 0 .. total-1 chunk after chunk; key g
-  // sits in register i = g / NT of thread g % NT.  Only the kept slots are
-  // read: chunk c holds g in [start_c, start_c+1).
-  const uint2* cu = a.cand + (size_t)u * S * a.cslots;
+  // The unit's candidates, numbered g = 0 .. total-1 chunk after chunk and
+  // then through the spill pool (chunk S, stored right after chunk S-1's
+  // slots); key g sits in register i = g / NT of thread g % NT.  Only the kept
+  // slots are read: chunk c holds g in [start_c, start_c+1).
+  const uint2* cu = a.cand + (size_t)u * a.ustride;
   const int nk = (int)((total + NT - 1) / NT);        // rows in use, <= KPT
   uint32_t key[KPT];
   int32_t pos[KPT];
@@ -1558,7 +1588,7 @@ __device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShar
     if (i < nk && g < total) {
       uint32_t c = 0;                                 // last chunk with start_c <= g
 #pragma unroll
-      for (int step = kFilterMaxSplits / 2; step >= 1; step >>= 1)
+      for (int step = kMergeStarts / 2; step >= 1; step >>= 1)
         if (start_s[c + step] <= g) c += step;
       const uint2 kv = cu[(size_t)c * a.cslots + (g - start_s[c])];
       key[i] = kv.x;
@@ -1671,6 +1701,8 @@ hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int 
   a.qt = (float*)(ws + plan.off_qt);
   a.cnt = (int32_t*)(ws + plan.off_cnt);
   a.cand = (uint2*)(ws + plan.off_cand);
+  a.spill_cap = plan.spill_cap;
+  a.ustride = plan.ustride;
   a.idx = idx;
   if ((long)plan.units * plan.splits > INT32_MAX) return hipErrorInvalidConfiguration;
   AppendArgs ap;

@@ -9,9 +9,9 @@
 //   out = g * o_sparse + (1 - g) * o_lin
 // One 1024-thread workgroup per (batch row, KV head).  Thread (row block rb,
 // column j) holds rows rb*RPT .. rb*RPT + RPT - 1 of column j of S: it issues
-// all of their loads first, then updates and writes them back and adds their
-// contributions to the G numerators of column j in row order; the row blocks'
-// partial numerators are then added in block order.  Denominators and gates
+// all of their loads first, then updates and writes them back and forms each
+// head's numerator over them in row order; the row blocks' partial
+// numerators are then added in block order.  Denominators and gates
 // are fixed-order sums over d formed while the loads are in flight.
 #include "device_common.hpp"
 #include "kernels.h"
@@ -76,22 +76,22 @@ __global__ __launch_bounds__(kGateThreads) void linear_gate_kernel(
     for (int i = 0; i < D; ++i) x = __builtin_fmaf(wg[i], bf16_at(qb, (size_t)g * D + i), x);
     gate[g] = 1.0f / (1.0f + expf(-x));
   }
-  float acc[G];
+  if (update) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) acc[g] = 0.0f;
-#pragma unroll
-  for (int r = 0; r < RPT; ++r) {
-    const int i = rb * RPT + r;
-    float sij = sv[r];
-    if (update) {
-      sij = __builtin_fmaf(phk[i], vn[j], sij);
-      Su[(size_t)i * D + j] = sij;
+    for (int r = 0; r < RPT; ++r) {
+      const int i = rb * RPT + r;
+      sv[r] = __builtin_fmaf(phk[i], vn[j], sv[r]);
+      Su[(size_t)i * D + j] = sv[r];
     }
-#pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = __builtin_fmaf(phq[g][i], sij, acc[g]);
   }
+  // one head at a time (its rows in order), so only the rows stay in registers
+#pragma unroll 1
+  for (int g = 0; g < G; ++g) {
+    float acc = 0.0f;
 #pragma unroll
-  for (int g = 0; g < G; ++g) num[rb][g][j] = acc[g];
+    for (int r = 0; r < RPT; ++r) acc = __builtin_fmaf(phq[g][rb * RPT + r], sv[r], acc);
+    num[rb][g][j] = acc;
+  }
   __syncthreads();
 
   for (int t = tid; t < G * D; t += NT) {

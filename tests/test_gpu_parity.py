@@ -743,6 +743,29 @@ def test_topm_sample_overestimate_falls_back_exactly():
     assert set(rows.tolist()) <= set(gi[0, 0].tolist())
 
 
+@pytest.mark.parametrize("d,r", [(128, 32), (64, 16)])
+def test_topm_clustered_high_scores(d, r):
+    """Runs of consecutive high-scoring positions (a relevant passage) fill the
+    filter's per-wave candidate lists, which then go to the unit's spill pool;
+    the selection must stay exact.  Unit (0, 0): 3000 rows inside one chunk;
+    (0, 1): 1500 rows across a chunk boundary; (1, 0): none; (1, 1): 40000 rows,
+    more candidates than the merge holds, so the exact fallback runs."""
+    _say("case: topm clustered d=%d r=%d" % (d, r))
+    B, Hq, Hkv, N, M = 2, 8, 2, 65536, 2048
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, N, seed=23)
+    K64 = f64(K)
+    qbar = f64(q).reshape(B, Hkv, Hq // Hkv, d).mean(axis=2)
+    runs = {(0, 0): (10000, 13000), (0, 1): (7500, 9000), (1, 1): (20000, 60000)}
+    for (b, h), (lo, hi) in runs.items():
+        K64[b, h, lo:hi] += 3.0 * qbar[b, h]
+    P64 = P.double().numpy()
+    kp = oracle_kp(K64, P64)
+    gi = _topm_check_against_oracle(q, P, kp, M, N)
+    # the recipe does what it is for: the runs dominate their units' selections
+    assert np.isin(np.arange(7500, 9000), gi[0, 1]).mean() > 0.98
+    assert np.isin(gi[0, 0], np.arange(10000, 13000)).mean() > 0.98
+
+
 # ------------------------------------------------------------------ decode step
 
 @pytest.mark.parametrize("B,Hq,Hkv,d,r,N,M", [

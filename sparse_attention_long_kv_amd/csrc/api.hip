@@ -109,6 +109,16 @@ extern "C" int sparse_attn_topm(const sa_shape* shape, const float* scores,
   st = check_topm_common(shape, seq_lens, n_max, M, idx, workspace, ws_bytes, &plan);
   if (st != SA_OK) return st;
   const LaunchCommon c = common(*shape, stream);
+  // the filter path over the given scores where it applies (sampled bound,
+  // filter, merge: the same idx as the chunk-exact path, in fewer bytes)
+  FilterPlan fplan;
+  st = plan_filter(*shape, n_max, M, &fplan);
+  if (st != SA_OK) return st;
+  if (fplan.enabled)
+    return finish(run_filter_select(c, fplan, kSelectBound | kSelectChunks | kSelectMerge,
+                                    nullptr, nullptr, nullptr, seq_lens, n_max, M, idx,
+                                    workspace, nullptr, nullptr, scores),
+                  c.stream);
   return finish(run_select(c, plan, kSelectChunks | kSelectMerge, false, nullptr, nullptr, nullptr,
                            scores, seq_lens, n_max, M, idx, workspace),
                 c.stream);

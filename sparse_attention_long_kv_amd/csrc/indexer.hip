@@ -966,10 +966,17 @@ __device__ __forceinline__ uint32_t block_scan_small(uint32_t v, uint32_t* wtot,
   return wb + inc;
 }
 
+// A position's score comes from its FP8 code row (R = 16 or 32 codes,
+// scored against the unit's indexer query) or, for a selection over scores
+// the caller already holds (sparse_attn_topm), from one fp32 value per
+// position: R = kScoreInput.
+constexpr int kScoreInput = 1;
+
 struct FilterArgs {
   const uint16_t* q;
   const float* P;
   const uint8_t* kp;
+  const float* scores;   // [units][n_max] when R == kScoreInput
   const int32_t* seq_lens;
   int n_max, Ncap, Hq, Hkv, G, M, S, chunk, cap, cslots, spill_cap;
   int64_t ustride;   // pairs per unit in cand: S * cslots, then spill_cap
@@ -1035,9 +1042,9 @@ __device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<k
   // loads go out first
   constexpr int kTotal = kSampleBlocks * kSampleBlock;
   const bool all = len <= kTotal;
-  const uint8_t* kpu = a.kp + (size_t)u * a.Ncap * R;
   uint32_t key[kSampleKeys];
   uint4 c0[kSampleKeys], c1[kSampleKeys];
+  float sv[kSampleKeys];
   bool ok[kSampleKeys];
 #pragma unroll
   for (int i = 0; i < kSampleKeys; ++i) {
@@ -1046,23 +1053,34 @@ __device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<k
     const int p = all ? slot
                       : (int)(((int64_t)blk * (len - kSampleBlock)) / (kSampleBlocks - 1)) + off;
     ok[i] = p < len && len > a.M;
-    const uint8_t* row = kpu + (size_t)(ok[i] ? p : 0) * R;
-    c0[i] = load16(row);
-    if (R == 32) c1[i] = load16(row + 16);
+    if constexpr (R == kScoreInput) {
+      sv[i] = a.scores[(size_t)u * a.n_max + (ok[i] ? p : 0)];
+    } else {
+      const uint8_t* row = a.kp + ((size_t)u * a.Ncap + (ok[i] ? p : 0)) * R;
+      c0[i] = load16(row);
+      if (R == 32) c1[i] = load16(row + 16);
+    }
   }
   prologue();
-  if (tid < R) a.qt[(size_t)u * 32 + tid] = sh.qt[tid];
+  if constexpr (R != kScoreInput) {
+    if (tid < R) a.qt[(size_t)u * 32 + tid] = sh.qt[tid];
+  }
   if (len <= a.M) {                                   // every valid position is selected
     if (tid == 0) a.thr[u] = 1u;
     return;
   }
-  float qlo[16], qhi[16];
-  query_halves<R>(sh.qt, qlo, qhi);
+  if constexpr (R == kScoreInput) {
 #pragma unroll
-  for (int i = 0; i < kSampleKeys; ++i) {
-    float s = score16(qlo, c0[i]);
-    if (R == 32) s = s + score16(qhi, c1[i]);
-    key[i] = ok[i] ? score_key(s + 0.0f) : 0u;
+    for (int i = 0; i < kSampleKeys; ++i) key[i] = ok[i] ? score_key(sv[i] + 0.0f) : 0u;
+  } else {
+    float qlo[16], qhi[16];
+    query_halves<R>(sh.qt, qlo, qhi);
+#pragma unroll
+    for (int i = 0; i < kSampleKeys; ++i) {
+      float s = score16(qlo, c0[i]);
+      if (R == 32) s = s + score16(qhi, c1[i]);
+      key[i] = ok[i] ? score_key(s + 0.0f) : 0u;
+    }
   }
   // the k-th largest sample key, k ~ kSampleSafety * M * (sample size) / len;
   // a sample of the whole unit gives the exact M-th key
@@ -1089,8 +1107,9 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(const FilterArgs
   __shared__ SelectShared<kSampleThreads> sh;
   const int u = blockIdx.x;
   sample_bound<D, R>(a, sh, u, [&] {
-    indexer_query<D, R, kSampleThreads>(a.q, a.P, u / a.Hkv, u % a.Hkv, a.G, a.Hq, sh.qt,
-                                        sh.part);
+    if constexpr (R != kScoreInput)
+      indexer_query<D, R, kSampleThreads>(a.q, a.P, u / a.Hkv, u % a.Hkv, a.G, a.Hq, sh.qt,
+                                          sh.part);
   });
 }
 
@@ -1226,41 +1245,10 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
     if (threadIdx.x == 0) *cnt = 0;
     return;
   }
-  // key >= thr  <=>  score >= thrf for every score the chains can produce
-  // (no NaN; -0 and +0 share the key of +0, and -0 >= +0 holds)
+  // key >= thr  <=>  score >= thrf for every score that is not NaN (the
+  // chains produce none; -0 and +0 share the key of +0, and -0 >= +0 holds)
   const float thrf = key_score(a.thr[u]);
   uint2* lc = a.cand + (size_t)u * a.ustride + (size_t)c * a.cslots;
-  // this chunk's rows only: loads past the valid positions return zero
-  const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(a.kp + ((size_t)u * a.Ncap + base) * R, (uint32_t)nv * R);
-  // Lane l scores position base + i*NT + 64w + l on its own (both 16-byte
-  // halves of an r = 32 row), so no cross-lane step is needed; the workgroup's
-  // 8 waves read each 512-position row together (one contiguous stream per
-  // workgroup: measured 8-10 us faster than a contiguous range per wave).
-  const uint32_t voff = (uint32_t)((w * kWave + lane) * R);
-  constexpr int kLoadsPerIter = R / 16;
-  constexpr int kBatch = SA_FILTER_LOADS_IN_FLIGHT / kLoadsPerIter;
-  // Two register sets: while one batch of rows is scored the next one is in
-  // flight (software pipelining keeps the memory queue full).
-  struct Batch {
-    uint4 a[kBatch], b[kBatch];
-  };
-  auto load_batch = [&](Batch& bt, int i0) {
-#pragma unroll
-    for (int x = 0; x < kBatch; ++x) {
-      const uint32_t off = voff + (uint32_t)((i0 + x) * NT * R);
-      bt.a[x] = buffer_load16(rs, off, 0);
-      if (R == 32) bt.b[x] = buffer_load16(rs, off + 16, 0);
-    }
-  };
-  const int rows = (nv + NT - 1) / NT;
-  Batch b0, b1;
-  load_batch(b0, 0);
-  if (kBatch < rows) load_batch(b1, kBatch);
-  // the query is the same for every lane: read with scalar loads it stays in
-  // scalar registers (an FMA takes one scalar operand), saving 32 VGPRs
-  float qlo[16], qhi[16];
-  query_halves<R>(a.qt + (size_t)u * 32, qlo, qhi);
   uint32_t wc = 0;                                    // positions in this wave's list
   // A full list goes to the unit's spill pool (clustered high scores): one
   // lane reserves its slots with an atomic, the wave copies it out, and the
@@ -1278,37 +1266,110 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
     }
     wc = 0;
   };
-  auto score_batch = [&](const Batch& bt, int i0) {
-#pragma unroll
-    for (int x = 0; x < kBatch; ++x) {
-      const int p = base + (i0 + x) * NT + w * kWave + lane;
-      // the same two chains, added in the same order, as the paired-lane
-      // scoring of the other kernels: identical bits
-      float s = score16(qlo, bt.a[x]);
-      if (R == 32) s = s + score16(qhi, bt.b[x]);
-      const bool ge = s >= thrf, in = p < pend;
-      const bool sel = ge && in;
-      const uint64_t m = ballot(ge) & ballot(in);     // (two compares, no select)
-      const uint32_t n = (uint32_t)popc64(m);
-      if (wc + n > (uint32_t)a.cap) spill_list();     // wave-uniform, rare
-      const uint32_t slot = wc + __builtin_amdgcn_mbcnt_hi(
-                                     (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      if (sel && slot < (uint32_t)a.cap) {
-        sk[w][slot] = __float_as_uint(s);               // keyed when written out
-        sp[w][slot] = p;
-      }
-      wc += n;
+  // One position per lane (the call is wave-uniform): keep it if it is in the
+  // chunk and its score reaches the bound.
+  auto keep = [&](float s, int p) {
+    const bool ge = s >= thrf, in = p < pend;
+    const bool sel = ge && in;
+    const uint64_t m = ballot(ge) & ballot(in);       // (two compares, no select)
+    const uint32_t n = (uint32_t)popc64(m);
+    if (wc + n > (uint32_t)a.cap) spill_list();       // wave-uniform, rare
+    const uint32_t slot = wc + __builtin_amdgcn_mbcnt_hi(
+                                   (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (sel && slot < (uint32_t)a.cap) {
+      sk[w][slot] = __float_as_uint(s);               // keyed when written out
+      sp[w][slot] = p;
     }
+    wc += n;
   };
-  // The last batch may reach past the chunk's rows (kBatch need not divide
-  // them): those loads fall outside the descriptor's range and read zero, and
-  // their positions are at or past pend, so nothing of them is kept.
-  for (int i0 = 0; i0 < rows; i0 += 2 * kBatch) {    // block-uniform trip count
-    score_batch(b0, i0);
-    if (i0 + 2 * kBatch < rows) load_batch(b0, i0 + 2 * kBatch);
-    if (i0 + kBatch < rows) {
-      score_batch(b1, i0 + kBatch);
-      if (i0 + 3 * kBatch < rows) load_batch(b1, i0 + 3 * kBatch);
+  // Loads cover this chunk's rows only: past its valid positions they return
+  // zero, and those positions (at or past pend) are never kept.  Two
+  // register sets: while one batch is scored the next one is in flight
+  // (software pipelining keeps the memory queue full).  Every trip count is
+  // block-uniform.
+  if constexpr (R == kScoreInput) {
+    // Lane l of wave w holds positions base + 4(i NT + 64w + l) + e, e < 4:
+    // one 16-byte load of four scores.
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(a.scores + (size_t)u * a.n_max + base, (uint32_t)nv * 4u);
+    const uint32_t voff = (uint32_t)((w * kWave + lane) * 16);
+    constexpr int kBatch = SA_FILTER_LOADS_IN_FLIGHT;
+    struct Batch {
+      uint4 v[kBatch];
+    };
+    auto load_batch = [&](Batch& bt, int i0) {
+#pragma unroll
+      for (int x = 0; x < kBatch; ++x) bt.v[x] = buffer_load16(rs, voff + (uint32_t)((i0 + x) * NT * 16), 0);
+    };
+    auto score_batch = [&](const Batch& bt, int i0) {
+#pragma unroll
+      for (int x = 0; x < kBatch; ++x) {
+        const int p = base + 4 * ((i0 + x) * NT + w * kWave + lane);
+        keep(__uint_as_float(bt.v[x].x), p);
+        keep(__uint_as_float(bt.v[x].y), p + 1);
+        keep(__uint_as_float(bt.v[x].z), p + 2);
+        keep(__uint_as_float(bt.v[x].w), p + 3);
+      }
+    };
+    const int rows = (nv + 4 * NT - 1) / (4 * NT);
+    Batch b0, b1;
+    load_batch(b0, 0);
+    if (kBatch < rows) load_batch(b1, kBatch);
+    for (int i0 = 0; i0 < rows; i0 += 2 * kBatch) {
+      score_batch(b0, i0);
+      if (i0 + 2 * kBatch < rows) load_batch(b0, i0 + 2 * kBatch);
+      if (i0 + kBatch < rows) {
+        score_batch(b1, i0 + kBatch);
+        if (i0 + 3 * kBatch < rows) load_batch(b1, i0 + 3 * kBatch);
+      }
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(a.kp + ((size_t)u * a.Ncap + base) * R, (uint32_t)nv * R);
+    // Lane l scores position base + i*NT + 64w + l on its own (both 16-byte
+    // halves of an r = 32 row), so no cross-lane step is needed; the
+    // workgroup's 8 waves read each 512-position row together (one
+    // contiguous stream per workgroup: measured 8-10 us faster than a
+    // contiguous range per wave).
+    const uint32_t voff = (uint32_t)((w * kWave + lane) * R);
+    constexpr int kLoadsPerIter = R / 16;
+    constexpr int kBatch = SA_FILTER_LOADS_IN_FLIGHT / kLoadsPerIter;
+    struct Batch {
+      uint4 a[kBatch], b[kBatch];
+    };
+    auto load_batch = [&](Batch& bt, int i0) {
+#pragma unroll
+      for (int x = 0; x < kBatch; ++x) {
+        const uint32_t off = voff + (uint32_t)((i0 + x) * NT * R);
+        bt.a[x] = buffer_load16(rs, off, 0);
+        if (R == 32) bt.b[x] = buffer_load16(rs, off + 16, 0);
+      }
+    };
+    const int rows = (nv + NT - 1) / NT;
+    Batch b0, b1;
+    load_batch(b0, 0);
+    if (kBatch < rows) load_batch(b1, kBatch);
+    // the query is the same for every lane: read with scalar loads it stays
+    // in scalar registers (an FMA takes one scalar operand), saving 32 VGPRs
+    float qlo[16], qhi[16];
+    query_halves<R>(a.qt + (size_t)u * 32, qlo, qhi);
+    auto score_batch = [&](const Batch& bt, int i0) {
+#pragma unroll
+      for (int x = 0; x < kBatch; ++x) {
+        // the same two chains, added in the same order, as the paired-lane
+        // scoring of the other kernels: identical bits
+        float sc = score16(qlo, bt.a[x]);
+        if (R == 32) sc = sc + score16(qhi, bt.b[x]);
+        keep(sc, base + (i0 + x) * NT + w * kWave + lane);
+      }
+    };
+    for (int i0 = 0; i0 < rows; i0 += 2 * kBatch) {
+      score_batch(b0, i0);
+      if (i0 + 2 * kBatch < rows) load_batch(b0, i0 + 2 * kBatch);
+      if (i0 + kBatch < rows) {
+        score_batch(b1, i0 + kBatch);
+        if (i0 + 3 * kBatch < rows) load_batch(b1, i0 + 3 * kBatch);
+      }
     }
   }
   // The lists go out only once every wave has finished reading: stores mixed
@@ -1495,16 +1556,19 @@ __device__ __forceinline__ void select_unit_streaming(const FilterArgs& a, Selec
   constexpr int NT = kMergeThreads;
   const int tid = threadIdx.x;
   for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
-  if (tid < R) sh.qt[tid] = a.qt[(size_t)u * 32 + tid];
+  if (R != kScoreInput && tid < R) sh.qt[tid] = a.qt[(size_t)u * 32 + tid];
   __syncthreads();
   float qlo[16], qhi[16];
-  query_halves<R>(sh.qt, qlo, qhi);
-  const uint8_t* kpu = a.kp + (size_t)u * a.Ncap * R;
+  if constexpr (R != kScoreInput) query_halves<R>(sh.qt, qlo, qhi);
+  auto score_at = [&](int p) {
+    if constexpr (R == kScoreInput) return a.scores[(size_t)u * a.n_max + p];
+    else return position_score<R>(qlo, qhi, a.kp + ((size_t)u * a.Ncap + p) * R);
+  };
   auto visit3 = [&](auto&& f) {
     for (int p0 = 0; p0 < len; p0 += NT) {
       const int p = p0 + tid;
       const bool ok = p < len;
-      const float s = position_score<R>(qlo, qhi, kpu + (size_t)(ok ? p : 0) * R);
+      const float s = score_at(ok ? p : 0);
       f(ok ? score_key(s + 0.0f) : 0u, p, ok);
     }
   };
@@ -1676,14 +1740,28 @@ static void launch_filter_dr(const FilterArgs& a, const AppendArgs* ap, const De
     hipLaunchKernelGGL((filter_merge_kernel<D, R>), dim3(units), dim3(kMergeThreads), 0, st, a);
 }
 
+// The three stages over scores the caller holds (sparse_attn_topm).
+static void launch_filter_scores(const FilterArgs& a, int stages, int units, hipStream_t st) {
+  constexpr int D = 128, R = kScoreInput;           // D plays no part in selection
+  if (stages & kSelectBound)
+    hipLaunchKernelGGL((sample_kernel<D, R>), dim3(units), dim3(kSampleThreads), 0, st, a);
+  if (stages & kSelectChunks)
+    hipLaunchKernelGGL((filter_kernel<D, R>), dim3((unsigned)(units * a.S)), dim3(kChunkThreads),
+                       0, st, a);
+  if (stages & kSelectMerge)
+    hipLaunchKernelGGL((filter_merge_kernel<D, R>), dim3(units), dim3(kMergeThreads), 0, st, a);
+}
+
 hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int stages,
                              const void* q, const float* P, const uint8_t* kp,
                              const int32_t* seq_lens, int n_max, int M, int32_t* idx,
-                             void* workspace, const AppendRows* rows, const AttendFused* att) {
+                             void* workspace, const AppendRows* rows, const AttendFused* att,
+                             const float* scores) {
   FilterArgs a;
   a.q = (const uint16_t*)q;
   a.P = P;
   a.kp = kp;
+  a.scores = scores;
   a.seq_lens = seq_lens;
   a.n_max = n_max;
   a.Ncap = c.Ncap;
@@ -1741,6 +1819,11 @@ hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int 
     da.po = (float*)(pw + dp.off_o);
   }
   const DecodeArgs* dap = att ? &da : nullptr;
+  if (scores) {
+    if (rows || att) return hipErrorInvalidValue;
+    launch_filter_scores(a, stages, plan.units, c.stream);
+    return hipGetLastError();
+  }
   if (c.D == 128 && c.R == 32) launch_filter_dr<128, 32>(a, app, dap, stages, plan.units, c.stream);
   else if (c.D == 128 && c.R == 16) launch_filter_dr<128, 16>(a, app, dap, stages, plan.units, c.stream);
   else if (c.D == 64 && c.R == 32) launch_filter_dr<64, 32>(a, app, dap, stages, plan.units, c.stream);

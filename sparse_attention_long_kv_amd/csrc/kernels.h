@@ -56,12 +56,14 @@ struct AttendFused {
 // (sampled bound; with `rows`, the same launch first appends those rows),
 // kSelectChunks (filtering chunks), kSelectMerge (with `att`, each merge
 // workgroup then attends over the selection, followed by the split merge
-// when there are several splits; needs G d <= 1024).
+// when there are several splits; needs G d <= 1024).  With `scores`
+// ([B][Hkv][n_max] fp32), the stages select over those scores instead of
+// scoring the FP8 cache (q, P, kp unused; no rows, no att).
 hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int stages,
                              const void* q, const float* P, const uint8_t* kp,
                              const int32_t* seq_lens, int n_max, int M, int32_t* idx,
                              void* workspace, const AppendRows* rows = nullptr,
-                             const AttendFused* att = nullptr);
+                             const AttendFused* att = nullptr, const float* scores = nullptr);
 hipError_t run_decode(const LaunchCommon& c, const DecodePlan& plan, const void* q,
                       const void* k_cache, const void* v_cache, const int32_t* idx, int M,
                       float scale, void* out, float* lse, void* workspace);

@@ -138,7 +138,8 @@ int sparse_attn_index_score(const sa_shape* shape, const void* q, const float* P
  * IndexCache article, "DeepSeek Sparse Attention": keep the k most relevant
  * positions; JSSA article: every KV head (GQA group) selects its own set.
  *
- * scores   [B][Hkv][n_max] fp32 (as written by sparse_attn_index_score).
+ * scores   [B][Hkv][n_max] fp32 (as written by sparse_attn_index_score; no
+ *          NaN among the first len_b of a row), read in place.
  * idx      [B][Hkv][M] int32 out: the positions n < len with the M largest
  *          scores, equal scores ordered by lower position; ascending; when
  *          fewer than M positions are valid, all of them followed by -1.
@@ -154,8 +155,9 @@ int sparse_attn_topm(const sa_shape* shape, const float* scores,
                      void* stream);
 
 /* ---------------------------------------------------------------------------
- * sparse_attn_index_topm -- steps 2 and 3 fused in one launch: the scores are
- * kept on chip and never written.  Produces exactly the idx that
+ * sparse_attn_index_topm -- steps 2 and 3 fused: the scores are kept on chip
+ * and never written (three launches, listed under
+ * sparse_attn_index_topm_stage).  Produces exactly the idx that
  * sparse_attn_index_score followed by sparse_attn_topm produces.
  * Arguments as in those two calls.
  * ------------------------------------------------------------------------- */
@@ -178,8 +180,9 @@ int sparse_attn_index_topm(const sa_shape* shape, const void* q, const float* P,
  *                        keys at or above the bound (or the chunk's exact
  *                        top-M, chunk-exact method);
  *   SA_STAGE_MERGE       exact top-M over the kept keys, written to idx (a
- *                        head whose bound turned out too high is selected
- *                        again exactly from the FP8 cache).
+ *                        head whose bound turned out too high, or that kept
+ *                        more keys than the merge holds, is selected again
+ *                        exactly from the FP8 cache).
  * idx is only written by SA_STAGE_MERGE (and may be NULL for the others).
  * Returns SA_ERR_INVALID for an unknown stage.
  * ------------------------------------------------------------------------- */

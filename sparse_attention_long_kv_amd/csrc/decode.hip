@@ -93,58 +93,91 @@ __global__ __launch_bounds__(kBlock) void gather_rows_kernel(const int32_t* __re
   }
 }
 
-// Merge the S partial states of one unit (one workgroup per unit).  A separate
-// launch orders the partial writes before these reads without device-scope
-// fences inside the attention kernel.
+// Merge the S partial states of one unit's head: one workgroup of D threads
+// per (unit, head), thread dd owning output dimension dd.  A separate launch
+// orders the partial writes before these reads without device-scope fences
+// inside the attention kernel.  Every state of the head is loaded at once;
+// the weights 2^(m_s - m) and l = sum_s l_s 2^(m_s - m) are formed in split
+// order, and o = sum_s o_s 2^(m_s - m) / l in split order from loads issued
+// eight splits at a time.
+constexpr int kMaxSplitsCombine = 256;     // splits per unit the planners produce, at most
+
 template <int D>
-__global__ __launch_bounds__(kBlock) void combine_kernel(const DecodeArgs a) {
-  __shared__ float fm[kMaxHeads], fl[kMaxHeads];
-  const int G = a.G;
-  const int u = blockIdx.x;
+__global__ __launch_bounds__(D) void combine_kernel(const DecodeArgs a) {
+  __shared__ float sm[kMaxSplitsCombine], sw[kMaxSplitsCombine];
+  __shared__ float fm, fl;
+  const int G = a.G, S = a.S;
+  const int u = blockIdx.x / G, g = blockIdx.x % G;
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int tid = threadIdx.x;
-  const size_t ubase = (size_t)u * a.S * G;
-  if (tid < G) {
-    const int g = tid;
-    float mt = -__builtin_inff();
-    for (int s2 = 0; s2 < a.S; ++s2) mt = fmaxf(mt, a.pm[ubase + (size_t)s2 * G + g]);
-    float lt = 0.0f;
-    for (int s2 = 0; s2 < a.S; ++s2)
-      lt += a.pl[ubase + (size_t)s2 * G + g] * merge_scale(a.pm[ubase + (size_t)s2 * G + g], mt);
-    fm[g] = mt;
-    fl[g] = lt;
+  const size_t ubase = (size_t)u * S * G;
+  float lv[kMaxSplitsCombine / D];
+#pragma unroll
+  for (int k = 0; k < kMaxSplitsCombine / D; ++k) {
+    const int s2 = tid + k * D;
+    lv[k] = 0.0f;
+    if (s2 < S) {
+      sm[s2] = a.pm[ubase + (size_t)s2 * G + g];
+      lv[k] = a.pl[ubase + (size_t)s2 * G + g];
+    }
   }
   __syncthreads();
-  for (int t = tid; t < G * D; t += kBlock) {
-    const int g = t / D, dd = t % D;
-    const float mt = fm[g], lt = fl[g];
-    float ot = 0.0f;
-    for (int s2 = 0; s2 < a.S; ++s2) {
-      const size_t pi = ubase + (size_t)s2 * G + g;
-      ot += a.po[pi * D + dd] * merge_scale(a.pm[pi], mt);
-    }
-    const int hq = h * G + g;
-    const float val = lt > 0.0f ? ot / lt : 0.0f;
-    a.out[((size_t)b * a.Hq + hq) * D + dd] = (uint16_t)f32_to_bf16_bits(val);
-    if (dd == 0 && a.lse)
-      a.lse[(size_t)b * a.Hq + hq] =
-          lt > 0.0f ? (mt + log2f(lt)) * 0.69314718055994530942f : -__builtin_inff();
+  if (tid == 0) {
+    float mt = -__builtin_inff();
+    for (int s2 = 0; s2 < S; ++s2) mt = fmaxf(mt, sm[s2]);
+    fm = mt;
   }
+  __syncthreads();
+  const float mt = fm;
+#pragma unroll
+  for (int k = 0; k < kMaxSplitsCombine / D; ++k) {
+    const int s2 = tid + k * D;
+    if (s2 < S) {
+      const float w = merge_scale(sm[s2], mt);
+      sw[s2] = w;
+      sm[s2] = lv[k] * w;                       // l_s 2^(m_s - m)
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float lt = 0.0f;
+    for (int s2 = 0; s2 < S; ++s2) lt += sm[s2];
+    fl = lt;
+  }
+  const float* po = a.po + ubase * D + (size_t)g * D + tid;   // split s2 at s2 * G * D
+  float ot = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = s0 + k < S ? po[(size_t)(s0 + k) * G * D] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (s0 + k < S) ot += v[k] * sw[s0 + k];
+  }
+  __syncthreads();
+  const float lt = fl;
+  const int hq = h * G + g;
+  const float val = lt > 0.0f ? ot / lt : 0.0f;
+  a.out[((size_t)b * a.Hq + hq) * D + tid] = (uint16_t)f32_to_bf16_bits(val);
+  if (tid == 0 && a.lse)
+    a.lse[(size_t)b * a.Hq + hq] =
+        lt > 0.0f ? (mt + log2f(lt)) * 0.69314718055994530942f : -__builtin_inff();
 }
 
 template <int D>
 static void launch_decode_d(const DecodeArgs& a, dim3 grid, int units, hipStream_t st) {
   const size_t lds = (size_t)kAttendWaves * a.G * D * sizeof(float);
   hipLaunchKernelGGL((decode_kernel<D>), grid, dim3(kAttendThreads), lds, st, a);
-  if (a.S > 1) hipLaunchKernelGGL((combine_kernel<D>), dim3(units), dim3(kBlock), 0, st, a);
+  if (a.S > 1) hipLaunchKernelGGL((combine_kernel<D>), dim3(units * a.G), dim3(D), 0, st, a);
 }
 
 hipError_t run_combine(const LaunchCommon& c, const DecodeArgs& a) {
   if (a.S <= 1) return hipSuccess;
+  if (a.S > kMaxSplitsCombine) return hipErrorInvalidConfiguration;
   if (c.D == 128)
-    hipLaunchKernelGGL((combine_kernel<128>), dim3(c.units), dim3(kBlock), 0, c.stream, a);
+    hipLaunchKernelGGL((combine_kernel<128>), dim3(c.units * a.G), dim3(128), 0, c.stream, a);
   else
-    hipLaunchKernelGGL((combine_kernel<64>), dim3(c.units), dim3(kBlock), 0, c.stream, a);
+    hipLaunchKernelGGL((combine_kernel<64>), dim3(c.units * a.G), dim3(64), 0, c.stream, a);
   return hipGetLastError();
 }
 
@@ -175,6 +208,7 @@ hipError_t run_dense_decode(const LaunchCommon& c, const DecodePlan& plan, const
   const long blocks = (long)plan.units * plan.splits;
   if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
   if (c.G < 1 || c.G > kMaxHeads) return hipErrorInvalidConfiguration;
+  if (a.S > kMaxSplitsCombine) return hipErrorInvalidConfiguration;
   if (c.D == 128) {
     hipLaunchKernelGGL((dense_decode_kernel<128>), dim3((unsigned)blocks), dim3(kAttendThreads),
                        (size_t)kAttendWaves * c.G * 128 * sizeof(float), c.stream, a);
@@ -229,6 +263,7 @@ hipError_t run_decode(const LaunchCommon& c, const DecodePlan& plan, const void*
   const long blocks = (long)plan.units * plan.splits;
   if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
   if (c.G < 1 || c.G > kMaxHeads) return hipErrorInvalidConfiguration;
+  if (a.S > kMaxSplitsCombine) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks);
   if (c.D == 128) launch_decode_d<128>(a, grid, plan.units, c.stream);
   else launch_decode_d<64>(a, grid, plan.units, c.stream);

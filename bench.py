@@ -11,7 +11,8 @@ same workgroups, by gather-free sparse attention over the selected rows.  Inputs
 Prints ONE JSON line:
   value         decode steps/s (N=1 GPU; whole-job throughput)
   hbm_gbps      algorithmic bytes per step / step time
-  roofline      the dominant kernel (scoring + candidate filter) against 8 TB/s
+  roofline      the dominant kernel (scoring + candidate filter) against 8 TB/s,
+                and against this device's measured streaming-read rate
   cold_step_us  steps timed one at a time after a cache-evicting read
                 (median, p10, p90, and per launch)
   cpu_baseline  the fp64 oracle on the host, on a bounded sample of units
@@ -622,6 +623,23 @@ def main(argv=None):
                 "median_us_per_call": {k: round(float(np.median([r[i] for r in per])), 2)
                                        for i, k in enumerate(names)}}
 
+    # this device's streaming-read rate (context for the roofline): one
+    # contiguous read of 1 GiB with the filter's load pattern
+    rbuf = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        sa.sparse_attn_stream_read(rbuf, sink)
+    pool = timer.create(20)
+    for k in range(10):
+        timer.record(pool[2 * k], stream)
+        sa.sparse_attn_stream_read(rbuf, sink)
+        timer.record(pool[2 * k + 1], stream)
+    torch.cuda.synchronize()
+    read_us = 1e3 * sum(timer.elapsed_ms(pool[2 * k], pool[2 * k + 1]) for k in range(10)) / 10
+    timer.destroy(pool)
+    del rbuf, sink
+    read_gbps = 2 ** 30 / (read_us * 1e-6) / 1e9
+
     bytes_k = algorithmic_bytes(wl)
     step_bytes = sum(bytes_k.values())
     steps_per_s = 1e3 / ms_per_step
@@ -638,7 +656,9 @@ def main(argv=None):
                 "kernel": "%s (sparse_attn_decode_step_stage, SA_STEP_CANDIDATES)"
                           % DOMINANT_KERNEL,
                 "bytes_per_launch": bytes_k[dom], "avg_launch_us": round(dom_us, 2),
-                "source_hash": src_hash}
+                "source_hash": src_hash,
+                "read_ceiling_gbps": round(read_gbps, 1),
+                "frac_of_read_ceiling": round(dom_gbps / read_gbps, 4)}
 
     res = {
         "metric": METRIC, "value": round(steps_per_s, 2), "unit": "steps/s",

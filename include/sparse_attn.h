@@ -323,6 +323,17 @@ int sparse_attn_gather_kv(const sa_shape* shape, const int32_t* idx, int32_t M,
                           const void* k_cache, const void* v_cache, void* k_out, void* v_out,
                           void* stream);
 
+/* sparse_attn_stream_read -- measurement helper, not part of the method:
+ * reads the `bytes` bytes at `buf` once, front to back, with the load pattern
+ * of the filter stage (512-thread workgroups of 256 KiB each, 16-byte loads,
+ * four in flight per thread), so that a caller can time this device's
+ * streaming-read rate beside the kernels' (the practical ceiling under the
+ * nominal HBM peak).  buf: 16-byte aligned device memory; bytes: a positive
+ * multiple of 256 KiB; sink: one device uint32 that a value derived from the
+ * data may be written to (it keeps the loads from being optimised away and
+ * means nothing).  Returns SA_ERR_INVALID for anything else. */
+int sparse_attn_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Bytes of workspace that sparse_attn_topm, sparse_attn_index_topm(_stage),
  * sparse_attn_decode and sparse_attn_decode_step(_stage) need for this shape,
  * n_max and M (host only, pure).

@@ -12,7 +12,7 @@ from ._lib import (  # noqa: F401
     sparse_attn_decode_step, sparse_attn_decode_step_stage, SA_STEP_APPEND_BOUND,
     SA_STEP_CANDIDATES, SA_STEP_MERGE, SA_STEP_ATTEND, SA_STEP_SELECT_ATTEND,
     sparse_attn_linear_gate, sparse_attn_dense_decode, sparse_attn_dense_workspace_size,
-    sparse_attn_gather_kv,
+    sparse_attn_gather_kv, sparse_attn_stream_read,
     sparse_attn_workspace_size, sparse_attn_status_string, LIB_PATH,
     SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP,
 )

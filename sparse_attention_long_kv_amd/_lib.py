@@ -74,6 +74,7 @@ _SIGS = {
     "sparse_attn_dense_decode": [_SP, _VP, _VP, _VP, _VP, _I32, ctypes.c_float, _VP, _VP, _VP,
                                  _SZ, _VP],
     "sparse_attn_gather_kv": [_SP, _VP, _I32, _VP, _VP, _VP, _VP, _VP],
+    "sparse_attn_stream_read": [_VP, _SZ, _VP, _VP],
     "sparse_attn_workspace_size": [_SP, _I32, _I32],
     "sparse_attn_dense_workspace_size": [_SP, _I32],
     "sparse_attn_status_string": [ctypes.c_int],
@@ -300,6 +301,15 @@ def sparse_attn_dense_decode(shape, q, k_cache, v_cache, seq_lens, n_max, softma
 
 def sparse_attn_dense_workspace_size(shape, n_max):
     return int(load().sparse_attn_dense_workspace_size(_sh(shape), int(n_max)))
+
+
+def sparse_attn_stream_read(buf, sink):
+    """Measurement helper: one streaming read of the whole of `buf` (a device
+    tensor of a multiple of 256 KiB); `sink` is a one-element int32 device
+    tensor the kernel may write (it keeps the loads alive)."""
+    p = _dev_ptr(buf, buf.dtype, name="buf")
+    _call("sparse_attn_stream_read", p, buf.numel() * buf.element_size(),
+          _dev_ptr(sink, torch.int32, (1,), "sink"), _stream(buf))
 
 
 def sparse_attn_gather_kv(shape, idx, M, k_cache, v_cache, k_out, v_out):

@@ -344,3 +344,10 @@ extern "C" int sparse_attn_linear_gate(const sa_shape* shape, const void* q, con
                 c.stream);
 }
 
+extern "C" int sparse_attn_stream_read(const void* buf, size_t bytes, uint32_t* sink,
+                                       void* stream) {
+  if (!ptr_ok(buf, A16) || !ptr_ok(sink, A4)) return SA_ERR_INVALID;
+  if (bytes == 0 || bytes % (256 * 1024) != 0 || bytes / (256 * 1024) > INT32_MAX)
+    return SA_ERR_INVALID;
+  return finish(run_stream_read(buf, bytes, sink, (hipStream_t)stream), (hipStream_t)stream);
+}

@@ -171,6 +171,34 @@ static void launch_decode_d(const DecodeArgs& a, dim3 grid, int units, hipStream
   if (a.S > 1) hipLaunchKernelGGL((combine_kernel<D>), dim3(units * a.G), dim3(D), 0, st, a);
 }
 
+// Streaming read of a buffer (a measurement helper): workgroup w reads the
+// w-th 256 KiB, each thread four 16-byte loads per round.
+constexpr size_t kStreamBytesPerBlock = 256 * 1024;
+
+__global__ __launch_bounds__(512) void stream_read_kernel(const uint4* __restrict__ p,
+                                                          uint32_t* sink) {
+  constexpr int kPer = (int)(kStreamBytesPerBlock / 16);     // 16384 loads per workgroup
+  const uint4* base = p + (size_t)blockIdx.x * kPer;
+  uint32_t acc = 0u;
+  for (int i = threadIdx.x; i < kPer; i += 512 * 4) {
+    uint4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = base[i + k * 512];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc ^= v[k].x + v[k].y + v[k].z + v[k].w;
+  }
+  if (acc == 0x9E3779B9u) *sink = acc;
+}
+
+hipError_t run_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st) {
+  const size_t blocks = bytes / kStreamBytesPerBlock;
+  if (blocks == 0 || blocks * kStreamBytesPerBlock != bytes || blocks > INT32_MAX)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(512), 0, st,
+                     (const uint4*)buf, sink);
+  return hipGetLastError();
+}
+
 hipError_t run_combine(const LaunchCommon& c, const DecodeArgs& a) {
   if (a.S <= 1) return hipSuccess;
   if (a.S > kMaxSplitsCombine) return hipErrorInvalidConfiguration;

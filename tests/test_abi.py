@@ -117,6 +117,16 @@ def test_bad_shapes_are_rejected(lib):
                P, 1 << 20, None) == sa.SA_ERR_INVALID
 
 
+def test_stream_read_rejects_bad_arguments(lib):
+    """The measurement helper checks its buffer, size and sink on the host."""
+    P = ctypes.c_void_p(_FAKE)
+    odd = ctypes.c_void_p(_FAKE + 2)
+    for buf, nbytes, sink in [(None, 1 << 20, P), (odd, 1 << 20, P), (P, 1 << 20, None),
+                              (P, 0, P), (P, 100, P), (P, (1 << 18) + 16, P)]:
+        assert _st(lib, "sparse_attn_stream_read", buf, ctypes.c_size_t(nbytes), sink,
+                   None) == sa.SA_ERR_INVALID, (buf, nbytes, sink)
+
+
 def test_bad_arguments_are_rejected(lib):
     wl = WORKLOADS["tiny"]
     sh = _shape(wl)

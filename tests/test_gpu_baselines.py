@@ -130,3 +130,17 @@ def test_gather_then_attend(B, Hq, Hkv, d, N, M, lens):
             o, _ = oracle.sparse_attention(q64[b, h * G:(h + 1) * G], K64[b, h], V64[b, h],
                                            idx[b, h], default_scale(d))
             check_attention(go[b, h * G:(h + 1) * G], o, "unit (%d, %d)" % (b, h))
+
+
+def test_stream_read_runs_over_whole_buffers():
+    """The measurement helper reads buffers of multiples of 256 KiB and
+    reports no error; the sink is written only for one data-dependent value
+    (never for this buffer of ones), so it keeps its contents."""
+    _say("case: stream read")
+    buf = torch.ones(1 << 20, dtype=torch.int32, device="cuda")      # 4 MiB
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    sa.sparse_attn_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
+    with pytest.raises(sa.SparseAttnError):
+        sa.sparse_attn_stream_read(buf[:1000], sink)

@@ -932,19 +932,21 @@ __global__ __launch_bounds__(kChunkThreads, 4) void chunk_select_kernel(const Se
 //     largest sample key, k ~ 3 M (sample size) / len, as a bound thr that
 //     about 3M keys of the unit reach (the whole unit when it has at most
 //     1024 positions: then k = M and thr is the exact M-th key).
-//  2. filter_kernel: chunks of the unit stream their FP8 rows, score every
-//     position and append each score >= thr, with its position, to an LDS
-//     list of the wave that scored it (ballot + bit count, no key held in
-//     registers); once every wave has finished reading, the 8 lists go out
-//     back to back as the chunk's candidates, packed (key, position) pairs
-//     in no particular order.
+//  2. filter_kernel: chunks of the unit stream their FP8 rows (or the given
+//     scores), score every position and append each score >= thr, with its
+//     position, to an LDS list of the wave that scored it (ballot + bit
+//     count, no key held in registers); a list that fills up goes to the
+//     unit's spill pool (clustered high scores); once every wave has
+//     finished reading, the 8 lists go out back to back as the chunk's
+//     candidates, packed (key, position) pairs in no particular order.
 //  3. merge (filter_merge_kernel, or select_attend_kernel in the decode
-//     step): if no list overflowed and at least M keys reached thr, then
-//     thr <= the M-th largest key of the unit, so the candidates hold every
-//     selected position; they are loaded into registers, the exact M-th key
-//     is found among them and idx is emitted through a bitmap of positions.
-//     Otherwise the workgroup selects exactly by streaming the unit's rows
-//     again and marking the selection in the bitmap (slow but rare).
+//     step): if the kept keys fit the merge (chunk lists plus spill pool) and
+//     at least M of them reached thr, then thr <= the M-th largest key of the
+//     unit, so the candidates hold every selected position; they are loaded
+//     into registers, the exact M-th key is found among them and idx is
+//     emitted through a bitmap of positions.  Otherwise the workgroup selects
+//     exactly by streaming the unit's rows again and marking the selection in
+//     the bitmap (slow but rare).
 // Keys are bit-identical to the chunk-exact path's, so both give the same idx.
 
 // Inclusive prefix sum over the block in thread order (wtot: NT/64 words of LDS).
@@ -1374,8 +1376,9 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
   }
   // The lists go out only once every wave has finished reading: stores mixed
   // into the read stream cost far more (measured), and one 8-byte store per
-  // candidate costs less than two 4-byte ones.  A count past cap means the
-  // wave's list overflowed: the chunk is marked -1 and the merge falls back.
+  // candidate costs less than two 4-byte ones.  (Full lists went to the
+  // spill pool, so no list holds more than cap; a count past cap would mark
+  // the chunk -1 and send the merge to the exact fallback.)
   if (lane == 0) wn[w] = wc;
   __syncthreads();
   uint32_t off = 0, total = 0;
@@ -1547,8 +1550,9 @@ __device__ __forceinline__ void emit_selected(SelectShared<NT>& sh, uint32_t* bm
     for (int j = tid; j < M; j += NT) idx_u[j] = out[j];
 }
 
-// Exact selection of one unit by streaming its rows again (the filter's
-// bound was above the M-th key, or a list overflowed).
+// Exact selection of one unit by streaming its rows (or scores) again: the
+// filter's bound was above the M-th key, or the unit kept more keys than the
+// merge holds.
 template <int D, int R>
 __device__ __forceinline__ void select_unit_streaming(const FilterArgs& a, SelectShared<kMergeThreads>& sh,
                                                    uint32_t* bm, int u, int b, int h, int len,

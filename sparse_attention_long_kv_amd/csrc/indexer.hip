@@ -117,71 +117,6 @@ __device__ __forceinline__ uint4 load16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-// ------------------------------------------------------------------ scores
-
-constexpr int kScorePositionsPerBlock = 8192;
-
-template <int D, int R>
-__global__ __launch_bounds__(256) void index_score_kernel(
-    const uint16_t* __restrict__ q, const float* __restrict__ P, const uint8_t* __restrict__ kp,
-    const int32_t* __restrict__ seq_lens, int n_max, int Ncap, int Hq, int Hkv, int G,
-    int blocks_per_unit, float* __restrict__ scores) {
-  __shared__ float qt[32];
-  __shared__ double part[kBlock];
-  const int u = blockIdx.x / blocks_per_unit, blk = blockIdx.x % blocks_per_unit;
-  const int b = u / Hkv, h = u % Hkv;
-  indexer_query<D, R>(q, P, b, h, G, Hq, qt, part);
-  float ql[16];
-  lane_query<R>(qt, ql);
-  const int len = seq_lens ? min(max(seq_lens[b], 0), n_max) : n_max;
-  const int w = threadIdx.x / kWave, lane = lane_id();
-  constexpr int kPPW = kWave * 16 / R;              // positions per wave instruction
-  constexpr int kIters = kScorePositionsPerBlock / (4 * kPPW);
-  const uint8_t* kpu = kp + (size_t)u * Ncap * R;
-  float* su = scores + (size_t)u * n_max;
-  const int pos_lane = (R == 32) ? (lane >> 1) : lane;
-  const int blk0 = blk * kScorePositionsPerBlock;
-  const int nv = min(max(len - blk0, 0), kScorePositionsPerBlock);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(kpu + (size_t)blk0 * R, (uint32_t)nv * R);
-  constexpr int kBatch = 8;
-  static_assert(kIters % kBatch == 0, "batches");
-  for (int it0 = 0; it0 < kIters; it0 += kBatch) {
-    if (blk0 + (it0 * 4 + w) * kPPW >= n_max) break;      // uniform per wave
-    uint4 c[kBatch];
-#pragma unroll
-    for (int x = 0; x < kBatch; ++x)
-      c[x] = buffer_load16(rs, (uint32_t)(lane * 16 + ((it0 + x) * 4 + w) * kPPW * R), 0);
-#pragma unroll
-    for (int x = 0; x < kBatch; ++x) {
-      const int p0 = blk0 + ((it0 + x) * 4 + w) * kPPW;
-      const int p = p0 + pos_lane;
-      float s = lane_score<R>(ql, c[x]);
-      if (p >= len) s = -__builtin_inff();
-      const bool writer = (R == 32) ? ((lane & 1) == 0) : true;
-      if (writer && p < n_max) su[p] = s;
-    }
-  }
-}
-
-hipError_t run_index_score(const LaunchCommon& c, const void* q, const float* P,
-                           const uint8_t* kp, const int32_t* seq_lens, int n_max,
-                           float* scores) {
-  const int bpu = (n_max + kScorePositionsPerBlock - 1) / kScorePositionsPerBlock;
-  const long blocks = (long)bpu * c.units;
-  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)blocks), block(kBlock);
-  const uint16_t* qq = (const uint16_t*)q;
-#define SA_LAUNCH_SCORE(DD, RR)                                                            \
-  hipLaunchKernelGGL((index_score_kernel<DD, RR>), grid, block, 0, c.stream, qq, P, kp,    \
-                     seq_lens, n_max, c.Ncap, c.Hq, c.Hkv, c.G, bpu, scores)
-  if (c.D == 128 && c.R == 32) SA_LAUNCH_SCORE(128, 32);
-  else if (c.D == 128 && c.R == 16) SA_LAUNCH_SCORE(128, 16);
-  else if (c.D == 64 && c.R == 32) SA_LAUNCH_SCORE(64, 32);
-  else SA_LAUNCH_SCORE(64, 16);
-#undef SA_LAUNCH_SCORE
-  return hipGetLastError();
-}
-
 // ------------------------------------------------------------------ select
 
 struct SelectArgs {
@@ -1026,6 +961,92 @@ __device__ __forceinline__ void query_halves(const float* qt, float (&qlo)[16], 
     qlo[k] = qt[k];
     qhi[k] = R == 32 ? qt[16 + k] : 0.0f;
   }
+}
+
+// ------------------------------------------------------------------ scores
+
+// sparse_attn_index_score: the filter stage's stream without the filter.
+// Each 512-thread workgroup forms the unit's query (indexer_query: the same
+// bits in every kernel) and scores a chunk of 2048 positions, lane l of wave
+// w position base + i*512 + 64w + l on its own (both 16-byte halves of an
+// r = 32 row; the chains of position_score), two rows of loads in flight;
+// every position n < n_max gets one coalesced 4-byte store (-inf from len_b
+// on).  Small chunks, many workgroups: the stores of one spread out over the
+// reads of the others (measured at 128K: 2048 positions 222 us, 8192 236,
+// 32768 253, 1024 232; pairs of lanes per position over 8192, 243).
+constexpr int kScoreThreads = 512;
+constexpr int kScorePositionsPerBlock = 2048;
+
+template <int D, int R>
+__global__ __launch_bounds__(kScoreThreads) void index_score_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ P, const uint8_t* __restrict__ kp,
+    const int32_t* __restrict__ seq_lens, int n_max, int Ncap, int Hq, int Hkv, int G,
+    int blocks_per_unit, float* __restrict__ scores) {
+  constexpr int NT = kScoreThreads;
+  __shared__ float qt[32];
+  __shared__ double part[NT];
+  const int u = blockIdx.x / blocks_per_unit, blk = blockIdx.x % blocks_per_unit;
+  const int b = u / Hkv, h = u % Hkv;
+  const int tid = threadIdx.x;
+  const int len = seq_lens ? min(max(seq_lens[b], 0), n_max) : n_max;
+  const int base = blk * kScorePositionsPerBlock;
+  const int nw = min(n_max - base, kScorePositionsPerBlock);     // positions written
+  const int nv = min(max(len - base, 0), nw);                      // ... of which valid
+  // this chunk's valid rows only: loads past them return zero
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(kp + ((size_t)u * Ncap + base) * R, (uint32_t)nv * R);
+  const uint32_t voff = (uint32_t)(tid * R);
+  const int rows = (nw + NT - 1) / NT;
+  uint4 a0 = make_uint4(0u, 0u, 0u, 0u), b0 = a0, a1 = a0, b1 = a0;
+  a0 = buffer_load16(rs, voff, 0);
+  if (R == 32) b0 = buffer_load16(rs, voff + 16, 0);
+  if (rows > 1) {
+    a1 = buffer_load16(rs, voff + NT * R, 0);
+    if (R == 32) b1 = buffer_load16(rs, voff + NT * R + 16, 0);
+  }
+  indexer_query<D, R, NT>(q, P, b, h, G, Hq, qt, part);
+  float qlo[16], qhi[16];
+  query_halves<R>(qt, qlo, qhi);
+  float* su = scores + (size_t)u * n_max + base;
+  auto put = [&](const uint4& ca, const uint4& cb, int i) {
+    const int p = i * NT + tid;                       // within the chunk
+    float s = score16(qlo, ca);
+    if (R == 32) s = s + score16(qhi, cb);
+    if (p < nw) su[p] = base + p < len ? s : -__builtin_inff();
+  };
+  for (int i = 0; i < rows; i += 2) {                 // block-uniform
+    put(a0, b0, i);
+    if (i + 2 < rows) {
+      a0 = buffer_load16(rs, voff + (uint32_t)((i + 2) * NT * R), 0);
+      if (R == 32) b0 = buffer_load16(rs, voff + (uint32_t)((i + 2) * NT * R) + 16, 0);
+    }
+    if (i + 1 < rows) {
+      put(a1, b1, i + 1);
+      if (i + 3 < rows) {
+        a1 = buffer_load16(rs, voff + (uint32_t)((i + 3) * NT * R), 0);
+        if (R == 32) b1 = buffer_load16(rs, voff + (uint32_t)((i + 3) * NT * R) + 16, 0);
+      }
+    }
+  }
+}
+
+hipError_t run_index_score(const LaunchCommon& c, const void* q, const float* P,
+                           const uint8_t* kp, const int32_t* seq_lens, int n_max,
+                           float* scores) {
+  const int bpu = (n_max + kScorePositionsPerBlock - 1) / kScorePositionsPerBlock;
+  const long blocks = (long)bpu * c.units;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks), block(kScoreThreads);
+  const uint16_t* qq = (const uint16_t*)q;
+#define SA_LAUNCH_SCORE(DD, RR)                                                            \
+  hipLaunchKernelGGL((index_score_kernel<DD, RR>), grid, block, 0, c.stream, qq, P, kp,    \
+                     seq_lens, n_max, c.Ncap, c.Hq, c.Hkv, c.G, bpu, scores)
+  if (c.D == 128 && c.R == 32) SA_LAUNCH_SCORE(128, 32);
+  else if (c.D == 128 && c.R == 16) SA_LAUNCH_SCORE(128, 16);
+  else if (c.D == 64 && c.R == 32) SA_LAUNCH_SCORE(64, 32);
+  else SA_LAUNCH_SCORE(64, 16);
+#undef SA_LAUNCH_SCORE
+  return hipGetLastError();
 }
 
 // The bound stage for unit u (the whole workgroup; it synchronises).

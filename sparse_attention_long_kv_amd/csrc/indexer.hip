@@ -944,7 +944,8 @@ __device__ __forceinline__ int unit_len(const int32_t* seq_lens, int b, int n_ma
 }
 
 // Score of one whole position by one thread: the same 16-code chains, added
-// in the same order, as the paired-lane scoring, hence the same bits.
+// in the same order, as the paired-lane scoring of the chunk-exact kernel,
+// hence the same bits.
 template <int R>
 __device__ __forceinline__ float position_score(const float (&qlo)[16], const float (&qhi)[16],
                                                 const uint8_t* row) {
@@ -1380,7 +1381,7 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
 #pragma unroll
       for (int x = 0; x < kBatch; ++x) {
         // the same two chains, added in the same order, as the paired-lane
-        // scoring of the other kernels: identical bits
+        // scoring of the chunk-exact kernel: identical bits
         float sc = score16(qlo, bt.a[x]);
         if (R == 32) sc = sc + score16(qhi, bt.b[x]);
         keep(sc, base + (i0 + x) * NT + w * kWave + lane);

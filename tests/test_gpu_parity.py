@@ -766,6 +766,69 @@ def test_topm_clustered_high_scores(d, r):
     assert np.isin(gi[0, 0], np.arange(10000, 13000)).mean() > 0.98
 
 
+def test_decode_step_with_clustered_high_scores():
+    """The fused decode step (append + bound, candidates, select + attend in
+    one workgroup) over units whose high scores come in runs, so that wave
+    lists spill: the same caches, idx, out and lse as the three separate
+    calls, and the oracle's selection and attention on the checked units."""
+    _say("case: decode step, clustered")
+    B, Hq, Hkv, d, r, N, M = 2, 8, 2, 128, 32, 65536, 2048
+    G = Hq // Hkv
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, N, seed=29)
+    K64 = f64(K)
+    qbar = f64(q).reshape(B, Hkv, G, d).mean(axis=2)
+    runs = {(0, 0): (10000, 13000), (1, 1): (31000, 34500)}     # one across a chunk boundary
+    for (b, h), (lo, hi) in runs.items():
+        K64[b, h, lo:hi] += 3.0 * qbar[b, h]
+    K = torch.from_numpy(K64).to(torch.bfloat16)
+    K64 = f64(K)                        # the cache holds the bf16-rounded keys
+    g = torch.Generator().manual_seed(31)
+    k_new = torch.randn(B, Hkv, 1, d, generator=g).to(torch.bfloat16)
+    v_new = torch.randn(B, Hkv, 1, d, generator=g).to(torch.bfloat16)
+    pos = torch.full((B,), N - 1, dtype=torch.int32)
+    sh = _shape_of(B, Hq, Hkv, d, r, N)
+    res = []
+    for fused in (False, True):
+        Kd, Vd = _dev(K), _dev(V)
+        kp = torch.empty(B, Hkv, N, r, dtype=torch.uint8, device="cuda")
+        sa.sparse_attn_project_keys(sh, Kd, _dev(P), 0, N, kp)
+        ws = sa.alloc_workspace(sh, N, M)
+        idx = torch.full((B, Hkv, M), -9, dtype=torch.int32, device="cuda")
+        out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+        if fused:
+            sa.sparse_attn_decode_step(sh, _dev(pos), _dev(k_new), _dev(v_new), _dev(q), _dev(P),
+                                       Kd, Vd, kp, None, N, M, default_scale(d), idx, out, lse,
+                                       ws)
+        else:
+            sa.sparse_attn_append_kv(sh, _dev(pos), _dev(k_new), _dev(v_new), _dev(P), Kd, Vd, kp)
+            sa.sparse_attn_index_topm(sh, _dev(q), _dev(P), kp, None, N, M, idx, ws)
+            sa.sparse_attn_decode(sh, _dev(q), Kd, Vd, idx, M, default_scale(d), out, lse, ws)
+        torch.cuda.synchronize()
+        res.append((Kd, Vd, kp, idx, out, lse))
+    for x, y in zip(res[0], res[1]):
+        assert torch.equal(x, y)
+    _, _, _, idx, out, _ = res[1]
+    gi, go = idx.cpu().numpy(), f64(out)
+    P64 = P.double().numpy()
+    q64 = f64(q)
+    for (b, h), (lo, hi) in runs.items():
+        K0, V0 = K64[b, h], f64(V)[b, h]
+        kp0 = oracle.project_keys(K0, P64[h])[None, None]
+        K2, V2, kp2 = oracle.append_kv(K0[None, None], V0[None, None], kp0,
+                                       pos.numpy()[b:b + 1], f64(k_new)[b:b + 1, h:h + 1],
+                                       f64(v_new)[b:b + 1, h:h + 1], P64[h:h + 1])
+        qg = q64[b, h * G:(h + 1) * G]
+        oi, oo, _, sc = oracle.decode_step_unit(qg, K2[0, 0], V2[0, 0], kp2[0, 0], P64[h], N, M,
+                                                default_scale(d))
+        swaps = check_topm_unit(gi[b, h], sc, M, N)
+        _say("  unit", (b, h), "band swaps", swaps)
+        assert np.isin(gi[b, h], np.arange(lo, hi)).mean() > 0.9
+        if not np.array_equal(gi[b, h], oi):
+            oo, _ = oracle.sparse_attention(qg, K2[0, 0], V2[0, 0], gi[b, h], default_scale(d))
+        check_attention(go[b, h * G:(h + 1) * G], oo, "clustered unit %s" % ((b, h),))
+
+
 # ------------------------------------------------------------------ decode step
 
 @pytest.mark.parametrize("B,Hq,Hkv,d,r,N,M", [

@@ -466,7 +466,19 @@ def cpu_baseline(inp, wl, n_units, min_seconds=10.0, seed=0):
         step_all = wall / done * wl.B * wl.Hkv
         res["all_threads"] = {"value": round(1.0 / step_all, 4), "threads": threads,
                               "unit_steps": done, "seconds_measured": round(wall, 2)}
+    res["cpu_model"] = _cpu_model()
     return res
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main(argv=None):

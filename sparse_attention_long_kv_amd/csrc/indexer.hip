@@ -227,6 +227,22 @@ __device__ void pick_bin(Sh& sh, int width, uint32_t target, uint32_t& path, uin
   path = (path << width) | b;
 }
 
+// hist[bin] += 1 for every active lane.  Lanes whose bin is the first active
+// lane's add together with one atomic: runs of equal keys (ties, or a digit
+// all the keys share) would otherwise queue on one LDS address, 64 per wave.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin) {
+  const uint32_t lead = __builtin_amdgcn_readfirstlane(bin);
+  const bool same = bin == lead;
+  const uint64_t m = ballot(same);
+  if (same) {
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (below == 0u) atomicAdd(&hist[lead], (uint32_t)popc64(m));
+  } else {
+    atomicAdd(&hist[bin], 1u);
+  }
+}
+
 // One radix level over keys produced by `visit(f)`, which calls f(key, valid)
 // for each key this thread owns.  Keys off `path` (and invalid ones) count
 // into the lane's private dummy bin so the atomics need no branch.
@@ -243,7 +259,7 @@ __device__ __forceinline__ void radix_level(Sh& sh, int top, int lo, uint32_t ta
   asm volatile("" : "+v"(pth));
   visit([&](uint32_t k, bool valid) {
     const bool on = valid && (top >= 32 || (k >> top) == pth);
-    atomicAdd(&sh.hist[on ? ((k >> lo) & digit_mask) : dummy], 1u);
+    hist_add(sh.hist, on ? ((k >> lo) & digit_mask) : dummy);
   });
   __syncthreads();
   pick_bin<NT>(sh, width, target, path, above);
@@ -1443,7 +1459,7 @@ __device__ __forceinline__ void emit_bitmap(SelectShared<NT>& sh, uint32_t* bm, 
     const uint32_t dummy = (uint32_t)(kBins + lane);
     visit([&](uint32_t k, int p, bool valid) {
       const bool e = valid && k == t;
-      atomicAdd(&sh.hist[e ? (~(uint32_t)p >> kTopShift) : dummy], 1u);
+      hist_add(sh.hist, e ? (~(uint32_t)p >> kTopShift) : dummy);
     });
     __syncthreads();
     uint32_t tp, np, ep;
@@ -1586,20 +1602,43 @@ __device__ __forceinline__ void select_unit_streaming(const FilterArgs& a, Selec
   __syncthreads();
   float qlo[16], qhi[16];
   if constexpr (R != kScoreInput) query_halves<R>(sh.qt, qlo, qhi);
-  auto score_at = [&](int p) {
-    if constexpr (R == kScoreInput) return a.scores[(size_t)u * a.n_max + p];
-    else return position_score<R>(qlo, qhi, a.kp + ((size_t)u * a.Ncap + p) * R);
-  };
+  // Every pass visits the thread's positions p0 + tid in order, the loads of
+  // kAhead of them going out before any is scored (the chains and their
+  // order are position_score's).
+  constexpr int kAhead = 2;
   auto visit3 = [&](auto&& f) {
-    for (int p0 = 0; p0 < len; p0 += NT) {
-      const int p = p0 + tid;
-      const bool ok = p < len;
-      const float s = score_at(ok ? p : 0);
-      f(ok ? score_key(s + 0.0f) : 0u, p, ok);
+    for (int p0 = 0; p0 < len; p0 += NT * kAhead) {   // block-uniform
+      uint4 ca[kAhead], cb[kAhead];
+      float sv[kAhead];
+#pragma unroll
+      for (int k = 0; k < kAhead; ++k) {
+        const int p = p0 + k * NT + tid;
+        const int pc = p < len ? p : 0;
+        if constexpr (R == kScoreInput) {
+          sv[k] = a.scores[(size_t)u * a.n_max + pc];
+        } else {
+          const uint8_t* row = a.kp + ((size_t)u * a.Ncap + pc) * R;
+          ca[k] = load16(row);
+          if (R == 32) cb[k] = load16(row + 16);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kAhead; ++k) {
+        const int p = p0 + k * NT + tid;
+        const bool ok = p < len;
+        float s;
+        if constexpr (R == kScoreInput) {
+          s = sv[k];
+        } else {
+          s = score16(qlo, ca[k]);
+          if (R == 32) s = s + score16(qhi, cb[k]);
+        }
+        f(ok ? score_key(s + 0.0f) : 0u, p, ok);
+      }
     }
   };
   const uint32_t dummy = (uint32_t)(kBins + lane_id());
-  visit3([&](uint32_t k, int, bool ok) { atomicAdd(&sh.hist[ok ? (k >> kTopShift) : dummy], 1u); });
+  visit3([&](uint32_t k, int, bool ok) { hist_add(sh.hist, ok ? (k >> kTopShift) : dummy); });
   __syncthreads();
   uint32_t t, need, eq;
   finish_threshold<NT>(sh, (uint32_t)a.M, t, need, eq, [&](auto&& f) {

@@ -478,15 +478,17 @@ def _bench_sequence(inp, sh, M, ws):
     return kp, idx, out, lse
 
 
-@pytest.mark.parametrize("name", ["longctx_128k", "gqa7_16k"])
-def test_full_size_step_on_sampled_units(name):
+@pytest.mark.parametrize("name,over", [("longctx_128k", {}), ("gqa7_16k", {}),
+                                       ("longctx_128k", {"d": 64, "r": 16})])
+def test_full_size_step_on_sampled_units(name, over):
     """Whole workload at its real size; the oracle checks a sample of units
     (first, last, and two seeded ones), and every unit is checked for
     properties that hold at any size: idx ascending, distinct, in range and
     -1-padded only past the valid count; the two-call selection equals the
     one-call selection; nearly all planted rows are selected."""
-    wl = WORKLOADS[name]
-    _say("case: full size", wl.name, "B=%d Hkv=%d N=%d M=%d" % (wl.B, wl.Hkv, wl.N, wl.M))
+    wl = scaled(WORKLOADS[name], **over) if over else WORKLOADS[name]
+    _say("case: full size", wl.name, "B=%d Hkv=%d d=%d r=%d N=%d M=%d"
+         % (wl.B, wl.Hkv, wl.d, wl.r, wl.N, wl.M))
     inp = make_decode_inputs(wl, seed=7, device="cuda")
     rng = np.random.default_rng(11)
     picks = sorted({(0, 0), (wl.B - 1, wl.Hkv - 1)}

@@ -512,7 +512,7 @@ def main(argv=None):
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every step of this path is independent per "
-              "(batch row, KV head) unit and this build runs on a single MI355X; "
+              "(batch row, KV head) unit and this benchmark measures a single MI355X; "
               "--gpus %d is not supported." % a.gpus, file=sys.stderr)
         sys.exit(2)
 

@@ -281,6 +281,8 @@ int sparse_attn_decode_step_stage(const sa_shape* shape, int32_t stage, const in
  * w_gate   [Hq][d] fp32; g = 1 / (1 + exp(-(w[hq] . q[hq]))).
  * o_sparse [B][Hq][d] bf16 (output of sparse_attn_decode).
  * out      [B][Hq][d] bf16: g * o_sparse + (1 - g) * (phi(q)^T S) / (phi(q)^T z).
+ *          With an empty state (phi(q)^T z == 0, i.e. z == 0: no token was ever
+ *          added) the linear read-out is 0 and out = g * o_sparse.
  * ------------------------------------------------------------------------- */
 int sparse_attn_linear_gate(const sa_shape* shape, const void* q,
                             const void* k_new, const void* v_new, float* S,

@@ -238,13 +238,18 @@ def linear_gate(q_group, S, z, w_gate, o_sparse):
 
     LISA news items: the linear and sparse branches are merged by a gating
     mechanism.  Reading: o_lin = (phi(q)^T S) / (phi(q)^T z); per query head
-    g = sigmoid(w . q); out = g * o_sparse + (1 - g) * o_lin.
+    g = sigmoid(w . q); out = g * o_sparse + (1 - g) * o_lin.  An empty
+    memory (phi(q)^T z = 0, which with phi > 0 and z a sum of phi values
+    means no token was ever added, so S = 0 too) reads out o_lin = 0: the
+    linear branch then contributes nothing instead of 0 / 0.
     q_group, w_gate, o_sparse: [G, d]; S: [d, d]; z: [d].
     Returns (out [G, d], o_lin [G, d], g [G]).
     """
     q = _f64(q_group)
     phq = elu_plus_one(q)
-    o_lin = (phq @ _f64(S)) / (phq @ _f64(z))[:, None]
+    num = phq @ _f64(S)
+    den = (phq @ _f64(z))[:, None]
+    o_lin = np.divide(num, den, out=np.zeros_like(num), where=den != 0)
     with np.errstate(over="ignore"):
         g = 1.0 / (1.0 + np.exp(-np.sum(_f64(w_gate) * q, axis=1)))
     out = g[:, None] * _f64(o_sparse) + (1.0 - g)[:, None] * o_lin

@@ -7,6 +7,8 @@
 //   S += phi(k) v^T,  z += phi(k)                      (update_state != 0)
 //   o_lin = (phi(q)^T S) / (phi(q)^T z),  g = sigmoid(w . q)
 //   out = g * o_sparse + (1 - g) * o_lin
+// An empty memory (phi(q)^T z = 0: with phi > 0 and z a sum of phi values,
+// no token was ever added) reads out o_lin = 0 instead of 0 / 0.
 // One 1024-thread workgroup per (batch row, KV head).  Thread (row block rb,
 // column j) holds rows rb*RPT .. rb*RPT + RPT - 1 of column j of S: it issues
 // all of their loads first, then updates and writes them back and forms each
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(kGateThreads) void linear_gate_kernel(
     float nsum = 0.0f;
 #pragma unroll
     for (int r = 0; r < RB; ++r) nsum += num[r][g][jj];
-    const float olin = nsum / den[g];
+    const float olin = den[g] != 0.0f ? nsum / den[g] : 0.0f;
     const size_t oi = ((size_t)b * Hq + (size_t)h * G + g) * D + jj;
     const float osp = bf16_at(o_sparse, oi);
     const float gg = gate[g];

@@ -363,6 +363,33 @@ def test_linear_gate_matches_oracle(G, d):
     assert torch.equal(S_before, Sd)
 
 
+def test_linear_gate_empty_state_reads_out_zero():
+    """A fresh state (S = 0, z = 0) read without an update: the linear read-out
+    is defined as 0, so out = g * o_sparse (the oracle's reading), finite."""
+    _say("case: linear_gate empty state")
+    B, Hkv, G, d = 2, 2, 4, 128
+    Hq = G * Hkv
+    sh = _shape_of(B, Hq, Hkv, d, 16, 8)
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, 16, 8, seed=3)
+    g = torch.Generator().manual_seed(4)
+    w = (0.5 * torch.randn(Hq, d, generator=g)).float()
+    o_sp = torch.randn(B, Hq, d, generator=g).to(torch.bfloat16)
+    Sd = torch.zeros(B, Hkv, d, d, dtype=torch.float32, device="cuda")
+    zd = torch.zeros(B, Hkv, d, dtype=torch.float32, device="cuda")
+    out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device="cuda")
+    sa.sparse_attn_linear_gate(sh, _dev(q), _dev(K[:, :, 0]), _dev(V[:, :, 0]), Sd, zd,
+                               _dev(w), _dev(o_sp), out, False)
+    got = f64(out)
+    assert np.all(np.isfinite(got))
+    for b in range(B):
+        for h in range(Hkv):
+            o, o_lin, _ = oracle.linear_gate(f64(q)[b, h * G:(h + 1) * G], np.zeros((d, d)),
+                                             np.zeros(d), w.double().numpy()[h * G:(h + 1) * G],
+                                             f64(o_sp)[b, h * G:(h + 1) * G])
+            assert np.all(o_lin == 0.0)
+            check_attention(got[b, h * G:(h + 1) * G], o, "empty state")
+
+
 # ------------------------------------------------------------------ whole step
 
 def _run_step(inp, sh, M, ws, fused=True):

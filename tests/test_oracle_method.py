@@ -336,3 +336,18 @@ def test_linear_branch_equals_kernelised_attention_sum():
     np.testing.assert_allclose(out1, o_sp, rtol=1e-12, atol=1e-12)
     out0, _, g0 = linear_gate(q, S, z, -big, o_sp)
     np.testing.assert_allclose(out0, o_lin, rtol=1e-12, atol=1e-12)
+
+
+def test_linear_gate_empty_memory_reads_out_zero():
+    """With no token added (S = 0, z = 0) the read-out phi(q)^T z is 0; the
+    reading defines the linear branch's output as 0 then, so the mix is the
+    sparse branch scaled by the gate (scipy's logistic function)."""
+    rng = np.random.default_rng(5)
+    G, d = 3, 8
+    q = rng.standard_normal((G, d))
+    w = rng.standard_normal((G, d))
+    o_sp = rng.standard_normal((G, d))
+    out, o_lin, g = linear_gate(q, np.zeros((d, d)), np.zeros(d), w, o_sp)
+    assert np.all(o_lin == 0.0) and np.all(np.isfinite(out))
+    gate = scipy.special.expit(np.sum(w * q, axis=1))
+    np.testing.assert_allclose(out, gate[:, None] * o_sp, rtol=1e-14, atol=0)

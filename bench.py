@@ -400,22 +400,31 @@ def ingest_counters(fetch_csv, write_csv, calib_mib, kernel=DOMINANT_KERNEL):
 
 
 def cpu_baseline(inp, wl, n_units, min_seconds=10.0, seed=0):
-    """Time the oracle on a bounded sample of (batch row, KV head) units: the
-    sampled units' decode steps are repeated until at least `min_seconds` of
-    oracle time has been measured (each unit's FP8 cache is prepared by the
-    oracle beforehand, untimed: it is cache state, not part of the step)."""
+    """Time the oracle on a bounded sample of (batch row, KV head) units.
+
+    The sampled units' decode steps are repeated until enough oracle time has
+    been measured, first one unit at a time on one thread (numpy/BLAS pinned
+    to one thread), then with the units running concurrently on every host
+    thread this process may use (at most 16: the host's share of one GPU),
+    each call's BLAS still on one thread.  At least that many units are
+    sampled, so every thread has its own.  Each unit's FP8 cache is prepared
+    by the oracle beforehand, untimed: it is cache state, not part of the
+    step.  The headline value is the all-threads rate; `cores` is the number
+    of threads it used."""
+    import concurrent.futures as cf
     import numpy as np
-    import torch
     from threadpoolctl import threadpool_limits
     import oracle
     from workloads import default_scale
 
+    available = len(os.sched_getaffinity(0))
+    threads = max(1, min(16, available))
     rng = np.random.default_rng(seed)
-    units = rng.choice(wl.B * wl.Hkv, size=min(n_units, wl.B * wl.Hkv), replace=False)
+    units = rng.choice(wl.B * wl.Hkv, size=min(max(n_units, threads), wl.B * wl.Hkv),
+                       replace=False)
     G = wl.G
     P64 = inp.P.double().cpu().numpy()
     q64 = inp.q.double().cpu().numpy()
-    total, count = 0.0, 0
     with threadpool_limits(limits=1):
         prepared = []
         for u in units:
@@ -425,29 +434,6 @@ def cpu_baseline(inp, wl, n_units, min_seconds=10.0, seed=0):
             kp = oracle.project_keys(K, P64[h])            # cache state: not timed
             kn = inp.k_new[b, h].double().cpu().numpy()
             prepared.append((b, h, K, V, kp, kn))
-        while total < min_seconds or count < len(prepared):
-            for b, h, K, V, kp, kn in prepared:
-                t0 = time.perf_counter()
-                kp[wl.N - 1] = oracle.project_keys(kn, P64[h])[0]
-                K[wl.N - 1] = kn[0]
-                oracle.decode_step_unit(q64[b, h * G:(h + 1) * G], K, V, kp, P64[h], wl.N,
-                                        wl.M, default_scale(wl.d))
-                total += time.perf_counter() - t0
-                count += 1
-        per_unit = total / count
-        step_s = per_unit * wl.B * wl.Hkv
-        res = {"value": round(1.0 / step_s, 4), "unit": "steps/s", "cores": 1, "kind": "oracle",
-               "sample": "%d unit-steps over %d sampled of the %d (batch row, KV head) units "
-                         "of one step, scaled to the whole step (%.4f s per unit, numpy fp64, "
-                         "BLAS pinned to 1 thread)" % (count, len(units), wl.B * wl.Hkv,
-                                                       per_unit),
-               "seconds_measured": round(total, 2)}
-        # the same oracle on every host thread this process may use (at most
-        # 16): the sampled units run concurrently, one per thread, each call's
-        # BLAS still on one thread (numpy releases the interpreter lock in its
-        # array work)
-        import concurrent.futures as cf
-        threads = max(1, min(16, len(os.sched_getaffinity(0)), len(prepared)))
 
         def one(item):
             b, h, K, V, kp, kn = item
@@ -456,29 +442,58 @@ def cpu_baseline(inp, wl, n_units, min_seconds=10.0, seed=0):
             oracle.decode_step_unit(q64[b, h * G:(h + 1) * G], K, V, kp, P64[h], wl.N, wl.M,
                                     default_scale(wl.d))
 
+        total, count = 0.0, 0
+        while total < min_seconds or count < len(prepared):
+            for item in prepared:
+                t0 = time.perf_counter()
+                one(item)
+                total += time.perf_counter() - t0
+                count += 1
+        per_unit = total / count
+        single = {"value": round(1.0 / (per_unit * wl.B * wl.Hkv), 4), "threads": 1,
+                  "unit_steps": count, "seconds_measured": round(total, 2)}
+
         done, wall = 0, 0.0
         with cf.ThreadPoolExecutor(threads) as ex:
-            while wall < min_seconds / 2:
+            while wall < min_seconds / 2 or done < len(prepared):
                 t0 = time.perf_counter()
                 list(ex.map(one, prepared))
                 wall += time.perf_counter() - t0
                 done += len(prepared)
         step_all = wall / done * wl.B * wl.Hkv
-        res["all_threads"] = {"value": round(1.0 / step_all, 4), "threads": threads,
-                              "unit_steps": done, "seconds_measured": round(wall, 2)}
-    res["cpu_model"] = _cpu_model()
-    return res
+    return {"value": round(1.0 / step_all, 4), "unit": "steps/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of the %d (batch row, KV head) units of one step, run "
+                      "concurrently on %d host threads (%d unit-steps in %.1f s of wall "
+                      "clock), scaled to the whole step; numpy fp64, BLAS one thread per "
+                      "call" % (len(prepared), wl.B * wl.Hkv, threads, done, wall),
+            "seconds_measured": round(wall, 2),
+            "cores_available": available,
+            "single_thread": single,
+            "cpu_model": _cpu_model()}
 
 
 def _cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family/model/stepping
+    numbers (some hosts report only a short model name) and the count of
+    logical CPUs the machine has."""
+    info, n = {}, 0
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    continue
+                k, v = (x.strip() for x in line.split(":", 1))
+                if k == "processor":
+                    n += 1
+                elif k not in info:
+                    info[k] = v
     except OSError:
-        pass
-    return None
+        return None
+    name = info.get("model name", "unknown")
+    return "%s (%s, family %s model %s stepping %s; %d logical CPUs on the host)" % (
+        name, info.get("vendor_id", "?"), info.get("cpu family", "?"), info.get("model", "?"),
+        info.get("stepping", "?"), n)
 
 
 def main(argv=None):

@@ -336,6 +336,21 @@ int sparse_attn_gather_kv(const sa_shape* shape, const int32_t* idx, int32_t M,
  * means nothing).  Returns SA_ERR_INVALID for anything else. */
 int sparse_attn_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/* sparse_attn_selection_fallbacks -- diagnostic, not part of the method: of
+ * the (b, KV head) units of the last selection that ran in `workspace` with
+ * this shape, n_max and M (sparse_attn_topm, sparse_attn_index_topm(_stage),
+ * sparse_attn_decode_step(_stage)), how many were selected by the exact
+ * streaming pass over the unit's codes or scores (taken when the sampled
+ * bound kept fewer than M positions, or more than the merge holds) rather
+ * than from the kept candidates.  Either way the selection is exact; the
+ * count shows which path served a shape.  count: one device int32, written
+ * on `stream` (-1 when the shape uses the chunk-exact method, which has no
+ * such fallback).  Returns SA_ERR_INVALID for a bad pointer, n_max or M,
+ * SA_ERR_WORKSPACE when the workspace is missing or too small. */
+int sparse_attn_selection_fallbacks(const sa_shape* shape, int32_t n_max, int32_t M,
+                                    const void* workspace, size_t ws_bytes, int32_t* count,
+                                    void* stream);
+
 /* Bytes of workspace that sparse_attn_topm, sparse_attn_index_topm(_stage),
  * sparse_attn_decode and sparse_attn_decode_step(_stage) need for this shape,
  * n_max and M (host only, pure).

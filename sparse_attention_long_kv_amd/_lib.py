@@ -75,6 +75,7 @@ _SIGS = {
                                  _SZ, _VP],
     "sparse_attn_gather_kv": [_SP, _VP, _I32, _VP, _VP, _VP, _VP, _VP],
     "sparse_attn_stream_read": [_VP, _SZ, _VP, _VP],
+    "sparse_attn_selection_fallbacks": [_SP, _I32, _I32, _VP, _SZ, _VP, _VP],
     "sparse_attn_workspace_size": [_SP, _I32, _I32],
     "sparse_attn_dense_workspace_size": [_SP, _I32],
     "sparse_attn_status_string": [ctypes.c_int],
@@ -336,3 +337,12 @@ def sparse_attn_linear_gate(shape, q, k_new, v_new, S, z, w_gate, o_sparse, out,
           _dev_ptr(o_sparse, torch.bfloat16, (B, Hq, d), "o_sparse"),
           _dev_ptr(out, torch.bfloat16, (B, Hq, d), "out"), int(bool(update_state)),
           _stream(q))
+
+
+def sparse_attn_selection_fallbacks(shape, n_max, M, workspace, count):
+    """Diagnostic: units of the last selection in `workspace` (same shape,
+    n_max, M) that took the exact streaming pass, written to `count` (a
+    one-element int32 device tensor); -1 for shapes without a filter path."""
+    _call("sparse_attn_selection_fallbacks", _sh(shape), int(n_max), int(M),
+          _dev_ptr(workspace, torch.uint8, name="workspace"), workspace.numel(),
+          _dev_ptr(count, torch.int32, (1,), "count"), _stream(workspace))

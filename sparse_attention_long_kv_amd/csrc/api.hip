@@ -351,3 +351,19 @@ extern "C" int sparse_attn_stream_read(const void* buf, size_t bytes, uint32_t* 
     return SA_ERR_INVALID;
   return finish(run_stream_read(buf, bytes, sink, (hipStream_t)stream), (hipStream_t)stream);
 }
+
+extern "C" int sparse_attn_selection_fallbacks(const sa_shape* shape, int32_t n_max, int32_t M,
+                                               const void* workspace, size_t ws_bytes,
+                                               int32_t* count, void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  if (!ptr_ok(count, A4)) return SA_ERR_INVALID;
+  if (n_max < 1 || n_max > shape->capacity || M < 1 || M > n_max) return SA_ERR_INVALID;
+  if (!ptr_ok(workspace, kAlign) || ws_bytes < workspace_bytes(*shape, n_max, M))
+    return SA_ERR_WORKSPACE;
+  FilterPlan fplan;
+  st = plan_filter(*shape, n_max, M, &fplan);
+  if (st != SA_OK) return st;
+  const LaunchCommon c = common(*shape, stream);
+  return finish(run_count_fallbacks(c, fplan, workspace, count), c.stream);
+}

@@ -145,6 +145,8 @@ int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* p) {
   off = align_up(off + (size_t)units * sizeof(uint32_t), kAlign);
   p->off_qt = off;
   off = align_up(off + (size_t)units * 32 * sizeof(float), kAlign);
+  p->off_path = off;
+  off = align_up(off + (size_t)units * sizeof(int32_t), kAlign);
   // A wave list that fills up goes to the unit's spill pool (one atomic
   // reservation per full list), which follows the unit's chunk slots; its
   // count follows the unit's chunk counts.  Half of the merge's capacity:

@@ -52,7 +52,9 @@ constexpr int kFilterMaxChunk = 32768;   // positions per filter workgroup, at m
 constexpr int kFilterWaves = 8;          // lists per chunk (one per wave of 512 threads)
 constexpr int kSampleBlocks = 128;       // sampled position blocks per unit
 constexpr int kSampleBlock = 8;          // positions per sampled block (256 B of FP8 rows)
-constexpr int kSampleSafety = 3;         // the bound aims at ~3 M keys per unit
+constexpr int kSampleSafety = 3;         // the bound aims at ~3 M keys per unit...
+constexpr int kFilterKeepTarget = kFilterSlots / 4 * 3;   // ...but at most 12288 (3/4 of
+                                         // the merge's slots: >= 2 M up to kFilterMaxM)
 
 // The filter path's merge workgroup can go on to attend over its selection
 // when the 16 waves' G x d output tiles fit the merge's 64 KB bitmap.
@@ -67,7 +69,8 @@ struct FilterPlan {
   int cslots;       // candidate slots per chunk = 8 * cap (one list per wave)
   int spill_cap;    // slots of the unit's spill pool (lists that filled up mid-chunk)
   int64_t ustride;  // pairs per unit: splits * cslots chunk slots, then the spill pool
-  size_t off_thr, off_qt, off_cnt, off_cand, end;
+  size_t off_thr, off_qt, off_path, off_cnt, off_cand, end;   // off_path: per unit, how the
+                                         // last merge selected (0 kept keys, 1 exact pass)
 };
 
 struct DecodePlan {

@@ -935,6 +935,8 @@ struct FilterArgs {
   int64_t ustride;   // pairs per unit in cand: S * cslots, then spill_cap
   uint32_t* thr;     // [units]
   float* qt;         // [units][32] indexer queries (written by the bound stage)
+  int32_t* path;     // [units] how the merge selected: 0 from the kept keys, 1 by the
+                     // exact streaming pass (a diagnostic, read by sparse_attn_selection_fallbacks)
   int32_t* cnt;      // [units][S + 1] kept positions per chunk (-1 when a wave list
                      // overflowed), then the pairs reserved in the spill pool (zeroed by
                      // the bound stage)
@@ -1122,12 +1124,14 @@ __device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<k
       key[i] = ok[i] ? score_key(s + 0.0f) : 0u;
     }
   }
-  // the k-th largest sample key, k ~ kSampleSafety * M * (sample size) / len;
-  // a sample of the whole unit gives the exact M-th key
+  // the k-th largest sample key, k ~ keep * (sample size) / len, so that
+  // about keep = min(kSampleSafety M, kFilterKeepTarget) keys of the unit
+  // reach it: enough above M for the sample's noise, and well inside the
+  // merge's kFilterSlots (a sample of the whole unit gives the exact M-th key)
   const int ns = all ? len : kTotal;
+  const int64_t keep = min((int64_t)kSampleSafety * a.M, (int64_t)kFilterKeepTarget);
   uint32_t k = all ? (uint32_t)a.M
-                   : (uint32_t)min((int64_t)ns,
-                                   ((int64_t)kSampleSafety * a.M * ns + len - 1) / len);
+                   : (uint32_t)min((int64_t)ns, (keep * ns + len - 1) / len);
   k = max(k, 1u);
   const uint32_t dummy = (uint32_t)(kBins + lane_id());
 #pragma unroll
@@ -1678,6 +1682,7 @@ __device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShar
       out[j] = j < len ? j : -1;
       if (idx_u) idx_u[j] = out[j];
     }
+    if (write_idx && tid == 0) a.path[u] = 0;
     __syncthreads();
     return;
   }
@@ -1696,6 +1701,7 @@ __device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShar
   __syncthreads();
   const uint32_t total = red[0];
   __syncthreads();                                    // red is reused below
+  if (write_idx && tid == 0) a.path[u] = total < (uint32_t)M ? 1 : 0;
   if (total < (uint32_t)M) {                          // block-uniform (0 after an overflow)
     select_unit_streaming<D, R>(a, sh, ms.bm, u, b, h, len, idx_u);
     __syncthreads();
@@ -1787,6 +1793,30 @@ __global__ __launch_bounds__(kMergeThreads) void select_attend_kernel(const Filt
 }
 
 
+// Units of the last filter-path selection that took the exact streaming
+// pass (path flag 1); -1 when the shape has no filter path (path == null).
+__global__ __launch_bounds__(256) void count_fallbacks_kernel(const int32_t* __restrict__ path,
+                                                              int units, int32_t* count) {
+  __shared__ uint32_t part[256 / kWave];
+  uint32_t n = 0;
+  if (path)
+    for (int u = threadIdx.x; u < units; u += 256) n += path[u] == 1 ? 1u : 0u;
+  n = wave_sum_u32(n);
+  if (lane_id() == 0) part[threadIdx.x / kWave] = n;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *count = path ? (int32_t)(part[0] + part[1] + part[2] + part[3]) : -1;
+}
+
+hipError_t run_count_fallbacks(const LaunchCommon& c, const FilterPlan& plan,
+                               const void* workspace, int32_t* count) {
+  const int32_t* path =
+      plan.enabled ? (const int32_t*)((const char*)workspace + plan.off_path) : nullptr;
+  hipLaunchKernelGGL(count_fallbacks_kernel, dim3(1), dim3(256), 0, c.stream, path, c.units,
+                     count);
+  return hipGetLastError();
+}
+
 template <int D, int R>
 static void launch_filter_dr(const FilterArgs& a, const AppendArgs* ap, const DecodeArgs* da,
                              int stages, int units, hipStream_t st) {
@@ -1842,6 +1872,7 @@ hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int 
   char* ws = (char*)workspace;
   a.thr = (uint32_t*)(ws + plan.off_thr);
   a.qt = (float*)(ws + plan.off_qt);
+  a.path = (int32_t*)(ws + plan.off_path);
   a.cnt = (int32_t*)(ws + plan.off_cnt);
   a.cand = (uint2*)(ws + plan.off_cand);
   a.spill_cap = plan.spill_cap;

@@ -64,6 +64,10 @@ hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int 
                              const int32_t* seq_lens, int n_max, int M, int32_t* idx,
                              void* workspace, const AppendRows* rows = nullptr,
                              const AttendFused* att = nullptr, const float* scores = nullptr);
+// Diagnostic: units of the last filter-path selection in `workspace` that
+// took the exact streaming pass, written to *count (-1 without a filter path).
+hipError_t run_count_fallbacks(const LaunchCommon& c, const FilterPlan& plan,
+                               const void* workspace, int32_t* count);
 hipError_t run_decode(const LaunchCommon& c, const DecodePlan& plan, const void* q,
                       const void* k_cache, const void* v_cache, const int32_t* idx, int M,
                       float scale, void* out, float* lse, void* workspace);

@@ -66,6 +66,55 @@ def test_hand_example_decode_step():
                                atol=1e-14)
 
 
+def _check_batched_golden(step_fn):
+    """Run a decode_step implementation on the batched hand example; raise
+    AssertionError on any difference from the hand-derived values."""
+    ex = _load("hand_examples.json")["decode_step_batched"]
+    K = np.array(ex["K"], dtype=np.float64)
+    V = np.array(ex["V"], dtype=np.float64)
+    q = np.array(ex["q"], dtype=np.float64)
+    P = np.array(ex["P"], dtype=np.float64)
+    kp = np.stack([np.stack([project_keys(K[b, h], P[h]) for h in range(ex["Hkv"])])
+                   for b in range(ex["B"])])
+    idx, out, lse = step_fn(q, K, V, kp, P, ex["seq_lens"], ex["M"], ex["scale"])
+    assert idx.tolist() == ex["expect_idx"]
+    want_out = np.array([[[_ev(v) for v in row] for row in rows] for rows in ex["expect_out"]])
+    want_lse = np.array([[_ev(v) for v in row] for row in ex["expect_lse"]])
+    np.testing.assert_allclose(out, want_out, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse, want_lse, rtol=1e-13, atol=1e-13)
+
+
+def test_hand_example_batched_decode_step():
+    """Two batch rows of different valid lengths, two KV heads with groups of
+    three query heads: every head's output is its own group's selection (see
+    tests/golden/README.md for the derivation)."""
+    _check_batched_golden(decode_step)
+
+
+def _mutant(find, replace):
+    """oracle.decode_step with one planted mistake (source text substituted)."""
+    import inspect
+    from oracle import jssa
+    src = inspect.getsource(jssa.decode_step)
+    assert find in src, find
+    ns = dict(vars(jssa))
+    exec(compile(src.replace(find, replace), "<mutant>", "exec"), ns)
+    return ns["decode_step"]
+
+
+@pytest.mark.parametrize("find,replace", [
+    # query head hq read as belonging to KV head hq % Hkv instead of hq // G
+    ("qg = q[b, h * G:(h + 1) * G]", "qg = q[b, h::Hkv]"),
+    # every batch row scored over all cached rows instead of its own length
+    ("int(seq_lens[b])", "k_cache.shape[2]"),
+    # outputs written to the wrong query heads
+    ("out[b, h * G:(h + 1) * G] = o", "out[b, h::Hkv] = o"),
+])
+def test_batched_golden_catches_planted_mistakes(find, replace):
+    with pytest.raises(AssertionError):
+        _check_batched_golden(_mutant(find, replace))
+
+
 def test_hand_example_linear_gate():
     ex = _load("hand_examples.json")["linear_gate"]
     K = np.array(ex["K"], dtype=np.float64)

@@ -132,9 +132,13 @@ int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* p) {
     chunk = align_up((size_t)ceil_div(n_max, max_splits), kChunkBlock);
     splits = ceil_div(n_max, chunk);
   }
+  // Wave lists of twice the kept keys a list expects (the bound keeps about
+  // min(kSampleSafety M, kFilterKeepTarget) keys per unit, spread evenly over
+  // the lists), so that only clustered high scores spill.
   const int64_t lists = splits * kFilterWaves;
+  const int64_t keep = std::min<int64_t>((int64_t)kSampleSafety * M, kFilterKeepTarget);
   int64_t cap = kFilterMinCap;
-  while (cap < kFilterMaxCap && cap * 2 * lists <= kFilterSlots) cap *= 2;
+  while (cap < kFilterMaxCap && cap * lists < 2 * keep) cap *= 2;
   p->enabled = true;
   p->chunk = (int)chunk;
   p->splits = (int)splits;

@@ -45,7 +45,7 @@ struct TopmPlan {
 // or a list overflowed.
 constexpr int kFilterMaxN = 1 << 19;     // merge marks selected positions in an LDS bitmap
 constexpr int kFilterMaxM = 6144;        // selected positions staged in LDS by the merge
-constexpr int kFilterSlots = 16384;      // candidate slots per unit (16 per merge thread)
+constexpr int kFilterSlots = 16384;      // kept keys the merge holds per unit (16 per thread)
 constexpr int kFilterMinCap = 128;       // slots per wave list, at least
 constexpr int kFilterMaxCap = 512;       // slots per wave list, at most (staged in LDS)
 constexpr int kFilterMaxChunk = 32768;   // positions per filter workgroup, at most

@@ -1130,6 +1130,10 @@ __device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<k
   // merge's kFilterSlots (a sample of the whole unit gives the exact M-th key)
   const int ns = all ? len : kTotal;
   const int64_t keep = min((int64_t)kSampleSafety * a.M, (int64_t)kFilterKeepTarget);
+  if (!all && keep >= len) {                          // keep every position (len < 12288):
+    if (tid == 0) a.thr[u] = score_key(-__builtin_inff());   // the key of -inf, below all
+    return;
+  }
   uint32_t k = all ? (uint32_t)a.M
                    : (uint32_t)min((int64_t)ns, (keep * ns + len - 1) / len);
   k = max(k, 1u);

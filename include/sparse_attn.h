@@ -73,7 +73,9 @@ typedef enum sa_status {
   SA_ERR_INVALID = -1,     /* bad argument: null/misaligned pointer, bad size */
   SA_ERR_UNSUPPORTED = -2, /* valid but outside the supported shape limits */
   SA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
-  SA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+  SA_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  SA_ERR_TOO_LARGE = -5    /* the shape needs more scratch than the no-allocation
+                              entry point holds (SA_NOALLOC_SCRATCH_BYTES) */
 } sa_status;
 
 /* ---------------------------------------------------------------------------
@@ -239,6 +241,32 @@ int sparse_attn_decode_step(const sa_shape* shape, const int32_t* pos, int32_t T
                             uint8_t* kp_cache, const int32_t* seq_lens, int32_t n_max,
                             int32_t M, float softmax_scale, int32_t* idx, void* out,
                             float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sparse_attn_decode_step_noalloc -- sparse_attn_decode_step for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments and results (the
+ * same kernels), but no workspace argument: the workspace is a static device
+ * array of SA_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU,
+ * held from the library's load until the process ends.  The call allocates
+ * nothing; its first call on a device (that device current in the calling
+ * thread, the device the stream and buffers belong to) looks the array's
+ * address up once.
+ * Limit: shapes with sparse_attn_workspace_size(shape, n_max, M) >
+ * SA_NOALLOC_SCRATCH_BYTES return SA_ERR_TOO_LARGE and launch nothing.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (they need no clearing: the step initialises what it reads), so
+ * calls that overlap on one GPU (other streams, other threads) race; order
+ * them on one stream.
+ * ------------------------------------------------------------------------- */
+#define SA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int sparse_attn_decode_step_noalloc(const sa_shape* shape, const int32_t* pos, int32_t T,
+                                    const void* k_new, const void* v_new, const void* q,
+                                    const float* P, void* k_cache, void* v_cache,
+                                    uint8_t* kp_cache, const int32_t* seq_lens, int32_t n_max,
+                                    int32_t M, float softmax_scale, int32_t* idx, void* out,
+                                    float* lse, void* stream);
 
 /* sparse_attn_decode_step_stage -- the launches of sparse_attn_decode_step,
  * one call each (for timing or scheduling): SA_STEP_APPEND_BOUND, then

@@ -21,6 +21,8 @@ SA_ERR_INVALID = -1
 SA_ERR_UNSUPPORTED = -2
 SA_ERR_WORKSPACE = -3
 SA_ERR_HIP = -4
+SA_ERR_TOO_LARGE = -5
+SA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class SparseAttnError(RuntimeError):
@@ -70,6 +72,8 @@ _SIGS = {
     "sparse_attn_decode_step_stage": [_SP, _I32, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                       _VP, _I32, _I32, ctypes.c_float, _VP, _VP, _VP, _VP, _SZ,
                                       _VP],
+    "sparse_attn_decode_step_noalloc": [_SP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                        _VP, _I32, _I32, ctypes.c_float, _VP, _VP, _VP, _VP],
     "sparse_attn_linear_gate": [_SP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP],
     "sparse_attn_dense_decode": [_SP, _VP, _VP, _VP, _VP, _I32, ctypes.c_float, _VP, _VP, _VP,
                                  _SZ, _VP],
@@ -254,7 +258,8 @@ def _step_args(shape, pos, k_new, v_new, q, P, k_cache, v_cache, kp_cache, seq_l
             _dev_ptr(idx, torch.int32, (B, Hkv, M), "idx"),
             _dev_ptr(out, torch.bfloat16, (B, Hq, d), "out"),
             _opt_ptr(lse, torch.float32, (B, Hq), "lse"),
-            _dev_ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), _stream(q))
+            None if workspace is None else _dev_ptr(workspace, torch.uint8, name="workspace"),
+            0 if workspace is None else workspace.numel(), _stream(q))
 
 
 def sparse_attn_decode_step(shape, pos, k_new, v_new, q, P, k_cache, v_cache, kp_cache,
@@ -270,6 +275,16 @@ def sparse_attn_decode_step_stage(shape, stage, pos, k_new, v_new, q, P, k_cache
     _call("sparse_attn_decode_step_stage", _sh(shape), int(stage),
           *_step_args(shape, pos, k_new, v_new, q, P, k_cache, v_cache, kp_cache, seq_lens,
                       n_max, M, softmax_scale, idx, out, lse, workspace))
+
+
+def sparse_attn_decode_step_noalloc(shape, pos, k_new, v_new, q, P, k_cache, v_cache, kp_cache,
+                                    seq_lens, n_max, M, softmax_scale, idx, out, lse):
+    """sparse_attn_decode_step with the library's static per-GPU scratch as its
+    workspace (no allocation; shapes whose workspace exceeds
+    SA_NOALLOC_SCRATCH_BYTES raise with SA_ERR_TOO_LARGE)."""
+    args = _step_args(shape, pos, k_new, v_new, q, P, k_cache, v_cache, kp_cache, seq_lens,
+                      n_max, M, softmax_scale, idx, out, lse, None)
+    _call("sparse_attn_decode_step_noalloc", _sh(shape), *(args[:16] + args[18:]))
 
 
 def sparse_attn_decode(shape, q, k_cache, v_cache, idx, M, softmax_scale, out, lse, workspace):

@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparse_attn.so")
 
-HIP_SOURCES = ["api.hip", "append.hip", "indexer.hip", "decode.hip", "linear_gate.hip"]
+HIP_SOURCES = ["api.hip", "append.hip", "indexer.hip", "decode.hip", "linear_gate.hip",
+               "noalloc.hip"]
 CXX_SOURCES = ["host_plan.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

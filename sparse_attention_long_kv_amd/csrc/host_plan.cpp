@@ -204,6 +204,8 @@ extern "C" const char* sparse_attn_status_string(int status) {
     case SA_ERR_UNSUPPORTED: return "unsupported shape or size";
     case SA_ERR_WORKSPACE: return "workspace missing or too small";
     case SA_ERR_HIP: return "HIP runtime or launch error";
+    case SA_ERR_TOO_LARGE:
+      return "shape needs more scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }

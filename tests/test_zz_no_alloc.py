@@ -1,0 +1,74 @@
+"""sparse_attn_decode_step_noalloc against sparse_attn_decode_step (GPU).
+
+The entry point for callers that cannot allocate runs the decode step with
+the library's static per-GPU scratch as its workspace.  Called through the C
+ABI twice in a row -- the second call on a smaller shape, so it reads the
+scratch the first one left -- it must write the same caches, idx, out and
+lse, bit for bit, as the allocating entry point on the same inputs.  A shape
+whose workspace exceeds the scratch is refused on the host.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_long_kv_amd as sa
+from workloads import WORKLOADS, make_decode_inputs, scaled, default_scale
+
+pytestmark = pytest.mark.gpu
+
+
+def _step(wl, noalloc):
+    inp = make_decode_inputs(wl, seed=21, device="cuda")
+    sh = sa.make_shape(wl.B, wl.Hq, wl.Hkv, wl.d, wl.r, wl.N)
+    kp = torch.empty(wl.B, wl.Hkv, wl.N, wl.r, dtype=torch.uint8, device="cuda")
+    sa.sparse_attn_project_keys(sh, inp.k_cache, inp.P, 0, wl.N, kp)
+    idx = torch.full((wl.B, wl.Hkv, wl.M), -9, dtype=torch.int32, device="cuda")
+    out = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(wl.B, wl.Hq, dtype=torch.float32, device="cuda")
+    args = (sh, inp.pos, inp.k_new, inp.v_new, inp.q, inp.P, inp.k_cache, inp.v_cache, kp,
+            inp.seq_lens, wl.N, wl.M, default_scale(wl.d), idx, out, lse)
+    if noalloc:
+        sa.sparse_attn_decode_step_noalloc(*args)
+    else:
+        sa.sparse_attn_decode_step(*args, sa.alloc_workspace(sh, wl.N, wl.M))
+    torch.cuda.synchronize()
+    return inp.k_cache, inp.v_cache, kp, idx, out, lse
+
+
+def test_noalloc_step_equals_the_allocating_step_twice():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sa.load()
+    # a workload-shaped call, then a smaller one (fewer units, context and budget)
+    shapes = [scaled(WORKLOADS["gqa7_16k"], N=8192, M=1024, B=4),
+              scaled(WORKLOADS["lisa_32k"], N=4096, M=512, B=2)]
+    for wl in shapes:
+        print("case: noalloc step", wl.name, "B=%d Hkv=%d N=%d M=%d" % (wl.B, wl.Hkv, wl.N, wl.M),
+              flush=True)
+        sh = sa.make_shape(wl.B, wl.Hq, wl.Hkv, wl.d, wl.r, wl.N)
+        assert sa.sparse_attn_workspace_size(sh, wl.N, wl.M) <= sa.SA_NOALLOC_SCRATCH_BYTES
+        ref = _step(wl, noalloc=False)
+        got = _step(wl, noalloc=True)
+        for name, x, y in zip(("k_cache", "v_cache", "kp", "idx", "out", "lse"), ref, got):
+            assert torch.equal(x, y), name
+        gi = got[3].cpu().numpy()
+        assert np.all(np.diff(gi, axis=-1) > 0)
+        del ref, got
+
+
+def test_noalloc_refuses_a_shape_beyond_its_scratch():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sa.load()
+    wl = scaled(WORKLOADS["longctx_128k"], B=64)
+    sh = sa.make_shape(wl.B, wl.Hq, wl.Hkv, wl.d, wl.r, wl.N)
+    assert sa.sparse_attn_workspace_size(sh, wl.N, wl.M) > sa.SA_NOALLOC_SCRATCH_BYTES
+    # host check only: tiny stand-in tensors never reach a kernel, so build the
+    # call with the C ABI directly (the binding would check tensor shapes)
+    import ctypes
+    lib = sa.load()
+    st = lib.sparse_attn_decode_step_noalloc(ctypes.byref(sh), None, 1, None, None, None, None,
+                                             None, None, None, None, wl.N, wl.M, 0.1, None, None,
+                                             None, None)
+    assert st == sa.SA_ERR_TOO_LARGE

@@ -136,12 +136,9 @@ struct SelectArgs {
 #ifndef SA_CHUNK_LOADS_IN_FLIGHT
 #define SA_CHUNK_LOADS_IN_FLIGHT 8
 #endif
-// ... and in the filter kernel, per batch (two batches alternate): 2 (one
-// 512-position row per batch at r = 32) keeps it near 40 VGPRs, so four
-// 512-thread workgroups share a CU and every chunk of a 128K step is resident
-// at once (measured at 128K: 2 -> 187.5 us, 4 -> 188.9, 6 -> 189.4, 8 -> 190.4)
+// ... and in the filter's code stream (two groups of half of them alternate)
 #ifndef SA_FILTER_LOADS_IN_FLIGHT
-#define SA_FILTER_LOADS_IN_FLIGHT 2
+#define SA_FILTER_LOADS_IN_FLIGHT 4
 #endif
 
 // Radix digits of the 32-bit keys, most significant first: [20, 32) holds the
@@ -1271,6 +1268,68 @@ __global__ __launch_bounds__(kSampleThreads) void append_bound_kernel(const Filt
   });
 }
 
+// The FP8 code stream is read once: non-temporal loads (measured on a plain
+// streaming read: 6.1 TB/s with the default policy, 6.6-7.1 TB/s
+// non-temporal, but only when each wave's load covers 1 KB of contiguous
+// bytes -- two 16-byte halves of 32-byte rows loaded lane by lane, each load
+// spanning 2 KB, lose the gain).
+constexpr int kStreamPolicy = 2;   // nt
+
+__device__ __forceinline__ uint4 stream_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const sa_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kStreamPolicy);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Scores of the nv code rows (R bytes each) at the start of `rs`, read as
+// contiguous 16-byte lanes: in round k the workgroup reads bytes
+// [16 NT k, 16 NT (k + 1)), thread t the 16 bytes at 16 NT k + 16 t, that is
+// position PR k + 16 t / R (PR = 16 NT / R positions per round) -- for
+// r = 32 one half (t & 1) of the row.  The two lanes of an r = 32 row each
+// form their half's 16-code chain and add the other's with one DPP step
+// (lo + hi and hi + lo are the same sum), and the even lane owns the
+// position.  keep(s, p, owner) is called by every lane (a wave-uniform call)
+// with p relative to the start; rows past nv read as zero.  L loads per lane
+// are in flight: two groups of L / 2 rounds alternate, one scored while the
+// other loads.  qt: the unit's 32-float indexer query.
+template <int R, int NT, int L, class Keep>
+__device__ __forceinline__ void stream_code_scores(__amdgpu_buffer_rsrc_t rs, int nv,
+                                                   const float* qt, Keep keep) {
+  static_assert(R == 16 || R == 32, "rank");
+  constexpr int PR = NT * 16 / R;
+  constexpr int H = L / 2 > 0 ? L / 2 : 1;
+  const int t = threadIdx.x;
+  const int lane_pos = t * 16 / R;
+  const bool owner = R == 16 || (t & 1) == 0;
+  float ql[16];
+  const int qoff = R == 32 ? 16 * (t & 1) : 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) ql[k] = qt[qoff + k];
+  const int rounds = (nv + PR - 1) / PR;
+  uint4 ga[H], gb[H];
+  auto load = [&](uint4 (&g)[H], int k0) {
+#pragma unroll
+    for (int x = 0; x < H; ++x) g[x] = stream_load16(rs, (uint32_t)((k0 + x) * NT * 16 + t * 16));
+  };
+  auto score = [&](const uint4 (&g)[H], int k0) {
+#pragma unroll
+    for (int x = 0; x < H; ++x) {
+      float s = score16(ql, g[x]);
+      if (R == 32) s = s + dpp_f<kDppQuadSwap1>(s);
+      keep(s, (k0 + x) * PR + lane_pos, owner);
+    }
+  };
+  load(ga, 0);
+  if (H < rounds) load(gb, H);
+  for (int k0 = 0; k0 < rounds; k0 += 2 * H) {        // block-uniform trip counts
+    score(ga, k0);
+    if (k0 + 2 * H < rounds) load(ga, k0 + 2 * H);
+    if (k0 + H < rounds) {
+      score(gb, k0 + H);
+      if (k0 + 3 * H < rounds) load(gb, k0 + 3 * H);
+    }
+  }
+}
+
 template <int D, int R>
 __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs a) {
   constexpr int NT = kChunkThreads;
@@ -1316,8 +1375,8 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
   };
   // One position per lane (the call is wave-uniform): keep it if it is in the
   // chunk and its score reaches the bound.
-  auto keep = [&](float s, int p) {
-    const bool ge = s >= thrf, in = p < pend;
+  auto keep = [&](float s, int p, bool owner) {
+    const bool ge = s >= thrf, in = owner && p < pend;
     const bool sel = ge && in;
     const uint64_t m = ballot(ge) & ballot(in);       // (two compares, no select)
     const uint32_t n = (uint32_t)popc64(m);
@@ -1347,16 +1406,16 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
     };
     auto load_batch = [&](Batch& bt, int i0) {
 #pragma unroll
-      for (int x = 0; x < kBatch; ++x) bt.v[x] = buffer_load16(rs, voff + (uint32_t)((i0 + x) * NT * 16), 0);
+      for (int x = 0; x < kBatch; ++x) bt.v[x] = stream_load16(rs, voff + (uint32_t)((i0 + x) * NT * 16));
     };
     auto score_batch = [&](const Batch& bt, int i0) {
 #pragma unroll
       for (int x = 0; x < kBatch; ++x) {
         const int p = base + 4 * ((i0 + x) * NT + w * kWave + lane);
-        keep(__uint_as_float(bt.v[x].x), p);
-        keep(__uint_as_float(bt.v[x].y), p + 1);
-        keep(__uint_as_float(bt.v[x].z), p + 2);
-        keep(__uint_as_float(bt.v[x].w), p + 3);
+        keep(__uint_as_float(bt.v[x].x), p, true);
+        keep(__uint_as_float(bt.v[x].y), p + 1, true);
+        keep(__uint_as_float(bt.v[x].z), p + 2, true);
+        keep(__uint_as_float(bt.v[x].w), p + 3, true);
       }
     };
     const int rows = (nv + 4 * NT - 1) / (4 * NT);
@@ -1374,51 +1433,9 @@ __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs 
   } else {
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(a.kp + ((size_t)u * a.Ncap + base) * R, (uint32_t)nv * R);
-    // Lane l scores position base + i*NT + 64w + l on its own (both 16-byte
-    // halves of an r = 32 row), so no cross-lane step is needed; the
-    // workgroup's 8 waves read each 512-position row together (one
-    // contiguous stream per workgroup: measured 8-10 us faster than a
-    // contiguous range per wave).
-    const uint32_t voff = (uint32_t)((w * kWave + lane) * R);
-    constexpr int kLoadsPerIter = R / 16;
-    constexpr int kBatch = SA_FILTER_LOADS_IN_FLIGHT / kLoadsPerIter;
-    struct Batch {
-      uint4 a[kBatch], b[kBatch];
-    };
-    auto load_batch = [&](Batch& bt, int i0) {
-#pragma unroll
-      for (int x = 0; x < kBatch; ++x) {
-        const uint32_t off = voff + (uint32_t)((i0 + x) * NT * R);
-        bt.a[x] = buffer_load16(rs, off, 0);
-        if (R == 32) bt.b[x] = buffer_load16(rs, off + 16, 0);
-      }
-    };
-    const int rows = (nv + NT - 1) / NT;
-    Batch b0, b1;
-    load_batch(b0, 0);
-    if (kBatch < rows) load_batch(b1, kBatch);
-    // the query is the same for every lane: read with scalar loads it stays
-    // in scalar registers (an FMA takes one scalar operand), saving 32 VGPRs
-    float qlo[16], qhi[16];
-    query_halves<R>(a.qt + (size_t)u * 32, qlo, qhi);
-    auto score_batch = [&](const Batch& bt, int i0) {
-#pragma unroll
-      for (int x = 0; x < kBatch; ++x) {
-        // the same two chains, added in the same order, as the paired-lane
-        // scoring of the chunk-exact kernel: identical bits
-        float sc = score16(qlo, bt.a[x]);
-        if (R == 32) sc = sc + score16(qhi, bt.b[x]);
-        keep(sc, base + (i0 + x) * NT + w * kWave + lane);
-      }
-    };
-    for (int i0 = 0; i0 < rows; i0 += 2 * kBatch) {
-      score_batch(b0, i0);
-      if (i0 + 2 * kBatch < rows) load_batch(b0, i0 + 2 * kBatch);
-      if (i0 + kBatch < rows) {
-        score_batch(b1, i0 + kBatch);
-        if (i0 + 3 * kBatch < rows) load_batch(b1, i0 + 3 * kBatch);
-      }
-    }
+    stream_code_scores<R, NT, SA_FILTER_LOADS_IN_FLIGHT>(
+        rs, nv, a.qt + (size_t)u * 32,
+        [&](float sc, int p, bool owner) { keep(sc, base + p, owner); });
   }
   // The lists go out only once every wave has finished reading: stores mixed
   // into the read stream cost far more (measured), and one 8-byte store per

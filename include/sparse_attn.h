@@ -379,6 +379,25 @@ int sparse_attn_selection_fallbacks(const sa_shape* shape, int32_t n_max, int32_
                                     const void* workspace, size_t ws_bytes, int32_t* count,
                                     void* stream);
 
+/* sparse_attn_selection_plan -- diagnostic, host only: which method the fused
+ * selection (sparse_attn_index_topm, sparse_attn_decode_step) uses for this
+ * shape, n_max and M on the calling thread's current device:
+ *   SA_PLAN_CHUNK_EXACT (0)  chunks hand over their exact top-M, then a merge
+ *                            launch (n_max > 2^19, M > 6144 or M = n_max);
+ *   SA_PLAN_FILTER (1)       sampled bound, filtering chunks, merge (and, in
+ *                            the decode step, attention in the merge launch);
+ *   SA_PLAN_UNIT (2)         sampled bound, then one workgroup per (b, KV head)
+ *                            unit streams, merges and attends in one launch
+ *                            (when the units fill whole rounds of the device's
+ *                            compute units, units >= 256, G d <= 1024, M <= 2048).
+ * Every plan gives the same idx, out and lse bits.  The environment variable
+ * SPARSE_ATTN_UNIT_WG=0 turns SA_PLAN_UNIT off (a testing aid).  Returns the
+ * plan, or SA_ERR_INVALID / SA_ERR_UNSUPPORTED for arguments the selection
+ * rejects. */
+enum sa_plan { SA_PLAN_CHUNK_EXACT = 0, SA_PLAN_FILTER = 1, SA_PLAN_UNIT = 2 };
+
+int sparse_attn_selection_plan(const sa_shape* shape, int32_t n_max, int32_t M);
+
 /* Bytes of workspace that sparse_attn_topm, sparse_attn_index_topm(_stage),
  * sparse_attn_decode and sparse_attn_decode_step(_stage) need for this shape,
  * n_max and M (host only, pure).

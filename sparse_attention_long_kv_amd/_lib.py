@@ -22,6 +22,7 @@ SA_ERR_UNSUPPORTED = -2
 SA_ERR_WORKSPACE = -3
 SA_ERR_HIP = -4
 SA_ERR_TOO_LARGE = -5
+SA_PLAN_CHUNK_EXACT, SA_PLAN_FILTER, SA_PLAN_UNIT = 0, 1, 2
 SA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -80,6 +81,7 @@ _SIGS = {
     "sparse_attn_gather_kv": [_SP, _VP, _I32, _VP, _VP, _VP, _VP, _VP],
     "sparse_attn_stream_read": [_VP, _SZ, _VP, _VP],
     "sparse_attn_selection_fallbacks": [_SP, _I32, _I32, _VP, _SZ, _VP, _VP],
+    "sparse_attn_selection_plan": [_SP, _I32, _I32],
     "sparse_attn_workspace_size": [_SP, _I32, _I32],
     "sparse_attn_dense_workspace_size": [_SP, _I32],
     "sparse_attn_status_string": [ctypes.c_int],
@@ -361,3 +363,12 @@ def sparse_attn_selection_fallbacks(shape, n_max, M, workspace, count):
     _call("sparse_attn_selection_fallbacks", _sh(shape), int(n_max), int(M),
           _dev_ptr(workspace, torch.uint8, name="workspace"), workspace.numel(),
           _dev_ptr(count, torch.int32, (1,), "count"), _stream(workspace))
+
+
+def sparse_attn_selection_plan(shape, n_max, M):
+    """Diagnostic: the selection method for this shape on the current device
+    (SA_PLAN_CHUNK_EXACT, SA_PLAN_FILTER or SA_PLAN_UNIT)."""
+    st = load().sparse_attn_selection_plan(_sh(shape), int(n_max), int(M))
+    if st < 0:
+        raise SparseAttnError("sparse_attn_selection_plan", st, sparse_attn_status_string(st))
+    return st

@@ -1,6 +1,7 @@
 // C-ABI entry points: host-side checks, planning, launches.
 #include <cmath>
 #include <cstdlib>
+#include <mutex>
 
 #include "host_plan.h"
 #include "kernels.h"
@@ -25,6 +26,28 @@ int finish(hipError_t launch, hipStream_t stream) {
     if (hipGetLastError() != hipSuccess) return SA_ERR_HIP;
   }
   return SA_OK;
+}
+
+// Compute units of the current device (0 if unknown), for the plan that runs
+// one workgroup per unit when the units fill the chip.  SPARSE_ATTN_UNIT_WG=0
+// in the environment keeps the chunked filter plan instead (both give the
+// same bits; a testing aid).
+int unit_cu_count() {
+  const char* e = std::getenv("SPARSE_ATTN_UNIT_WG");
+  if (e && e[0] == '0') return 0;
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static int cache[kMaxDev];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 LaunchCommon common(const sa_shape& s, void* stream) {
@@ -139,7 +162,7 @@ int index_topm_stages(const sa_shape* shape, int stages, const void* q, const fl
                          /*need_idx=*/(stages & kSelectMerge) != 0);
   if (st != SA_OK) return st;
   FilterPlan fplan;
-  st = plan_filter(*shape, n_max, M, &fplan);
+  st = plan_filter(*shape, n_max, M, &fplan, unit_cu_count());
   if (st != SA_OK) return st;
   const LaunchCommon c = common(*shape, stream);
   if (fplan.enabled)
@@ -200,13 +223,29 @@ int decode_step_stages(const sa_shape* shape, int stages, const int32_t* pos, in
   st = check_topm_common(shape, seq_lens, n_max, M, idx, workspace, ws_bytes, &tplan);
   if (st != SA_OK) return st;
   FilterPlan fplan;
-  st = plan_filter(*shape, n_max, M, &fplan);
+  st = plan_filter(*shape, n_max, M, &fplan, unit_cu_count());
   if (st != SA_OK) return st;
   DecodePlan dplan;
   st = plan_decode(*shape, M, &dplan);
   if (st != SA_OK) return st;
   const LaunchCommon c = common(*shape, stream);
   hipError_t e = hipSuccess;
+  if (fplan.unit_wg) {
+    // One workgroup per unit: the candidates stage is the rest of the step
+    // (filter, merge and attention in one launch); the later stages have
+    // nothing left to do.
+    const AttendFused att{&dplan, k_cache, v_cache, softmax_scale, out, lse, workspace};
+    if (stages & kStepAppend) {
+      const AppendRows rows{pos, T, k_new, v_new, k_cache, v_cache};
+      e = run_filter_select(c, fplan, kSelectBound, q, P, kp_cache, seq_lens, n_max, M, idx,
+                            workspace, &rows);
+      if (e != hipSuccess) return finish(e, c.stream);
+    }
+    if (stages & kStepCandidates)
+      e = run_filter_select(c, fplan, kSelectChunks, q, P, kp_cache, seq_lens, n_max, M, idx,
+                            workspace, nullptr, &att);
+    return finish(e, c.stream);
+  }
   if (stages & kStepAppend) {
     if (fplan.enabled) {
       const AppendRows rows{pos, T, k_new, v_new, k_cache, v_cache};
@@ -362,8 +401,22 @@ extern "C" int sparse_attn_selection_fallbacks(const sa_shape* shape, int32_t n_
   if (!ptr_ok(workspace, kAlign) || ws_bytes < workspace_bytes(*shape, n_max, M))
     return SA_ERR_WORKSPACE;
   FilterPlan fplan;
-  st = plan_filter(*shape, n_max, M, &fplan);
+  st = plan_filter(*shape, n_max, M, &fplan, unit_cu_count());
   if (st != SA_OK) return st;
   const LaunchCommon c = common(*shape, stream);
   return finish(run_count_fallbacks(c, fplan, workspace, count), c.stream);
+}
+
+extern "C" int sparse_attn_selection_plan(const sa_shape* shape, int32_t n_max, int32_t M) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  if (n_max < 1 || n_max > shape->capacity || M < 1 || M > n_max) return SA_ERR_INVALID;
+  TopmPlan tplan;
+  st = plan_topm(*shape, n_max, M, &tplan);
+  if (st != SA_OK) return st;
+  FilterPlan fplan;
+  st = plan_filter(*shape, n_max, M, &fplan, unit_cu_count());
+  if (st != SA_OK) return st;
+  if (!fplan.enabled) return SA_PLAN_CHUNK_EXACT;
+  return fplan.unit_wg ? SA_PLAN_UNIT : SA_PLAN_FILTER;
 }

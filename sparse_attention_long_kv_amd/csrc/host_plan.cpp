@@ -115,11 +115,44 @@ size_t dense_workspace_bytes(const sa_shape& s, int n_max) {
   return std::max<size_t>(dp.end, kAlign);
 }
 
-int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* p) {
+int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* p, int cu_count) {
   const int64_t units = (int64_t)s.batch * s.num_kv_heads;
   *p = FilterPlan{};
   p->units = (int)units;
   if (n_max > kFilterMaxN || M > kFilterMaxM || M >= n_max) return SA_OK;
+  const int64_t keep_target = std::min<int64_t>((int64_t)kSampleSafety * M, kFilterKeepTarget);
+  // One workgroup per unit when the units fill whole rounds of the CUs (at
+  // least kUnitMinFill of them), the attention needs no split (units >=
+  // kDecodeTargetBlocks) and fits the merge's LDS (G d <= kFusedAttendMaxGD),
+  // and the wave lists hold twice the kept keys they expect.
+  if (cu_count > 0 && units >= kDecodeTargetBlocks &&
+      (s.num_q_heads / s.num_kv_heads) * s.head_dim <= kFusedAttendMaxGD &&
+      2 * keep_target <= (int64_t)kUnitWaves * kUnitCap) {
+    const int64_t rounds = (units + cu_count - 1) / cu_count;
+    if ((double)units >= kUnitMinFill * (double)(rounds * cu_count)) {
+      p->enabled = true;
+      p->unit_wg = true;
+      p->chunk = (int)align_up((size_t)n_max, kChunkBlock);
+      p->splits = 1;
+      p->cap = kUnitCap;
+      p->cslots = 0;
+      p->spill_cap = kFilterSlots / 2;
+      p->ustride = p->spill_cap;
+      size_t off = 0;
+      p->off_thr = off;
+      off = align_up(off + (size_t)units * sizeof(uint32_t), kAlign);
+      p->off_qt = off;
+      off = align_up(off + (size_t)units * 32 * sizeof(float), kAlign);
+      p->off_path = off;
+      off = align_up(off + (size_t)units * sizeof(int32_t), kAlign);
+      p->off_cnt = off;
+      off = align_up(off + (size_t)units * 2 * sizeof(int32_t), kAlign);
+      p->off_cand = off;                       // the spill pool, (key, position) pairs
+      off = align_up(off + (size_t)units * p->ustride * 2 * sizeof(uint32_t), kAlign);
+      p->end = off;
+      return SA_OK;
+    }
+  }
   // Chunks as large as 32768 positions (fewer, longer workgroups stream
   // better: about two rounds of the chip's slots), smaller while the grid is
   // short of 1024 workgroups, but never more than 16 per unit (lists keep
@@ -136,9 +169,8 @@ int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* p) {
   // min(kSampleSafety M, kFilterKeepTarget) keys per unit, spread evenly over
   // the lists), so that only clustered high scores spill.
   const int64_t lists = splits * kFilterWaves;
-  const int64_t keep = std::min<int64_t>((int64_t)kSampleSafety * M, kFilterKeepTarget);
   int64_t cap = kFilterMinCap;
-  while (cap < kFilterMaxCap && cap * lists < 2 * keep) cap *= 2;
+  while (cap < kFilterMaxCap && cap * lists < 2 * keep_target) cap *= 2;
   p->enabled = true;
   p->chunk = (int)chunk;
   p->splits = (int)splits;

@@ -60,8 +60,16 @@ constexpr int kFilterKeepTarget = kFilterSlots / 4 * 3;   // ...but at most 1228
 // when the 16 waves' G x d output tiles fit the merge's 64 KB bitmap.
 constexpr int kFusedAttendMaxGD = (kFilterMaxN / 8) / (16 * 4);   // G d <= 1024
 
+// One workgroup per unit (the units fill the chip): a 1024-thread workgroup
+// streams the whole unit, keeps its candidates in 16 LDS wave lists, merges
+// them and attends, in one launch.
+constexpr int kUnitWaves = 16;
+constexpr int kUnitCap = 768;            // slots per wave list
+constexpr double kUnitMinFill = 0.9;     // units / (CUs x rounds of workgroups), at least
+
 struct FilterPlan {
   bool enabled;
+  bool unit_wg;     // one workgroup per unit (splits = 1, lists in LDS, spill pool only)
   int units;
   int chunk;        // positions per filter workgroup (multiple of 512)
   int splits;       // chunks per unit
@@ -94,7 +102,10 @@ int plan_decode(const sa_shape& s, int M, DecodePlan* out);
 int plan_dense(const sa_shape& s, int n_max, DecodePlan* out);
 size_t dense_workspace_bytes(const sa_shape& s, int n_max);
 // Fills `out`; out->enabled is false when the shape needs the chunk-exact path.
-int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* out);
+// cu_count > 0 (the device's compute units) allows the one-workgroup-per-unit
+// plan where it applies (its workspace never exceeds the chunked plan's, so
+// workspace_bytes, which plans with cu_count = 0, covers both).
+int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* out, int cu_count = 0);
 // Where the fused merge + attention keeps its split states: past the filter
 // path's workspace.
 inline size_t fused_partials_offset(const FilterPlan& fp) { return align_up(fp.end, kAlign); }

@@ -1681,21 +1681,26 @@ struct MergeShared {
 };
 
 // The merge of unit u by the whole workgroup (it synchronises).  Leaves the
-// unit's M selected positions, ascending and -1 padded, in ms.sh.list (as
-// int32) and, when write_idx, also in idx.
-template <int D, int R>
-__device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShared& ms, int u,
-                                                  bool write_idx) {
+// unit's M selected positions, ascending and -1 padded, in sh.list (as int32)
+// and, when write_idx, also in idx (and the unit's path flag).  The kept
+// candidates come from S + 1 sources: S lists, then the spill pool.
+// count_of(c) (c <= S; called by one wave, lane c) gives source c's count
+// (-1: the list overflowed; the pool's count is compared with a.spill_cap);
+// pair_of(c, j) gives (key, position) of entry j of source c.  bm: the
+// bitmap of kBitmapWords words (also the fallback's); start_s and red:
+// kMergeStarts and kMergeThreads / kWave words.
+template <int D, int R, class CountOf, class PairOf>
+__device__ __forceinline__ void merge_unit_core(const FilterArgs& a, SelectShared<kMergeThreads>& sh,
+                                                uint32_t* bm, uint32_t* start_s, uint32_t* red,
+                                                int u, bool write_idx, int S, CountOf count_of,
+                                                PairOf pair_of) {
   constexpr int NT = kMergeThreads;
   constexpr int KPT = kFilterMergeKeys;
   static_assert(kFilterMaxM <= kListCap - kWave, "the selection is staged in LDS");
-  SelectShared<NT>& sh = ms.sh;
-  uint32_t* start_s = ms.start_s;
-  uint32_t* red = ms.red;
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int len = unit_len(a.seq_lens, b, a.n_max);
-  const int M = a.M, S = a.S;
+  const int M = a.M;
   int32_t* idx_u = write_idx ? a.idx + (size_t)u * M : nullptr;
   int32_t* out = reinterpret_cast<int32_t*>(sh.list);
   if (len <= M) {                                     // every valid position, in order
@@ -1707,12 +1712,12 @@ __device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShar
     __syncthreads();
     return;
   }
-  // Per-chunk counts (S <= 16), with the spill pool as chunk S: one wave
-  // forms their exclusive prefix; a chunk whose lists overflowed (-1), a pool
-  // that ran out, or more candidates than the registers hold send the unit
-  // to the exact fallback.
+  // Per-source counts (S < kMergeStarts), the spill pool last: one wave forms
+  // their exclusive prefix; a list that overflowed (-1), a pool that ran out,
+  // or more candidates than the registers hold send the unit to the exact
+  // fallback.
   if (w == 0) {
-    const int c = lane <= S ? a.cnt[(size_t)u * (S + 1) + lane] : 0;
+    const int c = lane <= S ? count_of(lane) : 0;
     const bool over = ballot(c < 0 || (lane == S && c > a.spill_cap)) != 0;
     const uint32_t v = (uint32_t)max(c, 0);
     const uint32_t incl = wave_inclusive_scan(v);
@@ -1724,15 +1729,13 @@ __device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShar
   __syncthreads();                                    // red is reused below
   if (write_idx && tid == 0) a.path[u] = total < (uint32_t)M ? 1 : 0;
   if (total < (uint32_t)M) {                          // block-uniform (0 after an overflow)
-    select_unit_streaming<D, R>(a, sh, ms.bm, u, b, h, len, idx_u);
+    select_unit_streaming<D, R>(a, sh, bm, u, b, h, len, idx_u);
     __syncthreads();
     return;
   }
-  // The unit's candidates, numbered g = 0 .. total-1 chunk after chunk and
-  // then through the spill pool (chunk S, stored right after chunk S-1's
-  // slots); key g sits in register i = g / NT of thread g % NT.  Only the kept
-  // slots are read: chunk c holds g in [start_c, start_c+1).
-  const uint2* cu = a.cand + (size_t)u * a.ustride;
+  // The unit's candidates, numbered g = 0 .. total-1 source after source; key
+  // g sits in register i = g / NT of thread g % NT.  Source c holds g in
+  // [start_c, start_c+1).
   const int nk = (int)((total + NT - 1) / NT);        // rows in use, <= KPT
   uint32_t key[KPT];
   int32_t pos[KPT];
@@ -1742,11 +1745,11 @@ __device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShar
     pos[i] = 0;
     const uint32_t g = (uint32_t)(i * NT + tid);
     if (i < nk && g < total) {
-      uint32_t c = 0;                                 // last chunk with start_c <= g
+      uint32_t c = 0;                                 // last source with start_c <= g
 #pragma unroll
       for (int step = kMergeStarts / 2; step >= 1; step >>= 1)
         if (start_s[c + step] <= g) c += step;
-      const uint2 kv = cu[(size_t)c * a.cslots + (g - start_s[c])];
+      const uint2 kv = pair_of(c, g - start_s[c]);
       key[i] = kv.x;
       pos[i] = (int32_t)kv.y;
     }
@@ -1762,7 +1765,7 @@ __device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShar
   for (int off = 32; off >= 1; off >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
   if (lane == 0) red[w] = kmax;
   for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
-  __syncthreads();
+  __syncthreads();                                    // (sources are no longer read)
   kmax = 0u;
 #pragma unroll
   for (int ww = 0; ww < NT / kWave; ++ww) kmax = max(kmax, red[ww]);
@@ -1783,7 +1786,20 @@ __device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShar
   });
   // the candidates are in no particular order: emit through a bitmap of the
   // unit's positions
-  emit_selected<NT>(sh, ms.bm, len, t, need, eq, M, nk, key, pos, idx_u);
+  emit_selected<NT>(sh, bm, len, t, need, eq, M, nk, key, pos, idx_u);
+}
+
+// The merge over the filter kernel's chunk lists and the unit's spill pool
+// (in the workspace).
+template <int D, int R>
+__device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShared& ms, int u,
+                                                  bool write_idx) {
+  const int S = a.S;
+  const uint2* cu = a.cand + (size_t)u * a.ustride;
+  merge_unit_core<D, R>(
+      a, ms.sh, ms.bm, ms.start_s, ms.red, u, write_idx, S,
+      [&](int c) { return a.cnt[(size_t)u * (S + 1) + c]; },
+      [&](uint32_t c, uint32_t j) { return cu[(size_t)c * a.cslots + j]; });
 }
 
 template <int D, int R>
@@ -1814,6 +1830,103 @@ __global__ __launch_bounds__(kMergeThreads) void select_attend_kernel(const Filt
 }
 
 
+// ------------------------------------------------------------------ one workgroup per unit
+//
+// When the units fill the chip, one 1024-thread workgroup per unit runs the
+// rest of the step after the bound in one launch: it streams the unit's
+// codes (stream_code_scores, 16 KB of contiguous rows per round), keeps every
+// score >= the unit's bound in the LDS list of the wave that scored it (a
+// full list goes to the unit's spill pool, as in the filter kernel), merges
+// exactly over the 16 lists and the pool (merge_unit_core: the candidates
+// never travel through HBM) and, with ATTEND, attends over the selection it
+// leaves in LDS (AttendWave, the attention kernels' arithmetic, one split).
+
+#ifndef SA_UNIT_LOADS_IN_FLIGHT
+#define SA_UNIT_LOADS_IN_FLIGHT 4
+#endif
+
+struct UnitShared {
+  union {
+    struct {
+      float s[kUnitWaves][kUnitCap];        // kept scores (keyed when merged)
+      int32_t p[kUnitWaves][kUnitCap];      // and their positions
+    } lists;
+    uint32_t bm[kBitmapWords];              // the merge's bitmap; then the output tiles
+  } u;
+  SelectShared<kMergeThreads> sh;
+  uint32_t start_s[kMergeStarts];
+  uint32_t red[kMergeThreads / kWave];
+  uint32_t wn[kUnitWaves];
+  uint32_t spill_n;
+  float sm[kAttendWaves][kMaxHeads], sl[kAttendWaves][kMaxHeads];
+};
+static_assert(kUnitWaves == kMergeThreads / kWave, "one list per wave");
+static_assert(kUnitWaves + 1 <= kMergeStarts, "the lists and the pool fit the merge's table");
+
+template <int D, int R, bool ATTEND>
+__global__ __launch_bounds__(kMergeThreads) void unit_kernel(const FilterArgs a,
+                                                             const DecodeArgs d) {
+  static_assert(kAttendThreads == kMergeThreads, "one workgroup shape for every phase");
+  __shared__ UnitShared us;
+  const int u = blockIdx.x;
+  const int b = u / a.Hkv;
+  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  const int len = unit_len(a.seq_lens, b, a.n_max);
+  if (tid == 0) us.spill_n = 0u;
+  __syncthreads();
+  uint32_t wc = 0;                                    // positions in this wave's list
+  if (len > a.M) {                                    // block-uniform (else all are taken)
+    // key >= thr  <=>  score >= thrf (see filter_kernel)
+    const float thrf = key_score(a.thr[u]);
+    uint2* spill_u = a.cand + (size_t)u * a.ustride;
+    auto spill_list = [&]() {                         // wave-uniform, rare
+      uint32_t at = 0u;
+      if (lane == 0) at = atomicAdd(&us.spill_n, wc);
+      at = (uint32_t)__shfl((int)at, 0, kWave);
+      if (at + wc <= (uint32_t)a.spill_cap) {
+        for (int j = lane; j < (int)wc; j += kWave)
+          spill_u[at + j] = make_uint2(score_key(us.u.lists.s[w][j] + 0.0f),
+                                       (uint32_t)us.u.lists.p[w][j]);
+      }
+      wc = 0;
+    };
+    auto keep = [&](float sc, int p, bool owner) {
+      const bool ge = sc >= thrf, in = owner && p < len;
+      const bool sel = ge && in;
+      const uint64_t m = ballot(ge) & ballot(in);
+      const uint32_t n = (uint32_t)popc64(m);
+      if (wc + n > (uint32_t)kUnitCap) spill_list();
+      const uint32_t slot = wc + __builtin_amdgcn_mbcnt_hi(
+                                     (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (sel && slot < (uint32_t)kUnitCap) {
+        us.u.lists.s[w][slot] = sc;
+        us.u.lists.p[w][slot] = p;
+      }
+      wc += n;
+    };
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(a.kp + (size_t)u * a.Ncap * R, (uint32_t)len * R);
+    stream_code_scores<R, kMergeThreads, SA_UNIT_LOADS_IN_FLIGHT>(rs, len, a.qt + (size_t)u * 32,
+                                                                  keep);
+  }
+  if (lane == 0) us.wn[w] = wc;
+  __syncthreads();                                    // lists, counts and spill writes done
+  merge_unit_core<D, R>(
+      a, us.sh, us.u.bm, us.start_s, us.red, u, true, kUnitWaves,
+      [&](int c) { return c < kUnitWaves ? (int)us.wn[c] : (int)us.spill_n; },
+      [&](uint32_t c, uint32_t j) {
+        return c < (uint32_t)kUnitWaves
+                   ? make_uint2(score_key(us.u.lists.s[c][j] + 0.0f), (uint32_t)us.u.lists.p[c][j])
+                   : a.cand[(size_t)u * a.ustride + j];
+      });
+  if constexpr (ATTEND) {
+    AttendWave<D, kAttendWaves> aw;
+    aw.init(d, u);
+    aw.rows(d, reinterpret_cast<const int32_t*>(us.sh.list), d.M);
+    aw.finish(d, u, 0, us.sm, us.sl, reinterpret_cast<float*>(us.u.bm));
+  }
+}
+
 // Units of the last filter-path selection that took the exact streaming
 // pass (path flag 1); -1 when the shape has no filter path (path == null).
 __global__ __launch_bounds__(256) void count_fallbacks_kernel(const int32_t* __restrict__ path,
@@ -1840,7 +1953,22 @@ hipError_t run_count_fallbacks(const LaunchCommon& c, const FilterPlan& plan,
 
 template <int D, int R>
 static void launch_filter_dr(const FilterArgs& a, const AppendArgs* ap, const DecodeArgs* da,
-                             int stages, int units, hipStream_t st) {
+                             int stages, int units, bool unit_wg, hipStream_t st) {
+  if (unit_wg) {
+    // the bound as below; then one launch for the rest (no merge launch)
+    if ((stages & kSelectBound) && ap)
+      hipLaunchKernelGGL((append_bound_kernel<D, R>), dim3(units), dim3(kSampleThreads), 0, st, a,
+                         *ap);
+    else if (stages & kSelectBound)
+      hipLaunchKernelGGL((sample_kernel<D, R>), dim3(units), dim3(kSampleThreads), 0, st, a);
+    if ((stages & kSelectChunks) && da)
+      hipLaunchKernelGGL((unit_kernel<D, R, true>), dim3(units), dim3(kMergeThreads), 0, st, a,
+                         *da);
+    else if (stages & kSelectChunks)
+      hipLaunchKernelGGL((unit_kernel<D, R, false>), dim3(units), dim3(kMergeThreads), 0, st, a,
+                         DecodeArgs{});
+    return;
+  }
   if ((stages & kSelectBound) && ap)
     hipLaunchKernelGGL((append_bound_kernel<D, R>), dim3(units), dim3(kSampleThreads), 0, st, a,
                        *ap);
@@ -1937,16 +2065,18 @@ hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int 
   }
   const DecodeArgs* dap = att ? &da : nullptr;
   if (scores) {
-    if (rows || att) return hipErrorInvalidValue;
+    if (rows || att || plan.unit_wg) return hipErrorInvalidValue;
     launch_filter_scores(a, stages, plan.units, c.stream);
     return hipGetLastError();
   }
-  if (c.D == 128 && c.R == 32) launch_filter_dr<128, 32>(a, app, dap, stages, plan.units, c.stream);
-  else if (c.D == 128 && c.R == 16) launch_filter_dr<128, 16>(a, app, dap, stages, plan.units, c.stream);
-  else if (c.D == 64 && c.R == 32) launch_filter_dr<64, 32>(a, app, dap, stages, plan.units, c.stream);
-  else launch_filter_dr<64, 16>(a, app, dap, stages, plan.units, c.stream);
+  const bool uw = plan.unit_wg;
+  if (uw && att && da.S != 1) return hipErrorInvalidConfiguration;
+  if (c.D == 128 && c.R == 32) launch_filter_dr<128, 32>(a, app, dap, stages, plan.units, uw, c.stream);
+  else if (c.D == 128 && c.R == 16) launch_filter_dr<128, 16>(a, app, dap, stages, plan.units, uw, c.stream);
+  else if (c.D == 64 && c.R == 32) launch_filter_dr<64, 32>(a, app, dap, stages, plan.units, uw, c.stream);
+  else launch_filter_dr<64, 16>(a, app, dap, stages, plan.units, uw, c.stream);
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess && att && (stages & kSelectMerge)) e = run_combine(c, da);
+  if (e == hipSuccess && att && !uw && (stages & kSelectMerge)) e = run_combine(c, da);
   return e;
 }
 

@@ -10,6 +10,7 @@
 // Signed overflow anywhere in the planning arithmetic aborts (UBSan).
 #include <cstdio>
 #include <cstdlib>
+#include <initializer_list>
 #include <vector>
 
 #include "host_plan.h"
@@ -92,6 +93,20 @@ static void check_one(const sa_shape& s, int n_max, int M) {
   CHECK(ws >= fp.end, "ws covers the filter plan");
   if (fused_attend_ok(s, fp))
     CHECK(ws >= fused_partials_offset(fp) + dp.end, "ws covers the fused partials");
+  // the one-workgroup-per-unit plan (on devices of these compute-unit counts)
+  for (int cus : {80, 256, 304}) {
+    FilterPlan up;
+    CHECK(plan_filter(s, n_max, M, &up, cus) == SA_OK, "plan_filter(cu)");
+    CHECK(up.enabled, "unit plan keeps the filter path enabled");
+    if (!up.unit_wg) continue;
+    CHECK(up.splits == 1 && up.cap == kUnitCap && up.ustride == up.spill_cap, "unit plan shape");
+    CHECK(units >= kDecodeTargetBlocks && dp.splits == 1, "unit plan: attention unsplit");
+    CHECK(up.off_thr == fp.off_thr && up.off_qt == fp.off_qt && up.off_path == fp.off_path,
+          "thr, qt and path flags where the chunked plan has them");
+    CHECK(up.off_cand >= up.off_cnt + (size_t)units * 2 * 4, "unit counts fit");
+    CHECK(up.end >= up.off_cand + (size_t)units * up.ustride * 8, "spill pools fit");
+    CHECK(up.end <= ws, "the workspace size covers the unit plan");
+  }
 }
 
 int main() {

@@ -1009,3 +1009,123 @@ def test_decode_step_equals_the_three_calls(name, N, T, lens, M):
             oo, _ = oracle.sparse_attention(qg, K2[0, 0], V2[0, 0], gi[b, h],
                                             default_scale(wl.d))
         check_attention(go[b, h * G:(h + 1) * G], oo, "unit %s" % ((b, h),))
+
+
+# ------------------------------------------------------------------ one workgroup per unit
+
+UNIT_CASES = [
+    # (B, Hq, Hkv, d, r, N, M, seq_lens): 256 units each, so the units fill the
+    # chip's 256 compute units and the decode step runs one workgroup per unit
+    (32, 32, 8, 128, 32, 8192, 1024, None),
+    (16, 128, 16, 64, 16, 5000, 700, "ragged"),       # G = 8, d = 64, short and empty rows
+    (64, 16, 4, 128, 32, 4096, 2048, None),           # M at the plan's limit
+]
+
+
+def _unit_inputs(B, Hq, Hkv, d, r, N, seed):
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, N, seed=seed)
+    G = Hq // Hkv
+    qbar = f64(q).reshape(B, Hkv, G, d).mean(axis=2)
+    rng = np.random.default_rng(seed)
+    K64 = f64(K)
+    for b in range(B):
+        for h in range(Hkv):
+            rows = rng.choice(N, size=max(1, N // 100), replace=False)
+            K64[b, h, rows] += 2.0 * qbar[b, h]
+    # a run of high scores in two units: their wave lists fill and spill
+    K64[0, 0, 1000:2500] += 3.0 * qbar[0, 0]
+    K64[B - 1, Hkv - 1, 100:3100] += 3.0 * qbar[B - 1, Hkv - 1]
+    return q, torch.from_numpy(K64).to(torch.bfloat16), V, P
+
+
+@pytest.mark.parametrize("case", UNIT_CASES)
+def test_unit_workgroup_plan_equals_chunked_plan(case, monkeypatch):
+    """The one-workgroup-per-unit plan (stream, merge over LDS wave lists and
+    attend in one launch) writes the same caches, idx, out and lse, bit for
+    bit, as the chunked filter plan (SPARSE_ATTN_UNIT_WG=0), for the whole
+    step and for the selection alone; the oracle checks three units."""
+    B, Hq, Hkv, d, r, N, M, lens = case
+    _say("case: unit plan", case)
+    sh = _shape_of(B, Hq, Hkv, d, r, N)
+    G = Hq // Hkv
+    q, K, V, P = _unit_inputs(B, Hq, Hkv, d, r, N, seed=B + Hkv)
+    if lens == "ragged":
+        lens = [N, 0, 700, 1, N - 3, 2000] + [N] * (B - 6)
+    sl = None if lens is None else _dev(torch.tensor(lens, dtype=torch.int32))
+    g = torch.Generator().manual_seed(3)
+    k_new = torch.randn(B, Hkv, 1, d, generator=g).to(torch.bfloat16)
+    v_new = torch.randn(B, Hkv, 1, d, generator=g).to(torch.bfloat16)
+    Ls = [N if lens is None else lens[b] for b in range(B)]
+    pos = torch.tensor([max(L - 1, 0) for L in Ls], dtype=torch.int32)
+    res, plans = {}, {}
+    for flag in ("1", "0"):
+        monkeypatch.setenv("SPARSE_ATTN_UNIT_WG", flag)
+        plans[flag] = sa.sparse_attn_selection_plan(sh, N, M)
+        Kd, Vd = _dev(K), _dev(V)
+        kp = torch.empty(B, Hkv, N, r, dtype=torch.uint8, device="cuda")
+        sa.sparse_attn_project_keys(sh, Kd, _dev(P), 0, N, kp)
+        ws = sa.alloc_workspace(sh, N, M)
+        idx = torch.full((B, Hkv, M), -9, dtype=torch.int32, device="cuda")
+        out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+        for stage in (sa.SA_STEP_APPEND_BOUND, sa.SA_STEP_CANDIDATES, sa.SA_STEP_SELECT_ATTEND):
+            sa.sparse_attn_decode_step_stage(sh, stage, _dev(pos), _dev(k_new), _dev(v_new),
+                                             _dev(q), _dev(P), Kd, Vd, kp, sl, N, M,
+                                             default_scale(d), idx, out, lse, ws)
+        fb = _fallbacks(sh, N, M, ws)
+        idx2 = torch.full_like(idx, -9)
+        sa.sparse_attn_index_topm(sh, _dev(q), _dev(P), kp, sl, N, M, idx2, ws)
+        torch.cuda.synchronize()
+        res[flag] = (Kd, Vd, kp, idx, out, lse, idx2)
+        assert fb == 0, (flag, fb)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert plans["1"] == sa.SA_PLAN_UNIT, plans
+    assert plans["0"] == sa.SA_PLAN_FILTER, plans
+    for name, x, y in zip(("k", "v", "kp", "idx", "out", "lse", "idx_topm"), res["1"], res["0"]):
+        assert torch.equal(x, y), name
+    Kd, Vd, kp, idx, out, lse, idx2 = res["1"]
+    assert torch.equal(idx, idx2)
+    gi, go = idx.cpu().numpy(), f64(out)
+    q64, P64, K64, V64 = f64(q), P.double().numpy(), f64(K), f64(V)
+    for b, h in sorted({(0, 0), (B - 1, Hkv - 1), (min(2, B - 1), 1 % Hkv)}):
+        L = Ls[b]
+        # the oracle's own caches of the unit: its projection of the rows,
+        # then its append of the new token
+        kp0 = oracle.project_keys(K64[b, h], P64[h])[None, None]
+        K2, V2, kp2 = oracle.append_kv(K64[b, h][None, None], V64[b, h][None, None], kp0,
+                                       pos.numpy()[b:b + 1], f64(k_new)[b:b + 1, h:h + 1],
+                                       f64(v_new)[b:b + 1, h:h + 1], P64[h:h + 1])
+        qg = q64[b, h * G:(h + 1) * G]
+        oi, oo, _, sc = oracle.decode_step_unit(qg, K2[0, 0], V2[0, 0], kp2[0, 0], P64[h], L, M,
+                                                default_scale(d))
+        swaps = check_topm_unit(gi[b, h], sc, M, L)
+        _say("  unit", (b, h), "L", L, "band swaps", swaps)
+        if not np.array_equal(gi[b, h], oi):
+            oo, _ = oracle.sparse_attention(qg, K2[0, 0], V2[0, 0], gi[b, h], default_scale(d))
+        check_attention(go[b, h * G:(h + 1) * G], oo, "unit plan %s" % ((b, h),))
+
+
+def test_unit_workgroup_plan_falls_back_exactly():
+    """All scores equal in one unit of a unit-plan shape: its wave lists fill,
+    the spill pool runs out, and the workgroup selects exactly by streaming
+    the unit again (the lowest positions); the other units are unaffected."""
+    _say("case: unit plan, exact fallback")
+    B, Hq, Hkv, d, r, N, M = 32, 32, 8, 64, 16, 32768, 512
+    sh = _shape_of(B, Hq, Hkv, d, r, N)
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, N, seed=51)
+    P64 = P.double().numpy()
+    kp = oracle_kp(f64(K), P64)
+    kp[3, 5] = 0x38                                       # every code 1.0 in unit (3, 5)
+    ws = sa.alloc_workspace(sh, N, M)
+    idx = torch.empty(B, Hkv, M, dtype=torch.int32, device="cuda")
+    sa.sparse_attn_index_topm(sh, _dev(q), _dev(P), _dev(kp), None, N, M, idx, ws)
+    fb = _fallbacks(sh, N, M, ws)
+    gi = idx.cpu().numpy()
+    G = Hq // Hkv
+    assert fb == 1, fb
+    for b, h in ((3, 5), (0, 0), (B - 1, Hkv - 1)):
+        qt = oracle.indexer_query(f64(q)[b, h * G:(h + 1) * G], P64[h])
+        s = oracle.index_scores(qt, kp[b, h])
+        check_topm_unit(gi[b, h], s, M, N)
+    # unit (3, 5): every score equal, so the M lowest positions
+    assert gi[3, 5].tolist() == list(range(M))

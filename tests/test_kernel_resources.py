@@ -25,7 +25,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(bl.HIPCC) and shutil.which("h
                                 reason="hipcc not available")
 
 # kernels on the decode step and the extensions (mangled-name fragments)
-HOT = ("append_bound_kernel", "sample_kernel", "filter_kernel", "filter_merge_kernel",
+HOT = ("append_bound_kernel", "sample_kernel", "filter_kernel", "filter_merge_kernel", "unit_kernel",
        "select_attend_kernel", "decode_kernel", "combine_kernel", "append_kv_kernel",
        "linear_gate_kernel", "index_score_kernel")
 

@@ -35,17 +35,42 @@ sys.path.insert(0, ROOT)
 METRIC = "decode steps/sec and achieved HBM GB/s at N=128K, M=2048, r=32"
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-DOMINANT_KERNEL = "filter_kernel"
+DOMINANT_KERNEL = "unit_kernel"       # the dominant launch of the 128K step (one workgroup per unit)
+KERNEL_SOURCES = ("indexer.hip", "device_common.hpp", "attend_common.hpp")
+PLAN_NAMES = {0: "chunk_exact", 1: "filter", 2: "unit_workgroup"}
+STAGE_NAMES = {1: "SA_STEP_APPEND_BOUND", 2: "SA_STEP_CANDIDATES", 3: "SA_STEP_MERGE",
+               4: "SA_STEP_ATTEND", 5: "SA_STEP_SELECT_ATTEND"}
 
 
-def measure_baselines(sa, torch, inp, wl, sh, kp, idx, ws, timer, stream, reps):
+def step_stages(sa, sh, wl):
+    """The launches of one decode step as the library plans them for this
+    shape on this device: (plan, [(name, stage, kernel)], algorithmic bytes
+    per launch, name of the dominant launch).  With one workgroup per unit
+    the candidates stage is the rest of the step (filter, merge and attention
+    in one launch); otherwise the step is append + bound, candidates, and
+    select + attend."""
+    plan = sa.sparse_attn_selection_plan(sh, wl.N, wl.M)
+    ab = algorithmic_bytes(wl)
+    if plan == sa.SA_PLAN_UNIT:
+        stages = [("append_bound", sa.SA_STEP_APPEND_BOUND, "append_bound_kernel"),
+                  ("filter_merge_attend", sa.SA_STEP_CANDIDATES, "unit_kernel")]
+        nbytes = {"append_bound": ab["append_bound"],
+                  "filter_merge_attend": ab["candidates"] + ab["select_attend"]}
+        return plan, stages, nbytes, "filter_merge_attend"
+    stages = [("append_bound", sa.SA_STEP_APPEND_BOUND, "append_bound_kernel"),
+              ("candidates", sa.SA_STEP_CANDIDATES, "filter_kernel"),
+              ("select_attend", sa.SA_STEP_SELECT_ATTEND, "select_attend_kernel")]
+    return plan, stages, ab, "candidates"
+
+
+def measure_baselines(sa, torch, inp, wl, sh, kp, idx, ws, timer, stream, reps, flush):
     """The JSSA article's two comparisons, on this GPU, outside the timed
     region: full attention over every cached row (its opening paragraph
     compares decoding throughput against it) and gather-then-attend ("Why
     token selection is not enough": the copy took more than half of the
     sparse-attention time at large batch) against the gather-free attention.
-    Every timed call is preceded by an untimed candidates stage (a 1 GB
-    stream) so that no call finds its rows left in the caches by the last."""
+    Every timed call is preceded by an untimed 2 GiB read so that no call
+    finds its rows left in the caches by the last."""
     from workloads import default_scale
     scale = default_scale(wl.d)
     dev = inp.q.device
@@ -58,9 +83,6 @@ def measure_baselines(sa, torch, inp, wl, sh, kp, idx, ws, timer, stream, reps):
     Kg = torch.empty(wl.B, wl.Hkv, wl.M, wl.d, dtype=torch.bfloat16, device=dev)
     Vg = torch.empty_like(Kg)
     glens = inp.seq_lens.clamp(max=wl.M).to(torch.int32)
-    flush = lambda: sa.sparse_attn_decode_step_stage(
-        sh, sa.SA_STEP_CANDIDATES, inp.pos, inp.k_new, inp.v_new, inp.q, inp.P, inp.k_cache,
-        inp.v_cache, kp, inp.seq_lens, wl.N, wl.M, scale, idx, out, None, ws)
     calls = {
         "dense": lambda: sa.sparse_attn_dense_decode(sh, inp.q, inp.k_cache, inp.v_cache,
                                                      inp.seq_lens, wl.N, scale, out, None, dws),
@@ -123,7 +145,69 @@ def _host_timed(torch, fn, reps):
     return 1e6 * (time.perf_counter() - t0) / reps
 
 
-def measure_extensions(sa, torch, dev, reps):
+def _step_calls(sa, sh, wl, x, kp, idx, out, ws, scale):
+    """The decode step of inputs x as its launches (one call each)."""
+    _, stages, _, _ = step_stages(sa, sh, wl)
+    return [(lambda st=st: sa.sparse_attn_decode_step_stage(
+        sh, st, x.pos, x.k_new, x.v_new, x.q, x.P, x.k_cache, x.v_cache, kp, x.seq_lens, wl.N,
+        wl.M, scale, idx, out, None, ws)) for _, st, _ in stages]
+
+
+def _cold_us(torch, timer, stream, fn, flusher, n):
+    """Median, p10 and p90 microseconds of fn timed alone after a cache-evicting
+    read each time (HIP events on the library's stream)."""
+    import numpy as np
+    fn()
+    pool = timer.create(2 * n)
+    for k in range(n):
+        flusher()
+        timer.record(pool[2 * k], stream)
+        fn()
+        timer.record(pool[2 * k + 1], stream)
+    torch.cuda.synchronize()
+    us = [1e3 * timer.elapsed_ms(pool[2 * k], pool[2 * k + 1]) for k in range(n)]
+    timer.destroy(pool)
+    return {"median_us": round(float(np.median(us)), 2),
+            "p10_us": round(float(np.percentile(us, 10)), 2),
+            "p90_us": round(float(np.percentile(us, 90)), 2), "steps": n}
+
+
+def measure_small_workloads(sa, torch, dev, timer, stream, flusher, reps):
+    """The decode step of the two single-layer workloads that fit in the 256 MB
+    last-level cache -- gqa7_16k (B8 Hq28 Hkv4 N16384 M2048, 50.9 MB per step)
+    and lisa_32k's sparse branch (B16 Hq32 Hkv8 N32768 M1024, 202.6 MB) --
+    timed cold (each step after a 2 GiB read, so the bytes come from HBM)
+    and back to back; GB/s of algorithmic bytes from the cold median."""
+    from workloads import WORKLOADS, make_decode_inputs, default_scale
+    res = {}
+    for name in ("gqa7_16k", "lisa_32k"):
+        wl = WORKLOADS[name]
+        sh = sa.make_shape(wl.B, wl.Hq, wl.Hkv, wl.d, wl.r, wl.N)
+        x = make_decode_inputs(wl, seed=0, device=dev)
+        kp = torch.empty(wl.B, wl.Hkv, wl.N, wl.r, dtype=torch.uint8, device=dev)
+        sa.sparse_attn_project_keys(sh, x.k_cache, x.P, 0, wl.N, kp)
+        ws = sa.alloc_workspace(sh, wl.N, wl.M, device=dev)
+        idx = torch.empty(wl.B, wl.Hkv, wl.M, dtype=torch.int32, device=dev)
+        out = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.bfloat16, device=dev)
+        calls = _step_calls(sa, sh, wl, x, kp, idx, out, ws, default_scale(wl.d))
+        plan, stages, nbytes, _ = step_stages(sa, sh, wl)
+
+        def step():
+            for c in calls:
+                c()
+        cold = _cold_us(torch, timer, stream, step, flusher, reps)
+        step_bytes = sum(nbytes.values())
+        res[name] = {"plan": PLAN_NAMES.get(plan, str(plan)),
+                     "launches": [k for _, _, k in stages],
+                     "cold": cold, "back_to_back_us": round(_host_timed(torch, step, 3 * reps), 2),
+                     "step_bytes": step_bytes,
+                     "cold_hbm_gbps": round(step_bytes / (cold["median_us"] * 1e-6) / 1e9, 1)}
+        del x, kp, ws
+        torch.cuda.empty_cache()
+    return res
+
+
+def measure_extensions(sa, torch, dev, reps, timer=None, stream=None, flusher=None):
     """The two extensions at their own workloads, outside the timed region.
 
     Cross-layer index reuse (IndexCache pages: layers that reuse the indices
@@ -136,7 +220,10 @@ def measure_extensions(sa, torch, dev, reps):
     sparse one through a gate): the decode step of lisa_32k followed by
     sparse_attn_linear_gate (state update and mix), against the decode step
     alone and against full attention over every cached row.  The linear state
-    holds arbitrary values here (its cost does not depend on them)."""
+    holds arbitrary values here (its cost does not depend on them).
+
+    Both are timed back to back (host clock) and, with a flusher, cold (each
+    eight-layer or hybrid step after a 2 GiB read)."""
     from workloads import WORKLOADS, make_decode_inputs, default_scale
     res = {}
 
@@ -153,14 +240,12 @@ def measure_extensions(sa, torch, dev, reps):
     idx = [torch.empty(B, Hkv, M, dtype=torch.int32, device=dev) for _ in range(wl.layers)]
     out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)
     scale = default_scale(d)
-    stages = (sa.SA_STEP_APPEND_BOUND, sa.SA_STEP_CANDIDATES, sa.SA_STEP_SELECT_ATTEND)
+    full_calls = [_step_calls(sa, sh, wl, layers[l], kps[l], idx[l], out, ws, scale)
+                  for l in range(wl.layers)]
 
     def full(l):
-        x = layers[l]
-        for st in stages:
-            sa.sparse_attn_decode_step_stage(sh, st, x.pos, x.k_new, x.v_new, x.q, x.P,
-                                             x.k_cache, x.v_cache, kps[l], x.seq_lens, N, M,
-                                             scale, idx[l], out, None, ws)
+        for c in full_calls[l]:
+            c()
 
     def reused(l, src):
         x = layers[l]
@@ -200,7 +285,12 @@ def measure_extensions(sa, torch, dev, reps):
         "bytes_per_8_layer_step_every_layer_indexed": bytes_all,
         "hbm_gbps": round(bytes_reuse / (t_reuse * 1e-6) / 1e9, 1),
     }
-    del layers, kps, ws, idx
+    if flusher is not None:
+        cold = _cold_us(torch, timer, stream, step_reuse, flusher, reps)
+        res["index_reuse"]["cold"] = cold
+        res["index_reuse"]["cold_hbm_gbps"] = round(
+            bytes_reuse / (cold["median_us"] * 1e-6) / 1e9, 1)
+    del layers, kps, ws, idx, full_calls
     torch.cuda.empty_cache()
 
     wl = WORKLOADS["lisa_32k"]
@@ -217,12 +307,11 @@ def measure_extensions(sa, torch, dev, reps):
     S = torch.zeros(B, Hkv, d, d, dtype=torch.float32, device=dev)
     z = torch.ones(B, Hkv, d, dtype=torch.float32, device=dev)
     scale = default_scale(d)
+    sparse_calls = _step_calls(sa, sh, wl, x, kp, idx1, o_sp, ws, scale)
 
     def sparse_step():
-        for st in stages:
-            sa.sparse_attn_decode_step_stage(sh, st, x.pos, x.k_new, x.v_new, x.q, x.P,
-                                             x.k_cache, x.v_cache, kp, x.seq_lens, N, M, scale,
-                                             idx1, o_sp, None, ws)
+        for c in sparse_calls:
+            c()
 
     def gate():
         sa.sparse_attn_linear_gate(sh, x.q, x.k_new.view(B, Hkv, d), x.v_new.view(B, Hkv, d),
@@ -251,6 +340,11 @@ def measure_extensions(sa, torch, dev, reps):
         "bytes_per_hybrid_step": hybrid_bytes,
         "hbm_gbps": round(hybrid_bytes / (t_hybrid * 1e-6) / 1e9, 1),
     }
+    if flusher is not None:
+        cold = _cold_us(torch, timer, stream, hybrid_step, flusher, reps)
+        res["gated_hybrid"]["cold"] = cold
+        res["gated_hybrid"]["cold_hbm_gbps"] = round(
+            hybrid_bytes / (cold["median_us"] * 1e-6) / 1e9, 1)
     return res
 
 
@@ -381,7 +475,7 @@ def ingest_counters(fetch_csv, write_csv, calib_mib, kernel=DOMINANT_KERNEL):
         out[label] = {"counter_kib_per_dispatch": kern, "dispatches": n,
                       "calibration_kib": calib, "scale": scale,
                       "bytes_per_launch": kern * 1024.0 * scale}
-    src_hash = _source_hash(["indexer.hip", "device_common.hpp"])
+    src_hash = _source_hash(KERNEL_SOURCES)
     entry = {"source_hash": src_hash,
              "bytes_per_launch": round(out["fetch"]["bytes_per_launch"]
                                        + out["write"]["bytes_per_launch"]),
@@ -496,6 +590,89 @@ def _cpu_model():
         info.get("stepping", "?"), n)
 
 
+class ReadFlush:
+    """A 2 GiB streaming read (sparse_attn_stream_read) that evicts the 256 MB
+    last-level cache before a cold measurement (a read, not a write: a write
+    flush leaves dirty lines whose write-back lands in the next launch)."""
+
+    def __init__(self, sa, torch, dev):
+        self.sa = sa
+        self.buf = torch.empty(2 ** 31, dtype=torch.uint8, device=dev)
+        self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def __call__(self):
+        self.sa.sparse_attn_stream_read(self.buf, self.sink)
+
+
+def cold_steps(timer, stream, calls, names, flusher, n):
+    """Steps timed one at a time, each after a cache-evicting read: median,
+    p10, p90 of the step and the median of each launch (microseconds)."""
+    import numpy as np
+    n_ev = len(calls) + 1
+    pool = timer.create(n_ev * n)
+    for k in range(n):
+        flusher()
+        rec = pool[k * n_ev:(k + 1) * n_ev]
+        for i, call in enumerate(calls):
+            timer.record(rec[i], stream)
+            call()
+        timer.record(rec[-1], stream)
+    import torch
+    torch.cuda.synchronize()
+    per = [[1e3 * timer.elapsed_ms(pool[k * n_ev + i], pool[k * n_ev + i + 1])
+            for i in range(len(calls))] for k in range(n)]
+    us = [1e3 * timer.elapsed_ms(pool[k * n_ev], pool[k * n_ev + n_ev - 1]) for k in range(n)]
+    timer.destroy(pool)
+    q10, q50, q90 = (float(np.percentile(us, p)) for p in (10, 50, 90))
+    return {"steps": n, "read_flush_mib": 2048, "median_us": round(q50, 2),
+            "p10_us": round(q10, 2), "p90_us": round(q90, 2),
+            "median_us_per_call": {k: round(float(np.median([r[i] for r in per])), 2)
+                                   for i, k in enumerate(names)}}
+
+
+def stream_read_gbps(sa, torch, dev, timer, stream, reps=10):
+    """This device's streaming-read rate: one read of 1 GiB with the fastest
+    pattern measured here (sparse_attn_stream_read), GB/s averaged over reps."""
+    rbuf = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        sa.sparse_attn_stream_read(rbuf, sink)
+    pool = timer.create(2 * reps)
+    for k in range(reps):
+        timer.record(pool[2 * k], stream)
+        sa.sparse_attn_stream_read(rbuf, sink)
+        timer.record(pool[2 * k + 1], stream)
+    torch.cuda.synchronize()
+    us = 1e3 * sum(timer.elapsed_ms(pool[2 * k], pool[2 * k + 1]) for k in range(reps)) / reps
+    timer.destroy(pool)
+    return 2 ** 30 / (us * 1e-6) / 1e9
+
+
+def row_read_gbps(sa, torch, sh, idx, wl, inp, timer, stream, flusher, reps=5):
+    """The selected K and V rows (the step's idx) read alone, after a
+    cache-evicting read each time: into registers with the attention's lane
+    layout, and straight into LDS.  GB/s of the rows' bytes."""
+    sink = torch.zeros(1, dtype=torch.int32, device=inp.q.device)
+    valid = int((idx >= 0).sum().item())
+    nbytes = valid * wl.d * 2 * 2
+    res = {}
+    for mode, name in ((0, "registers"), (1, "lds")):
+        sa.sparse_attn_row_read(sh, idx, wl.M, inp.k_cache, inp.v_cache, mode, sink)
+        pool = timer.create(2 * reps)
+        for k in range(reps):
+            flusher()
+            timer.record(pool[2 * k], stream)
+            sa.sparse_attn_row_read(sh, idx, wl.M, inp.k_cache, inp.v_cache, mode, sink)
+            timer.record(pool[2 * k + 1], stream)
+        torch.cuda.synchronize()
+        us = 1e3 * sum(timer.elapsed_ms(pool[2 * k], pool[2 * k + 1])
+                       for k in range(reps)) / reps
+        timer.destroy(pool)
+        res[name] = {"us": round(us, 2), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    res["bytes"] = nbytes
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -552,8 +729,10 @@ def main(argv=None):
     scale = default_scale(wl.d)
     torch.cuda.synchronize()
 
-    # the three launches of sparse_attn_decode_step, one call each
-    names = ("append_bound", "candidates", "select_attend")
+    # the launches of sparse_attn_decode_step, one call each, as the library
+    # plans them for this shape and device
+    plan, stages, bytes_k, dom = step_stages(sa, sh, wl)
+    names = tuple(n for n, _, _ in stages)
     ev = {k: [] for k in names}
     lse = None
 
@@ -561,12 +740,11 @@ def main(argv=None):
         return lambda: sa.sparse_attn_decode_step_stage(
             sh, st, inp.pos, inp.k_new, inp.v_new, inp.q, inp.P, inp.k_cache, inp.v_cache, kp,
             inp.seq_lens, wl.N, wl.M, scale, idx, out, lse, ws)
-    calls = tuple(stage(st) for st in (sa.SA_STEP_APPEND_BOUND, sa.SA_STEP_CANDIDATES,
-                                       sa.SA_STEP_SELECT_ATTEND))
+    calls = tuple(stage(st) for _, st, _ in stages)
 
     timer = HipTimer()
     stream = torch.cuda.current_stream(dev).cuda_stream    # the stream every call launches on
-    dom_i = names.index("candidates")
+    dom_i = names.index(dom)
 
     def step(rec, every_call=False):
         # rec: this step's events.  In the timed region only the dominant call
@@ -624,68 +802,35 @@ def main(argv=None):
     # cold steps (informational): each step alone, bracketed by events, after
     # a 2 GiB read that evicts the 256 MB last-level cache.  (A write flush
     # would leave up to 256 MB of dirty lines whose write-back then lands in
-    # the step's filter launch: ~55 us there, measured.)
+    # the step's first large launch: ~55 us there, measured.)
+    flusher = ReadFlush(sa, torch, dev)
     cold = None
     if a.cold_steps > 0:
-        flush = torch.ones(2 ** 29, dtype=torch.float32, device=dev)
-        acc = torch.empty((), dtype=torch.float32, device=dev)
-        pool = timer.create(n_ev * a.cold_steps)
-        for k in range(a.cold_steps):
-            torch.sum(flush, dim=0, out=acc)
-            rec = pool[k * n_ev:(k + 1) * n_ev]
-            for i, call in enumerate(calls):
-                timer.record(rec[i], stream)
-                call()
-            timer.record(rec[-1], stream)
-        torch.cuda.synchronize()
-        per = [[1e3 * timer.elapsed_ms(pool[k * n_ev + i], pool[k * n_ev + i + 1])
-                for i in range(len(calls))] for k in range(a.cold_steps)]
-        us = [1e3 * timer.elapsed_ms(pool[k * n_ev], pool[k * n_ev + n_ev - 1])
-              for k in range(a.cold_steps)]
-        timer.destroy(pool)
-        del flush, acc
-        q10, q50, q90 = (float(np.percentile(us, p)) for p in (10, 50, 90))
-        cold = {"steps": a.cold_steps, "read_flush_mib": 2048, "median_us": round(q50, 2),
-                "p10_us": round(q10, 2), "p90_us": round(q90, 2),
-                "median_us_per_call": {k: round(float(np.median([r[i] for r in per])), 2)
-                                       for i, k in enumerate(names)}}
+        cold = cold_steps(timer, stream, calls, names, flusher, a.cold_steps)
 
-    # this device's streaming-read rate (context for the roofline): one
-    # contiguous read of 1 GiB with the filter's load pattern
-    rbuf = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
-    sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    for _ in range(3):
-        sa.sparse_attn_stream_read(rbuf, sink)
-    pool = timer.create(20)
-    for k in range(10):
-        timer.record(pool[2 * k], stream)
-        sa.sparse_attn_stream_read(rbuf, sink)
-        timer.record(pool[2 * k + 1], stream)
-    torch.cuda.synchronize()
-    read_us = 1e3 * sum(timer.elapsed_ms(pool[2 * k], pool[2 * k + 1]) for k in range(10)) / 10
-    timer.destroy(pool)
-    del rbuf, sink
-    read_gbps = 2 ** 30 / (read_us * 1e-6) / 1e9
+    # this device's read ceilings (context for the roofline): the fastest
+    # streaming read measured here, and the selected rows read alone
+    read_gbps = stream_read_gbps(sa, torch, dev, timer, stream)
+    row_read = row_read_gbps(sa, torch, sh, idx, wl, inp, timer, stream, flusher)
 
-    bytes_k = algorithmic_bytes(wl)
     step_bytes = sum(bytes_k.values())
     steps_per_s = 1e3 / ms_per_step
     hbm_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # dominant kernel: filter_kernel, the one launch of the candidates stage
-    dom = "candidates"
+    dom_kernel = dict((n, k) for n, _, k in stages)[dom]
     dom_gbps = bytes_k[dom] / (dom_us * 1e-6) / 1e9
-    src_hash = _source_hash(["indexer.hip", "device_common.hpp"])
-    traffic = measured_traffic(DOMINANT_KERNEL, src_hash)
+    src_hash = _source_hash(KERNEL_SOURCES)
+    traffic = measured_traffic(dom_kernel, src_hash)
     roofline = {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
                 "traffic": traffic,
-                "kernel": "%s (sparse_attn_decode_step_stage, SA_STEP_CANDIDATES)"
-                          % DOMINANT_KERNEL,
+                "kernel": "%s (sparse_attn_decode_step_stage, %s)" % (dom_kernel, STAGE_NAMES[
+                    dict((n, st) for n, st, _ in stages)[dom]]),
                 "bytes_per_launch": bytes_k[dom], "avg_launch_us": round(dom_us, 2),
                 "source_hash": src_hash,
                 "read_ceiling_gbps": round(read_gbps, 1),
-                "frac_of_read_ceiling": round(dom_gbps / read_gbps, 4)}
+                "frac_of_read_ceiling": round(dom_gbps / read_gbps, 4),
+                "row_read_ceiling_gbps": row_read}
 
     res = {
         "metric": METRIC, "value": round(steps_per_s, 2), "unit": "steps/s",
@@ -700,6 +845,7 @@ def main(argv=None):
                    "head_dim": wl.d, "context_N": wl.N, "rank_r": wl.r, "budget_M": wl.M},
         "tokens_per_s": round(steps_per_s * wl.B, 1),
         "step_bytes": step_bytes,
+        "plan": PLAN_NAMES.get(plan, str(plan)),
         "kernel_us_breakdown_pass": {k: round(v, 2) for k, v in kern_us.items()},
         "kernel_gbps_breakdown_pass": {k: round(bytes_k[k] / (kern_us[k] * 1e-6) / 1e9, 1)
                                        for k in kern_us
@@ -712,7 +858,7 @@ def main(argv=None):
     if a.baseline_reps > 0:
         print("bench: comparison baselines", file=sys.stderr, flush=True)
         b = measure_baselines(sa, torch, inp, wl, sh, kp, idx, ws, timer, stream,
-                              a.baseline_reps)
+                              a.baseline_reps, flusher)
         b["dense_speedup_of_step"] = round(b["dense_attention_us"] / (1e3 * ms_per_step), 2)
         res["baselines"] = b
     if a.cpu_units > 0:
@@ -722,7 +868,10 @@ def main(argv=None):
         print("bench: extensions", file=sys.stderr, flush=True)
         del inp, kp, ws, idx, out
         torch.cuda.empty_cache()
-        res["extensions"] = measure_extensions(sa, torch, dev, a.ext_reps)
+        res["small_workloads"] = measure_small_workloads(sa, torch, dev, timer, stream, flusher,
+                                                         max(a.ext_reps, 10))
+        res["extensions"] = measure_extensions(sa, torch, dev, a.ext_reps, timer, stream,
+                                               flusher)
     else:
         res["extensions"] = None
     print(json.dumps(res), flush=True)

@@ -354,15 +354,30 @@ int sparse_attn_gather_kv(const sa_shape* shape, const int32_t* idx, int32_t M,
                           void* stream);
 
 /* sparse_attn_stream_read -- measurement helper, not part of the method:
- * reads the `bytes` bytes at `buf` once, front to back, with the load pattern
- * of the filter stage (512-thread workgroups of 256 KiB each, 16-byte loads,
- * four in flight per thread), so that a caller can time this device's
+ * reads the `bytes` bytes at `buf` once, front to back, with the fastest
+ * streaming pattern measured on this GPU (512-thread workgroups of 4 MiB
+ * each, every wave load 1 KB of contiguous bytes, four 16-byte loads per
+ * thread in flight, non-temporal), so that a caller can time the device's
  * streaming-read rate beside the kernels' (the practical ceiling under the
  * nominal HBM peak).  buf: 16-byte aligned device memory; bytes: a positive
- * multiple of 256 KiB; sink: one device uint32 that a value derived from the
+ * multiple of 4 MiB; sink: one device uint32 that a value derived from the
  * data may be written to (it keeps the loads from being optimised away and
  * means nothing).  Returns SA_ERR_INVALID for anything else. */
 int sparse_attn_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
+/* sparse_attn_row_read -- measurement helper, not part of the method: reads
+ * the rows the gather-free attention reads -- for every unit u and j < M, the
+ * d bf16 values of k_cache[u][idx[u][j]] and of v_cache[u][idx[u][j]]
+ * (entries outside [0, Ncap) skipped) -- once each, non-temporal, one
+ * 16-wave workgroup per unit, and computes nothing: the random-row floor the
+ * attention is measured against.  mode 0: into registers, with the
+ * attention's lane layout; mode 1: straight into LDS (buffer loads to LDS,
+ * whole rows per wave load).  idx, k_cache, v_cache as for
+ * sparse_attn_decode; sink as for sparse_attn_stream_read.  Returns
+ * SA_ERR_INVALID for a bad pointer, M < 1 or another mode. */
+int sparse_attn_row_read(const sa_shape* shape, const int32_t* idx, int32_t M,
+                         const void* k_cache, const void* v_cache, int32_t mode, uint32_t* sink,
+                         void* stream);
 
 /* sparse_attn_selection_fallbacks -- diagnostic, not part of the method: of
  * the (b, KV head) units of the last selection that ran in `workspace` with

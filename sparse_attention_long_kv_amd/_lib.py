@@ -80,6 +80,7 @@ _SIGS = {
                                  _SZ, _VP],
     "sparse_attn_gather_kv": [_SP, _VP, _I32, _VP, _VP, _VP, _VP, _VP],
     "sparse_attn_stream_read": [_VP, _SZ, _VP, _VP],
+    "sparse_attn_row_read": [_SP, _VP, _I32, _VP, _VP, _I32, _VP, _VP],
     "sparse_attn_selection_fallbacks": [_SP, _I32, _I32, _VP, _SZ, _VP, _VP],
     "sparse_attn_selection_plan": [_SP, _I32, _I32],
     "sparse_attn_workspace_size": [_SP, _I32, _I32],
@@ -323,7 +324,7 @@ def sparse_attn_dense_workspace_size(shape, n_max):
 
 def sparse_attn_stream_read(buf, sink):
     """Measurement helper: one streaming read of the whole of `buf` (a device
-    tensor of a multiple of 256 KiB); `sink` is a one-element int32 device
+    tensor of a multiple of 4 MiB); `sink` is a one-element int32 device
     tensor the kernel may write (it keeps the loads alive)."""
     p = _dev_ptr(buf, buf.dtype, name="buf")
     _call("sparse_attn_stream_read", p, buf.numel() * buf.element_size(),
@@ -372,3 +373,13 @@ def sparse_attn_selection_plan(shape, n_max, M):
     if st < 0:
         raise SparseAttnError("sparse_attn_selection_plan", st, sparse_attn_status_string(st))
     return st
+
+
+def sparse_attn_row_read(shape, idx, M, k_cache, v_cache, mode, sink):
+    """Measurement helper: read the selected K and V rows once and nothing else
+    (mode 0: into registers, 1: into LDS)."""
+    B, Hkv, d, Nc = shape.batch, shape.num_kv_heads, shape.head_dim, shape.capacity
+    _call("sparse_attn_row_read", _sh(shape), _dev_ptr(idx, torch.int32, (B, Hkv, M), "idx"),
+          int(M), _dev_ptr(k_cache, torch.bfloat16, (B, Hkv, Nc, d), "k_cache"),
+          _dev_ptr(v_cache, torch.bfloat16, (B, Hkv, Nc, d), "v_cache"), int(mode),
+          _dev_ptr(sink, torch.int32, (1,), "sink"), _stream(idx))

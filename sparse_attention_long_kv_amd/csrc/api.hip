@@ -386,7 +386,7 @@ extern "C" int sparse_attn_linear_gate(const sa_shape* shape, const void* q, con
 extern "C" int sparse_attn_stream_read(const void* buf, size_t bytes, uint32_t* sink,
                                        void* stream) {
   if (!ptr_ok(buf, A16) || !ptr_ok(sink, A4)) return SA_ERR_INVALID;
-  if (bytes == 0 || bytes % (256 * 1024) != 0 || bytes / (256 * 1024) > INT32_MAX)
+  if (bytes == 0 || bytes % ((size_t)4 << 20) != 0 || bytes / ((size_t)4 << 20) > INT32_MAX)
     return SA_ERR_INVALID;
   return finish(run_stream_read(buf, bytes, sink, (hipStream_t)stream), (hipStream_t)stream);
 }
@@ -419,4 +419,16 @@ extern "C" int sparse_attn_selection_plan(const sa_shape* shape, int32_t n_max, 
   if (st != SA_OK) return st;
   if (!fplan.enabled) return SA_PLAN_CHUNK_EXACT;
   return fplan.unit_wg ? SA_PLAN_UNIT : SA_PLAN_FILTER;
+}
+
+extern "C" int sparse_attn_row_read(const sa_shape* shape, const int32_t* idx, int32_t M,
+                                    const void* k_cache, const void* v_cache, int32_t mode,
+                                    uint32_t* sink, void* stream) {
+  int st = check_shape(shape);
+  if (st != SA_OK) return st;
+  if (!ptr_ok(idx, A4) || !ptr_ok(k_cache, A16) || !ptr_ok(v_cache, A16) || !ptr_ok(sink, A4))
+    return SA_ERR_INVALID;
+  if (M < 1 || (mode != 0 && mode != 1)) return SA_ERR_INVALID;
+  const LaunchCommon c = common(*shape, stream);
+  return finish(run_row_read(c, idx, M, k_cache, v_cache, mode, sink), c.stream);
 }

@@ -172,18 +172,25 @@ static void launch_decode_d(const DecodeArgs& a, dim3 grid, int units, hipStream
 }
 
 // Streaming read of a buffer (a measurement helper): workgroup w reads the
-// w-th 256 KiB, each thread four 16-byte loads per round.
-constexpr size_t kStreamBytesPerBlock = 256 * 1024;
+// w-th 4 MiB, each wave load 1 KB of contiguous bytes (16 per lane), four
+// loads per thread in flight, non-temporal (the pattern that read fastest on
+// this GPU in a sweep of workgroup sizes, bytes per workgroup, loads in
+// flight and cache policies: ~7 TB/s).
+constexpr size_t kStreamBytesPerBlock = 4u << 20;
+constexpr int kStreamThreads = 512;
 
-__global__ __launch_bounds__(512) void stream_read_kernel(const uint4* __restrict__ p,
-                                                          uint32_t* sink) {
-  constexpr int kPer = (int)(kStreamBytesPerBlock / 16);     // 16384 loads per workgroup
-  const uint4* base = p + (size_t)blockIdx.x * kPer;
+__global__ __launch_bounds__(kStreamThreads) void stream_read_kernel(const uint8_t* __restrict__ p,
+                                                                     uint32_t* sink) {
+  const __amdgpu_buffer_rsrc_t r =
+      make_rsrc(p + (size_t)blockIdx.x * kStreamBytesPerBlock, (uint32_t)kStreamBytesPerBlock);
+  constexpr uint32_t kStep = kStreamThreads * 16 * 4;
   uint32_t acc = 0u;
-  for (int i = threadIdx.x; i < kPer; i += 512 * 4) {
-    uint4 v[4];
+  for (uint32_t base = 0; base < (uint32_t)kStreamBytesPerBlock; base += kStep) {
+    sa_u32x4 v[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = base[i + k * 512];
+    for (int k = 0; k < 4; ++k)
+      v[k] = __builtin_amdgcn_raw_buffer_load_b128(
+          r, (int)(base + k * kStreamThreads * 16 + threadIdx.x * 16), 0, kRowLoadPolicy);
 #pragma unroll
     for (int k = 0; k < 4; ++k) acc ^= v[k].x + v[k].y + v[k].z + v[k].w;
   }
@@ -194,8 +201,101 @@ hipError_t run_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStr
   const size_t blocks = bytes / kStreamBytesPerBlock;
   if (blocks == 0 || blocks * kStreamBytesPerBlock != bytes || blocks > INT32_MAX)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(512), 0, st,
-                     (const uint4*)buf, sink);
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(kStreamThreads), 0, st,
+                     (const uint8_t*)buf, sink);
+  return hipGetLastError();
+}
+
+// Reads of the selected rows alone (a measurement helper): one 16-wave
+// workgroup per unit, wave w taking tiles w, w + 16, ... of 16 selected rows,
+// every K and V row of a tile read once with the non-temporal policy, and
+// nothing computed.  MODE 0: into registers with AttendWave's lane layout;
+// MODE 1: straight into LDS (buffer loads to LDS, each wave load a run of
+// whole rows, one tile per wave in flight).
+template <int D, int MODE>
+__global__ __launch_bounds__(kAttendThreads) void row_read_kernel(const int32_t* __restrict__ idx,
+                                                                 int M, int Ncap,
+                                                                 const uint16_t* __restrict__ k,
+                                                                 const uint16_t* __restrict__ v,
+                                                                 uint32_t* sink) {
+  constexpr int W = kAttendWaves;
+  constexpr int RB = D * 2;                           // bytes per row
+  constexpr int TB = 16 * RB;                         // bytes per 16-row tile (K or V)
+  extern __shared__ uint8_t lds_raw[];
+  const int u = blockIdx.x;
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int q4 = lane >> 4, n16 = lane & 15;
+  const int32_t* iu = idx + (size_t)u * M;
+  const uint32_t ub = (uint32_t)Ncap * RB;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (size_t)u * Ncap * D, ub);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + (size_t)u * Ncap * D, ub);
+  const int ntile = (M + 15) >> 4;
+  auto row_off = [&](int j) -> uint32_t {
+    const int n = j < M ? iu[j] : -1;
+    return (unsigned)n < (unsigned)Ncap ? (uint32_t)n * RB : kOffNone;
+  };
+  uint32_t acc = 0u;
+  for (int tt = w; tt < ntile; tt += W) {
+    if (MODE == 0) {
+      const int tk = 4 * (n16 & 3) + (n16 >> 2);
+      const uint32_t kb = row_off(tt * 16 + tk);
+      sa_u32x4 kx[D / 32];
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+        kx[i] = __builtin_amdgcn_raw_buffer_load_b128(
+            rk, (int)(kb == kOffNone ? kOffNone : kb + 16u * q4 + 64u * i), 0, kRowLoadPolicy);
+      typename VRaw<D>::type vx[4];
+#pragma unroll
+      for (int vv = 0; vv < 4; ++vv) {
+        const uint32_t vb = row_off(tt * 16 + 4 * vv + q4);
+        vx[vv] = load_v_raw<D>(rv, vb == kOffNone ? kOffNone : vb + (uint32_t)(D / 16 * n16) * 2u);
+      }
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) acc ^= kx[i].x + kx[i].w;
+#pragma unroll
+      for (int vv = 0; vv < 4; ++vv) {
+        if constexpr (D == 128) acc ^= vx[vv].x + vx[vv].w;
+        else acc ^= vx[vv].x + vx[vv].y;
+      }
+    } else {
+      // each 1 KB wave load covers 1024 / RB whole rows: lane l reads 16
+      // bytes of row (l * 16) / RB of its group
+      constexpr int RPL = 1024 / RB;                  // rows per wave load
+      constexpr int NL = TB / 1024;                   // wave loads per tile (K or V)
+      char __attribute__((address_space(3)))* lb =
+          (char __attribute__((address_space(3)))*)(lds_raw) + (size_t)w * 2 * TB;
+#pragma unroll
+      for (int i = 0; i < 2 * NL; ++i) {
+        const int row = tt * 16 + (i % NL) * RPL + (lane * 16) / RB;
+        const uint32_t rb = row_off(row);
+        const uint32_t off = rb == kOffNone ? kOffNone : rb + (uint32_t)((lane * 16) % RB);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            i < NL ? rk : rv, (__attribute__((address_space(3))) void*)(lb + i * 1024), 16, off, 0,
+            0, kRowLoadPolicy);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      const uint32_t* lw = reinterpret_cast<const uint32_t*>(lds_raw + (size_t)w * 2 * TB);
+#pragma unroll
+      for (int i = 0; i < 2 * NL; ++i) acc ^= lw[i * 256 + lane * 4];
+    }
+  }
+  if (acc == 0x9E3779B9u) *sink = acc;
+}
+
+hipError_t run_row_read(const LaunchCommon& c, const int32_t* idx, int M, const void* k_cache,
+                        const void* v_cache, int mode, uint32_t* sink) {
+  const dim3 grid((unsigned)c.units), block(kAttendThreads);
+  const size_t lds = mode == 1 ? (size_t)kAttendWaves * 2 * 16 * c.D * 2 : 0;
+  const uint16_t* kk = (const uint16_t*)k_cache;
+  const uint16_t* vv = (const uint16_t*)v_cache;
+  if (c.D == 128 && mode == 0)
+    hipLaunchKernelGGL((row_read_kernel<128, 0>), grid, block, 0, c.stream, idx, M, c.Ncap, kk, vv, sink);
+  else if (c.D == 128)
+    hipLaunchKernelGGL((row_read_kernel<128, 1>), grid, block, lds, c.stream, idx, M, c.Ncap, kk, vv, sink);
+  else if (mode == 0)
+    hipLaunchKernelGGL((row_read_kernel<64, 0>), grid, block, 0, c.stream, idx, M, c.Ncap, kk, vv, sink);
+  else
+    hipLaunchKernelGGL((row_read_kernel<64, 1>), grid, block, lds, c.stream, idx, M, c.Ncap, kk, vv, sink);
   return hipGetLastError();
 }
 

@@ -80,8 +80,11 @@ hipError_t run_gather_kv(const LaunchCommon& c, const int32_t* idx, int M, const
                          const void* v_cache, void* k_out, void* v_out);
 struct DecodeArgs;
 // Merge of the split states when DecodeArgs::S > 1 (no launch otherwise).
-// Streaming read of `bytes` (a positive multiple of 256 KiB) at buf.
+// Streaming read of `bytes` (a positive multiple of 4 MiB) at buf.
 hipError_t run_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
+// Reads of the selected K and V rows alone (mode 0: into registers, 1: into LDS).
+hipError_t run_row_read(const LaunchCommon& c, const int32_t* idx, int M, const void* k_cache,
+                        const void* v_cache, int mode, uint32_t* sink);
 
 hipError_t run_combine(const LaunchCommon& c, const DecodeArgs& a);
 hipError_t run_linear_gate(const LaunchCommon& c, const void* q, const void* k_new,

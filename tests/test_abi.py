@@ -121,10 +121,23 @@ def test_stream_read_rejects_bad_arguments(lib):
     """The measurement helper checks its buffer, size and sink on the host."""
     P = ctypes.c_void_p(_FAKE)
     odd = ctypes.c_void_p(_FAKE + 2)
-    for buf, nbytes, sink in [(None, 1 << 20, P), (odd, 1 << 20, P), (P, 1 << 20, None),
-                              (P, 0, P), (P, 100, P), (P, (1 << 18) + 16, P)]:
+    for buf, nbytes, sink in [(None, 1 << 22, P), (odd, 1 << 22, P), (P, 1 << 22, None),
+                              (P, 0, P), (P, 100, P), (P, 1 << 20, P), (P, (1 << 22) + 16, P)]:
         assert _st(lib, "sparse_attn_stream_read", buf, ctypes.c_size_t(nbytes), sink,
                    None) == sa.SA_ERR_INVALID, (buf, nbytes, sink)
+
+
+def test_row_read_rejects_bad_arguments(lib):
+    wl = WORKLOADS["tiny"]
+    sh = _shape(wl)
+    P = ctypes.c_void_p(_FAKE)
+    odd = ctypes.c_void_p(_FAKE + 2)
+    by = ctypes.byref(sh)
+    for idx, M, k, v, mode, sink in [(None, 4, P, P, 0, P), (P, 0, P, P, 0, P),
+                                     (P, 4, odd, P, 0, P), (P, 4, P, None, 1, P),
+                                     (P, 4, P, P, 2, P), (P, 4, P, P, 0, None)]:
+        assert _st(lib, "sparse_attn_row_read", by, idx, M, k, v, mode, sink,
+                   None) == sa.SA_ERR_INVALID, (idx, M, mode)
 
 
 def test_bad_arguments_are_rejected(lib):

@@ -133,7 +133,7 @@ def test_gather_then_attend(B, Hq, Hkv, d, N, M, lens):
 
 
 def test_stream_read_runs_over_whole_buffers():
-    """The measurement helper reads buffers of multiples of 256 KiB and
+    """The measurement helper reads buffers of multiples of 4 MiB and
     reports no error; the sink is written only for one data-dependent value
     (never for this buffer of ones), so it keeps its contents."""
     _say("case: stream read")
@@ -144,3 +144,26 @@ def test_stream_read_runs_over_whole_buffers():
     assert int(sink.item()) == 7
     with pytest.raises(sa.SparseAttnError):
         sa.sparse_attn_stream_read(buf[:1000], sink)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_row_read_runs_over_selected_rows(d):
+    """The random-row measurement helper reads the selected rows (padding and
+    out-of-range entries skipped) in both modes without error; the sink keeps
+    its contents for these rows of ones."""
+    _say("case: row read d=%d" % d)
+    B, Hq, Hkv, N, M = 2, 8, 2, 5000, 700
+    sh = sa.make_shape(B, Hq, Hkv, d, 16, N)
+    K = torch.ones(B, Hkv, N, d, dtype=torch.bfloat16, device="cuda")
+    V = torch.ones_like(K)
+    rng = np.random.default_rng(3)
+    idx = np.stack([np.stack([np.sort(rng.choice(N, M, replace=False)) for _ in range(Hkv)])
+                    for _ in range(B)]).astype(np.int32)
+    idx[0, 1, -50:] = -1
+    idx[1, 0, ::9] = N + 3
+    idx = torch.from_numpy(idx).cuda()
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    for mode in (0, 1):
+        sa.sparse_attn_row_read(sh, idx, M, K, V, mode, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7

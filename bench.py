@@ -46,17 +46,13 @@ def step_stages(sa, sh, wl):
     """The launches of one decode step as the library plans them for this
     shape on this device: (plan, [(name, stage, kernel)], algorithmic bytes
     per launch, name of the dominant launch).  With one workgroup per unit
-    the candidates stage is the rest of the step (filter, merge and attention
-    in one launch); otherwise the step is append + bound, candidates, and
-    select + attend."""
+    the whole step is one launch (append, bound, filter, merge, attention);
+    otherwise it is append + bound, candidates, and select + attend."""
     plan = sa.sparse_attn_selection_plan(sh, wl.N, wl.M)
     ab = algorithmic_bytes(wl)
     if plan == sa.SA_PLAN_UNIT:
-        stages = [("append_bound", sa.SA_STEP_APPEND_BOUND, "append_bound_kernel"),
-                  ("filter_merge_attend", sa.SA_STEP_CANDIDATES, "unit_kernel")]
-        nbytes = {"append_bound": ab["append_bound"],
-                  "filter_merge_attend": ab["candidates"] + ab["select_attend"]}
-        return plan, stages, nbytes, "filter_merge_attend"
+        stages = [("step", sa.SA_STEP_APPEND_BOUND, "unit_kernel")]
+        return plan, stages, {"step": sum(ab.values())}, "step"
     stages = [("append_bound", sa.SA_STEP_APPEND_BOUND, "append_bound_kernel"),
               ("candidates", sa.SA_STEP_CANDIDATES, "filter_kernel"),
               ("select_attend", sa.SA_STEP_SELECT_ATTEND, "select_attend_kernel")]

@@ -186,6 +186,10 @@ int sparse_attn_index_topm(const sa_shape* shape, const void* q, const float* P,
  *                        more keys than the merge holds, is selected again
  *                        exactly from the FP8 cache).
  * idx is only written by SA_STAGE_MERGE (and may be NULL for the others).
+ * Where one workgroup per unit serves the shape (sparse_attn_selection_plan
+ * gives SA_PLAN_UNIT), SA_STAGE_CANDIDATES is the whole selection in one
+ * launch (bound, filter and merge: it writes idx) and the other two stages
+ * launch nothing.
  * Returns SA_ERR_INVALID for an unknown stage.
  * ------------------------------------------------------------------------- */
 enum sa_stage { SA_STAGE_BOUND = 1, SA_STAGE_CANDIDATES = 2, SA_STAGE_MERGE = 3 };
@@ -275,8 +279,12 @@ int sparse_attn_decode_step_noalloc(const sa_shape* shape, const int32_t* pos, i
  * idx) followed by SA_STEP_ATTEND (writes out, lse).  Both endings give the
  * same bits.  SA_STEP_SELECT_ATTEND is one launch (plus the split merge when
  * the attention is split) when the filter path serves the shape and
- * G * head_dim <= 1024, else the two stages' launches.  Run the stages in
- * order on one stream with identical arguments.
+ * G * head_dim <= 1024, else the two stages' launches.  Where one workgroup
+ * per unit serves the shape (sparse_attn_selection_plan gives SA_PLAN_UNIT),
+ * SA_STEP_APPEND_BOUND is the whole step in one launch (append, bound,
+ * filter, merge and attention: it writes the caches, idx, out and lse) and
+ * the later stages launch nothing.  Run the stages in order on one stream
+ * with identical arguments.
  * Returns SA_ERR_INVALID for an unknown stage. */
 enum sa_step_stage {
   SA_STEP_APPEND_BOUND = 1,
@@ -401,8 +409,8 @@ int sparse_attn_selection_fallbacks(const sa_shape* shape, int32_t n_max, int32_
  *                            launch (n_max > 2^19, M > 6144 or M = n_max);
  *   SA_PLAN_FILTER (1)       sampled bound, filtering chunks, merge (and, in
  *                            the decode step, attention in the merge launch);
- *   SA_PLAN_UNIT (2)         sampled bound, then one workgroup per (b, KV head)
- *                            unit streams, merges and attends in one launch
+ *   SA_PLAN_UNIT (2)         one workgroup per (b, KV head) unit appends,
+ *                            bounds, streams, merges and attends in one launch
  *                            (when the units fill whole rounds of the device's
  *                            compute units, units >= 256, G d <= 1024, M <= 2048).
  * Every plan gives the same idx, out and lse bits.  The environment variable

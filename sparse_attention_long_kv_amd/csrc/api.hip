@@ -231,19 +231,15 @@ int decode_step_stages(const sa_shape* shape, int stages, const int32_t* pos, in
   const LaunchCommon c = common(*shape, stream);
   hipError_t e = hipSuccess;
   if (fplan.unit_wg) {
-    // One workgroup per unit: the candidates stage is the rest of the step
-    // (filter, merge and attention in one launch); the later stages have
-    // nothing left to do.
+    // One workgroup per unit: the whole step is one launch (append, bound,
+    // filter, merge and attention), made by the first stage; the later
+    // stages have nothing left to do.
     const AttendFused att{&dplan, k_cache, v_cache, softmax_scale, out, lse, workspace};
     if (stages & kStepAppend) {
       const AppendRows rows{pos, T, k_new, v_new, k_cache, v_cache};
-      e = run_filter_select(c, fplan, kSelectBound, q, P, kp_cache, seq_lens, n_max, M, idx,
-                            workspace, &rows);
-      if (e != hipSuccess) return finish(e, c.stream);
-    }
-    if (stages & kStepCandidates)
       e = run_filter_select(c, fplan, kSelectChunks, q, P, kp_cache, seq_lens, n_max, M, idx,
-                            workspace, nullptr, &att);
+                            workspace, &rows, &att);
+    }
     return finish(e, c.stream);
   }
   if (stages & kStepAppend) {

@@ -1069,8 +1069,9 @@ hipError_t run_index_score(const LaunchCommon& c, const void* q, const float* P,
 // prologue() runs while the sampled rows are in flight (every thread calls
 // it) and leaves the unit's indexer query in sh.qt.
 template <int D, int R, class Prologue>
-__device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<kSampleThreads>& sh,
-                                             int u, Prologue prologue) {
+__device__ __forceinline__ uint32_t sample_bound(const FilterArgs& a,
+                                                 SelectShared<kSampleThreads>& sh, int u,
+                                                 Prologue prologue) {
   constexpr int NT = kSampleThreads;
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int tid = threadIdx.x;
@@ -1106,7 +1107,7 @@ __device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<k
   }
   if (len <= a.M) {                                   // every valid position is selected
     if (tid == 0) a.thr[u] = 1u;
-    return;
+    return 1u;
   }
   if constexpr (R == kScoreInput) {
 #pragma unroll
@@ -1128,8 +1129,9 @@ __device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<k
   const int ns = all ? len : kTotal;
   const int64_t keep = min((int64_t)kSampleSafety * a.M, (int64_t)kFilterKeepTarget);
   if (!all && keep >= len) {                          // keep every position (len < 12288):
-    if (tid == 0) a.thr[u] = score_key(-__builtin_inff());   // the key of -inf, below all
-    return;
+    const uint32_t low = score_key(-__builtin_inff());   // the key of -inf, below all
+    if (tid == 0) a.thr[u] = low;
+    return low;
   }
   uint32_t k = all ? (uint32_t)a.M
                    : (uint32_t)min((int64_t)ns, (keep * ns + len - 1) / len);
@@ -1145,6 +1147,7 @@ __device__ __forceinline__ void sample_bound(const FilterArgs& a, SelectShared<k
     for (int i = 0; i < kSampleKeys; ++i) f(key[i], key[i] != 0u);
   });
   if (tid == 0) a.thr[u] = t;
+  return t;
 }
 
 template <int D, int R>
@@ -1844,12 +1847,20 @@ __global__ __launch_bounds__(kMergeThreads) void select_attend_kernel(const Filt
 #ifndef SA_UNIT_LOADS_IN_FLIGHT
 #define SA_UNIT_LOADS_IN_FLIGHT 4
 #endif
+// waves that stream (the others wait at the merge's first barrier); the
+// lists' LDS is shared out among them
+#ifndef SA_UNIT_STREAM_WAVES
+#define SA_UNIT_STREAM_WAVES 16
+#endif
+constexpr int kUnitStreamWaves = SA_UNIT_STREAM_WAVES;
+constexpr int kUnitListCap = kUnitWaves * kUnitCap / kUnitStreamWaves;   // slots per list
+static_assert(kUnitStreamWaves >= 1 && kUnitStreamWaves <= kUnitWaves, "streaming waves");
 
 struct UnitShared {
   union {
     struct {
-      float s[kUnitWaves][kUnitCap];        // kept scores (keyed when merged)
-      int32_t p[kUnitWaves][kUnitCap];      // and their positions
+      float s[kUnitStreamWaves][kUnitListCap];     // kept scores (keyed when merged)
+      int32_t p[kUnitStreamWaves][kUnitListCap];   // and their positions
     } lists;
     uint32_t bm[kBitmapWords];              // the merge's bitmap; then the output tiles
   } u;
@@ -1861,23 +1872,40 @@ struct UnitShared {
   float sm[kAttendWaves][kMaxHeads], sl[kAttendWaves][kMaxHeads];
 };
 static_assert(kUnitWaves == kMergeThreads / kWave, "one list per wave");
-static_assert(kUnitWaves + 1 <= kMergeStarts, "the lists and the pool fit the merge's table");
+static_assert(kUnitStreamWaves + 1 <= kMergeStarts, "the lists and the pool fit the merge's table");
 
 template <int D, int R, bool ATTEND>
 __global__ __launch_bounds__(kMergeThreads) void unit_kernel(const FilterArgs a,
+                                                             const AppendArgs ap,
                                                              const DecodeArgs d) {
-  static_assert(kAttendThreads == kMergeThreads, "one workgroup shape for every phase");
+  static_assert(kAttendThreads == kMergeThreads && kSampleThreads == kMergeThreads,
+                "one workgroup shape for every phase");
   __shared__ UnitShared us;
   const int u = blockIdx.x;
   const int b = u / a.Hkv;
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
   const int len = unit_len(a.seq_lens, b, a.n_max);
   if (tid == 0) us.spill_n = 0u;
+  // The decode step's prologue (the new rows appended, the indexer query
+  // formed) and the sampled bound, as append_bound_kernel forms them (the
+  // same arithmetic, so the same bits), with the query left in us.sh.qt and
+  // the bound returned to every thread.
+  const uint32_t thr = sample_bound<D, R>(a, us.sh, u, [&] {
+    if (ap.T > 0)
+      append_rows_and_query<D, R, kMergeThreads>(a, ap, u, us.sh.qt, us.sh.part);
+    else
+      indexer_query<D, R, kMergeThreads>(a.q, a.P, b, u % a.Hkv, a.G, a.Hq, us.sh.qt,
+                                          us.sh.part);
+  });
+  // every store of the new rows has completed before any wave streams the
+  // codes or, later, reads the rows (long since, in practice: the bound's
+  // selection ran in between)
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   uint32_t wc = 0;                                    // positions in this wave's list
-  if (len > a.M) {                                    // block-uniform (else all are taken)
+  if (len > a.M && w < kUnitStreamWaves) {            // wave-uniform (else all are taken)
     // key >= thr  <=>  score >= thrf (see filter_kernel)
-    const float thrf = key_score(a.thr[u]);
+    const float thrf = key_score(thr);
     uint2* spill_u = a.cand + (size_t)u * a.ustride;
     auto spill_list = [&]() {                         // wave-uniform, rare
       uint32_t at = 0u;
@@ -1895,10 +1923,10 @@ __global__ __launch_bounds__(kMergeThreads) void unit_kernel(const FilterArgs a,
       const bool sel = ge && in;
       const uint64_t m = ballot(ge) & ballot(in);
       const uint32_t n = (uint32_t)popc64(m);
-      if (wc + n > (uint32_t)kUnitCap) spill_list();
+      if (wc + n > (uint32_t)kUnitListCap) spill_list();
       const uint32_t slot = wc + __builtin_amdgcn_mbcnt_hi(
                                      (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      if (sel && slot < (uint32_t)kUnitCap) {
+      if (sel && slot < (uint32_t)kUnitListCap) {
         us.u.lists.s[w][slot] = sc;
         us.u.lists.p[w][slot] = p;
       }
@@ -1906,16 +1934,16 @@ __global__ __launch_bounds__(kMergeThreads) void unit_kernel(const FilterArgs a,
     };
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(a.kp + (size_t)u * a.Ncap * R, (uint32_t)len * R);
-    stream_code_scores<R, kMergeThreads, SA_UNIT_LOADS_IN_FLIGHT>(rs, len, a.qt + (size_t)u * 32,
-                                                                  keep);
+    stream_code_scores<R, kUnitStreamWaves * kWave, SA_UNIT_LOADS_IN_FLIGHT>(
+        rs, len, us.sh.qt, keep);
   }
-  if (lane == 0) us.wn[w] = wc;
+  if (lane == 0 && w < kUnitStreamWaves) us.wn[w] = wc;
   __syncthreads();                                    // lists, counts and spill writes done
   merge_unit_core<D, R>(
-      a, us.sh, us.u.bm, us.start_s, us.red, u, true, kUnitWaves,
-      [&](int c) { return c < kUnitWaves ? (int)us.wn[c] : (int)us.spill_n; },
+      a, us.sh, us.u.bm, us.start_s, us.red, u, true, kUnitStreamWaves,
+      [&](int c) { return c < kUnitStreamWaves ? (int)us.wn[c] : (int)us.spill_n; },
       [&](uint32_t c, uint32_t j) {
-        return c < (uint32_t)kUnitWaves
+        return c < (uint32_t)kUnitStreamWaves
                    ? make_uint2(score_key(us.u.lists.s[c][j] + 0.0f), (uint32_t)us.u.lists.p[c][j])
                    : a.cand[(size_t)u * a.ustride + j];
       });
@@ -1955,18 +1983,17 @@ template <int D, int R>
 static void launch_filter_dr(const FilterArgs& a, const AppendArgs* ap, const DecodeArgs* da,
                              int stages, int units, bool unit_wg, hipStream_t st) {
   if (unit_wg) {
-    // the bound as below; then one launch for the rest (no merge launch)
-    if ((stages & kSelectBound) && ap)
-      hipLaunchKernelGGL((append_bound_kernel<D, R>), dim3(units), dim3(kSampleThreads), 0, st, a,
-                         *ap);
-    else if (stages & kSelectBound)
-      hipLaunchKernelGGL((sample_kernel<D, R>), dim3(units), dim3(kSampleThreads), 0, st, a);
+    // one launch for the whole selection (and the append and attention when
+    // given), made by the candidates stage; the bound and merge stages have
+    // nothing of their own
+    AppendArgs none{};
+    none.T = 0;
     if ((stages & kSelectChunks) && da)
       hipLaunchKernelGGL((unit_kernel<D, R, true>), dim3(units), dim3(kMergeThreads), 0, st, a,
-                         *da);
+                         ap ? *ap : none, *da);
     else if (stages & kSelectChunks)
       hipLaunchKernelGGL((unit_kernel<D, R, false>), dim3(units), dim3(kMergeThreads), 0, st, a,
-                         DecodeArgs{});
+                         ap ? *ap : none, DecodeArgs{});
     return;
   }
   if ((stages & kSelectBound) && ap)

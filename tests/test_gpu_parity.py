@@ -1129,3 +1129,49 @@ def test_unit_workgroup_plan_falls_back_exactly():
         check_topm_unit(gi[b, h], s, M, N)
     # unit (3, 5): every score equal, so the M lowest positions
     assert gi[3, 5].tolist() == list(range(M))
+
+
+@pytest.mark.parametrize("d,r", [(128, 32), (64, 16)])
+def test_unit_workgroup_step_scores_the_new_token(d, r):
+    """With one workgroup per unit the append, the bound and the stream share
+    one launch: the stream must score the codes the append just wrote, not
+    what the row held before.  Each unit's new token is k_new = 5 qbar (far
+    above every cached row's score) over a cached row that scores low, so it
+    must be selected (and first, being the largest); the step must equal the
+    three separate calls bit for bit."""
+    B, Hq, Hkv, N, M = 32, 32, 8, 4096, 256
+    _say("case: unit plan appends and scores the new token d=%d r=%d" % (d, r))
+    G = Hq // Hkv
+    sh = _shape_of(B, Hq, Hkv, d, r, N)
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, N, seed=61)
+    qbar = f64(q).reshape(B, Hkv, G, d).mean(axis=2)
+    K64 = f64(K)
+    K64[:, :, N - 1] = -3.0 * qbar                          # the row before the append: low
+    K = torch.from_numpy(K64).to(torch.bfloat16)
+    k_new = torch.from_numpy(5.0 * qbar[:, :, None, :]).to(torch.bfloat16)
+    v_new = torch.randn(B, Hkv, 1, d, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16)
+    pos = torch.full((B,), N - 1, dtype=torch.int32)
+    res = []
+    for fused in (True, False):
+        Kd, Vd = _dev(K), _dev(V)
+        kp = torch.empty(B, Hkv, N, r, dtype=torch.uint8, device="cuda")
+        sa.sparse_attn_project_keys(sh, Kd, _dev(P), 0, N, kp)
+        ws = sa.alloc_workspace(sh, N, M)
+        idx = torch.full((B, Hkv, M), -9, dtype=torch.int32, device="cuda")
+        out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+        if fused:
+            sa.sparse_attn_decode_step(sh, _dev(pos), _dev(k_new), _dev(v_new), _dev(q), _dev(P),
+                                       Kd, Vd, kp, None, N, M, default_scale(d), idx, out, lse, ws)
+        else:
+            sa.sparse_attn_append_kv(sh, _dev(pos), _dev(k_new), _dev(v_new), _dev(P), Kd, Vd, kp)
+            sa.sparse_attn_index_topm(sh, _dev(q), _dev(P), kp, None, N, M, idx, ws)
+            sa.sparse_attn_decode(sh, _dev(q), Kd, Vd, idx, M, default_scale(d), out, lse, ws)
+        torch.cuda.synchronize()
+        res.append((Kd, Vd, kp, idx, out, lse))
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert sa.sparse_attn_selection_plan(sh, N, M) == sa.SA_PLAN_UNIT
+    for name, x, y in zip(("k", "v", "kp", "idx", "out", "lse"), res[0], res[1]):
+        assert torch.equal(x, y), name
+    gi = res[0][3].cpu().numpy()
+    assert np.all(gi[:, :, -1] == N - 1), "the new token must be selected in every unit"

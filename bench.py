@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode steps/sec and achieved HBM GB/s at N=128K, M=2048, r=32"
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+EVENT_EVERY = 4                       # timed steps between two bracketed dominant launches
 DOMINANT_KERNEL = "unit_kernel"       # the dominant launch of the 128K step (one workgroup per unit)
 KERNEL_SOURCES = ("indexer.hip", "device_common.hpp", "attend_common.hpp")
 PLAN_NAMES = {0: "chunk_exact", 1: "filter", 2: "unit_workgroup"}
@@ -744,7 +745,8 @@ def main(argv=None):
 
     def step(rec, every_call=False):
         # rec: this step's events.  In the timed region only the dominant call
-        # is bracketed (two events); the breakdown pass brackets every call.
+        # is bracketed (two events), in every EVENT_EVERY-th step; the
+        # breakdown pass brackets every call.
         for i, call in enumerate(calls):
             if rec is not None and (every_call or i == dom_i):
                 timer.record(rec[i if every_call else 0], stream)
@@ -775,7 +777,10 @@ def main(argv=None):
     dom_ev = []
     pool = timer.create(2 * a.steps)
     for k in range(a.steps):
-        step(pool[2 * k:2 * k + 2])           # HIP events around the dominant call
+        # HIP events around the dominant call of every EVENT_EVERY-th step
+        # (each event pair costs the GPU ~4 us: on every step it would slow
+        # the very steps being timed)
+        step(pool[2 * k:2 * k + 2] if k % EVENT_EVERY == 0 else None)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -823,6 +828,7 @@ def main(argv=None):
                 "kernel": "%s (sparse_attn_decode_step_stage, %s)" % (dom_kernel, STAGE_NAMES[
                     dict((n, st) for n, st, _ in stages)[dom]]),
                 "bytes_per_launch": bytes_k[dom], "avg_launch_us": round(dom_us, 2),
+                "launches_timed": len(dom_ev), "events_every_steps": EVENT_EVERY,
                 "source_hash": src_hash,
                 "read_ceiling_gbps": round(read_gbps, 1),
                 "frac_of_read_ceiling": round(dom_gbps / read_gbps, 4),

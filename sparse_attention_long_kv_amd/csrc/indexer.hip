@@ -1068,10 +1068,17 @@ hipError_t run_index_score(const LaunchCommon& c, const void* q, const float* P,
 // The bound stage for unit u (the whole workgroup; it synchronises).
 // prologue() runs while the sampled rows are in flight (every thread calls
 // it) and leaves the unit's indexer query in sh.qt.
-template <int D, int R, class Prologue>
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// after_sample() runs once the sample has been scored (every global load of
+// the bound has returned), before its selection (LDS work only).
+template <int D, int R, class Prologue, class AfterSample = NoHook>
 __device__ __forceinline__ uint32_t sample_bound(const FilterArgs& a,
                                                  SelectShared<kSampleThreads>& sh, int u,
-                                                 Prologue prologue) {
+                                                 Prologue prologue,
+                                                 AfterSample after_sample = AfterSample()) {
   constexpr int NT = kSampleThreads;
   const int b = u / a.Hkv, h = u % a.Hkv;
   const int tid = threadIdx.x;
@@ -1136,6 +1143,7 @@ __device__ __forceinline__ uint32_t sample_bound(const FilterArgs& a,
   uint32_t k = all ? (uint32_t)a.M
                    : (uint32_t)min((int64_t)ns, (keep * ns + len - 1) / len);
   k = max(k, 1u);
+  after_sample();
   const uint32_t dummy = (uint32_t)(kBins + lane_id());
 #pragma unroll
   for (int i = 0; i < kSampleKeys; ++i)
@@ -1294,43 +1302,79 @@ __device__ __forceinline__ uint4 stream_load16(__amdgpu_buffer_rsrc_t r, uint32_
 // with p relative to the start; rows past nv read as zero.  L loads per lane
 // are in flight: two groups of L / 2 rounds alternate, one scored while the
 // other loads.  qt: the unit's 32-float indexer query.
+template <int R, int NT, int L>
+struct CodeStream {
+  static_assert(R == 16 || R == 32, "rank");
+  static constexpr int PR = NT * 16 / R;              // positions per round
+  static constexpr int H = L / 2 > 0 ? L / 2 : 1;     // rounds per load group
+  __amdgpu_buffer_rsrc_t rs;
+  int rounds;
+  bool issued;
+  uint4 ga[H], gb[H];
+
+  __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t r, int nv) {
+    rs = r;
+    rounds = (nv + PR - 1) / PR;
+    issued = false;
+  }
+  __device__ __forceinline__ void load(uint4 (&g)[H], int k0) {
+#pragma unroll
+    for (int x = 0; x < H; ++x)
+      g[x] = stream_load16(rs, (uint32_t)((k0 + x) * NT * 16 + threadIdx.x * 16));
+  }
+  // the first two groups of loads (may be issued early, before the query and
+  // the bound are known)
+  __device__ __forceinline__ void issue_first() {
+    load(ga, 0);
+    if (H < rounds) load(gb, H);
+    issued = true;
+  }
+  template <class Keep>
+  __device__ __forceinline__ void run(const float* qt, Keep keep) {
+    const int t = threadIdx.x;
+    const int lane_pos = t * 16 / R;
+    const bool owner = R == 16 || (t & 1) == 0;
+    float ql[16];
+    const int qoff = R == 32 ? 16 * (t & 1) : 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ql[k] = qt[qoff + k];
+    auto score = [&](const uint4 (&g)[H], int k0) {
+#pragma unroll
+      for (int x = 0; x < H; ++x) {
+        float s = score16(ql, g[x]);
+        if (R == 32) s = s + dpp_f<kDppQuadSwap1>(s);
+        keep(s, (k0 + x) * PR + lane_pos, owner);
+      }
+    };
+    if (!issued) issue_first();
+    for (int k0 = 0; k0 < rounds; k0 += 2 * H) {      // block-uniform trip counts
+      score(ga, k0);
+      if (k0 + 2 * H < rounds) load(ga, k0 + 2 * H);
+      if (k0 + H < rounds) {
+        score(gb, k0 + H);
+        if (k0 + 3 * H < rounds) load(gb, k0 + 3 * H);
+      }
+    }
+  }
+};
+
+// Scores of the nv code rows (R bytes each) at the start of `rs`, read as
+// contiguous 16-byte lanes: in round k the workgroup reads bytes
+// [16 NT k, 16 NT (k + 1)), thread t the 16 bytes at 16 NT k + 16 t, that is
+// position PR k + 16 t / R (PR = 16 NT / R positions per round) -- for
+// r = 32 one half (t & 1) of the row.  The two lanes of an r = 32 row each
+// form their half's 16-code chain and add the other's with one DPP step
+// (lo + hi and hi + lo are the same sum), and the even lane owns the
+// position.  keep(s, p, owner) is called by every lane (a wave-uniform call)
+// with p relative to the start; rows past nv read as zero.  L loads per lane
+// are in flight: two groups of L / 2 rounds alternate, one scored while the
+// other loads.  qt: the unit's 32-float indexer query.
 template <int R, int NT, int L, class Keep>
 __device__ __forceinline__ void stream_code_scores(__amdgpu_buffer_rsrc_t rs, int nv,
                                                    const float* qt, Keep keep) {
-  static_assert(R == 16 || R == 32, "rank");
-  constexpr int PR = NT * 16 / R;
-  constexpr int H = L / 2 > 0 ? L / 2 : 1;
-  const int t = threadIdx.x;
-  const int lane_pos = t * 16 / R;
-  const bool owner = R == 16 || (t & 1) == 0;
-  float ql[16];
-  const int qoff = R == 32 ? 16 * (t & 1) : 0;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) ql[k] = qt[qoff + k];
-  const int rounds = (nv + PR - 1) / PR;
-  uint4 ga[H], gb[H];
-  auto load = [&](uint4 (&g)[H], int k0) {
-#pragma unroll
-    for (int x = 0; x < H; ++x) g[x] = stream_load16(rs, (uint32_t)((k0 + x) * NT * 16 + t * 16));
-  };
-  auto score = [&](const uint4 (&g)[H], int k0) {
-#pragma unroll
-    for (int x = 0; x < H; ++x) {
-      float s = score16(ql, g[x]);
-      if (R == 32) s = s + dpp_f<kDppQuadSwap1>(s);
-      keep(s, (k0 + x) * PR + lane_pos, owner);
-    }
-  };
-  load(ga, 0);
-  if (H < rounds) load(gb, H);
-  for (int k0 = 0; k0 < rounds; k0 += 2 * H) {        // block-uniform trip counts
-    score(ga, k0);
-    if (k0 + 2 * H < rounds) load(ga, k0 + 2 * H);
-    if (k0 + H < rounds) {
-      score(gb, k0 + H);
-      if (k0 + 3 * H < rounds) load(gb, k0 + 3 * H);
-    }
-  }
+  CodeStream<R, NT, L> cs;
+  cs.init(rs, nv);
+  cs.run(qt, keep);
 }
 
 template <int D, int R>
@@ -1845,12 +1889,12 @@ __global__ __launch_bounds__(kMergeThreads) void select_attend_kernel(const Filt
 // leaves in LDS (AttendWave, the attention kernels' arithmetic, one split).
 
 #ifndef SA_UNIT_LOADS_IN_FLIGHT
-#define SA_UNIT_LOADS_IN_FLIGHT 4
+#define SA_UNIT_LOADS_IN_FLIGHT 8
 #endif
 // waves that stream (the others wait at the merge's first barrier); the
 // lists' LDS is shared out among them
 #ifndef SA_UNIT_STREAM_WAVES
-#define SA_UNIT_STREAM_WAVES 16
+#define SA_UNIT_STREAM_WAVES 8
 #endif
 constexpr int kUnitStreamWaves = SA_UNIT_STREAM_WAVES;
 constexpr int kUnitListCap = kUnitWaves * kUnitCap / kUnitStreamWaves;   // slots per list
@@ -1886,24 +1930,43 @@ __global__ __launch_bounds__(kMergeThreads) void unit_kernel(const FilterArgs a,
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
   const int len = unit_len(a.seq_lens, b, a.n_max);
   if (tid == 0) us.spill_n = 0u;
+  const bool streams = len > a.M && w < kUnitStreamWaves;       // wave-uniform
+  CodeStream<R, kUnitStreamWaves * kWave, SA_UNIT_LOADS_IN_FLIGHT> cs;
+  cs.init(make_rsrc(a.kp + (size_t)u * a.Ncap * R, (uint32_t)len * R), len);
+  // The first rounds of the stream may be loaded while the bound is being
+  // selected, when they lie wholly below the first new row (so they cannot
+  // read a code the append is writing).
+  const long first_new = ap.T > 0 ? (long)ap.pos[b] : (long)len;
+  const bool early =
+      streams && first_new >= (long)(2 * decltype(cs)::H) * decltype(cs)::PR;
   // The decode step's prologue (the new rows appended, the indexer query
   // formed) and the sampled bound, as append_bound_kernel forms them (the
   // same arithmetic, so the same bits), with the query left in us.sh.qt and
   // the bound returned to every thread.
-  const uint32_t thr = sample_bound<D, R>(a, us.sh, u, [&] {
-    if (ap.T > 0)
-      append_rows_and_query<D, R, kMergeThreads>(a, ap, u, us.sh.qt, us.sh.part);
-    else
-      indexer_query<D, R, kMergeThreads>(a.q, a.P, b, u % a.Hkv, a.G, a.Hq, us.sh.qt,
-                                          us.sh.part);
-  });
+  const uint32_t thr = sample_bound<D, R>(
+      a, us.sh, u,
+      [&] {
+        if (ap.T > 0)
+          append_rows_and_query<D, R, kMergeThreads>(a, ap, u, us.sh.qt, us.sh.part);
+        else
+          indexer_query<D, R, kMergeThreads>(a.q, a.P, b, u % a.Hkv, a.G, a.Hq, us.sh.qt,
+                                              us.sh.part);
+      },
+      [&] {
+        if (early) {
+          // the new rows' stores complete first (the bound's loads have all
+          // returned by now, so this waits for nothing else)
+          __builtin_amdgcn_s_waitcnt(0);
+          cs.issue_first();
+        }
+      });
   // every store of the new rows has completed before any wave streams the
-  // codes or, later, reads the rows (long since, in practice: the bound's
-  // selection ran in between)
-  __builtin_amdgcn_s_waitcnt(0);
+  // codes or, later, reads the rows (done above when the first loads went
+  // out early; long since, in practice: the bound's selection ran between)
+  if (!cs.issued) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   uint32_t wc = 0;                                    // positions in this wave's list
-  if (len > a.M && w < kUnitStreamWaves) {            // wave-uniform (else all are taken)
+  if (streams) {                                      // (else all are taken)
     // key >= thr  <=>  score >= thrf (see filter_kernel)
     const float thrf = key_score(thr);
     uint2* spill_u = a.cand + (size_t)u * a.ustride;
@@ -1932,10 +1995,7 @@ __global__ __launch_bounds__(kMergeThreads) void unit_kernel(const FilterArgs a,
       }
       wc += n;
     };
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(a.kp + (size_t)u * a.Ncap * R, (uint32_t)len * R);
-    stream_code_scores<R, kUnitStreamWaves * kWave, SA_UNIT_LOADS_IN_FLIGHT>(
-        rs, len, us.sh.qt, keep);
+    cs.run(us.sh.qt, keep);
   }
   if (lane == 0 && w < kUnitStreamWaves) us.wn[w] = wc;
   __syncthreads();                                    // lists, counts and spill writes done

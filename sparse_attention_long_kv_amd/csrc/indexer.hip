@@ -1729,18 +1729,17 @@ struct MergeShared {
 
 // The merge of unit u by the whole workgroup (it synchronises).  Leaves the
 // unit's M selected positions, ascending and -1 padded, in sh.list (as int32)
-// and, when write_idx, also in idx (and the unit's path flag).  The kept
-// candidates come from S + 1 sources: S lists, then the spill pool.
-// count_of(c) (c <= S; called by one wave, lane c) gives source c's count
-// (-1: the list overflowed; the pool's count is compared with a.spill_cap);
-// pair_of(c, j) gives (key, position) of entry j of source c.  bm: the
-// bitmap of kBitmapWords words (also the fallback's); start_s and red:
-// kMergeStarts and kMergeThreads / kWave words.
-template <int D, int R, class CountOf, class PairOf>
+// and, when write_idx, also in idx (and the unit's path flag).
+// gather(key, pos, nk, total) puts the unit's kept candidates (key, position)
+// into the threads' registers in any order (key 0 = empty slot; rows >= nk,
+// block-uniform, are all empty) and sets total to their number, or to 0 when
+// a list overflowed or they do not fit the registers (the unit then takes the
+// exact fallback); it synchronises.  bm: the bitmap of kBitmapWords words
+// (also the fallback's); red: kMergeThreads / kWave words.
+template <int D, int R, class Gather>
 __device__ __forceinline__ void merge_unit_core(const FilterArgs& a, SelectShared<kMergeThreads>& sh,
-                                                uint32_t* bm, uint32_t* start_s, uint32_t* red,
-                                                int u, bool write_idx, int S, CountOf count_of,
-                                                PairOf pair_of) {
+                                                uint32_t* bm, uint32_t* red, int u,
+                                                bool write_idx, Gather gather) {
   constexpr int NT = kMergeThreads;
   constexpr int KPT = kFilterMergeKeys;
   static_assert(kFilterMaxM <= kListCap - kWave, "the selection is staged in LDS");
@@ -1759,47 +1758,16 @@ __device__ __forceinline__ void merge_unit_core(const FilterArgs& a, SelectShare
     __syncthreads();
     return;
   }
-  // Per-source counts (S < kMergeStarts), the spill pool last: one wave forms
-  // their exclusive prefix; a list that overflowed (-1), a pool that ran out,
-  // or more candidates than the registers hold send the unit to the exact
-  // fallback.
-  if (w == 0) {
-    const int c = lane <= S ? count_of(lane) : 0;
-    const bool over = ballot(c < 0 || (lane == S && c > a.spill_cap)) != 0;
-    const uint32_t v = (uint32_t)max(c, 0);
-    const uint32_t incl = wave_inclusive_scan(v);
-    if (lane < kMergeStarts) start_s[lane] = lane <= S ? incl - v : 0xFFFFFFFFu;
-    if (lane == kWave - 1) red[0] = (over || incl > (uint32_t)(NT * KPT)) ? 0u : incl;
-  }
-  __syncthreads();
-  const uint32_t total = red[0];
-  __syncthreads();                                    // red is reused below
+  uint32_t key[KPT];
+  int32_t pos[KPT];
+  int nk;
+  uint32_t total;
+  gather(key, pos, nk, total);
   if (write_idx && tid == 0) a.path[u] = total < (uint32_t)M ? 1 : 0;
   if (total < (uint32_t)M) {                          // block-uniform (0 after an overflow)
     select_unit_streaming<D, R>(a, sh, bm, u, b, h, len, idx_u);
     __syncthreads();
     return;
-  }
-  // The unit's candidates, numbered g = 0 .. total-1 source after source; key
-  // g sits in register i = g / NT of thread g % NT.  Source c holds g in
-  // [start_c, start_c+1).
-  const int nk = (int)((total + NT - 1) / NT);        // rows in use, <= KPT
-  uint32_t key[KPT];
-  int32_t pos[KPT];
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    key[i] = 0u;
-    pos[i] = 0;
-    const uint32_t g = (uint32_t)(i * NT + tid);
-    if (i < nk && g < total) {
-      uint32_t c = 0;                                 // last source with start_c <= g
-#pragma unroll
-      for (int step = kMergeStarts / 2; step >= 1; step >>= 1)
-        if (start_s[c + step] <= g) c += step;
-      const uint2 kv = pair_of(c, g - start_s[c]);
-      key[i] = kv.x;
-      pos[i] = (int32_t)kv.y;
-    }
   }
   const uint32_t thr = a.thr[u];
   uint32_t kmax = 0u;
@@ -1820,10 +1788,9 @@ __device__ __forceinline__ void merge_unit_core(const FilterArgs& a, SelectShare
   const int lsh = span ? max(__clz((int)span) - 1, 0) : 0;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) key[i] = key[i] ? ((key[i] - thr) << lsh) + 1u : 0u;
-  const uint32_t dummy = (uint32_t)(kBins + lane);
 #pragma unroll
   for (int i = 0; i < KPT; ++i)
-    if (i < nk) atomicAdd(&sh.hist[key[i] ? (key[i] >> kTopShift) : dummy], 1u);
+    if (i < nk && key[i] != 0u) atomicAdd(&sh.hist[key[i] >> kTopShift], 1u);
   __syncthreads();
   uint32_t t, need, eq;
   finish_threshold<NT>(sh, (uint32_t)M, t, need, eq, [&](auto&& f) {
@@ -1837,16 +1804,52 @@ __device__ __forceinline__ void merge_unit_core(const FilterArgs& a, SelectShare
 }
 
 // The merge over the filter kernel's chunk lists and the unit's spill pool
-// (in the workspace).
+// (in the workspace): the unit's candidates are numbered g = 0 .. total-1
+// chunk after chunk, the pool last (one wave forms the exclusive prefix of
+// the counts), and candidate g sits in register g / NT of thread g % NT,
+// found by bisection of the prefix.  A chunk whose lists overflowed (-1), a
+// pool that ran out, or more candidates than the registers hold give total 0.
 template <int D, int R>
 __device__ __forceinline__ void filter_merge_unit(const FilterArgs& a, MergeShared& ms, int u,
                                                   bool write_idx) {
+  constexpr int NT = kMergeThreads;
+  constexpr int KPT = kFilterMergeKeys;
   const int S = a.S;
   const uint2* cu = a.cand + (size_t)u * a.ustride;
+  uint32_t* start_s = ms.start_s;
+  uint32_t* red = ms.red;
   merge_unit_core<D, R>(
-      a, ms.sh, ms.bm, ms.start_s, ms.red, u, write_idx, S,
-      [&](int c) { return a.cnt[(size_t)u * (S + 1) + c]; },
-      [&](uint32_t c, uint32_t j) { return cu[(size_t)c * a.cslots + j]; });
+      a, ms.sh, ms.bm, red, u, write_idx,
+      [&](uint32_t (&key)[KPT], int32_t (&pos)[KPT], int& nk, uint32_t& total) {
+        const int tid = threadIdx.x, lane = lane_id();
+        if (tid < kWave) {
+          const int c = lane <= S ? a.cnt[(size_t)u * (S + 1) + lane] : 0;
+          const bool over = ballot(c < 0 || (lane == S && c > a.spill_cap)) != 0;
+          const uint32_t v = (uint32_t)max(c, 0);
+          const uint32_t incl = wave_inclusive_scan(v);
+          if (lane < kMergeStarts) start_s[lane] = lane <= S ? incl - v : 0xFFFFFFFFu;
+          if (lane == kWave - 1) red[0] = (over || incl > (uint32_t)(NT * KPT)) ? 0u : incl;
+        }
+        __syncthreads();
+        total = red[0];
+        nk = (int)((total + NT - 1) / NT);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+          key[i] = 0u;
+          pos[i] = 0;
+          const uint32_t g = (uint32_t)(i * NT + tid);
+          if (i < nk && g < total) {
+            uint32_t c = 0;                           // last chunk with start_c <= g
+#pragma unroll
+            for (int step = kMergeStarts / 2; step >= 1; step >>= 1)
+              if (start_s[c + step] <= g) c += step;
+            const uint2 kv = cu[(size_t)c * a.cslots + (g - start_s[c])];
+            key[i] = kv.x;
+            pos[i] = (int32_t)kv.y;
+          }
+        }
+        __syncthreads();                              // red is reused
+      });
 }
 
 template <int D, int R>
@@ -1898,7 +1901,13 @@ __global__ __launch_bounds__(kMergeThreads) void select_attend_kernel(const Filt
 #endif
 constexpr int kUnitStreamWaves = SA_UNIT_STREAM_WAVES;
 constexpr int kUnitListCap = kUnitWaves * kUnitCap / kUnitStreamWaves;   // slots per list
-static_assert(kUnitStreamWaves >= 1 && kUnitStreamWaves <= kUnitWaves, "streaming waves");
+static_assert(kUnitStreamWaves >= 1 && kUnitStreamWaves <= kUnitWaves &&
+                  kUnitWaves % kUnitStreamWaves == 0, "streaming waves");
+// merge registers per thread: a list's share, then the spill pool's
+constexpr int kUnitListRows = kUnitCap / kWave;                          // 12
+constexpr int kUnitSpillRows = kFilterMergeKeys - kUnitListRows;         // 4
+static_assert(kUnitListRows * kWave * kUnitWaves / kUnitStreamWaves >= kUnitListCap,
+              "a list fits its waves' registers");
 
 struct UnitShared {
   union {
@@ -1909,14 +1918,12 @@ struct UnitShared {
     uint32_t bm[kBitmapWords];              // the merge's bitmap; then the output tiles
   } u;
   SelectShared<kMergeThreads> sh;
-  uint32_t start_s[kMergeStarts];
   uint32_t red[kMergeThreads / kWave];
   uint32_t wn[kUnitWaves];
   uint32_t spill_n;
   float sm[kAttendWaves][kMaxHeads], sl[kAttendWaves][kMaxHeads];
 };
 static_assert(kUnitWaves == kMergeThreads / kWave, "one list per wave");
-static_assert(kUnitStreamWaves + 1 <= kMergeStarts, "the lists and the pool fit the merge's table");
 
 template <int D, int R, bool ATTEND>
 __global__ __launch_bounds__(kMergeThreads) void unit_kernel(const FilterArgs a,
@@ -1999,13 +2006,48 @@ __global__ __launch_bounds__(kMergeThreads) void unit_kernel(const FilterArgs a,
   }
   if (lane == 0 && w < kUnitStreamWaves) us.wn[w] = wc;
   __syncthreads();                                    // lists, counts and spill writes done
+  // The merge reads each wave list straight into registers: list c is read
+  // by waves c WPL .. c WPL + WPL - 1, each lane taking every (64 WPL)-th
+  // entry (at most kUnitListRows per thread), and the spill pool fills the
+  // remaining rows (at most kUnitSpillRows per thread: a larger pool sends the
+  // unit to the exact fallback, as an overflowing list does).
   merge_unit_core<D, R>(
-      a, us.sh, us.u.bm, us.start_s, us.red, u, true, kUnitStreamWaves,
-      [&](int c) { return c < kUnitStreamWaves ? (int)us.wn[c] : (int)us.spill_n; },
-      [&](uint32_t c, uint32_t j) {
-        return c < (uint32_t)kUnitStreamWaves
-                   ? make_uint2(score_key(us.u.lists.s[c][j] + 0.0f), (uint32_t)us.u.lists.p[c][j])
-                   : a.cand[(size_t)u * a.ustride + j];
+      a, us.sh, us.u.bm, us.red, u, true,
+      [&](uint32_t (&key)[kFilterMergeKeys], int32_t (&pos)[kFilterMergeKeys], int& nk,
+          uint32_t& total) {
+        constexpr int WPL = kUnitWaves / kUnitStreamWaves;   // merge waves per list
+        const int c = w / WPL;
+        const int j0 = (w % WPL) * kWave + lane;
+        const uint32_t nlist = us.wn[c];
+        const uint32_t nspill = us.spill_n;
+#pragma unroll
+        for (int i = 0; i < kUnitListRows; ++i) {
+          const int j = j0 + i * WPL * kWave;
+          key[i] = 0u;
+          pos[i] = 0;
+          if (j < (int)nlist) {
+            key[i] = score_key(us.u.lists.s[c][j] + 0.0f);
+            pos[i] = us.u.lists.p[c][j];
+          }
+        }
+        const bool spill_fits = nspill <= (uint32_t)(kUnitSpillRows * kMergeThreads);
+#pragma unroll
+        for (int i = kUnitListRows; i < kFilterMergeKeys; ++i) {
+          const uint32_t g = (uint32_t)((i - kUnitListRows) * kMergeThreads + tid);
+          key[i] = 0u;
+          pos[i] = 0;
+          if (spill_fits && g < nspill) {
+            const uint2 kv = a.cand[(size_t)u * a.ustride + g];
+            key[i] = kv.x;
+            pos[i] = (int32_t)kv.y;
+          }
+        }
+        nk = nspill > 0 ? kFilterMergeKeys : kUnitListRows;
+        uint32_t n = nspill;
+#pragma unroll
+        for (int cc = 0; cc < kUnitStreamWaves; ++cc) n += us.wn[cc];
+        total = spill_fits ? n : 0u;
+        __syncthreads();                              // the lists are read (bm aliases them)
       });
   if constexpr (ATTEND) {
     AttendWave<D, kAttendWaves> aw;

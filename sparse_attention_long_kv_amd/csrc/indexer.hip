@@ -1377,6 +1377,86 @@ __device__ __forceinline__ void stream_code_scores(__amdgpu_buffer_rsrc_t rs, in
   cs.run(qt, keep);
 }
 
+// The unit kernel's code stream: CodeStream's loads and scores, handed out
+// to the S streaming waves in chunks on demand.  A chunk is H consecutive 1 KB
+// wave loads (H KB of contiguous codes, H PW positions); wave w starts on
+// chunks w and S + w and takes each further chunk from an LDS counter that
+// starts at 2 S.  With a fixed split the waves of one SIMD do not keep pace
+// (instruction issue favours the older wave): measured at 131072 positions,
+// the later four of eight waves finished 5.8 us after the first four, whose
+// memory-level parallelism the tail then lacked.  On demand, the waves end
+// within a chunk of each other.  Loads past nv read as zero; keep(s, p, owner)
+// as for CodeStream.
+template <int R, int L>
+struct WaveStream {
+  static_assert(R == 16 || R == 32, "rank");
+  static constexpr int H = L / 2 > 0 ? L / 2 : 1;    // loads per chunk
+  static constexpr int PW = kWave * 16 / R;          // positions per wave load
+  __amdgpu_buffer_rsrc_t rs;
+  int nch, ca, cb;                                   // chunks; the two claimed (ca older)
+  bool issued;
+  uint4 ga[H], gb[H];
+
+  // positions covered by the chunks the S waves start on
+  static constexpr int first_span(int S) { return 2 * S * H * PW; }
+
+  __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t r, int nv, int w, int S) {
+    rs = r;
+    nch = (nv + H * PW - 1) / (H * PW);
+    ca = w;
+    cb = w + S;
+    issued = false;
+  }
+  __device__ __forceinline__ void load(uint4 (&g)[H], int c) {
+#pragma unroll
+    for (int x = 0; x < H; ++x)
+      g[x] = stream_load16(rs, (uint32_t)((c * H + x) * kWave * 16 + lane_id() * 16));
+  }
+  // the starting chunks' loads (may be issued early, before the query and the
+  // bound are known)
+  __device__ __forceinline__ void issue_first() {
+    if (ca < nch) load(ga, ca);
+    if (cb < nch) load(gb, cb);
+    issued = true;
+  }
+  template <class Keep>
+  __device__ __forceinline__ void run(const float* qt, uint32_t* next, Keep keep) {
+    const int lane = lane_id();
+    const int lane_pos = lane * 16 / R;
+    const bool owner = R == 16 || (lane & 1) == 0;
+    float ql[16];
+    const int qoff = R == 32 ? 16 * (lane & 1) : 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ql[k] = qt[qoff + k];
+    auto score = [&](const uint4 (&g)[H], int c) {
+#pragma unroll
+      for (int x = 0; x < H; ++x) {
+        float s = score16(ql, g[x]);
+        if (R == 32) s = s + dpp_f<kDppQuadSwap1>(s);
+        keep(s, (c * H + x) * PW + lane_pos, owner);
+      }
+    };
+    auto claim = [&]() {
+      uint32_t c = 0u;
+      if (lane == 0) c = atomicAdd(next, 1u);
+      return (int)__builtin_amdgcn_readlane(c, 0);
+    };
+    if (!issued) issue_first();
+    // Claims only grow, so when the older claim is past the end the younger
+    // one is too, and no load is left in flight at the exit.
+    for (;;) {                                        // wave-uniform trip count
+      if (ca >= nch) break;
+      score(ga, ca);
+      ca = claim();
+      if (ca < nch) load(ga, ca);
+      if (cb >= nch) break;
+      score(gb, cb);
+      cb = claim();
+      if (cb < nch) load(gb, cb);
+    }
+  }
+};
+
 template <int D, int R>
 __global__ __launch_bounds__(kChunkThreads) void filter_kernel(const FilterArgs a) {
   constexpr int NT = kChunkThreads;
@@ -1921,6 +2001,7 @@ struct UnitShared {
   uint32_t red[kMergeThreads / kWave];
   uint32_t wn[kUnitWaves];
   uint32_t spill_n;
+  uint32_t next;                            // the code stream's next free chunk
   float sm[kAttendWaves][kMaxHeads], sl[kAttendWaves][kMaxHeads];
 };
 static_assert(kUnitWaves == kMergeThreads / kWave, "one list per wave");
@@ -1936,16 +2017,18 @@ __global__ __launch_bounds__(kMergeThreads) void unit_kernel(const FilterArgs a,
   const int b = u / a.Hkv;
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
   const int len = unit_len(a.seq_lens, b, a.n_max);
-  if (tid == 0) us.spill_n = 0u;
+  if (tid == 0) {
+    us.spill_n = 0u;
+    us.next = (uint32_t)(2 * kUnitStreamWaves);     // the chunks after the starting ones
+  }
   const bool streams = len > a.M && w < kUnitStreamWaves;       // wave-uniform
-  CodeStream<R, kUnitStreamWaves * kWave, SA_UNIT_LOADS_IN_FLIGHT> cs;
-  cs.init(make_rsrc(a.kp + (size_t)u * a.Ncap * R, (uint32_t)len * R), len);
+  WaveStream<R, SA_UNIT_LOADS_IN_FLIGHT> cs;
+  cs.init(make_rsrc(a.kp + (size_t)u * a.Ncap * R, (uint32_t)len * R), len, w, kUnitStreamWaves);
   // The first rounds of the stream may be loaded while the bound is being
   // selected, when they lie wholly below the first new row (so they cannot
   // read a code the append is writing).
   const long first_new = ap.T > 0 ? (long)ap.pos[b] : (long)len;
-  const bool early =
-      streams && first_new >= (long)(2 * decltype(cs)::H) * decltype(cs)::PR;
+  const bool early = streams && first_new >= (long)decltype(cs)::first_span(kUnitStreamWaves);
   // The decode step's prologue (the new rows appended, the indexer query
   // formed) and the sampled bound, as append_bound_kernel forms them (the
   // same arithmetic, so the same bits), with the query left in us.sh.qt and
@@ -2002,7 +2085,7 @@ __global__ __launch_bounds__(kMergeThreads) void unit_kernel(const FilterArgs a,
       }
       wc += n;
     };
-    cs.run(us.sh.qt, keep);
+    cs.run(us.sh.qt, &us.next, keep);
   }
   if (lane == 0 && w < kUnitStreamWaves) us.wn[w] = wc;
   __syncthreads();                                    // lists, counts and spill writes done

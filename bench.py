@@ -38,7 +38,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 EVENT_EVERY = 4                       # timed steps between two bracketed dominant launches
 DOMINANT_KERNEL = "unit_kernel"       # the dominant launch of the 128K step (one workgroup per unit)
 KERNEL_SOURCES = ("indexer.hip", "device_common.hpp", "attend_common.hpp")
-PLAN_NAMES = {0: "chunk_exact", 1: "filter", 2: "unit_workgroup"}
+PLAN_NAMES = {0: "chunk_exact", 1: "filter", 2: "unit_workgroup", 3: "all_scores"}
 STAGE_NAMES = {1: "SA_STEP_APPEND_BOUND", 2: "SA_STEP_CANDIDATES", 3: "SA_STEP_MERGE",
                4: "SA_STEP_ATTEND", 5: "SA_STEP_SELECT_ATTEND"}
 
@@ -48,12 +48,20 @@ def step_stages(sa, sh, wl):
     shape on this device: (plan, [(name, stage, kernel)], algorithmic bytes
     per launch, name of the dominant launch).  With one workgroup per unit
     the whole step is one launch (append, bound, filter, merge, attention);
+    with every position scored it is append + scores, then select + attend;
     otherwise it is append + bound, candidates, and select + attend."""
     plan = sa.sparse_attn_selection_plan(sh, wl.N, wl.M)
     ab = algorithmic_bytes(wl)
     if plan == sa.SA_PLAN_UNIT:
         stages = [("step", sa.SA_STEP_APPEND_BOUND, "unit_kernel")]
         return plan, stages, {"step": sum(ab.values())}, "step"
+    if plan == sa.SA_PLAN_SCORES:
+        # append + every position scored, then select + attend over the scores
+        stages = [("append_score", sa.SA_STEP_APPEND_BOUND, "score_all_kernel"),
+                  ("select_attend", sa.SA_STEP_SELECT_ATTEND, "scores_select_attend_kernel")]
+        nbytes = {"append_score": ab["append_bound"] + ab["candidates"],
+                  "select_attend": ab["select_attend"]}
+        return plan, stages, nbytes, "select_attend"
     stages = [("append_bound", sa.SA_STEP_APPEND_BOUND, "append_bound_kernel"),
               ("candidates", sa.SA_STEP_CANDIDATES, "filter_kernel"),
               ("select_attend", sa.SA_STEP_SELECT_ATTEND, "select_attend_kernel")]

@@ -189,7 +189,10 @@ int sparse_attn_index_topm(const sa_shape* shape, const void* q, const float* P,
  * Where one workgroup per unit serves the shape (sparse_attn_selection_plan
  * gives SA_PLAN_UNIT), SA_STAGE_CANDIDATES is the whole selection in one
  * launch (bound, filter and merge: it writes idx) and the other two stages
- * launch nothing.
+ * launch nothing.  Where every position is scored (SA_PLAN_SCORES),
+ * SA_STAGE_BOUND writes every position's score to the workspace,
+ * SA_STAGE_CANDIDATES launches nothing and SA_STAGE_MERGE selects exactly
+ * over the scores.
  * Returns SA_ERR_INVALID for an unknown stage.
  * ------------------------------------------------------------------------- */
 enum sa_stage { SA_STAGE_BOUND = 1, SA_STAGE_CANDIDATES = 2, SA_STAGE_MERGE = 3 };
@@ -283,8 +286,10 @@ int sparse_attn_decode_step_noalloc(const sa_shape* shape, const int32_t* pos, i
  * per unit serves the shape (sparse_attn_selection_plan gives SA_PLAN_UNIT),
  * SA_STEP_APPEND_BOUND is the whole step in one launch (append, bound,
  * filter, merge and attention: it writes the caches, idx, out and lse) and
- * the later stages launch nothing.  Run the stages in order on one stream
- * with identical arguments.
+ * the later stages launch nothing.  Where every position is scored
+ * (SA_PLAN_SCORES), SA_STEP_APPEND_BOUND appends and scores every position,
+ * SA_STEP_CANDIDATES launches nothing, and the merge selects over the
+ * scores.  Run the stages in order on one stream with identical arguments.
  * Returns SA_ERR_INVALID for an unknown stage. */
 enum sa_step_stage {
   SA_STEP_APPEND_BOUND = 1,
@@ -412,12 +417,23 @@ int sparse_attn_selection_fallbacks(const sa_shape* shape, int32_t n_max, int32_
  *   SA_PLAN_UNIT (2)         one workgroup per (b, KV head) unit appends,
  *                            bounds, streams, merges and attends in one launch
  *                            (when the units fill whole rounds of the device's
- *                            compute units, units >= 256, G d <= 1024, M <= 2048).
- * Every plan gives the same idx, out and lse bits.  The environment variable
- * SPARSE_ATTN_UNIT_WG=0 turns SA_PLAN_UNIT off (a testing aid).  Returns the
- * plan, or SA_ERR_INVALID / SA_ERR_UNSUPPORTED for arguments the selection
- * rejects. */
-enum sa_plan { SA_PLAN_CHUNK_EXACT = 0, SA_PLAN_FILTER = 1, SA_PLAN_UNIT = 2 };
+ *                            compute units, units >= 256, G d <= 1024, M <= 2048);
+ *   SA_PLAN_SCORES (3)       every position is scored and written out (fp32,
+ *                            4 bytes per position of workspace), then an exact
+ *                            merge over all of a unit's scores (and, in the
+ *                            decode step, attention in the merge launch): no
+ *                            bound, no filter (n_max <= 16384, where the unit
+ *                            plan does not apply).
+ * Every plan gives the same idx, out and lse bits.  The environment variables
+ * SPARSE_ATTN_UNIT_WG=0 and SPARSE_ATTN_SCORES_PLAN=0 turn SA_PLAN_UNIT and
+ * SA_PLAN_SCORES off (testing aids).  Returns the plan, or SA_ERR_INVALID /
+ * SA_ERR_UNSUPPORTED for arguments the selection rejects. */
+enum sa_plan {
+  SA_PLAN_CHUNK_EXACT = 0,
+  SA_PLAN_FILTER = 1,
+  SA_PLAN_UNIT = 2,
+  SA_PLAN_SCORES = 3
+};
 
 int sparse_attn_selection_plan(const sa_shape* shape, int32_t n_max, int32_t M);
 

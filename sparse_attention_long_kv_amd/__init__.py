@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     sparse_attn_linear_gate, sparse_attn_dense_decode, sparse_attn_dense_workspace_size,
     sparse_attn_gather_kv, sparse_attn_stream_read, sparse_attn_row_read, sparse_attn_selection_fallbacks,
     sparse_attn_selection_plan, SA_PLAN_CHUNK_EXACT, SA_PLAN_FILTER, SA_PLAN_UNIT,
+    SA_PLAN_SCORES,
     sparse_attn_workspace_size, sparse_attn_status_string, LIB_PATH,
     SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP,
     SA_ERR_TOO_LARGE, SA_NOALLOC_SCRATCH_BYTES,

@@ -22,7 +22,7 @@ SA_ERR_UNSUPPORTED = -2
 SA_ERR_WORKSPACE = -3
 SA_ERR_HIP = -4
 SA_ERR_TOO_LARGE = -5
-SA_PLAN_CHUNK_EXACT, SA_PLAN_FILTER, SA_PLAN_UNIT = 0, 1, 2
+SA_PLAN_CHUNK_EXACT, SA_PLAN_FILTER, SA_PLAN_UNIT, SA_PLAN_SCORES = 0, 1, 2, 3
 SA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -368,7 +368,7 @@ def sparse_attn_selection_fallbacks(shape, n_max, M, workspace, count):
 
 def sparse_attn_selection_plan(shape, n_max, M):
     """Diagnostic: the selection method for this shape on the current device
-    (SA_PLAN_CHUNK_EXACT, SA_PLAN_FILTER or SA_PLAN_UNIT)."""
+    (SA_PLAN_CHUNK_EXACT, SA_PLAN_FILTER, SA_PLAN_UNIT or SA_PLAN_SCORES)."""
     st = load().sparse_attn_selection_plan(_sh(shape), int(n_max), int(M))
     if st < 0:
         raise SparseAttnError("sparse_attn_selection_plan", st, sparse_attn_status_string(st))

@@ -50,6 +50,15 @@ int unit_cu_count() {
   return cache[dev];
 }
 
+// The plan that scores every position (short units, too few for one
+// workgroup each) where it applies.  SPARSE_ATTN_SCORES_PLAN=0 in the
+// environment keeps the filter plan instead (both give the same bits; a
+// testing aid).
+bool scores_plan_on() {
+  const char* e = std::getenv("SPARSE_ATTN_SCORES_PLAN");
+  return !(e && e[0] == '0');
+}
+
 LaunchCommon common(const sa_shape& s, void* stream) {
   LaunchCommon c;
   c.B = s.batch;
@@ -135,7 +144,7 @@ extern "C" int sparse_attn_topm(const sa_shape* shape, const float* scores,
   // the filter path over the given scores where it applies (sampled bound,
   // filter, merge: the same idx as the chunk-exact path, in fewer bytes)
   FilterPlan fplan;
-  st = plan_filter(*shape, n_max, M, &fplan);
+  st = plan_filter(*shape, n_max, M, &fplan, 0, scores_plan_on());
   if (st != SA_OK) return st;
   if (fplan.enabled)
     return finish(run_filter_select(c, fplan, kSelectBound | kSelectChunks | kSelectMerge,
@@ -162,7 +171,7 @@ int index_topm_stages(const sa_shape* shape, int stages, const void* q, const fl
                          /*need_idx=*/(stages & kSelectMerge) != 0);
   if (st != SA_OK) return st;
   FilterPlan fplan;
-  st = plan_filter(*shape, n_max, M, &fplan, unit_cu_count());
+  st = plan_filter(*shape, n_max, M, &fplan, unit_cu_count(), scores_plan_on());
   if (st != SA_OK) return st;
   const LaunchCommon c = common(*shape, stream);
   if (fplan.enabled)
@@ -223,7 +232,7 @@ int decode_step_stages(const sa_shape* shape, int stages, const int32_t* pos, in
   st = check_topm_common(shape, seq_lens, n_max, M, idx, workspace, ws_bytes, &tplan);
   if (st != SA_OK) return st;
   FilterPlan fplan;
-  st = plan_filter(*shape, n_max, M, &fplan, unit_cu_count());
+  st = plan_filter(*shape, n_max, M, &fplan, unit_cu_count(), scores_plan_on());
   if (st != SA_OK) return st;
   DecodePlan dplan;
   st = plan_decode(*shape, M, &dplan);
@@ -397,7 +406,7 @@ extern "C" int sparse_attn_selection_fallbacks(const sa_shape* shape, int32_t n_
   if (!ptr_ok(workspace, kAlign) || ws_bytes < workspace_bytes(*shape, n_max, M))
     return SA_ERR_WORKSPACE;
   FilterPlan fplan;
-  st = plan_filter(*shape, n_max, M, &fplan, unit_cu_count());
+  st = plan_filter(*shape, n_max, M, &fplan, unit_cu_count(), scores_plan_on());
   if (st != SA_OK) return st;
   const LaunchCommon c = common(*shape, stream);
   return finish(run_count_fallbacks(c, fplan, workspace, count), c.stream);
@@ -411,9 +420,10 @@ extern "C" int sparse_attn_selection_plan(const sa_shape* shape, int32_t n_max, 
   st = plan_topm(*shape, n_max, M, &tplan);
   if (st != SA_OK) return st;
   FilterPlan fplan;
-  st = plan_filter(*shape, n_max, M, &fplan, unit_cu_count());
+  st = plan_filter(*shape, n_max, M, &fplan, unit_cu_count(), scores_plan_on());
   if (st != SA_OK) return st;
   if (!fplan.enabled) return SA_PLAN_CHUNK_EXACT;
+  if (fplan.all_scores) return SA_PLAN_SCORES;
   return fplan.unit_wg ? SA_PLAN_UNIT : SA_PLAN_FILTER;
 }
 

@@ -115,7 +115,8 @@ size_t dense_workspace_bytes(const sa_shape& s, int n_max) {
   return std::max<size_t>(dp.end, kAlign);
 }
 
-int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* p, int cu_count) {
+int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* p, int cu_count,
+                bool all_scores) {
   const int64_t units = (int64_t)s.batch * s.num_kv_heads;
   *p = FilterPlan{};
   p->units = (int)units;
@@ -152,6 +153,29 @@ int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* p, int cu_count
       p->end = off;
       return SA_OK;
     }
+  }
+  if (all_scores && n_max <= kScoresMaxN) {
+    // scoring workgroups of kScoreChunkMin positions or more, about one per
+    // CU (a 1024-thread workgroup fills one)
+    int64_t chunk = kScoreChunkMin;
+    while (chunk < n_max && units * ceil_div(n_max, chunk) > kDecodeTargetBlocks) chunk *= 2;
+    p->enabled = true;
+    p->all_scores = true;
+    p->chunk = (int)chunk;
+    p->splits = (int)ceil_div(n_max, chunk);
+    p->sstride = (int64_t)align_up((size_t)n_max, 4096);   // whole 4096-float rows of the layout
+    size_t off = 0;
+    p->off_thr = off;
+    off = align_up(off + (size_t)units * sizeof(uint32_t), kAlign);
+    p->off_qt = off;
+    off = align_up(off + (size_t)units * 32 * sizeof(float), kAlign);
+    p->off_path = off;
+    off = align_up(off + (size_t)units * sizeof(int32_t), kAlign);
+    p->off_cnt = off;                          // (no counts)
+    p->off_cand = off;                         // the scores, [units][sstride] floats
+    off = align_up(off + (size_t)units * p->sstride * sizeof(float), kAlign);
+    p->end = off;
+    return SA_OK;
   }
   // Chunks as large as 32768 positions (fewer, longer workgroups stream
   // better: about two rounds of the chip's slots), smaller while the grid is
@@ -208,10 +232,12 @@ size_t workspace_bytes(const sa_shape& s, int n_max, int M) {
     TopmPlan tp;
     if (plan_topm(s, n_max, M, &tp) != SA_OK) return 0;
     need = std::max(need, tp.end);
-    FilterPlan fp;
-    if (plan_filter(s, n_max, M, &fp) != SA_OK) return 0;
-    if (fp.enabled) need = std::max(need, fp.end);
-    if (fused_attend_ok(s, fp)) need = std::max(need, fused_partials_offset(fp) + dp.end);
+    for (bool all_scores : {false, true}) {
+      FilterPlan fp;
+      if (plan_filter(s, n_max, M, &fp, 0, all_scores) != SA_OK) return 0;
+      if (fp.enabled) need = std::max(need, fp.end);
+      if (fused_attend_ok(s, fp)) need = std::max(need, fused_partials_offset(fp) + dp.end);
+    }
   }
   return need;
 }

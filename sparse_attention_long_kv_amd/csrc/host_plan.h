@@ -67,9 +67,19 @@ constexpr int kUnitWaves = 16;
 constexpr int kUnitCap = 768;            // slots per wave list
 constexpr double kUnitMinFill = 0.9;     // units / (CUs x rounds of workgroups), at least
 
+// Short units, few of them: every position is scored (one launch, chunks of
+// the unit in parallel, a 4-byte score per position) and the merge selects
+// exactly over all of a unit's scores, held 16 per thread in position order
+// (no bound, no filter, no fallback).
+constexpr int kScoresMaxN = kFilterSlots;   // 16384 positions per unit, at most
+constexpr int kScoreChunkMin = 2048;        // positions per scoring workgroup, at least
+
 struct FilterPlan {
   bool enabled;
   bool unit_wg;     // one workgroup per unit (splits = 1, lists in LDS, spill pool only)
+  bool all_scores;  // every position scored, merge over the scores (chunk, splits: the
+                    // scoring workgroups; off_cand: the scores, sstride floats per unit)
+  int64_t sstride;
   int units;
   int chunk;        // positions per filter workgroup (multiple of 512)
   int splits;       // chunks per unit
@@ -103,9 +113,12 @@ int plan_dense(const sa_shape& s, int n_max, DecodePlan* out);
 size_t dense_workspace_bytes(const sa_shape& s, int n_max);
 // Fills `out`; out->enabled is false when the shape needs the chunk-exact path.
 // cu_count > 0 (the device's compute units) allows the one-workgroup-per-unit
-// plan where it applies (its workspace never exceeds the chunked plan's, so
-// workspace_bytes, which plans with cu_count = 0, covers both).
-int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* out, int cu_count = 0);
+// plan where it applies (its workspace never exceeds the chunked plan's);
+// all_scores allows the plan that scores every position, for units of at most
+// kScoresMaxN positions that the unit plan does not take.  workspace_bytes
+// covers every plan.
+int plan_filter(const sa_shape& s, int n_max, int M, FilterPlan* out, int cu_count = 0,
+                bool all_scores = false);
 // Where the fused merge + attention keeps its split states: past the filter
 // path's workspace.
 inline size_t fused_partials_offset(const FilterPlan& fp) { return align_up(fp.end, kAlign); }

@@ -929,6 +929,7 @@ struct FilterArgs {
   const float* scores;   // [units][n_max] when R == kScoreInput
   const int32_t* seq_lens;
   int n_max, Ncap, Hq, Hkv, G, M, S, chunk, cap, cslots, spill_cap;
+  int units;         // B * Hkv
   int64_t ustride;   // pairs per unit in cand: S * cslots, then spill_cap
   uint32_t* thr;     // [units]
   float* qt;         // [units][32] indexer queries (written by the bound stage)
@@ -939,6 +940,8 @@ struct FilterArgs {
                      // the bound stage)
   uint2* cand;       // per unit: [S][cslots] (key, position) of the kept positions (any
                      // order), then the spill pool [spill_cap] of lists that filled up
+  float* sc;         // the score-all plan: [units][sstride] scores, position order
+  int64_t sstride;
   int32_t* idx;
 };
 
@@ -1181,14 +1184,17 @@ struct AppendArgs {
   uint16_t* v_cache;
 };
 
-// The unit's first new row is appended (append_row's arithmetic) while its
-// indexer query is formed (indexer_query's arithmetic); both projections
-// share one load of the basis, and every global load of both goes out before
-// the first barrier.  Further new rows (T > 1) follow one at a time.  Leaves
-// the query in qt; part holds NT >= 512 + d doubles of LDS.
+// The unit's new rows t0 .. t1 - 1 (all of them by default) are appended
+// (append_row's arithmetic), the first while the indexer query is formed
+// (indexer_query's arithmetic); both projections share one load of the
+// basis, and every global load of both goes out before the first barrier.
+// Further rows follow one at a time.  Leaves the query in qt; part holds
+// NT >= 512 + d doubles of LDS.
 template <int D, int R, int NT>
 __device__ __forceinline__ void append_rows_and_query(const FilterArgs& a, const AppendArgs& ap,
-                                                      int u, float* qt, double* part) {
+                                                      int u, float* qt, double* part,
+                                                      int t0 = 0, int t1 = -1) {
+  if (t1 < 0) t1 = ap.T;
   constexpr int kPer = D / kProjParts;
   constexpr int kMeanT = 512;                       // threads [512, 512 + d) form the mean
   static_assert(kProjParts * 32 <= 256 && kMeanT + D <= NT, "thread roles");
@@ -1219,10 +1225,10 @@ __device__ __forceinline__ void append_rows_and_query(const FilterArgs& a, const
     return n >= 0 && n < a.Ncap;                    // block-uniform
   };
   size_t row0 = 0;
-  const bool ok0 = ap.T > 0 && row_of(0, row0);
+  const bool ok0 = t1 > t0 && row_of(t0, row0);
   if (ok0) {
-    const uint16_t* kr = ap.k_new + (size_t)u * ap.T * D;
-    const uint16_t* vr = ap.v_new + (size_t)u * ap.T * D;
+    const uint16_t* kr = ap.k_new + ((size_t)u * ap.T + t0) * D;
+    const uint16_t* vr = ap.v_new + ((size_t)u * ap.T + t0) * D;
     if (t < D / 8) {
       const size_t off = row0 * D + t * 8;
       *reinterpret_cast<uint4*>(ap.k_cache + off) = *reinterpret_cast<const uint4*>(kr + t * 8);
@@ -1258,7 +1264,7 @@ __device__ __forceinline__ void append_rows_and_query(const FilterArgs& a, const
     for (int q = 0; q < kProjParts; ++q) sum += part_q[q * R + t];
     qt[t] = (float)sum;
   }
-  for (int tok = 1; tok < ap.T; ++tok) {
+  for (int tok = t0 + 1; tok < t1; ++tok) {
     size_t row;
     if (!row_of(tok, row)) continue;
     append_row<D, R>(ap.k_new + ((size_t)u * ap.T + tok) * D,
@@ -1960,6 +1966,283 @@ __global__ __launch_bounds__(kMergeThreads) void select_attend_kernel(const Filt
 }
 
 
+// ------------------------------------------------------------------ every position scored
+//
+// Short units, few of them (at most kScoresMaxN positions, too few units for
+// one workgroup each): a first launch scores every position -- each
+// workgroup one chunk of a unit -- and the merge selects exactly over all of
+// a unit's scores, 16 per thread in registers.  No bound, no filter, no
+// fallback; the candidates the filter plan would keep are a third of such a
+// unit anyway.  Each scoring workgroup forms the unit's indexer query (the
+// bits every kernel forms) and appends the unit's new rows that fall in its
+// chunk (the last chunk also those past it); a chunk with no new row has all
+// of its code loads in flight before the query is formed.  The scores are
+// CodeStream's chains (the filter's bits).
+//
+// Layout: position p = 1024 r + t (t < 1024, r < 16) goes to float
+// 4096 (r / 4) + 4 t + r % 4 of the unit's array, so that merge thread t
+// loads its 16 scores (key register r = position 1024 r + t) as four 16-byte
+// loads.  Both launches keep a unit's workgroups on one XCD (workgroups are
+// handed to the 8 XCDs in turn), so the merges of its splits find its scores
+// in one L2.
+constexpr int kScoreAllThreads = kSampleThreads;   // the prologue's thread roles need 1024
+constexpr int kScoreAllLoads = 4;                  // 4 x 16 KB: a 2048-position chunk at once
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int scores_slot(int p) {
+  static_assert(kMergeThreads == 1024, "the layout follows the merge's 1024 threads");
+  const int r = p >> 10, t = p & 1023;
+  return ((r >> 2) << 12) | (t << 2) | (r & 3);
+}
+
+// Workgroup g of a units x per grid -> (unit, part) with a unit's parts on
+// one XCD when units divide evenly among them, else unit-major.
+__device__ __forceinline__ void xcd_unit_part(int g, int units, int per, int& u, int& part) {
+  if (units % kXcds == 0) {
+    const int x = g % kXcds, j = g / kXcds;
+    part = j % per;
+    u = x + kXcds * (j / per);
+  } else {
+    u = g / per;
+    part = g % per;
+  }
+}
+
+template <int D, int R>
+__global__ __launch_bounds__(kScoreAllThreads) void score_all_kernel(const FilterArgs a,
+                                                                     const AppendArgs ap) {
+  constexpr int NT = kScoreAllThreads;
+  __shared__ float qt[32];
+  __shared__ double part[NT];
+  int u, c;
+  xcd_unit_part(blockIdx.x, a.units, a.S, u, c);
+  const int b = u / a.Hkv, h = u % a.Hkv;
+  const int len = unit_len(a.seq_lens, b, a.n_max);
+  const int base = c * a.chunk;
+  const int nv = min(max(len - base, 0), a.chunk);
+  // the new rows this workgroup appends: those in [base, base + chunk), and
+  // for the last chunk every row past it too
+  int t0 = 0, t1 = 0;
+  if (ap.T > 0) {
+    const long p0 = ap.pos[b];
+    t0 = (int)min(max((long)base - p0, 0L), (long)ap.T);
+    t1 = c == a.S - 1 ? ap.T : (int)min(max((long)base + a.chunk - p0, 0L), (long)ap.T);
+  }
+  const bool fresh = t1 > t0;                         // block-uniform
+  CodeStream<R, NT, kScoreAllLoads> cs;
+  cs.init(make_rsrc(a.kp + ((size_t)u * a.Ncap + base) * R, (uint32_t)nv * R), nv);
+  if (!fresh && nv > 0) cs.issue_first();
+  if (fresh)
+    append_rows_and_query<D, R, NT>(a, ap, u, qt, part, t0, t1);
+  else
+    indexer_query<D, R, NT>(a.q, a.P, b, h, a.G, a.Hq, qt, part);
+  // a chunk with new rows reads its codes only once their stores completed
+  if (fresh) __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (c == 0 && threadIdx.x < R) a.qt[(size_t)u * 32 + threadIdx.x] = qt[threadIdx.x];
+  float* su = a.sc + (size_t)u * a.sstride;
+  if (nv > 0)
+    cs.run(qt, [&](float sc, int p, bool owner) {
+      if (owner && p < nv) su[scores_slot(base + p)] = sc;
+    });
+}
+
+// Exact threshold over keys whose scores lie in [smin, smax] (finite, smax >
+// smin; keys outside [klo, khi] -- NaN scores -- count as below or above
+// every score): the first level bins the scores by value, 4096 equal-width
+// bins (monotone in the key, so every key of a higher bin is larger), which
+// leaves few keys in the bin of the target-th largest where the scores
+// crowd; that bin's keys are then ranked directly (or, when it is large,
+// selected by radix levels over their keys).  Returns t, need and eq as
+// finish_threshold does.
+template <int NT, int K>
+__device__ __forceinline__ void threshold_by_value(SelectShared<NT>& sh, const uint32_t (&key)[K],
+                                                   uint32_t klo, uint32_t khi, uint32_t target,
+                                                   uint32_t& t_out, uint32_t& need_out,
+                                                   uint32_t& eq_out) {
+  const int tid = threadIdx.x;
+  const float smin = key_score(klo), smax = key_score(khi);
+  const float scale = (float)kBins / (smax - smin);
+  auto bin_of = [&](uint32_t k) -> uint32_t {
+    if (k > khi) return (uint32_t)kBins - 1u;
+    if (k < klo) return 0u;
+    const float x = (key_score(k) - smin) * scale;
+    return min((uint32_t)x, (uint32_t)kBins - 1u);
+  };
+  const uint32_t dummy = (uint32_t)(kBins + lane_id());
+#pragma unroll
+  for (int i = 0; i < K; ++i) hist_add(sh.hist, key[i] ? bin_of(key[i]) : dummy);
+  __syncthreads();
+  uint32_t path = 0, above = 0;
+  pick_bin<NT>(sh, kDigitBits, target, path, above);
+  const uint32_t bstar = path, nbin = sh.pick[2];
+  const uint32_t rank = target - above;
+  if (nbin <= (uint32_t)kRankMax && nbin <= (uint32_t)NT && nbin + 4 <= (uint32_t)SelectShared<NT>::kCap) {
+    if (tid == 0) sh.pick[3] = 0u;
+    if (tid < 4) sh.list[nbin + tid] = 0u;           // pad for rank_in_list
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+      if (key[i] && bin_of(key[i]) == bstar) sh.list[atomicAdd(&sh.pick[3], 1u)] = key[i];
+    __syncthreads();
+    uint32_t t, gt, eq;
+    rank_in_list<NT>(sh, nbin, rank, t, gt, eq);
+    t_out = t;
+    need_out = rank - gt;
+    eq_out = eq;
+    return;
+  }
+  // a crowded bin: the exact search over its keys alone (equal keys share a
+  // bin, every key above it is larger than all of them)
+  for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const bool in = key[i] && bin_of(key[i]) == bstar;
+    hist_add(sh.hist, in ? (key[i] >> kTopShift) : dummy);
+  }
+  __syncthreads();
+  finish_threshold<NT>(sh, rank, t_out, need_out, eq_out, [&](auto&& f) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) f(key[i], key[i] != 0u && bin_of(key[i]) == bstar);
+  });
+}
+
+// The merge of unit u over its scores (the whole workgroup; it synchronises):
+// position 1024 i + t sits in key register i of thread t, so register order
+// (i, wave, lane) is position order.  The M-th largest key is found exactly
+// (threshold_by_value, or finish_threshold over the keys when the scores
+// span no finite range) and the selection is emitted in register order
+// (emit_in_order: every key above it and, of the keys equal to it, the
+// lowest positions).  Leaves the M positions, ascending, in sh.list and, when
+// write_idx, in idx (with the unit's path flag 0).  interleaved: the scores
+// in score_all_kernel's layout, else in position order (a caller's).  red:
+// 2 NT / kWave words.
+__device__ __forceinline__ void scores_merge_unit(const FilterArgs& a,
+                                                  SelectShared<kMergeThreads>& sh,
+                                                  uint32_t* red, int u, bool write_idx,
+                                                  bool interleaved) {
+  constexpr int NT = kMergeThreads, K = kFilterMergeKeys, W = NT / kWave;
+  static_assert(NT * K >= kScoresMaxN && K % 4 == 0, "a unit's scores fit the registers");
+  static_assert(kFilterMaxM <= kListCap - kWave, "the selection is staged in LDS");
+  const int b = u / a.Hkv;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int len = unit_len(a.seq_lens, b, a.n_max);
+  const int M = a.M;
+  int32_t* idx_u = write_idx ? a.idx + (size_t)u * M : nullptr;
+  int32_t* out = reinterpret_cast<int32_t*>(sh.list);
+  if (write_idx && tid == 0) a.path[u] = 0;
+  if (len <= M) {                                     // every valid position, in order
+    for (int j = tid; j < M; j += NT) {
+      out[j] = j < len ? j : -1;
+      if (idx_u) idx_u[j] = out[j];
+    }
+    __syncthreads();
+    return;
+  }
+  const float* su = a.sc + (size_t)u * a.sstride;
+  uint32_t key[K];
+  if (interleaved) {                                  // block-uniform
+#pragma unroll
+    for (int i4 = 0; i4 < K / 4; ++i4) {
+      float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (4 * i4 * NT < len) v = *reinterpret_cast<const float4*>(su + (i4 << 12) + (tid << 2));
+      const float x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = (4 * i4 + e) * NT + tid;
+        key[4 * i4 + e] = p < len ? score_key(x[e] + 0.0f) : 0u;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const int p = i * NT + tid;
+      key[i] = p < len ? score_key(su[p] + 0.0f) : 0u;
+    }
+  }
+  // the range of the finite scores (keys outside [key(-inf), key(+inf)] are
+  // NaN scores)
+  const uint32_t kneg = score_key(-__builtin_inff()), kpos = score_key(__builtin_inff());
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    if (key[i] >= kneg && key[i] <= kpos) {
+      kmax = max(kmax, key[i]);
+      kmin = min(kmin, key[i]);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
+  }
+  if (lane == 0) {
+    red[w] = kmax;
+    red[W + w] = kmin;
+  }
+  for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
+  __syncthreads();
+  kmax = 0u;
+  kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int ww = 0; ww < W; ++ww) {
+    kmax = max(kmax, red[ww]);
+    kmin = min(kmin, red[W + ww]);
+  }
+  uint32_t t, need, eq;
+  const float smin = key_score(kmin), smax = key_score(kmax);
+  const bool by_value = kmin < kmax && smin > -__builtin_inff() && smax < __builtin_inff() &&
+                        smax - smin < __builtin_inff() &&
+                        (float)kBins / (smax - smin) < __builtin_inff();   // block-uniform
+  if (by_value) {
+    threshold_by_value<NT>(sh, key, kmin, kmax, (uint32_t)M, t, need, eq);
+  } else {
+    const uint32_t dummy = (uint32_t)(kBins + lane);
+#pragma unroll
+    for (int i = 0; i < K; ++i) hist_add(sh.hist, key[i] ? (key[i] >> kTopShift) : dummy);
+    __syncthreads();
+    finish_threshold<NT>(sh, (uint32_t)M, t, need, eq, [&](auto&& f) {
+#pragma unroll
+      for (int i = 0; i < K; ++i) f(key[i], key[i] != 0u);
+    });
+  }
+  emit_in_order(key, t, need, eq, sh, [&](int i, bool sel, uint32_t slot) {
+    out[sel ? slot : (uint32_t)(kListCap - kWave + lane)] = i * NT + tid;
+  });
+  if (idx_u)
+    for (int j = tid; j < M; j += NT) idx_u[j] = out[j];
+}
+
+template <bool INTERLEAVED>
+__global__ __launch_bounds__(kMergeThreads) void scores_merge_kernel(const FilterArgs a) {
+  __shared__ SelectShared<kMergeThreads> sh;
+  __shared__ uint32_t red[2 * kMergeThreads / kWave];
+  scores_merge_unit(a, sh, red, blockIdx.x, true, INTERLEAVED);
+}
+
+// Merge and attention in one launch, as select_attend_kernel: each of the
+// unit's d.S workgroups merges (split 0 writes idx) and attends over its
+// split of the selection it leaves in LDS.
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void scores_select_attend_kernel(const FilterArgs a,
+                                                                             const DecodeArgs d) {
+  static_assert(kAttendThreads == kMergeThreads, "one workgroup shape for both");
+  __shared__ SelectShared<kMergeThreads> sh;
+  __shared__ uint32_t red[2 * kMergeThreads / kWave];
+  __shared__ float sm[kAttendWaves][kMaxHeads], sl[kAttendWaves][kMaxHeads];
+  __shared__ float so[kFusedAttendMaxGD * kAttendWaves];   // the waves' output tiles
+  int u, split;
+  xcd_unit_part(blockIdx.x, a.units, d.S, u, split);
+  scores_merge_unit(a, sh, red, u, split == 0, true);
+  AttendWave<D, kAttendWaves> aw;
+  aw.init(d, u);
+  const int r0 = split * d.rps;
+  const int r1 = min(d.M, r0 + d.rps);
+  aw.rows(d, reinterpret_cast<const int32_t*>(sh.list) + r0, r1 - r0);
+  aw.finish(d, u, split, sm, sl, so);
+}
+
 // ------------------------------------------------------------------ one workgroup per unit
 //
 // When the units fill the chip, one 1024-thread workgroup per unit runs the
@@ -2166,7 +2449,24 @@ hipError_t run_count_fallbacks(const LaunchCommon& c, const FilterPlan& plan,
 
 template <int D, int R>
 static void launch_filter_dr(const FilterArgs& a, const AppendArgs* ap, const DecodeArgs* da,
-                             int stages, int units, bool unit_wg, hipStream_t st) {
+                             int stages, int units, bool unit_wg, bool all_scores,
+                             hipStream_t st) {
+  if (all_scores) {
+    // the bound stage scores every position (and appends), the merge stage
+    // selects over the scores (and attends); the candidates stage has
+    // nothing of its own
+    AppendArgs none{};
+    none.T = 0;
+    if (stages & kSelectBound)
+      hipLaunchKernelGGL((score_all_kernel<D, R>), dim3((unsigned)(units * a.S)),
+                         dim3(kScoreAllThreads), 0, st, a, ap ? *ap : none);
+    if ((stages & kSelectMerge) && da)
+      hipLaunchKernelGGL((scores_select_attend_kernel<D>), dim3((unsigned)(units * da->S)),
+                         dim3(kMergeThreads), 0, st, a, *da);
+    else if (stages & kSelectMerge)
+      hipLaunchKernelGGL(scores_merge_kernel<true>, dim3(units), dim3(kMergeThreads), 0, st, a);
+    return;
+  }
   if (unit_wg) {
     // one launch for the whole selection (and the append and attention when
     // given), made by the candidates stage; the bound and merge stages have
@@ -2229,6 +2529,7 @@ hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int 
   a.chunk = plan.chunk;
   a.cap = plan.cap;
   a.cslots = plan.cslots;
+  a.units = plan.units;
 
   char* ws = (char*)workspace;
   a.thr = (uint32_t*)(ws + plan.off_thr);
@@ -2238,6 +2539,8 @@ hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int 
   a.cand = (uint2*)(ws + plan.off_cand);
   a.spill_cap = plan.spill_cap;
   a.ustride = plan.ustride;
+  a.sc = plan.all_scores ? (float*)(ws + plan.off_cand) : nullptr;
+  a.sstride = plan.sstride;
   a.idx = idx;
   if ((long)plan.units * plan.splits > INT32_MAX) return hipErrorInvalidConfiguration;
   AppendArgs ap;
@@ -2278,15 +2581,23 @@ hipError_t run_filter_select(const LaunchCommon& c, const FilterPlan& plan, int 
   const DecodeArgs* dap = att ? &da : nullptr;
   if (scores) {
     if (rows || att || plan.unit_wg) return hipErrorInvalidValue;
-    launch_filter_scores(a, stages, plan.units, c.stream);
+    if (plan.all_scores) {                            // the caller's scores are the merge's
+      a.sc = const_cast<float*>(scores);
+      a.sstride = n_max;
+      if (stages & kSelectMerge)
+        hipLaunchKernelGGL(scores_merge_kernel<false>, dim3(plan.units), dim3(kMergeThreads), 0,
+                           c.stream, a);
+    } else {
+      launch_filter_scores(a, stages, plan.units, c.stream);
+    }
     return hipGetLastError();
   }
-  const bool uw = plan.unit_wg;
+  const bool uw = plan.unit_wg, as = plan.all_scores;
   if (uw && att && da.S != 1) return hipErrorInvalidConfiguration;
-  if (c.D == 128 && c.R == 32) launch_filter_dr<128, 32>(a, app, dap, stages, plan.units, uw, c.stream);
-  else if (c.D == 128 && c.R == 16) launch_filter_dr<128, 16>(a, app, dap, stages, plan.units, uw, c.stream);
-  else if (c.D == 64 && c.R == 32) launch_filter_dr<64, 32>(a, app, dap, stages, plan.units, uw, c.stream);
-  else launch_filter_dr<64, 16>(a, app, dap, stages, plan.units, uw, c.stream);
+  if (c.D == 128 && c.R == 32) launch_filter_dr<128, 32>(a, app, dap, stages, plan.units, uw, as, c.stream);
+  else if (c.D == 128 && c.R == 16) launch_filter_dr<128, 16>(a, app, dap, stages, plan.units, uw, as, c.stream);
+  else if (c.D == 64 && c.R == 32) launch_filter_dr<64, 32>(a, app, dap, stages, plan.units, uw, as, c.stream);
+  else launch_filter_dr<64, 16>(a, app, dap, stages, plan.units, uw, as, c.stream);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && att && !uw && (stages & kSelectMerge)) e = run_combine(c, da);
   return e;

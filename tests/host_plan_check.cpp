@@ -93,6 +93,33 @@ static void check_one(const sa_shape& s, int n_max, int M) {
   CHECK(ws >= fp.end, "ws covers the filter plan");
   if (fused_attend_ok(s, fp))
     CHECK(ws >= fused_partials_offset(fp) + dp.end, "ws covers the fused partials");
+  // the plan that scores every position
+  {
+    FilterPlan sp;
+    CHECK(plan_filter(s, n_max, M, &sp, 0, true) == SA_OK, "plan_filter(all_scores)");
+    CHECK(sp.enabled, "the scores plan keeps the filter path enabled");
+    CHECK(sp.all_scores == (n_max <= kScoresMaxN), "scores plan for n_max %d", n_max);
+    if (sp.all_scores) {
+      CHECK(!sp.unit_wg, "one plan at a time");
+      CHECK(sp.chunk >= kScoreChunkMin && sp.chunk % kChunkBlock == 0, "score chunk %d", sp.chunk);
+      CHECK((int64_t)sp.splits * sp.chunk >= n_max && (int64_t)(sp.splits - 1) * sp.chunk < n_max,
+            "score chunks cover n_max with none empty");
+      CHECK(units * sp.splits <= INT32_MAX, "score grid fits");
+      CHECK(sp.sstride >= n_max && sp.sstride % 4096 == 0, "score stride: whole rows of the layout");
+      CHECK(aligned(sp.off_cand) && aligned(sp.end), "scores align");
+      CHECK(sp.off_thr == fp.off_thr && sp.off_qt == fp.off_qt && sp.off_path == fp.off_path,
+            "thr, qt and path flags where the chunked plan has them");
+      CHECK(sp.off_cand >= sp.off_path + (size_t)units * 4, "scores after the path flags");
+      CHECK(sp.end >= sp.off_cand + (size_t)units * sp.sstride * 4, "scores fit");
+      // positions and offsets inside a unit's scores are formed in 32 bits
+      CHECK(sp.sstride <= INT32_MAX, "score offsets fit");
+      CHECK(ws >= sp.end, "ws %zu covers the scores plan %zu", ws, sp.end);
+      if (fused_attend_ok(s, sp))
+        CHECK(ws >= fused_partials_offset(sp) + dp.end, "ws covers the scores plan's partials");
+    } else {
+      CHECK(sp.end == fp.end && sp.splits == fp.splits, "no scores plan: the filter plan");
+    }
+  }
   // the one-workgroup-per-unit plan (on devices of these compute-unit counts)
   for (int cus : {80, 256, 304}) {
     FilterPlan up;

@@ -56,6 +56,19 @@ def _fallbacks(sh, n_max, M, ws):
     return int(cnt.item())
 
 
+def _use_plan(monkeypatch, plan):
+    """plan "filter": keep the sampled-bound filter plan where the plan that
+    scores every position would serve the shape (both give the same bits)."""
+    if plan == "filter":
+        monkeypatch.setenv("SPARSE_ATTN_SCORES_PLAN", "0")
+
+
+def _scores_shape(n_max, M):
+    """Whether the plan that scores every position serves a selection of
+    these sizes (on the chunked plans' shapes)."""
+    return n_max <= 16384 and M <= 6144 and M < n_max
+
+
 def _rand_inputs(B, Hq, Hkv, d, r, N, seed):
     g = torch.Generator().manual_seed(seed)
     q = torch.randn(B, Hq, d, generator=g).to(torch.bfloat16)
@@ -194,11 +207,21 @@ def _topm_case(name, seed=3):
     return (B, Hq, Hkv, d, r, N, n_max, lens, M), q, K, V, P
 
 
-@pytest.mark.parametrize("name", list(TOPM_CASES))
-def test_topm_fused_and_unfused_match_oracle(name):
+# every case as planned, and the short ones also with the filter plan
+TOPM_PARAMS = [(n, "planned") for n in TOPM_CASES] + [
+    (n, "filter") for n, c in TOPM_CASES.items() if _scores_shape(c[6], c[8])]
+
+
+@pytest.mark.parametrize("name,plan", TOPM_PARAMS)
+def test_topm_fused_and_unfused_match_oracle(name, plan, monkeypatch):
     (B, Hq, Hkv, d, r, N, n_max, lens, M), q, K, V, P = _topm_case(name)
-    _say("case: topm", name, "B=%d Hkv=%d n_max=%d M=%d" % (B, Hkv, n_max, M))
+    _say("case: topm", name, plan, "B=%d Hkv=%d n_max=%d M=%d" % (B, Hkv, n_max, M))
+    _use_plan(monkeypatch, plan)
     sh = _shape_of(B, Hq, Hkv, d, r, N)
+    want_plan = (sa.SA_PLAN_SCORES if plan == "planned" and _scores_shape(n_max, M) else
+                 sa.SA_PLAN_FILTER if n_max <= 2 ** 19 and M <= 6144 and M < n_max else
+                 sa.SA_PLAN_CHUNK_EXACT)
+    assert sa.sparse_attn_selection_plan(sh, n_max, M) == want_plan
     P64 = P.double().numpy()
     kp = oracle_kp(f64(K), P64)
     qd, Pd, kpd = _dev(q), _dev(P), _dev(kp)
@@ -213,8 +236,9 @@ def test_topm_fused_and_unfused_match_oracle(name):
     idx_s = torch.full_like(idx_f, -7)
     for stage in (sa.SA_STAGE_BOUND, sa.SA_STAGE_CANDIDATES, sa.SA_STAGE_MERGE):
         sa.sparse_attn_index_topm_stage(sh, stage, qd, Pd, kpd, sl, n_max, M, idx_s, ws)
-    # which method served the shape: the filter path's merge (no unit falls
-    # back to the exact streaming pass) inside its limits, else chunk-exact
+    # which method served the shape: the merge over the kept keys or the
+    # scores (no unit falls back to the exact streaming pass) inside the
+    # filter path's limits, else chunk-exact
     fb = _fallbacks(sh, n_max, M, ws)
     filter_path = n_max <= 2 ** 19 and M <= 6144 and M < n_max
     assert fb == (0 if filter_path else -1), (name, fb)
@@ -755,12 +779,15 @@ def test_topm_all_scores_equal_takes_lowest_positions():
     assert gi[0, 0].tolist() == list(range(M))
 
 
-def test_topm_ties_cut_by_m_take_lowest_positions():
+@pytest.mark.parametrize("plan", ["planned", "filter"])
+def test_topm_ties_cut_by_m_take_lowest_positions(plan, monkeypatch):
     """97 distinct FP8 rows repeated along the context: scores come in tie
-    groups of ~169 and M cuts one; the filter path (no list can overflow
-    here) must take, of the tied group, exactly the lowest positions, as the
-    chunk-exact path and the oracle do."""
-    _say("case: topm ties cut by M")
+    groups of ~169 and M cuts one; the merge over all scores (as planned)
+    and the filter path's merge (no list can overflow here) must take, of
+    the tied group, exactly the lowest positions, as the chunk-exact path and
+    the oracle do."""
+    _say("case: topm ties cut by M", plan)
+    _use_plan(monkeypatch, plan)
     B, Hq, Hkv, d, r, N, M = 1, 4, 1, 128, 32, 16384, 1000
     q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, 97, seed=23)
     P64 = P.double().numpy()
@@ -890,18 +917,24 @@ def test_decode_step_with_clustered_high_scores():
 
 # ------------------------------------------------------------------ decode step
 
-@pytest.mark.parametrize("B,Hq,Hkv,d,r,N,M", [
+SELECT_ATTEND_CASES = [
     (2, 8, 2, 128, 32, 8192, 512),     # G d = 512: one launch, then the split merge
     (1, 16, 1, 128, 16, 4096, 256),    # G d = 2048: merge and attention launched apart
     (3, 12, 1, 64, 16, 6000, 700),     # G d = 768, ragged tiles
     (1, 4, 1, 128, 32, 20000, 6144),   # the largest M the merge stages in LDS
-])
-def test_select_attend_stage_equals_merge_then_attend(B, Hq, Hkv, d, r, N, M):
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,r,N,M,plan", [
+    c + (p,) for c in SELECT_ATTEND_CASES for p in ("planned", "filter")
+    if p == "planned" or _scores_shape(c[5], c[6])])
+def test_select_attend_stage_equals_merge_then_attend(B, Hq, Hkv, d, r, N, M, plan, monkeypatch):
     """SA_STEP_SELECT_ATTEND (the merge workgroups go on to attend over the
     selection they hold) writes the same idx, out and lse, bit for bit, as
     SA_STEP_MERGE followed by SA_STEP_ATTEND; the attention of two units is
     checked against the oracle over the selected rows."""
-    _say("case: select+attend", B, Hq, Hkv, d, r, N, M)
+    _say("case: select+attend", B, Hq, Hkv, d, r, N, M, plan)
+    _use_plan(monkeypatch, plan)
     sh = _shape_of(B, Hq, Hkv, d, r, N)
     q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, N, seed=41)
     g = torch.Generator().manual_seed(42)
@@ -1060,6 +1093,7 @@ def test_unit_workgroup_plan_equals_chunked_plan(case, monkeypatch):
     res, plans = {}, {}
     for flag in ("1", "0"):
         monkeypatch.setenv("SPARSE_ATTN_UNIT_WG", flag)
+        monkeypatch.setenv("SPARSE_ATTN_SCORES_PLAN", flag)   # "0": the sampled-bound filter
         plans[flag] = sa.sparse_attn_selection_plan(sh, N, M)
         Kd, Vd = _dev(K), _dev(V)
         kp = torch.empty(B, Hkv, N, r, dtype=torch.uint8, device="cuda")
@@ -1175,3 +1209,114 @@ def test_unit_workgroup_step_scores_the_new_token(d, r):
         assert torch.equal(x, y), name
     gi = res[0][3].cpu().numpy()
     assert np.all(gi[:, :, -1] == N - 1), "the new token must be selected in every unit"
+
+
+# ------------------------------------------------------------------ every position scored
+
+SCORES_CASES = [
+    # (B, Hq, Hkv, d, r, N, M, T, seq_lens): few units, short enough that every
+    # position is scored and the merge selects over all of a unit's scores
+    (8, 28, 4, 128, 32, 16384, 2048, 1, None),              # the 16K GQA workload's shape
+    (3, 8, 2, 128, 32, 6000, 512, 3, [6000, 300, 2049]),    # new rows across a chunk edge; len <= M
+    (2, 8, 2, 64, 16, 16384, 1, 1, [16384, 9000]),          # d = 64, M = 1
+    (1, 4, 1, 128, 32, 3000, 2999, 1, None),                # M = n_max - 1
+    (2, 12, 2, 128, 16, 5000, 700, 2, [0, 1]),              # an empty unit, a unit of one row
+]
+
+
+@pytest.mark.parametrize("case", SCORES_CASES)
+def test_scores_plan_equals_filter_plan(case, monkeypatch):
+    """The plan that scores every position (the scores written out, then an
+    exact merge over all of a unit's scores with the attention in the merge
+    launch) writes the same caches, idx, out and lse, bit for bit, as the
+    sampled-bound filter plan (SPARSE_ATTN_SCORES_PLAN=0): through the staged
+    decode step, the staged fused selection and sparse_attn_topm over the
+    scores sparse_attn_index_score writes; the oracle checks three units."""
+    B, Hq, Hkv, d, r, N, M, T, lens = case
+    _say("case: scores plan", case)
+    sh = _shape_of(B, Hq, Hkv, d, r, N)
+    G = Hq // Hkv
+    q, K, V, P = _unit_inputs(B, Hq, Hkv, d, r, N, seed=B + Hkv + T)
+    sl = None if lens is None else _dev(torch.tensor(lens, dtype=torch.int32))
+    Ls = [N if lens is None else lens[b] for b in range(B)]
+    g = torch.Generator().manual_seed(7)
+    k_new = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16)
+    v_new = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16)
+    pos = torch.tensor([max(L - T, 0) for L in Ls], dtype=torch.int32)
+    scale = default_scale(d)
+    res, plans = {}, {}
+    for flag in ("1", "0"):
+        monkeypatch.setenv("SPARSE_ATTN_SCORES_PLAN", flag)
+        plans[flag] = sa.sparse_attn_selection_plan(sh, N, M)
+        Kd, Vd = _dev(K), _dev(V)
+        kp = torch.empty(B, Hkv, N, r, dtype=torch.uint8, device="cuda")
+        sa.sparse_attn_project_keys(sh, Kd, _dev(P), 0, N, kp)
+        ws = sa.alloc_workspace(sh, N, M)
+        idx = torch.full((B, Hkv, M), -9, dtype=torch.int32, device="cuda")
+        out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+        for stage in (sa.SA_STEP_APPEND_BOUND, sa.SA_STEP_CANDIDATES, sa.SA_STEP_SELECT_ATTEND):
+            sa.sparse_attn_decode_step_stage(sh, stage, _dev(pos), _dev(k_new), _dev(v_new),
+                                             _dev(q), _dev(P), Kd, Vd, kp, sl, N, M, scale, idx,
+                                             out, lse, ws)
+        fb = _fallbacks(sh, N, M, ws)
+        idx2 = torch.full_like(idx, -9)
+        for stage in (sa.SA_STAGE_BOUND, sa.SA_STAGE_CANDIDATES, sa.SA_STAGE_MERGE):
+            sa.sparse_attn_index_topm_stage(sh, stage, _dev(q), _dev(P), kp, sl, N, M, idx2, ws)
+        scores = torch.empty(B, Hkv, N, dtype=torch.float32, device="cuda")
+        sa.sparse_attn_index_score(sh, _dev(q), _dev(P), kp, sl, N, scores)
+        idx3 = torch.full_like(idx, -9)
+        sa.sparse_attn_topm(sh, scores, sl, N, M, idx3, ws)
+        torch.cuda.synchronize()
+        res[flag] = (Kd, Vd, kp, idx, out, lse, idx2, idx3)
+        if flag == "1":
+            assert fb == 0, fb                                # no bound, so no fallback
+    assert plans == {"1": sa.SA_PLAN_SCORES, "0": sa.SA_PLAN_FILTER}, plans
+    names = ("k", "v", "kp", "idx", "out", "lse", "idx_topm_stages", "idx_topm_scores")
+    for name, x, y in zip(names, res["1"], res["0"]):
+        assert torch.equal(x, y), name
+    Kd, Vd, kp, idx, out, lse, idx2, idx3 = res["1"]
+    assert torch.equal(idx, idx2) and torch.equal(idx, idx3)
+    gi, go = idx.cpu().numpy(), f64(out)
+    q64, P64, K64, V64 = f64(q), P.double().numpy(), f64(K), f64(V)
+    for b, h in sorted({(0, 0), (B - 1, Hkv - 1), (min(2, B - 1), 1 % Hkv)}):
+        L = Ls[b]
+        if L == 0:
+            assert np.all(gi[b, h] == -1)
+            continue
+        kp0 = oracle.project_keys(K64[b, h], P64[h])[None, None]
+        K2, V2, kp2 = oracle.append_kv(K64[b, h][None, None], V64[b, h][None, None], kp0,
+                                       pos.numpy()[b:b + 1], f64(k_new)[b:b + 1, h:h + 1],
+                                       f64(v_new)[b:b + 1, h:h + 1], P64[h:h + 1])
+        qg = q64[b, h * G:(h + 1) * G]
+        oi, oo, _, sc = oracle.decode_step_unit(qg, K2[0, 0], V2[0, 0], kp2[0, 0], P64[h], L, M,
+                                                scale)
+        swaps = check_topm_unit(gi[b, h], sc, M, L)
+        _say("  unit", (b, h), "L", L, "band swaps", swaps)
+        if not np.array_equal(gi[b, h], oi):
+            oo, _ = oracle.sparse_attention(qg, K2[0, 0], V2[0, 0], gi[b, h], scale)
+        check_attention(go[b, h * G:(h + 1) * G], oo, "scores plan %s" % ((b, h),))
+
+
+def test_scores_plan_all_equal_takes_lowest_positions():
+    """Every score of one unit equal (every code 1.0) under the plan that
+    scores every position: the merge's threshold is that score and the tie
+    goes to the M lowest positions; a unit of random scores beside it is
+    checked against the oracle's top-M."""
+    _say("case: scores plan, all equal")
+    B, Hq, Hkv, d, r, N, M = 1, 8, 2, 64, 16, 16384, 1000
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, N, seed=61)
+    P64 = P.double().numpy()
+    kp = oracle_kp(f64(K), P64)
+    kp[0, 1] = 0x38
+    sh = _shape_of(B, Hq, Hkv, d, r, N)
+    assert sa.sparse_attn_selection_plan(sh, N, M) == sa.SA_PLAN_SCORES
+    ws = sa.alloc_workspace(sh, N, M)
+    idx = torch.empty(B, Hkv, M, dtype=torch.int32, device="cuda")
+    sa.sparse_attn_index_topm(sh, _dev(q), _dev(P), _dev(kp), None, N, M, idx, ws)
+    gi = idx.cpu().numpy()
+    assert _fallbacks(sh, N, M, ws) == 0
+    assert gi[0, 1].tolist() == list(range(M))
+    G = Hq // Hkv
+    qt = oracle.indexer_query(f64(q)[0, 0:G], P64[0])
+    check_topm_unit(gi[0, 0], oracle.index_scores(qt, kp[0, 0]), M, N)

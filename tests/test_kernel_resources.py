@@ -26,6 +26,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(bl.HIPCC) and shutil.which("h
 
 # kernels on the decode step and the extensions (mangled-name fragments)
 HOT = ("append_bound_kernel", "sample_kernel", "filter_kernel", "filter_merge_kernel", "unit_kernel",
+       "score_all_kernel", "scores_merge_kernel", "scores_select_attend_kernel",
        "select_attend_kernel", "decode_kernel", "combine_kernel", "append_kv_kernel",
        "linear_gate_kernel", "index_score_kernel")
 

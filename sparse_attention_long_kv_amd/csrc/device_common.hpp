@@ -90,9 +90,20 @@ constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // row_half_mirror
 constexpr int kDppMirror = 0x140;     // row_mirror
 
+constexpr int kDppRowShr = 0x110;     // row_shr:n = kDppRowShr + n (n = 1 .. 15)
+constexpr int kDppRowBcast15 = 0x142; // lane 15 of each row to the next row
+constexpr int kDppRowBcast31 = 0x143; // lane 31 to rows 2 and 3
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// x moved by DPP control CTRL; rows outside ROW_MASK keep `old`, and with
+// ZERO a lane whose source lies outside its row reads 0.
+template <int CTRL, int ROW_MASK, bool ZERO>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROW_MASK, 0xF, ZERO);
 }
 
 // Sum over aligned groups of W lanes (W in 2, 4, 8, 16); every lane of the
@@ -140,14 +151,30 @@ __device__ __forceinline__ int popc64(uint64_t m) { return __builtin_popcountll(
 
 // Inclusive prefix sum across the 64 lanes of a wave (uint32).
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
-  const int l = lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off, kWave);
-    if (l >= off) x += y;
-  }
+  // Hillis-Steele shifts inside each 16-lane row, then every row adds the
+  // totals of the rows below it (row broadcasts): six DPP adds, no LDS trips
+  x += dpp_u32<kDppRowShr + 1, 0xF, true>(0u, x);
+  x += dpp_u32<kDppRowShr + 2, 0xF, true>(0u, x);
+  x += dpp_u32<kDppRowShr + 4, 0xF, true>(0u, x);
+  x += dpp_u32<kDppRowShr + 8, 0xF, true>(0u, x);
+  x += dpp_u32<kDppRowBcast15, 0xA, false>(0u, x);   // rows 1, 3 += lane 15 of rows 0, 2
+  x += dpp_u32<kDppRowBcast31, 0xC, false>(0u, x);   // rows 2, 3 += lane 31
   return x;
 }
+
+// Largest value over the wave (every lane receives it): the scan's steps
+// with max (0 is the identity), then lane 63's result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u32<kDppRowShr + 1, 0xF, true>(0u, x));
+  x = max(x, dpp_u32<kDppRowShr + 2, 0xF, true>(0u, x));
+  x = max(x, dpp_u32<kDppRowShr + 4, 0xF, true>(0u, x));
+  x = max(x, dpp_u32<kDppRowShr + 8, 0xF, true>(0u, x));
+  x = max(x, dpp_u32<kDppRowBcast15, 0xA, false>(0u, x));
+  x = max(x, dpp_u32<kDppRowBcast31, 0xC, false>(0u, x));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, kWave - 1);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) { return ~wave_max_u32(~x); }
 
 // Sum across a wave (every lane receives it).
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {

@@ -1862,8 +1862,7 @@ __device__ __forceinline__ void merge_unit_core(const FilterArgs& a, SelectShare
   // Every candidate is >= thr >= 1.  Spread the candidates' range over the
   // first radix digit: k' = ((key - thr) << lsh) + 1 (order-preserving, 0 is
   // left for "no key", bit 31 of k' - 1 stays clear so k' cannot overflow).
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
+  kmax = wave_max_u32(kmax);
   if (lane == 0) red[w] = kmax;
   for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
   __syncthreads();                                    // (sources are no longer read)
@@ -2069,9 +2068,10 @@ __device__ __forceinline__ void threshold_by_value(SelectShared<NT>& sh, const u
     const float x = (key_score(k) - smin) * scale;
     return min((uint32_t)x, (uint32_t)kBins - 1u);
   };
-  const uint32_t dummy = (uint32_t)(kBins + lane_id());
+  // (value bins rarely repeat within a wave: one plain atomic per key)
 #pragma unroll
-  for (int i = 0; i < K; ++i) hist_add(sh.hist, key[i] ? bin_of(key[i]) : dummy);
+  for (int i = 0; i < K; ++i)
+    if (key[i]) atomicAdd(&sh.hist[bin_of(key[i])], 1u);
   __syncthreads();
   uint32_t path = 0, above = 0;
   pick_bin<NT>(sh, kDigitBits, target, path, above);
@@ -2096,6 +2096,7 @@ __device__ __forceinline__ void threshold_by_value(SelectShared<NT>& sh, const u
   // bin, every key above it is larger than all of them)
   for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
   __syncthreads();
+  const uint32_t dummy = (uint32_t)(kBins + lane_id());
 #pragma unroll
   for (int i = 0; i < K; ++i) {
     const bool in = key[i] && bin_of(key[i]) == bstar;
@@ -2172,11 +2173,8 @@ __device__ __forceinline__ void scores_merge_unit(const FilterArgs& a,
       kmin = min(kmin, key[i]);
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
-  }
+  kmax = wave_max_u32(kmax);
+  kmin = wave_min_u32(kmin);
   if (lane == 0) {
     red[w] = kmax;
     red[W + w] = kmin;

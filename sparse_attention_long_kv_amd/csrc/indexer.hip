@@ -2046,14 +2046,14 @@ __global__ __launch_bounds__(kScoreAllThreads) void score_all_kernel(const Filte
     });
 }
 
-// Exact threshold over keys whose scores lie in [smin, smax] (finite, smax >
-// smin; keys outside [klo, khi] -- NaN scores -- count as below or above
-// every score): the first level bins the scores by value, 4096 equal-width
-// bins (monotone in the key, so every key of a higher bin is larger), which
-// leaves few keys in the bin of the target-th largest where the scores
-// crowd; that bin's keys are then ranked directly (or, when it is large,
-// selected by radix levels over their keys).  Returns t, need and eq as
-// finish_threshold does.
+// Exact threshold over keys whose scores all lie in [key_score(klo),
+// key_score(khi)] (finite, the first below the second; key 0: none): the
+// first level bins the scores by value, 4096 equal-width bins (monotone in
+// the key, so every key of a higher bin is larger, and equal keys share a
+// bin), which leaves few keys in the bin of the target-th largest where the
+// scores crowd; that bin's keys are then ranked directly (or, when it is
+// large, selected by radix levels over their keys).  Each key's bin is formed
+// once.  Returns t, need and eq as finish_threshold does.
 template <int NT, int K>
 __device__ __forceinline__ void threshold_by_value(SelectShared<NT>& sh, const uint32_t (&key)[K],
                                                    uint32_t klo, uint32_t khi, uint32_t target,
@@ -2062,16 +2062,17 @@ __device__ __forceinline__ void threshold_by_value(SelectShared<NT>& sh, const u
   const int tid = threadIdx.x;
   const float smin = key_score(klo), smax = key_score(khi);
   const float scale = (float)kBins / (smax - smin);
-  auto bin_of = [&](uint32_t k) -> uint32_t {
-    if (k > khi) return (uint32_t)kBins - 1u;
-    if (k < klo) return 0u;
-    const float x = (key_score(k) - smin) * scale;
-    return min((uint32_t)x, (uint32_t)kBins - 1u);
-  };
+  // a key's bin, or a lane's private dummy bin (>= kBins) for no key
+  const uint32_t dummy = (uint32_t)(kBins + lane_id());
+  uint32_t bn[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const float x = (key_score(key[i]) - smin) * scale;
+    bn[i] = key[i] ? min((uint32_t)x, (uint32_t)kBins - 1u) : dummy;
+  }
   // (value bins rarely repeat within a wave: one plain atomic per key)
 #pragma unroll
-  for (int i = 0; i < K; ++i)
-    if (key[i]) atomicAdd(&sh.hist[bin_of(key[i])], 1u);
+  for (int i = 0; i < K; ++i) atomicAdd(&sh.hist[bn[i]], 1u);
   __syncthreads();
   uint32_t path = 0, above = 0;
   pick_bin<NT>(sh, kDigitBits, target, path, above);
@@ -2083,7 +2084,7 @@ __device__ __forceinline__ void threshold_by_value(SelectShared<NT>& sh, const u
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < K; ++i)
-      if (key[i] && bin_of(key[i]) == bstar) sh.list[atomicAdd(&sh.pick[3], 1u)] = key[i];
+      if (bn[i] == bstar) sh.list[atomicAdd(&sh.pick[3], 1u)] = key[i];
     __syncthreads();
     uint32_t t, gt, eq;
     rank_in_list<NT>(sh, nbin, rank, t, gt, eq);
@@ -2092,20 +2093,15 @@ __device__ __forceinline__ void threshold_by_value(SelectShared<NT>& sh, const u
     eq_out = eq;
     return;
   }
-  // a crowded bin: the exact search over its keys alone (equal keys share a
-  // bin, every key above it is larger than all of them)
+  // a crowded bin: the exact search over its keys alone
   for (int bb = tid; bb < kBins + kWave; bb += NT) sh.hist[bb] = 0u;
   __syncthreads();
-  const uint32_t dummy = (uint32_t)(kBins + lane_id());
 #pragma unroll
-  for (int i = 0; i < K; ++i) {
-    const bool in = key[i] && bin_of(key[i]) == bstar;
-    hist_add(sh.hist, in ? (key[i] >> kTopShift) : dummy);
-  }
+  for (int i = 0; i < K; ++i) hist_add(sh.hist, bn[i] == bstar ? (key[i] >> kTopShift) : dummy);
   __syncthreads();
   finish_threshold<NT>(sh, rank, t_out, need_out, eq_out, [&](auto&& f) {
 #pragma unroll
-    for (int i = 0; i < K; ++i) f(key[i], key[i] != 0u && bin_of(key[i]) == bstar);
+    for (int i = 0; i < K; ++i) f(key[i], bn[i] == bstar);
   });
 }
 
@@ -2162,16 +2158,12 @@ __device__ __forceinline__ void scores_merge_unit(const FilterArgs& a,
       key[i] = p < len ? score_key(su[p] + 0.0f) : 0u;
     }
   }
-  // the range of the finite scores (keys outside [key(-inf), key(+inf)] are
-  // NaN scores)
-  const uint32_t kneg = score_key(-__builtin_inff()), kpos = score_key(__builtin_inff());
+  // the keys' range (key 0: none)
   uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
 #pragma unroll
   for (int i = 0; i < K; ++i) {
-    if (key[i] >= kneg && key[i] <= kpos) {
-      kmax = max(kmax, key[i]);
-      kmin = min(kmin, key[i]);
-    }
+    kmax = max(kmax, key[i]);
+    kmin = min(kmin, key[i] ? key[i] : 0xFFFFFFFFu);
   }
   kmax = wave_max_u32(kmax);
   kmin = wave_min_u32(kmin);
@@ -2189,8 +2181,12 @@ __device__ __forceinline__ void scores_merge_unit(const FilterArgs& a,
     kmin = min(kmin, red[W + ww]);
   }
   uint32_t t, need, eq;
+  // by value when every score is finite (keys outside [key(-inf), key(+inf)]
+  // are NaN scores) and the range and its bin width are finite
+  const uint32_t kneg = score_key(-__builtin_inff()), kpos = score_key(__builtin_inff());
   const float smin = key_score(kmin), smax = key_score(kmax);
-  const bool by_value = kmin < kmax && smin > -__builtin_inff() && smax < __builtin_inff() &&
+  const bool by_value = kmin < kmax && kmin >= kneg && kmax <= kpos &&
+                        smin > -__builtin_inff() && smax < __builtin_inff() &&
                         smax - smin < __builtin_inff() &&
                         (float)kBins / (smax - smin) < __builtin_inff();   // block-uniform
   if (by_value) {

@@ -4,7 +4,9 @@ hipcc reports each gfx950 kernel's resources (``-Rpass-analysis=
 kernel-resource-usage``).  Two properties the step's speed rests on are
 checked from that report, since neither shows up as a wrong result:
 
-* no kernel of the decode step keeps anything in scratch (private) memory:
+* no kernel of the decode step or of any selection plan (the chunk-exact
+  kernels, whose 16-32 keys per thread sit at the 128-register limit,
+  included) keeps anything in scratch (private) memory:
   a register array demoted to scratch turns every access into a memory round
   trip, and the dirty scratch lines are written back during the next launch
   (measured: +15 us on each of the two large launches of a 128K step);
@@ -24,8 +26,10 @@ from sparse_attention_long_kv_amd import build_lib as bl
 pytestmark = pytest.mark.skipif(not os.path.exists(bl.HIPCC) and shutil.which("hipcc") is None,
                                 reason="hipcc not available")
 
-# kernels on the decode step and the extensions (mangled-name fragments)
-HOT = ("append_bound_kernel", "sample_kernel", "filter_kernel", "filter_merge_kernel", "unit_kernel",
+# kernels of every selection plan, the decode step and the extensions
+# (mangled-name fragments; "merge_kernel" also matches the other merges)
+HOT = ("chunk_select_kernel", "merge_regs_kernel", "merge_kernel", "append_bound_kernel",
+       "sample_kernel", "filter_kernel", "filter_merge_kernel", "unit_kernel",
        "score_all_kernel", "scores_merge_kernel", "scores_select_attend_kernel",
        "select_attend_kernel", "decode_kernel", "combine_kernel", "append_kv_kernel",
        "linear_gate_kernel", "index_score_kernel")

@@ -2,16 +2,18 @@
 """Decode-step benchmark of the indexer-selected sparse attention library.
 
 One step = the whole hot path for one layer over the whole batch, i.e. one
-sparse_attn_decode_step called as its three launches: append the new token
-(K/V rows + FP8 projected key) with the sampled selection bound; score every
-position and keep the candidates; exact top-M per KV head followed, in the
-same workgroups, by gather-free sparse attention over the selected rows.  Inputs are synthetic
-(``workloads``) and resident in HBM before the timed region starts.
+sparse_attn_decode_step called as its launches as the library plans them
+(sparse_attn_decode_step_stage): append the new token (K/V rows + FP8
+projected key), the sampled selection bound, the scores of every position and
+the kept candidates, the exact top-M per KV head, and gather-free sparse
+attention over the selected rows.  At the 128K workload on a 256-CU MI355X
+that is one launch (one workgroup per (batch row, KV head) unit).  Inputs are
+synthetic (``workloads``) and resident in HBM before the timed region starts.
 
 Prints ONE JSON line:
   value         decode steps/s (N=1 GPU; whole-job throughput)
   hbm_gbps      algorithmic bytes per step / step time
-  roofline      the dominant kernel (scoring + candidate filter) against 8 TB/s,
+  roofline      the dominant kernel (the whole step at 128K) against 8 TB/s,
                 and against this device's measured streaming-read rate
   cold_step_us  steps timed one at a time after a cache-evicting read
                 (median, p10, p90, and per launch)

@@ -1221,6 +1221,9 @@ SCORES_CASES = [
     (2, 8, 2, 64, 16, 16384, 1, 1, [16384, 9000]),          # d = 64, M = 1
     (1, 4, 1, 128, 32, 3000, 2999, 1, None),                # M = n_max - 1
     (2, 12, 2, 128, 16, 5000, 700, 2, [0, 1]),              # an empty unit, a unit of one row
+    # more new rows in a chunk than are scored from their codes in LDS: the
+    # chunk's code loads wait for the rows' stores instead
+    (2, 8, 2, 128, 32, 6000, 512, 20, [6000, 2100]),
 ]
 
 

@@ -2240,21 +2240,25 @@ __global__ __launch_bounds__(kMergeThreads) void scores_select_attend_kernel(con
 // ------------------------------------------------------------------ one workgroup per unit
 //
 // When the units fill the chip, one 1024-thread workgroup per unit runs the
-// rest of the step after the bound in one launch: it streams the unit's
-// codes (stream_code_scores, 16 KB of contiguous rows per round), keeps every
-// score >= the unit's bound in the LDS list of the wave that scored it (a
-// full list goes to the unit's spill pool, as in the filter kernel), merges
-// exactly over the 16 lists and the pool (merge_unit_core: the candidates
-// never travel through HBM) and, with ATTEND, attends over the selection it
-// leaves in LDS (AttendWave, the attention kernels' arithmetic, one split).
+// whole step in one launch: it appends the new rows and forms the query and
+// the sampled bound (append_bound_kernel's arithmetic), streams the unit's
+// codes (WaveStream: chunks handed to the waves on demand), keeps every score
+// >= the bound in the LDS list of the wave that scored it (a full list goes
+// to the unit's spill pool, as in the filter kernel), merges exactly over the
+// lists and the pool (merge_unit_core: the candidates never travel through
+// HBM) and, with ATTEND, attends over the selection it leaves in LDS
+// (AttendWave, the attention kernels' arithmetic, one split).
 
+// Loads in flight per lane and the waves that stream (any others wait at the
+// merge's first barrier; the lists' LDS is shared out among the streaming
+// waves).  Measured at 128K with the chunks handed out on demand: all 16
+// waves with 4 loads 209.9-210.2 us per step, 8 with 8 211.2-212.7, 8 with 6
+// 210.0-210.7, 16 with 2 212.4-213.7, 8 with 4 239.
 #ifndef SA_UNIT_LOADS_IN_FLIGHT
-#define SA_UNIT_LOADS_IN_FLIGHT 8
+#define SA_UNIT_LOADS_IN_FLIGHT 4
 #endif
-// waves that stream (the others wait at the merge's first barrier); the
-// lists' LDS is shared out among them
 #ifndef SA_UNIT_STREAM_WAVES
-#define SA_UNIT_STREAM_WAVES 8
+#define SA_UNIT_STREAM_WAVES 16
 #endif
 constexpr int kUnitStreamWaves = SA_UNIT_STREAM_WAVES;
 constexpr int kUnitListCap = kUnitWaves * kUnitCap / kUnitStreamWaves;   // slots per list

@@ -157,9 +157,10 @@ int sparse_attn_topm(const sa_shape* shape, const float* scores,
                      void* stream);
 
 /* ---------------------------------------------------------------------------
- * sparse_attn_index_topm -- steps 2 and 3 fused: the scores are kept on chip
- * and never written (three launches, listed under
- * sparse_attn_index_topm_stage).  Produces exactly the idx that
+ * sparse_attn_index_topm -- steps 2 and 3 fused: at most three launches,
+ * listed under sparse_attn_index_topm_stage; the scores stay on chip, except
+ * under SA_PLAN_SCORES, which writes them to the workspace (4 bytes per
+ * position) for its merge.  Produces exactly the idx that
  * sparse_attn_index_score followed by sparse_attn_topm produces.
  * Arguments as in those two calls.
  * ------------------------------------------------------------------------- */

@@ -396,12 +396,37 @@ __device__ __forceinline__ void emit_in_order(const uint32_t (&key)[K], uint32_t
   }
   __syncthreads();
   // exclusive scan in (row, wave) order
-  const int sr = tid / W, sw = tid % W;
-  const uint32_t v = tid < K * W ? sh.seg[sw * K + sr] : 0u;
-  uint32_t total;
-  const uint32_t incl = block_inclusive_scan<NT>(v, sh, total);
-  __syncthreads();
-  if (tid < K * W) sh.seg[sw * K + sr] = incl - v;
+  if constexpr (K <= 16) {
+    // by one wave: lane l takes entries E l .. E l + E - 1 of that order
+    // (all its reads before its writes); two barriers fewer than the
+    // workgroup's scan
+    if (w == 0) {
+      constexpr int E = (K * W + kWave - 1) / kWave;
+      const int lane = lane_id();
+      uint32_t c[E], sum = 0u;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int f = E * lane + e, sr = f / W, sw = f % W;
+        c[e] = f < K * W ? sh.seg[sw * K + sr] : 0u;
+        sum += c[e];
+      }
+      uint32_t ex = wave_inclusive_scan(sum) - sum;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int f = E * lane + e, sr = f / W, sw = f % W;
+        if (f < K * W) sh.seg[sw * K + sr] = ex;
+        ex += c[e];
+      }
+    }
+  } else {
+    // (more keys per thread leave no registers for the one-wave form)
+    const int sr = tid / W, sw = tid % W;
+    const uint32_t v = tid < K * W ? sh.seg[sw * K + sr] : 0u;
+    uint32_t total;
+    const uint32_t incl = block_inclusive_scan<NT>(v, sh, total);
+    __syncthreads();
+    if (tid < K * W) sh.seg[sw * K + sr] = incl - v;
+  }
   __syncthreads();
   uint32_t pre[K];
 #pragma unroll
@@ -1364,17 +1389,7 @@ struct CodeStream {
   }
 };
 
-// Scores of the nv code rows (R bytes each) at the start of `rs`, read as
-// contiguous 16-byte lanes: in round k the workgroup reads bytes
-// [16 NT k, 16 NT (k + 1)), thread t the 16 bytes at 16 NT k + 16 t, that is
-// position PR k + 16 t / R (PR = 16 NT / R positions per round) -- for
-// r = 32 one half (t & 1) of the row.  The two lanes of an r = 32 row each
-// form their half's 16-code chain and add the other's with one DPP step
-// (lo + hi and hi + lo are the same sum), and the even lane owns the
-// position.  keep(s, p, owner) is called by every lane (a wave-uniform call)
-// with p relative to the start; rows past nv read as zero.  L loads per lane
-// are in flight: two groups of L / 2 rounds alternate, one scored while the
-// other loads.  qt: the unit's 32-float indexer query.
+// CodeStream over the nv rows of `rs` in one call: init, then run.
 template <int R, int NT, int L, class Keep>
 __device__ __forceinline__ void stream_code_scores(__amdgpu_buffer_rsrc_t rs, int nv,
                                                    const float* qt, Keep keep) {

@@ -2,9 +2,9 @@
 
 The entry point for callers that cannot allocate runs the decode step with
 the library's static per-GPU scratch as its workspace.  Called through the C
-ABI twice in a row -- the second call on a smaller shape, so it reads the
-scratch the first one left -- it must write the same caches, idx, out and
-lse, bit for bit, as the allocating entry point on the same inputs.  A shape
+ABI three times in a row -- each call on a smaller shape than the last, so it
+reads the scratch the one before left -- it must write the same caches, idx,
+out and lse, bit for bit, as the allocating entry point on the same inputs.  A shape
 whose workspace exceeds the scratch is refused on the host.
 """
 
@@ -40,14 +40,19 @@ def test_noalloc_step_equals_the_allocating_step_twice():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     sa.load()
-    # a workload-shaped call, then a smaller one (fewer units, context and budget)
-    shapes = [scaled(WORKLOADS["gqa7_16k"], N=8192, M=1024, B=4),
+    # workload-shaped calls, each smaller than the last (fewer units, context
+    # and budget): the first takes the sampled-bound filter plan, the others
+    # the plan that scores every position
+    shapes = [scaled(WORKLOADS["lisa_32k"], N=20000, M=1024, B=4),
+              scaled(WORKLOADS["gqa7_16k"], N=8192, M=1024, B=4),
               scaled(WORKLOADS["lisa_32k"], N=4096, M=512, B=2)]
     for wl in shapes:
         print("case: noalloc step", wl.name, "B=%d Hkv=%d N=%d M=%d" % (wl.B, wl.Hkv, wl.N, wl.M),
               flush=True)
         sh = sa.make_shape(wl.B, wl.Hq, wl.Hkv, wl.d, wl.r, wl.N)
         assert sa.sparse_attn_workspace_size(sh, wl.N, wl.M) <= sa.SA_NOALLOC_SCRATCH_BYTES
+        assert sa.sparse_attn_selection_plan(sh, wl.N, wl.M) == (
+            sa.SA_PLAN_FILTER if wl.N > 16384 else sa.SA_PLAN_SCORES)
         ref = _step(wl, noalloc=False)
         got = _step(wl, noalloc=True)
         for name, x, y in zip(("k_cache", "v_cache", "kp", "idx", "out", "lse"), ref, got):

@@ -1323,3 +1323,90 @@ def test_scores_plan_all_equal_takes_lowest_positions():
     G = Hq // Hkv
     qt = oracle.indexer_query(f64(q)[0, 0:G], P64[0])
     check_topm_unit(gi[0, 0], oracle.index_scores(qt, kp[0, 0]), M, N)
+
+
+def _sweep_shapes(n, seed=97):
+    """Seeded small shapes across the plans' parameters: batch, KV heads,
+    group size, head dim, rank, context, budget, new rows and ragged rows."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        B = int(rng.choice([1, 2, 3, 5]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 4, 7, 8]))
+        d = int(rng.choice([64, 128]))
+        r = int(rng.choice([16, 32]))
+        N = int(rng.choice([700, 2049, 5000, 12288, 16384, 20000]))
+        M = int(rng.choice([1, 64, 777, 2048]))
+        T = int(rng.choice([1, 2, 3]))
+        if M >= N:
+            continue
+        lens = [int(N if rng.random() < 0.5 else rng.integers(0, N + 1)) for _ in range(B)]
+        out.append((B, G * Hkv, Hkv, d, r, N, M, T, lens))
+    return out
+
+
+@pytest.mark.parametrize("case", _sweep_shapes(12))
+def test_plans_agree_across_a_shape_sweep(case, monkeypatch):
+    """Seeded shapes across the selection plans' parameters: the decode step
+    as planned, the decode step with the score-all plan turned off, and
+    append_kv + index_topm + decode write the same caches, idx, out and lse,
+    bit for bit; idx is ascending, in range and -1 padded in every unit; the
+    oracle checks the last unit's selection and attention."""
+    B, Hq, Hkv, d, r, N, M, T, lens = case
+    _say("case: sweep", case)
+    G = Hq // Hkv
+    sh = _shape_of(B, Hq, Hkv, d, r, N)
+    q, K, V, P = _rand_inputs(B, Hq, Hkv, d, r, N, seed=B * 131 + N + M)
+    g = torch.Generator().manual_seed(N + T)
+    k_new = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16)
+    v_new = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16)
+    pos = torch.tensor([max(L - T, 0) for L in lens], dtype=torch.int32)
+    sl = _dev(torch.tensor(lens, dtype=torch.int32))
+    scale = default_scale(d)
+    res = []
+    for mode in ("planned", "filter", "calls"):
+        monkeypatch.setenv("SPARSE_ATTN_SCORES_PLAN", "0" if mode == "filter" else "1")
+        Kd, Vd = _dev(K), _dev(V)
+        kp = torch.empty(B, Hkv, N, r, dtype=torch.uint8, device="cuda")
+        sa.sparse_attn_project_keys(sh, Kd, _dev(P), 0, N, kp)
+        ws = sa.alloc_workspace(sh, N, M)
+        idx = torch.full((B, Hkv, M), -9, dtype=torch.int32, device="cuda")
+        out = torch.empty(B, Hq, d, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+        if mode == "calls":
+            sa.sparse_attn_append_kv(sh, _dev(pos), _dev(k_new), _dev(v_new), _dev(P), Kd, Vd, kp)
+            sa.sparse_attn_index_topm(sh, _dev(q), _dev(P), kp, sl, N, M, idx, ws)
+            sa.sparse_attn_decode(sh, _dev(q), Kd, Vd, idx, M, scale, out, lse, ws)
+        else:
+            sa.sparse_attn_decode_step(sh, _dev(pos), _dev(k_new), _dev(v_new), _dev(q), _dev(P),
+                                       Kd, Vd, kp, sl, N, M, scale, idx, out, lse, ws)
+        torch.cuda.synchronize()
+        res.append((Kd, Vd, kp, idx, out, lse))
+    for other in res[1:]:
+        for name, x, y in zip(("k", "v", "kp", "idx", "out", "lse"), res[0], other):
+            assert torch.equal(x, y), name
+    gi, go = res[0][3].cpu().numpy(), f64(res[0][4])
+    for b in range(B):
+        n_sel = min(lens[b], M)
+        for h in range(Hkv):
+            row = gi[b, h]
+            assert np.all(row[n_sel:] == -1) and np.all(np.diff(row[:n_sel]) > 0), (b, h)
+            assert n_sel == 0 or (row[0] >= 0 and row[n_sel - 1] < lens[b]), (b, h)
+    b, h = B - 1, Hkv - 1
+    L = lens[b]
+    if L == 0:
+        return
+    P64 = P.double().numpy()
+    kp0 = oracle.project_keys(f64(K)[b, h], P64[h])[None, None]
+    K2, V2, kp2 = oracle.append_kv(f64(K)[b, h][None, None], f64(V)[b, h][None, None], kp0,
+                                   pos.numpy()[b:b + 1], f64(k_new)[b:b + 1, h:h + 1],
+                                   f64(v_new)[b:b + 1, h:h + 1], P64[h:h + 1])
+    qg = f64(q)[b, h * G:(h + 1) * G]
+    oi, oo, _, sc = oracle.decode_step_unit(qg, K2[0, 0], V2[0, 0], kp2[0, 0], P64[h], L, M,
+                                            scale)
+    swaps = check_topm_unit(gi[b, h], sc, M, L)
+    _say("  unit", (b, h), "L", L, "band swaps", swaps)
+    if not np.array_equal(gi[b, h], oi):
+        oo, _ = oracle.sparse_attention(qg, K2[0, 0], V2[0, 0], gi[b, h], scale)
+    check_attention(go[b, h * G:(h + 1) * G], oo, "sweep unit %s" % ((b, h),))

@@ -1410,3 +1410,63 @@ def test_plans_agree_across_a_shape_sweep(case, monkeypatch):
     if not np.array_equal(gi[b, h], oi):
         oo, _ = oracle.sparse_attention(qg, K2[0, 0], V2[0, 0], gi[b, h], scale)
     check_attention(go[b, h * G:(h + 1) * G], oo, "sweep unit %s" % ((b, h),))
+
+
+def _order_key(x):
+    """The order-preserving unsigned key of float32 values (IEEE bits, sign
+    flipped for positives, all bits flipped for negatives)."""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.int64)
+    return np.where(b >> 31, 0xFFFFFFFF - b, b | 0x80000000)
+
+
+def test_unit_plan_candidates_far_above_the_sample():
+    """Candidates over a huge range under one workgroup per unit: rows planted
+    between the sampled blocks (codes of magnitude 448 with the query's signs)
+    score far above every sampled row, so the merge's first radix level, spread
+    over the candidates' range, puts every ordinary candidate into a few
+    bins.  In unit (0, 0) 1500 equal planted rows: the M-th key is theirs and
+    ties cut it; in (0, 1) 1500 rows of graded scores; in (0, 2) 500 rows, all
+    selected, and the M-th key is an ordinary one among the crowded low bins.
+    Every unit's selection is the oracle's."""
+    _say("case: unit plan, candidates far above the sample")
+    B, Hq, Hkv, d, r, N, M = 32, 32, 8, 128, 32, 16384, 1024
+    G = Hq // Hkv
+    g = torch.Generator().manual_seed(71)
+    q = torch.randn(B, Hq, d, generator=g).to(torch.bfloat16)
+    P = torch.from_numpy(np.stack([orthonormal_basis(d, r, 71 * 31 + h)
+                                   for h in range(Hkv)]).astype(np.float32))
+    rng = np.random.default_rng(71)
+    # codes of magnitude below 2, either sign (no NaN codes)
+    kp = (rng.integers(0, 0x40, size=(B, Hkv, N, r)) |
+          (rng.integers(0, 2, size=(B, Hkv, N, r)) << 7)).astype(np.uint8)
+    starts = [(j * (N - 8)) // 127 for j in range(128)]
+    sampled = np.zeros(N, dtype=bool)
+    for s0 in starts:
+        sampled[s0:s0 + 8] = True
+    gaps = np.flatnonzero(~sampled)
+    P64 = P.double().numpy()
+    plants = {(0, 0): (1500, False), (0, 1): (1500, True), (0, 2): (500, False)}
+    for (b, h), (n_rows, graded) in plants.items():
+        qt = oracle.indexer_query(f64(q)[b, h * G:(h + 1) * G], P64[h])
+        sign = np.where(qt < 0, 0x80, 0).astype(np.uint8)
+        rows = gaps[:n_rows]
+        mag = np.full(n_rows, 0x7E, dtype=np.uint8)            # 448
+        if graded:
+            mag = (0x70 + rng.integers(0, 15, size=n_rows)).astype(np.uint8)   # 128 .. 448
+        kp[b, h, rows] = mag[:, None] | sign[None, :]
+        # the recipe does what it is for: the bound is the k-th largest of the
+        # 1024 sampled keys (k = 3 M 1024 / N, rounded up: 192), and every
+        # planted key lies more than four times the range from the bound to
+        # the largest sampled key above the bound (order-preserving keys)
+        s = oracle.index_scores(qt, kp[b, h])
+        ks = _order_key(s.astype(np.float32))
+        top = np.sort(ks[sampled])[::-1]
+        thr, smax = top[-(-3 * M * 1024 // N) - 1], top[0]
+        assert ks[rows].min() - thr > 4 * (smax - thr), (b, h)
+    sh = _shape_of(B, Hq, Hkv, d, r, N)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert sa.sparse_attn_selection_plan(sh, N, M) == sa.SA_PLAN_UNIT
+    gi = _topm_check_against_oracle(q, P, kp, M, N)
+    assert _topm_check_against_oracle.fallbacks == 0
+    assert gi[0, 0].tolist() == gaps[:M].tolist()              # ties: the lowest positions
+    assert set(gaps[:500].tolist()) <= set(gi[0, 2].tolist())

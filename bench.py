@@ -779,18 +779,21 @@ def main(argv=None):
         del x
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, back to back, synchronised on both sides
+    # timed region: exactly K steps, back to back, synchronised on both sides.
+    # The events for it are created beforehand (creating them is host work
+    # that would otherwise sit in the timed region while the GPU waits).
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dom_ev = []
+    pool = timer.create(2 * ((a.steps + EVENT_EVERY - 1) // EVENT_EVERY))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    dom_ev = []
-    pool = timer.create(2 * a.steps)
     for k in range(a.steps):
         # HIP events around the dominant call of every EVENT_EVERY-th step
         # (each event pair costs the GPU ~4 us: on every step it would slow
         # the very steps being timed)
-        step(pool[2 * k:2 * k + 2] if k % EVENT_EVERY == 0 else None)
+        j = k // EVENT_EVERY
+        step(pool[2 * j:2 * j + 2] if k % EVENT_EVERY == 0 else None)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

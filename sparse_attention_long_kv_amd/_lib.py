@@ -128,17 +128,19 @@ def _call(name, *args):
 
 
 def _dev_ptr(t, dtype, shape=None, name="tensor"):
+    # (the cheapest form of each check: a step call checks about a dozen
+    # tensors, and a Python decode loop launches at this rate)
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("%s must be on the GPU" % name)
     if t.dtype != dtype:
         raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != (shape if isinstance(shape, tuple) else tuple(shape)):
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
-    return _VP(t.data_ptr())
+    return t.data_ptr()                  # an int; ctypes passes it as void*
 
 
 def _opt_ptr(t, dtype, shape=None, name="tensor"):

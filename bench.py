@@ -38,6 +38,7 @@ METRIC = "decode steps/sec and achieved HBM GB/s at N=128K, M=2048, r=32"
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 EVENT_EVERY = 4                       # timed steps between two bracketed dominant launches
+RUN_LAUNCHES = 4                      # one-launch steps: back-to-back launches per event pair
 DOMINANT_KERNEL = "unit_kernel"       # the dominant launch of the 128K step (one workgroup per unit)
 KERNEL_SOURCES = ("indexer.hip", "device_common.hpp", "attend_common.hpp")
 PLAN_NAMES = {0: "chunk_exact", 1: "filter", 2: "unit_workgroup", 3: "all_scores"}
@@ -768,7 +769,7 @@ def main(argv=None):
             for i, k in enumerate(names):
                 ev[k].append((rec[i], rec[i + 1]))
         elif rec is not None:
-            dom_ev.append((rec[0], rec[1]))
+            dom_ev.append((rec[0], rec[1], 1))
 
     print("bench: warmup %d" % a.warmup, file=sys.stderr, flush=True)
     for _ in range(a.warmup):
@@ -782,24 +783,39 @@ def main(argv=None):
     # timed region: exactly K steps, back to back, synchronised on both sides.
     # The events for it are created beforehand (creating them is host work
     # that would otherwise sit in the timed region while the GPU waits).
+    # HIP events time the dominant launch.  An event pair costs the GPU time
+    # of its own (~1.5-2 us per bracketed launch here, against rocprofv3's
+    # durations), so pairs are sparse: when the step is that one launch, a
+    # pair brackets a run of RUN_LAUNCHES back-to-back launches in every
+    # 2 RUN_LAUNCHES steps; otherwise it brackets the dominant call of every
+    # EVENT_EVERY-th step.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    dom_ev = []
-    pool = timer.create(2 * ((a.steps + EVENT_EVERY - 1) // EVENT_EVERY))
+    one_launch = len(calls) == 1
+    run = RUN_LAUNCHES if one_launch else 1
+    period = 2 * RUN_LAUNCHES if one_launch else EVENT_EVERY
+    dom_ev = []                                 # (start event, end event, launches)
+    pool = timer.create(2 * ((a.steps + period - 1) // period))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for k in range(a.steps):
-        # HIP events around the dominant call of every EVENT_EVERY-th step
-        # (each event pair costs the GPU ~4 us: on every step it would slow
-        # the very steps being timed)
-        j = k // EVENT_EVERY
-        step(pool[2 * j:2 * j + 2] if k % EVENT_EVERY == 0 else None)
+        j, r = divmod(k, period)
+        if not one_launch:
+            step(pool[2 * j:2 * j + 2] if r == 0 else None)
+            continue
+        if r == 0:
+            timer.record(pool[2 * j], stream)
+        calls[0]()
+        if r == run - 1 or (r < run and k == a.steps - 1):
+            timer.record(pool[2 * j + 1], stream)
+            dom_ev.append((pool[2 * j], pool[2 * j + 1], r + 1))
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = start.elapsed_time(end)
     ms_per_step = 1e3 * wall / a.steps          # host clock around the K steps
-    dom_us = 1e3 * sum(timer.elapsed_ms(s0, s1) for s0, s1 in dom_ev) / len(dom_ev)
+    dom_launches = sum(n for _, _, n in dom_ev)
+    dom_us = 1e3 * sum(timer.elapsed_ms(s0, s1) for s0, s1, _ in dom_ev) / dom_launches
     timer.destroy(pool)
     # per-call breakdown (informational): a separate pass after the timed
     # region, every call bracketed by events
@@ -841,7 +857,8 @@ def main(argv=None):
                 "kernel": "%s (sparse_attn_decode_step_stage, %s)" % (dom_kernel, STAGE_NAMES[
                     dict((n, st) for n, st, _ in stages)[dom]]),
                 "bytes_per_launch": bytes_k[dom], "avg_launch_us": round(dom_us, 2),
-                "launches_timed": len(dom_ev), "events_every_steps": EVENT_EVERY,
+                "launches_timed": dom_launches, "event_pairs": len(dom_ev),
+                "launches_per_event_pair": run, "events_every_steps": period,
                 "source_hash": src_hash,
                 "read_ceiling_gbps": round(read_gbps, 1),
                 "frac_of_read_ceiling": round(dom_gbps / read_gbps, 4),

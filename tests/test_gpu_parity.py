@@ -1047,11 +1047,15 @@ def test_decode_step_equals_the_three_calls(name, N, T, lens, M):
 # ------------------------------------------------------------------ one workgroup per unit
 
 UNIT_CASES = [
-    # (B, Hq, Hkv, d, r, N, M, seq_lens): 256 units each, so the units fill the
-    # chip's 256 compute units and the decode step runs one workgroup per unit
+    # (B, Hq, Hkv, d, r, N, M, seq_lens[, T]): 256 units each, so the units
+    # fill the chip's 256 compute units and the decode step runs one workgroup
+    # per unit; T new rows per batch row (1 unless given)
     (32, 32, 8, 128, 32, 8192, 1024, None),
     (16, 128, 16, 64, 16, 5000, 700, "ragged"),       # G = 8, d = 64, short and empty rows
     (64, 16, 4, 128, 32, 4096, 2048, None),           # M at the plan's limit
+    # three new rows per unit, some of them inside the chunks the streaming
+    # waves load before the bound is known (rows below 2048)
+    (32, 32, 8, 128, 32, 8192, 1024, "ragged", 3),
 ]
 
 
@@ -1077,19 +1081,20 @@ def test_unit_workgroup_plan_equals_chunked_plan(case, monkeypatch):
     attend in one launch) writes the same caches, idx, out and lse, bit for
     bit, as the chunked filter plan (SPARSE_ATTN_UNIT_WG=0), for the whole
     step and for the selection alone; the oracle checks three units."""
-    B, Hq, Hkv, d, r, N, M, lens = case
+    B, Hq, Hkv, d, r, N, M, lens = case[:8]
+    T = case[8] if len(case) > 8 else 1
     _say("case: unit plan", case)
     sh = _shape_of(B, Hq, Hkv, d, r, N)
     G = Hq // Hkv
-    q, K, V, P = _unit_inputs(B, Hq, Hkv, d, r, N, seed=B + Hkv)
+    q, K, V, P = _unit_inputs(B, Hq, Hkv, d, r, N, seed=B + Hkv + T - 1)
     if lens == "ragged":
         lens = [N, 0, 700, 1, N - 3, 2000] + [N] * (B - 6)
     sl = None if lens is None else _dev(torch.tensor(lens, dtype=torch.int32))
     g = torch.Generator().manual_seed(3)
-    k_new = torch.randn(B, Hkv, 1, d, generator=g).to(torch.bfloat16)
-    v_new = torch.randn(B, Hkv, 1, d, generator=g).to(torch.bfloat16)
+    k_new = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16)
+    v_new = torch.randn(B, Hkv, T, d, generator=g).to(torch.bfloat16)
     Ls = [N if lens is None else lens[b] for b in range(B)]
-    pos = torch.tensor([max(L - 1, 0) for L in Ls], dtype=torch.int32)
+    pos = torch.tensor([max(L - T, 0) for L in Ls], dtype=torch.int32)
     res, plans = {}, {}
     for flag in ("1", "0"):
         monkeypatch.setenv("SPARSE_ATTN_UNIT_WG", flag)
